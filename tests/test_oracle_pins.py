@@ -1,0 +1,390 @@
+"""Pins for the CPU oracle against what the page and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+page prints (golden fixtures), closed forms, exact rational arithmetic, brute
+force on tiny inputs, special cases that reduce to a textbook formula, and an
+independent library (torch's float8 and bfloat16 casts, torch.autograd).
+"""
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import blockwise, codebook, fp8_e4m3, linear
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _read_golden(name):
+    vals = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                vals.append(line)
+    return vals
+
+
+# ------------------------------------------------------------------ codebook
+
+def test_codebook_equals_appendix_e_bit_exact():
+    printed = np.array([float(v) for v in _read_golden("nf4_appendix_e.txt")], dtype=np.float64)
+    assert printed.size == 16
+    # every printed value is exactly an fp32 value
+    assert np.all(printed.astype(F32).astype(np.float64) == printed)
+    assert np.array_equal(codebook.NF4.view(np.uint32), printed.astype(F32).view(np.uint32))
+
+
+def test_codebook_invariants():
+    q = codebook.NF4.astype(np.float64)
+    assert np.all(np.diff(q) > 0)
+    assert q[0] == -1.0 and q[15] == 1.0
+    assert q[codebook.ZERO_CODE] == 0.0 and not np.signbit(codebook.NF4[7])
+    # 2^(k-1) = 8 non-positive-side quantiles incl. the shared zero, 2^(k-1)+1 = 9 on the
+    # positive side; one duplicate zero removed -> 7 negative, 1 zero, 8 positive values
+    assert (q < 0).sum() == 7 and (q > 0).sum() == 8
+
+
+def test_codebook_matches_normal_quantile_construction():
+    derived = codebook.derive_from_quantiles()
+    q = codebook.NF4.astype(np.float64)
+    assert np.max(np.abs(derived - q)) <= 2.5e-7
+    assert derived[0] == -1.0 and derived[15] == 1.0 and derived[7] == 0.0
+
+
+# -------------------------------------------------------------- nearest code
+
+def _exact_midpoints():
+    q = [Fraction(float(v)) for v in codebook.NF4]
+    return [(q[i] + q[i + 1]) / 2 for i in range(15)]
+
+
+def test_nearest_code_equals_exact_threshold_count():
+    """code = #{i : x > m_i} with exact rational midpoints; a tie (x == m_i)
+    is not counted, i.e. goes to the lower index."""
+    mids = _exact_midpoints()
+    rng = np.random.default_rng(1)
+    xs = list(rng.uniform(-1, 1, 3000).astype(F32))
+    # every fp32 at and next to each midpoint
+    for m in mids:
+        c = F32(float(m))
+        for v in (np.nextafter(c, F32(-2)), c, np.nextafter(c, F32(2))):
+            xs.append(F32(v))
+    xs += [F32(-1), F32(1), F32(0), F32(-0.0), F32(1e-30), F32(-1e-30)]
+    xs = np.array(xs, dtype=F32)
+    got = blockwise.nearest_code(xs)
+    for x, g in zip(xs, got):
+        fx = Fraction(float(x))
+        assert g == sum(1 for m in mids if fx > m), float(x)
+
+
+def test_exact_midpoint_ties_go_to_lower_code():
+    mids = _exact_midpoints()
+    exact = [i for i, m in enumerate(mids) if Fraction(float(F32(float(m)))) == m]
+    assert exact == [2, 6, 7, 9, 11, 13]
+    xs = np.array([float(mids[i]) for i in exact], dtype=F32)
+    assert list(blockwise.nearest_code(xs)) == exact
+
+
+def test_nearest_code_minimises_reconstruction_error_bruteforce():
+    """Per element, the chosen code minimises |w - NF4[c] * absmax| in exact
+    arithmetic over all 16 codes, except inside a 1e-6 band around a decision
+    boundary where the fp32 rounding of w/absmax may decide."""
+    rng = np.random.default_rng(2)
+    w = (rng.standard_normal((4, 128)) * 0.02).astype(F32)
+    codes, c2 = blockwise.quantize_nf4(w)
+    q = [Fraction(float(v)) for v in codebook.NF4]
+    flat = w.reshape(-1)
+    ambiguous = 0
+    for i, (x, c) in enumerate(zip(flat, codes)):
+        a = Fraction(float(c2[i // 64]))
+        errs = [abs(Fraction(float(x)) - qq * a) for qq in q]
+        best = min(errs)
+        if errs[c] != best:
+            ambiguous += 1
+            assert (errs[c] - best) <= Fraction(1, 10 ** 6) * a
+    assert ambiguous <= 2
+
+
+def test_eq1_int8_special_case():
+    """With the uniform table {k/127}, the blockwise absmax quantiser is Eq. (1):
+    round(127 / absmax(X) * X) per block."""
+    table = (np.arange(-127, 128) / 127.0).astype(F32)
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal(64 * 50) * 3.0).astype(F32)
+    codes, c2 = blockwise.quantize_nf4(w, codebook=table)
+    got = codes.astype(np.int64) - 127
+    blk = np.arange(w.size) // 64
+    t = 127.0 * w.astype(np.float64) / c2[blk].astype(np.float64)
+    ref = np.rint(t).astype(np.int64)
+    near_half = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-5
+    assert np.array_equal(got[~near_half], ref[~near_half])
+    assert near_half.sum() <= 3
+    # the block's absmax element maps to +-127 exactly
+    for b in range(50):
+        j = np.argmax(np.abs(w[b * 64:(b + 1) * 64]))
+        assert abs(got[b * 64 + j]) == 127
+
+
+# -------------------------------------------------------- round trips, zeros
+
+def test_codebook_block_round_trip_exact():
+    vals = np.tile(codebook.NF4, 4)                       # 64 values, absmax 1
+    for scale in (1.0, 2.0 ** -7, 2.0 ** 5):
+        w = (vals * F32(scale)).astype(F32)
+        codes, c2 = blockwise.quantize_nf4(w)
+        assert list(codes) == list(range(16)) * 4
+        assert c2[0] == F32(scale)
+        st = blockwise.quantize(w, double_quant=False)
+        assert np.array_equal(st.dequantize(), w)
+
+
+def test_double_quant_round_trip_exact_when_absmax_shared():
+    """All blocks share one absmax: c2 - mu = 0, so c1 = 0 and c2_hat = mu = c2."""
+    block = np.tile(codebook.NF4, 4).astype(F32)
+    w = np.concatenate([block * F32(0.125)] * 300).astype(F32)   # 300 blocks, 2 groups
+    rng = np.random.default_rng(4)
+    for b in range(300):   # permute within blocks: codes differ, absmax does not
+        w[b * 64:(b + 1) * 64] = rng.permutation(w[b * 64:(b + 1) * 64])
+    st = blockwise.quantize(w, double_quant=True)
+    assert st.mu == F32(0.125)
+    assert np.all(st.scale2 == 0) and np.all(st.absmax_q == 0)
+    assert np.array_equal(st.dequantize(), w)
+
+
+def test_all_zero_block():
+    w = np.zeros(128, F32)
+    w[64:] = np.linspace(-1, 1, 64, dtype=F32)
+    codes, c2 = blockwise.quantize_nf4(w)
+    assert c2[0] == 0 and np.all(codes[:64] == codebook.ZERO_CODE)
+    st = blockwise.quantize(w, double_quant=False)
+    assert np.all(st.dequantize()[:64] == 0)
+
+
+def test_tail_block_and_packing():
+    w = np.array([0.5, -1.0, 0.25], dtype=F32)       # one short block, odd length
+    codes, c2 = blockwise.quantize_nf4(w)
+    assert c2.size == 1 and c2[0] == 1.0
+    assert codes[1] == 0
+    packed = blockwise.pack_nibbles(codes)
+    assert packed.size == 2 and (packed[1] >> 4) == 0
+    assert packed[0] == (codes[0] | (codes[1] << 4))
+    assert np.array_equal(blockwise.unpack_nibbles(packed, 3), codes)
+    assert list(blockwise.pack_nibbles(np.array([1, 2, 3, 4], np.uint8))) == [0x21, 0x43]
+
+
+# ------------------------------------------------------------------ E4M3
+
+def test_e4m3_decode_matches_torch():
+    b = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    ours = fp8_e4m3.DECODE
+    nan = np.isnan(b)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(b[~nan].view(np.uint32), ours[~nan].view(np.uint32))
+    assert fp8_e4m3.DECODE[0x7E] == 448.0 and fp8_e4m3.DECODE[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(5)
+    y = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.standard_normal(20000) * 0.01,
+        rng.standard_normal(20000) * 2.0 ** -8,
+        (fp8_e4m3.DECODE[:0x7E].astype(np.float64)[:-1] + fp8_e4m3.DECODE[1:0x7F].astype(np.float64)[:-1]) / 2,
+    ]).astype(F32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8_e4m3.encode(y), ref)
+
+
+def test_e4m3_encode_ties_saturation_and_identity():
+    enc = lambda v: int(fp8_e4m3.encode(np.array([v], F32))[0])  # noqa: E731
+    assert fp8_e4m3.DECODE[enc(1.0625)] == 1.0
+    assert fp8_e4m3.DECODE[enc(1.1875)] == 1.25
+    assert fp8_e4m3.DECODE[enc(3 * 2.0 ** -10)] == 2.0 ** -8
+    assert enc(2.0 ** -10) == 0x00 and enc(-(2.0 ** -10)) == 0x80
+    assert enc(448.0) == 0x7E and enc(1e9) == 0x7E and enc(-1e9) == 0xFE
+    assert enc(-0.0) == 0x80
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(fp8_e4m3.encode(fp8_e4m3.decode(codes)), codes)
+
+
+# ------------------------------------------------------------- exact mean
+
+def test_exact_mean_against_fractions():
+    rng = np.random.default_rng(6)
+    cases = [
+        rng.uniform(0, 0.1, 1000).astype(F32),
+        np.concatenate([rng.uniform(0, 1, 50) * 1e30, rng.uniform(0, 1, 50) * 1e-30]).astype(F32),
+        np.array([1e-45, 3e-45, 1e-44], F32),                     # subnormals
+        np.array([3.4e38, 3.4e38], F32),
+        (2.0 ** rng.integers(-140, 120, 500) * rng.uniform(1, 2, 500)).astype(F32),
+    ]
+    for c in cases:
+        exact = sum(Fraction(float(v)) for v in c) / len(c)
+        mu = blockwise.exact_mean_f32(c)
+        lo, hi = np.nextafter(mu, F32(-np.inf)), np.nextafter(mu, F32(np.inf))
+        e0 = abs(Fraction(float(mu)) - exact)
+        assert e0 <= abs(Fraction(float(lo)) - exact)
+        assert e0 <= abs(Fraction(float(hi)) - exact)
+
+
+def test_exact_mean_closed_forms():
+    assert blockwise.exact_mean_f32(np.full(777, 0.3, F32)) == F32(0.3)
+    assert blockwise.exact_mean_f32(np.array([1.0, 2.0], F32)) == F32(1.5)
+    # mean exactly halfway between two fp32 values -> even mantissa
+    a = F32(1.0)
+    b = np.nextafter(a, F32(2))                # 1 + 2^-23, odd mantissa
+    assert blockwise.exact_mean_f32(np.array([a, b], F32)) == a
+    c = np.nextafter(b, F32(2))                # 1 + 2^-22
+    assert blockwise.exact_mean_f32(np.array([b, c], F32)) == c
+
+
+# ----------------------------------------------- double quantisation, sizes
+
+def test_bits_per_param_closed_form_against_page():
+    g = dict(line.split() for line in _read_golden("dq_bits_per_param.txt"))
+    numel = 4096 * 4096
+    no_dq = blockwise.bits_per_param(numel, False)
+    dq = blockwise.bits_per_param(numel, True)
+    assert no_dq == 4.5 and no_dq - 4 == float(g["no_dq_constant_bits"])
+    assert dq - 4 == 8 / 64 + 32 / (64 * 256) + 32 / numel
+    assert round(dq - 4, 3) == float(g["dq_constant_bits"])
+    saving = no_dq - dq
+    assert round(saving, 3) == float(g["saving_bits"])
+    assert round(65e9 * saving / 8 / 1e9) == int(g["saving_65b_gigabytes"])
+
+
+def test_double_quant_error_bound_and_monotonicity():
+    rng = np.random.default_rng(7)
+    w = (rng.standard_t(5, 64 * 700) * 0.0155).astype(F32)
+    st = blockwise.quantize(w, double_quant=True)
+    c2, c2h = st.c2.astype(np.float64), st.c2_hat().astype(np.float64)
+    grp = np.arange(c2.size) // 256
+    c1 = st.scale2.astype(np.float64) * 448.0
+    # E4M3 keeps 3 mantissa bits: relative half-ulp 2^-4 of |c2 - mu|, plus
+    # the fp32 roundings of the scale and of the final sum.
+    d = np.abs(c2 - float(st.mu))
+    bound = d * 2.0 ** -4 + c1[grp] * 2.0 ** -9 * 2 ** -4 + 4 * np.spacing(c2.astype(F32)).astype(np.float64)
+    assert np.all(np.abs(c2h - c2) <= bound)
+    mu_f = float(np.mean(c2))
+    assert abs(float(st.mu) - mu_f) <= 1e-6 * mu_f
+    for g in range(grp.max() + 1):
+        sel = grp == g
+        order = np.argsort(c2[sel], kind="stable")
+        assert np.all(np.diff(c2h[sel][order]) >= 0)
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal(10000), rng.standard_normal(1000) * 1e-39,
+                        [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8]]).astype(F32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(blockwise.bf16_round(x).view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------- linear layer
+
+def _tiny_linear(seed, M=3, K=8, N=5, r=2):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((M, K)), rng.standard_normal((N, K)),
+            rng.standard_normal((K, r)), rng.standard_normal((r, N)), rng.standard_normal((M, N)))
+
+
+def test_forward_brute_force_loops():
+    X, W, A, B, _ = _tiny_linear(10)
+    s = 0.75
+    Y, XA = linear.forward(X, W, A, B, s)
+    M, K = X.shape
+    N, r = W.shape[0], A.shape[1]
+    for m, n in itertools.product(range(M), range(N)):
+        base = sum(X[m, k] * W[n, k] for k in range(K))
+        lora = sum(sum(X[m, k] * A[k, j] for k in range(K)) * B[j, n] for j in range(r))
+        assert math.isclose(Y[m, n], base + s * lora, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_forward_special_cases_and_torch_linear():
+    X, W, A, B, _ = _tiny_linear(11)
+    s = 2.0
+    Y, _ = linear.forward(X, W, A, B, s)
+    Yt = torch.nn.functional.linear(torch.from_numpy(X), torch.from_numpy(W)) + \
+        s * (torch.from_numpy(X) @ torch.from_numpy(A)) @ torch.from_numpy(B)
+    assert np.allclose(Y, Yt.numpy(), rtol=1e-12, atol=1e-12)
+    Y0, _ = linear.forward(X, W, A, np.zeros_like(B), s)          # B = 0: base linear
+    assert np.allclose(Y0, X @ W.T, rtol=1e-13, atol=1e-13)
+    Yw, _ = linear.forward(X, np.zeros_like(W), A, B, s)          # W = 0: pure adapter
+    assert np.allclose(Yw, s * X @ A @ B, rtol=1e-13, atol=1e-13)
+    Ys, _ = linear.forward(X, W, A, B, 0.0)                       # s = 0
+    assert np.allclose(Ys, X @ W.T, rtol=1e-13, atol=1e-13)
+
+
+def test_backward_finite_differences():
+    X, W, A, B, dY = _tiny_linear(12)
+    s = 0.5
+    dX, dA, dB = linear.backward(dY, X, W, A, B, s)
+
+    def loss(X_, A_, B_):
+        return float(np.sum(dY * linear.forward(X_, W, A_, B_, s)[0]))
+
+    h = 1e-6
+    for name, arr, grad in (("X", X, dX), ("A", A, dA), ("B", B, dB)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            args = {"X": X, "A": A, "B": B}
+            args[name] = p
+            lp = loss(args["X"], args["A"], args["B"])
+            args[name] = m
+            lm = loss(args["X"], args["A"], args["B"])
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), name
+
+
+def test_backward_matches_torch_autograd_fp64():
+    X, W, A, B, dY = _tiny_linear(13, M=4, K=16, N=8, r=3)
+    s = 0.25
+    tX, tA, tB = (torch.tensor(v, requires_grad=True) for v in (X, A, B))
+    Y = tX @ torch.from_numpy(W).T + s * (tX @ tA) @ tB
+    Y.backward(torch.from_numpy(dY))
+    dX, dA, dB = linear.backward(dY, X, W, A, B, s)
+    assert np.allclose(dX, tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dA, tA.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_flops_formula():
+    assert linear.flops(4096, 4096, 4096, 64) == 4 * 4096 ** 3 + 6 * 4096 * 64 * 8192
+
+
+# ------------------------------------------- pins catch planted oracle mistakes
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible mistakes in the oracle and check that a pin fails."""
+    X, W, A, B, dY = _tiny_linear(14)
+    s = 0.5
+    good = linear.backward(dY, X, W, A, B, s)
+
+    def bad_backward(dY_, X_, W_, A_, B_, s_):
+        dX, dA, dB = good
+        return dX, dA, dB / s_          # dropped scale on dB
+    h = 1e-6
+    num = np.zeros_like(B)
+    for idx in np.ndindex(B.shape):
+        p, m = B.copy(), B.copy()
+        p[idx] += h
+        m[idx] -= h
+        num[idx] = (np.sum(dY * linear.forward(X, W, A, p, s)[0]) -
+                    np.sum(dY * linear.forward(X, W, A, m, s)[0])) / (2 * h)
+    assert not np.allclose(bad_backward(dY, X, W, A, B, s)[2], num, rtol=1e-6, atol=1e-7)
+    # a tie rule to the upper index breaks the exact-midpoint pin
+    mids = _exact_midpoints()
+    x = F32(float(mids[7]))
+    upper = int(np.argmin(np.abs(x - codebook.NF4[::-1].astype(np.float64))))
+    assert 15 - upper != 7
