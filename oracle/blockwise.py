@@ -27,6 +27,13 @@ Readings where the page is silent or garbled (tags match the design notes):
   G9  a tail block (or 256-group) shorter than the block size takes its
       constant over the elements that exist.
   G11 the weight is flattened in its [out, in] row-major order.
+  G13 Eq. (1)'s constant must be finite: for a block whose absmax is an fp32
+      subnormal (0 < absmax < 2^-126) the reciprocal would overflow, so the
+      block and its absmax are first multiplied by 2^32 (exact for such
+      values) before the reciprocal and the product are taken.  The same
+      rule applies to the second-level constant c1 in double quantisation.
+      Codes of normal blocks are unaffected, and the rule keeps the codes
+      invariant under power-of-two scaling of a block.
 """
 
 from fractions import Fraction
@@ -39,6 +46,8 @@ from . import fp8_e4m3
 BLOCKSIZE = 64      # first-level block (elements of W per constant)
 BLOCKSIZE2 = 256    # second-level block (first-level constants per FP8 scale)
 FP8_MAX = np.float32(448.0)
+TINY = np.float32(2.0 ** -126)     # smallest normal fp32
+PRESCALE = np.float32(2.0 ** 32)   # G13
 
 _F32 = np.float32
 
@@ -112,9 +121,12 @@ def quantize_nf4(w, blocksize=BLOCKSIZE, codebook=NF4):
     if not np.all(np.isfinite(c2)):
         raise ValueError("non-finite input: NF4 codes are undefined")
     blk = np.arange(n) // blocksize
-    with np.errstate(divide="ignore"):
-        inv = np.where(c2 > 0, _F32(1.0) / np.where(c2 > 0, c2, _F32(1.0)), _F32(0.0)).astype(_F32)
-    x = (flat * inv[blk]).astype(_F32)
+    tiny = (c2 > 0) & (c2 < TINY)                       # G13
+    sc = np.where(tiny, PRESCALE, _F32(1.0)).astype(_F32)
+    cs = (c2 * sc).astype(_F32)
+    ws = (flat * sc[blk]).astype(_F32)
+    inv = np.where(cs > 0, _F32(1.0) / np.where(cs > 0, cs, _F32(1.0)), _F32(0.0)).astype(_F32)
+    x = (ws * inv[blk]).astype(_F32)
     codes = nearest_code(x, codebook).astype(np.uint8)
     codes[c2[blk] == 0] = ZERO_CODE
     return codes, c2
@@ -196,7 +208,9 @@ def double_quantize(c2, blocksize2=BLOCKSIZE2):
       d_b         = fp32(c2_b - mu)
       c1_g        = max |d_b| over group g of 256 constants        (G9 tail)
       absmax_q_b  = E4M3 byte of clamp(fp32(d_b * fp32(448 / c1_g)), +-448),
-                    nearest-even; all bytes 0 and scale 0 when c1_g == 0
+                    nearest-even; all bytes 0 and scale 0 when c1_g == 0;
+                    when c1_g is subnormal, d_b and c1_g are first
+                    multiplied by 2^32 (G13)
       scale2_g    = fp32(c1_g / 448)   (the page's second-level constant c1,
                     stored in the multiplicative form dequantisation uses)
     """
@@ -208,9 +222,12 @@ def double_quantize(c2, blocksize2=BLOCKSIZE2):
     grp = np.arange(nb) // blocksize2
     c1 = np.zeros(ng, dtype=_F32)
     np.maximum.at(c1, grp, np.abs(d))
-    with np.errstate(divide="ignore"):
-        f = np.where(c1 > 0, FP8_MAX / np.where(c1 > 0, c1, _F32(1.0)), _F32(0.0)).astype(_F32)
-    y = (d * f[grp]).astype(_F32)
+    tiny = (c1 > 0) & (c1 < TINY)                       # G13
+    sc = np.where(tiny, PRESCALE, _F32(1.0)).astype(_F32)
+    c1s = (c1 * sc).astype(_F32)
+    ds = (d * sc[grp]).astype(_F32)
+    f = np.where(c1s > 0, FP8_MAX / np.where(c1s > 0, c1s, _F32(1.0)), _F32(0.0)).astype(_F32)
+    y = (ds * f[grp]).astype(_F32)
     y = np.clip(y, -FP8_MAX, FP8_MAX).astype(_F32)
     q = fp8_e4m3.encode(y)
     q[c1[grp] == 0] = 0

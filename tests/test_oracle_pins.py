@@ -158,6 +158,32 @@ def test_double_quant_round_trip_exact_when_absmax_shared():
     assert np.array_equal(st.dequantize(), w)
 
 
+def test_codes_invariant_under_power_of_two_block_scaling():
+    """Codes depend only on w / absmax, so scaling a block by 2^e keeps them,
+    down to blocks of fp32 subnormals (reading G13 keeps the reciprocal finite)."""
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal(64 * 8)).astype(F32)
+    ref, _ = blockwise.quantize_nf4(w)
+    for e in (-20, -100, -126, -130, -140, 60):
+        ws = (w.astype(np.float64) * 2.0 ** e)
+        if e <= -126:
+            # keep only values whose scaled copy is exact in fp32 (subnormals drop low bits)
+            w2 = (np.round(w * 2.0 ** 6) / 2.0 ** 6).astype(F32)
+            ref2, _ = blockwise.quantize_nf4(w2)
+            ws = (w2.astype(np.float64) * 2.0 ** e)
+            assert np.all(ws.astype(F32).astype(np.float64) == ws)
+            codes, c2 = blockwise.quantize_nf4(ws.astype(F32))
+            assert np.array_equal(codes, ref2), e
+        else:
+            codes, c2 = blockwise.quantize_nf4(ws.astype(F32))
+            assert np.array_equal(codes, ref), e
+    # double quantisation of tiny, nearly equal constants stays finite and ordered
+    c2 = (np.float32(2.0 ** -140) * np.arange(1, 300)).astype(F32)
+    q, s2, mu = blockwise.double_quantize(c2)
+    rec = blockwise.dq_reconstruct(q, s2, mu)
+    assert np.all(np.isfinite(rec)) and np.all(np.diff(rec[:256]) >= 0)
+
+
 def test_all_zero_block():
     w = np.zeros(128, F32)
     w[64:] = np.linspace(-1, 1, 64, dtype=F32)
