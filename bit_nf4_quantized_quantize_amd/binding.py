@@ -1,0 +1,321 @@
+"""Thin ctypes binding of libqlora_nf4.so.
+
+Argument marshalling only: every step of quantisation, dequantisation and the
+linear layer runs in the library's HIP kernels.  PyTorch provides device
+memory (tensors) and the current HIP stream.  Functions carry the names of
+the C entry points (include/qlora_nf4.h) they call.
+
+The library is loaded on first use from this package directory; if it is
+missing or cannot be loaded, every call raises QLoraLibraryError (there is no
+fallback).
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
+
+QLORA_OK = 0
+QLORA_ERR_INVALID_ARG = -1
+QLORA_ERR_UNSUPPORTED_DTYPE = -2
+QLORA_ERR_WORKSPACE_TOO_SMALL = -3
+QLORA_ERR_MISALIGNED = -4
+QLORA_ERR_HIP = -5
+QLORA_DTYPE_F32 = 0
+QLORA_DTYPE_BF16 = 1
+BLOCKSIZE = 64
+BLOCKSIZE2 = 256
+MAX_RANK = 256
+
+# Every function declared in include/qlora_nf4.h.
+EXPORTED = (
+    "qlora_nf4_storage_bytes", "qlora_nf4_quantize_workspace", "qlora_linear_workspace",
+    "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
+    "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_profile_events",
+)
+QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
+
+
+class QLoraLibraryError(RuntimeError):
+    pass
+
+
+class QLoraError(RuntimeError):
+    def __init__(self, status, fn, message):
+        self.status = status
+        super().__init__(f"{fn} failed ({status}: {_status_text(status)}): {message}")
+
+
+class qlora_nf4_t(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32), ("blocksize2", ctypes.c_int32),
+        ("double_quant", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+        ("scale2", ctypes.c_void_p), ("offset", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_vp, _i64, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+_pdesc = ctypes.POINTER(qlora_nf4_t)
+
+
+def lib():
+    """The loaded library (raises QLoraLibraryError if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise QLoraLibraryError(f"{LIB_PATH} not found: build it with "
+                                "`python -m bit_nf4_quantized_quantize_amd.build`")
+    try:
+        L = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise QLoraLibraryError(f"cannot load {LIB_PATH}: {e}") from e
+    sig = {
+        "qlora_nf4_storage_bytes": (_i32, [_i64, _i32, ctypes.POINTER(_i64)]),
+        "qlora_nf4_quantize_workspace": (_i32, [_i64, _i32, ctypes.POINTER(_i64)]),
+        "qlora_linear_workspace": (_i32, [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+        "qlora_nf4_codebook": (_i32, [ctypes.POINTER(_f32)]),
+        "qlora_status_string": (ctypes.c_char_p, [_i32]),
+        "qlora_last_error": (ctypes.c_char_p, []),
+        "qlora_nf4_quantize": (_i32, [_vp, _i32, _pdesc, _vp, _i64, _vp]),
+        "qlora_nf4_dequantize": (_i32, [_pdesc, _vp, _i32, _vp]),
+        "qlora_linear_fwd": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i64, _vp]),
+        "qlora_linear_bwd": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
+        "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _status_text(status):
+    try:
+        return lib().qlora_status_string(status).decode()
+    except QLoraLibraryError:
+        return "?"
+
+
+def _check(status, fn):
+    if status != QLORA_OK:
+        raise QLoraError(status, fn, lib().qlora_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("qlora_nf4 tensors must live on a HIP device")
+
+
+# ------------------------------------------------------------ host queries
+
+def qlora_nf4_storage_bytes(numel, double_quant=True):
+    out = (_i64 * 5)()
+    _check(lib().qlora_nf4_storage_bytes(numel, int(double_quant), out), "qlora_nf4_storage_bytes")
+    return dict(zip(("codes", "absmax_q", "absmax", "scale2", "offset"), list(out)))
+
+
+def qlora_nf4_quantize_workspace(numel, double_quant=True):
+    ws = _i64(0)
+    _check(lib().qlora_nf4_quantize_workspace(numel, int(double_quant), ctypes.byref(ws)),
+           "qlora_nf4_quantize_workspace")
+    return ws.value
+
+
+def qlora_linear_workspace(M, N, K, r):
+    f, b = _i64(0), _i64(0)
+    _check(lib().qlora_linear_workspace(M, N, K, r, ctypes.byref(f), ctypes.byref(b)), "qlora_linear_workspace")
+    return f.value, b.value
+
+
+def qlora_nf4_codebook():
+    out = (_f32 * 16)()
+    _check(lib().qlora_nf4_codebook(out), "qlora_nf4_codebook")
+    return list(out)
+
+
+def qlora_profile_events(kernel, start=None, stop=None):
+    """Attach (or detach, with None) a pair of hipEvent_t handles (ints or
+    ctypes.c_void_p, created with hipEventCreate) to a kernel of the library
+    for the calling thread."""
+    kid = QLORA_KERNEL[kernel]
+    _check(lib().qlora_profile_events(kid, start, stop), "qlora_profile_events")
+
+
+# ----------------------------------------------------------- quantised weight
+
+class NF4Weight:
+    """Device buffers of one NF4-quantised weight [rows, cols] plus the C
+    descriptor that points at them."""
+
+    def __init__(self, rows, cols, double_quant=True, device=None):
+        self.rows, self.cols, self.double_quant = int(rows), int(cols), bool(double_quant)
+        sizes = qlora_nf4_storage_bytes(self.rows * self.cols, self.double_quant)
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        u8 = torch.uint8
+        # Pad every buffer to a 16-byte multiple so vector accesses never leave it.
+        pad = lambda n: max(16, (n + 15) // 16 * 16)  # noqa: E731
+        self.codes = torch.empty(pad(sizes["codes"]), dtype=u8, device=dev)
+        self.absmax_q = torch.empty(pad(sizes["absmax_q"]), dtype=u8, device=dev) if double_quant else None
+        self.absmax = torch.empty(pad(sizes["absmax"]) // 4, dtype=torch.float32, device=dev) if not double_quant else None
+        self.scale2 = torch.empty(pad(sizes["scale2"]) // 4, dtype=torch.float32, device=dev) if double_quant else None
+        self.offset = torch.empty(4, dtype=torch.float32, device=dev) if double_quant else None
+        self.sizes = sizes
+
+    @property
+    def numel(self):
+        return self.rows * self.cols
+
+    def desc(self):
+        d = qlora_nf4_t()
+        d.rows, d.cols = self.rows, self.cols
+        d.blocksize, d.blocksize2 = BLOCKSIZE, BLOCKSIZE2
+        d.double_quant = int(self.double_quant)
+        d.reserved = 0
+        d.codes = self.codes.data_ptr()
+        d.absmax_q = self.absmax_q.data_ptr() if self.absmax_q is not None else None
+        d.absmax = self.absmax.data_ptr() if self.absmax is not None else None
+        d.scale2 = self.scale2.data_ptr() if self.scale2 is not None else None
+        d.offset = self.offset.data_ptr() if self.offset is not None else None
+        return d
+
+    # host copies of the stored buffers, trimmed to their true sizes
+    def host(self):
+        s = self.sizes
+        out = {"codes": self.codes[:s["codes"]].cpu().numpy()}
+        if self.double_quant:
+            out["absmax_q"] = self.absmax_q[:s["absmax_q"]].cpu().numpy()
+            out["scale2"] = self.scale2[:s["scale2"] // 4].cpu().numpy()
+            out["offset"] = self.offset[:1].cpu().numpy()
+        else:
+            out["absmax"] = self.absmax[:s["absmax"] // 4].cpu().numpy()
+        return out
+
+
+# ---------------------------------------------------------- device entry points
+
+def qlora_nf4_quantize(w, double_quant=True, out=None, workspace=None, stream=None):
+    """Quantise fp32 or bf16 tensor `w` ([rows, cols] or 1-D) into an
+    NF4Weight (new or `out`).  `workspace`: optional uint8 device tensor of at
+    least qlora_nf4_quantize_workspace bytes."""
+    _need_cuda(w)
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    dtype = {torch.float32: QLORA_DTYPE_F32, torch.bfloat16: QLORA_DTYPE_BF16}.get(w.dtype)
+    if dtype is None:
+        raise ValueError("w must be float32 or bfloat16")
+    rows, cols = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, w.numel())
+    q = out if out is not None else NF4Weight(rows, cols, double_quant, w.device)
+    nws = qlora_nf4_quantize_workspace(q.numel, q.double_quant)
+    ws = workspace if workspace is not None else torch.empty(max(nws, 16), dtype=torch.uint8, device=w.device)
+    if ws.numel() < nws:
+        raise ValueError(f"quantize workspace needs {nws} bytes")
+    nws = ws.numel()
+    d = q.desc()
+    _check(lib().qlora_nf4_quantize(_ptr(w), dtype, ctypes.byref(d), _ptr(ws), nws, _stream(stream)),
+           "qlora_nf4_quantize")
+    q._ws = ws  # keep the workspace alive until the stream has used it
+    return q
+
+
+def qlora_nf4_dequantize(q, dtype=torch.bfloat16, out=None, stream=None):
+    code = {torch.float32: QLORA_DTYPE_F32, torch.bfloat16: QLORA_DTYPE_BF16}.get(dtype)
+    if code is None:
+        raise ValueError("dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
+    _need_cuda(out)
+    d = q.desc()
+    _check(lib().qlora_nf4_dequantize(ctypes.byref(d), _ptr(out), code, _stream(stream)), "qlora_nf4_dequantize")
+    return out
+
+
+def _bf16_2d(t, name, shape):
+    if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape {tuple(shape)}")
+
+
+class Workspace:
+    """Grow-only device scratch for the linear entry points."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _ws(nbytes, device, ws):
+    if ws is None:
+        ws = _default_ws.setdefault((device.type, device.index), Workspace())
+    return ws.get(nbytes, device)
+
+
+def qlora_linear_fwd(X, q, A, B, s, save_xa=True, Y=None, XA=None, workspace=None, stream=None):
+    """Y = X W_bf16^T + s (X A) B.  Returns (Y, XA or None)."""
+    _need_cuda(X, A, B)
+    M, K = X.shape
+    N, r = q.rows, A.shape[1]
+    _bf16_2d(X, "X", (M, q.cols))
+    _bf16_2d(A, "A", (K, r))
+    _bf16_2d(B, "B", (r, N))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    if save_xa and XA is None:
+        XA = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
+    nws, _ = qlora_linear_workspace(M, N, K, r)
+    ws = _ws(nws, X.device, workspace)
+    d = q.desc()
+    _check(lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s), _ptr(Y),
+                                  _ptr(XA) if save_xa else None, _ptr(ws), ws.numel(), _stream(stream)),
+           "qlora_linear_fwd")
+    return Y, (XA if save_xa else None)
+
+
+def qlora_linear_bwd(dY, X, XA, q, A, B, s, need_dx=True, dX=None, dA=None, dB=None, workspace=None, stream=None):
+    """Returns (dX or None, dA, dB) for Y = X W_bf16^T + s (X A) B."""
+    _need_cuda(dY, X, XA, A, B)
+    M, K = X.shape
+    N, r = q.rows, A.shape[1]
+    _bf16_2d(dY, "dY", (M, N))
+    _bf16_2d(X, "X", (M, q.cols))
+    _bf16_2d(XA, "XA", (M, r))
+    _bf16_2d(A, "A", (K, r))
+    _bf16_2d(B, "B", (r, N))
+    dev = X.device
+    if need_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty((K, r), dtype=torch.bfloat16, device=dev)
+    if dB is None:
+        dB = torch.empty((r, N), dtype=torch.bfloat16, device=dev)
+    _, nws = qlora_linear_workspace(M, N, K, r)
+    ws = _ws(nws, dev, workspace)
+    d = q.desc()
+    _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(XA), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s),
+                                  _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                  _stream(stream)),
+           "qlora_linear_bwd")
+    return (dX if need_dx else None), dA, dB

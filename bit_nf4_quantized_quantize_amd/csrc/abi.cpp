@@ -1,0 +1,349 @@
+// C ABI of the QLoRA NF4 library: argument validation (host only, before any
+// launch), workspace layout and kernel dispatch.  See include/qlora_nf4.h for
+// the contract of each entry point.
+#include "qlora_nf4.h"
+#include "qlora_nf4_profile.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.h"
+
+using namespace qlora;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+// Per-thread event pairs attached with qlora_profile_events.
+struct ProfPair {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local ProfPair g_prof[QLORA_KERNEL_COUNT];
+
+// Brackets one kernel launch with the attached events (if any).
+struct ProfScope {
+  const ProfPair& p;
+  hipStream_t s;
+  ProfScope(int id, hipStream_t stream) : p(g_prof[id]), s(stream) {
+    if (p.start) (void)hipEventRecord(p.start, s);
+  }
+  ~ProfScope() {
+    if (p.stop) (void)hipEventRecord(p.stop, s);
+  }
+};
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(QLORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxNumel = (int64_t)1 << 37;
+constexpr int64_t kAlign = 256;  // alignment of workspace regions
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int64_t nblocks(int64_t numel) { return ceil_div(numel, QLORA_NF4_BLOCKSIZE); }
+int64_t ngroups(int64_t numel) { return ceil_div(nblocks(numel), QLORA_NF4_BLOCKSIZE2); }
+
+// Validate the descriptor itself (shape, flags, buffer pointers).
+int check_desc(const qlora_nf4_t* q, const char* fn) {
+  if (!q) return fail(QLORA_ERR_INVALID_ARG, "%s: descriptor is NULL", fn);
+  if (q->rows < 0 || q->cols < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: negative shape", fn);
+  if (q->cols > 0 && q->rows > kMaxNumel / q->cols)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: rows*cols must be below 2^37", fn);
+  if (q->blocksize != QLORA_NF4_BLOCKSIZE || q->blocksize2 != QLORA_NF4_BLOCKSIZE2)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: blocksize must be 64 and blocksize2 256", fn);
+  if (q->double_quant != 0 && q->double_quant != 1)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: double_quant must be 0 or 1", fn);
+  if (q->rows * q->cols == 0) return QLORA_OK;
+  if (!q->codes) return fail(QLORA_ERR_INVALID_ARG, "%s: codes is NULL", fn);
+  if (!aligned16(q->codes)) return fail(QLORA_ERR_MISALIGNED, "%s: codes not 16-byte aligned", fn);
+  if (q->double_quant) {
+    if (!q->absmax_q || !q->scale2 || !q->offset)
+      return fail(QLORA_ERR_INVALID_ARG, "%s: absmax_q, scale2 and offset are required with double_quant", fn);
+    if (!aligned16(q->absmax_q) || !aligned16(q->scale2) || !aligned16(q->offset))
+      return fail(QLORA_ERR_MISALIGNED, "%s: constant buffers must be 16-byte aligned", fn);
+  } else {
+    if (!q->absmax) return fail(QLORA_ERR_INVALID_ARG, "%s: absmax is required without double_quant", fn);
+    if (!aligned16(q->absmax)) return fail(QLORA_ERR_MISALIGNED, "%s: absmax not 16-byte aligned", fn);
+  }
+  return QLORA_OK;
+}
+
+DQParams dq_params(const qlora_nf4_t* q) {
+  DQParams p;
+  p.absmax_q = q->absmax_q;
+  p.absmax = q->absmax;
+  p.scale2 = q->scale2;
+  p.offset = q->offset;
+  p.double_quant = q->double_quant;
+  return p;
+}
+
+// Workspace layouts ------------------------------------------------------
+
+int64_t quant_ws(int64_t numel, int dq) {
+  if (!dq || numel == 0) return 0;
+  const int64_t nb = nblocks(numel);
+  return round_up(nb * 4, kAlign) + round_up((int64_t)dq_mean_parts(nb) * kMeanDigits * 8, kAlign);
+}
+
+struct FwdWs {
+  int64_t at, bt, xas, total;  // byte offsets: A^T [r, K], B^T [N, rp], s*XA [M, rp]
+};
+FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
+  const int64_t rp = round_up(r, 64);
+  FwdWs w;
+  w.at = 0;
+  w.bt = w.at + round_up(r * K * 2, kAlign);
+  w.xas = w.bt + round_up(N * rp * 2, kAlign);
+  w.total = w.xas + round_up(M * rp * 2, kAlign);
+  return w;
+}
+
+struct BwdWs {
+  int64_t ts, ap, xap, part, total;  // s*T [M, rp], A [K, rp], XA [M, rp], fp32 partials
+  int splits_a, splits_b;
+};
+BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
+  const int64_t rp = round_up(r, 64);
+  BwdWs w;
+  w.splits_a = tn_splits(M, K, rp);
+  w.splits_b = tn_splits(M, rp, N);
+  const int64_t pa = (int64_t)w.splits_a * K * rp, pb = (int64_t)w.splits_b * rp * N;
+  w.ts = 0;
+  w.ap = w.ts + round_up(M * rp * 2, kAlign);
+  w.xap = w.ap + round_up(K * rp * 2, kAlign);
+  w.part = w.xap + round_up(M * rp * 2, kAlign);
+  w.total = w.part + round_up((pa > pb ? pa : pb) * 4, kAlign);
+  return w;
+}
+
+int check_linear_shape(const qlora_nf4_t* W, int64_t M, int32_t r, const char* fn) {
+  int st = check_desc(W, fn);
+  if (st) return st;
+  if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M < 0", fn);
+  if (W->rows <= 0 || W->cols <= 0 || W->rows % 64 || W->cols % 64)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: weight [N, K] needs N, K > 0 and multiples of 64 (got %lld x %lld)",
+                fn, (long long)W->rows, (long long)W->cols);
+  if (r < 1 || r > QLORA_MAX_RANK) return fail(QLORA_ERR_INVALID_ARG, "%s: rank r must be in [1, 256]", fn);
+  if (M > kMaxNumel / (W->rows > W->cols ? W->rows : W->cols))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: M too large", fn);
+  return QLORA_OK;
+}
+
+int check_ptr(const void* p, const char* name, const char* fn) {
+  if (!p) return fail(QLORA_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+  if (!aligned16(p)) return fail(QLORA_ERR_MISALIGNED, "%s: %s not 16-byte aligned", fn, name);
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_string(int32_t status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case QLORA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QLORA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case QLORA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* qlora_last_error(void) { return g_err; }
+
+int qlora_profile_events(int32_t kernel_id, void* start_event, void* stop_event) {
+  if (kernel_id < 0 || kernel_id >= QLORA_KERNEL_COUNT)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_profile_events: unknown kernel id %d", kernel_id);
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_profile_events: give both events or neither");
+  g_prof[kernel_id].start = (hipEvent_t)start_event;
+  g_prof[kernel_id].stop = (hipEvent_t)stop_event;
+  return QLORA_OK;
+}
+
+int qlora_nf4_codebook(float* out) {
+  if (!out) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_codebook: out is NULL");
+  memcpy(out, nf4_values().v, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_nf4_storage_bytes(int64_t numel, int32_t double_quant, int64_t* bytes) {
+  if (!bytes) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_storage_bytes: bytes is NULL");
+  if (numel < 0 || numel >= kMaxNumel) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_storage_bytes: bad numel");
+  if (double_quant != 0 && double_quant != 1)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_storage_bytes: double_quant must be 0 or 1");
+  bytes[0] = ceil_div(numel, 2);
+  bytes[1] = double_quant ? nblocks(numel) : 0;
+  bytes[2] = double_quant ? 0 : 4 * nblocks(numel);
+  bytes[3] = double_quant ? 4 * ngroups(numel) : 0;
+  bytes[4] = double_quant ? 4 : 0;
+  return QLORA_OK;
+}
+
+int qlora_nf4_quantize_workspace(int64_t numel, int32_t double_quant, int64_t* ws_bytes) {
+  if (!ws_bytes) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_quantize_workspace: ws_bytes is NULL");
+  if (numel < 0 || numel >= kMaxNumel) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_quantize_workspace: bad numel");
+  if (double_quant != 0 && double_quant != 1)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_quantize_workspace: double_quant must be 0 or 1");
+  *ws_bytes = quant_ws(numel, double_quant);
+  return QLORA_OK;
+}
+
+int qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r, int64_t* fwd_bytes, int64_t* bwd_bytes) {
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 || r < 1 || r > QLORA_MAX_RANK)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_linear_workspace: bad shape or rank");
+  if (fwd_bytes) *fwd_bytes = fwd_ws(M, N, K, r).total;
+  if (bwd_bytes) *bwd_bytes = bwd_ws(M, N, K, r).total;
+  return QLORA_OK;
+}
+
+int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q, void* ws, int64_t ws_bytes,
+                       void* stream) {
+  static const char* fn = "qlora_nf4_quantize";
+  int st = check_desc(q, fn);
+  if (st) return st;
+  if (w_dtype != QLORA_DTYPE_F32 && w_dtype != QLORA_DTYPE_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: w_dtype must be F32 or BF16", fn);
+  const int64_t numel = q->rows * q->cols;
+  if (numel == 0) return QLORA_OK;
+  if ((st = check_ptr(w, "w", fn))) return st;
+  const int64_t need = quant_ws(numel, q->double_quant);
+  if (ws_bytes < need) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)need);
+  if (need > 0 && (st = check_ptr(ws, "ws", fn))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nb = nblocks(numel);
+  float* c2 = q->double_quant ? (float*)ws : q->absmax;
+  hipError_t e;
+  {
+    ProfScope ps(QLORA_KERNEL_QUANTIZE, s);
+    e = launch_quantize(w, w_dtype == QLORA_DTYPE_BF16, numel, q->codes, c2, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (q->double_quant) {
+    uint64_t* parts = (uint64_t*)((char*)ws + round_up(nb * 4, kAlign));
+    e = launch_double_quant(c2, nb, parts, q->absmax_q, q->scale2, q->offset, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  return QLORA_OK;
+}
+
+int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, void* stream) {
+  static const char* fn = "qlora_nf4_dequantize";
+  int st = check_desc(q, fn);
+  if (st) return st;
+  if (out_dtype != QLORA_DTYPE_F32 && out_dtype != QLORA_DTYPE_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: out_dtype must be F32 or BF16", fn);
+  const int64_t numel = q->rows * q->cols;
+  if (numel == 0) return QLORA_OK;
+  if ((st = check_ptr(out, "out", fn))) return st;
+  hipError_t e;
+  {
+    ProfScope ps(QLORA_KERNEL_DEQUANTIZE, (hipStream_t)stream);
+    e = launch_dequantize(q->codes, numel, q->double_quant != 0, q->absmax_q, q->absmax, q->scale2, q->offset, out,
+                          out_dtype == QLORA_DTYPE_BF16, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void* A, const void* B, int32_t r, float s,
+                     void* Y, void* XA, void* ws, int64_t ws_bytes, void* stream) {
+  static const char* fn = "qlora_linear_fwd";
+  int st = check_linear_shape(W, M, r, fn);
+  if (st) return st;
+  if (M == 0) return QLORA_OK;
+  if ((st = check_ptr(X, "X", fn)) || (st = check_ptr(A, "A", fn)) || (st = check_ptr(B, "B", fn)) ||
+      (st = check_ptr(Y, "Y", fn)))
+    return st;
+  if (XA && !aligned16(XA)) return fail(QLORA_ERR_MISALIGNED, "%s: XA not 16-byte aligned", fn);
+  const int64_t N = W->rows, K = W->cols, rp = round_up(r, 64);
+  const FwdWs L = fwd_ws(M, N, K, r);
+  if (ws_bytes < L.total) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)L.total);
+  if ((st = check_ptr(ws, "ws", fn))) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* base = (char*)ws;
+  uint16_t* at = (uint16_t*)(base + L.at);
+  uint16_t* bt = (uint16_t*)(base + L.bt);
+  uint16_t* xas = (uint16_t*)(base + L.xas);
+  hipError_t e;
+  // A^T [r, K] (no padding: the NT product masks rows >= r)
+  if ((e = launch_transpose_pad((const uint16_t*)A, K, r, at, K, hs)) != hipSuccess) return hip_fail(e, fn);
+  if ((e = launch_transpose_pad((const uint16_t*)B, r, N, bt, rp, hs)) != hipSuccess) return hip_fail(e, fn);
+  if ((e = launch_gemm_nt((const uint16_t*)X, at, M, r, K, (uint16_t*)XA, xas, rp, s, hs)) != hipSuccess)
+    return hip_fail(e, fn);
+  {
+    ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
+    e = launch_fwd_main((const uint16_t*)X, M, K, W->codes, dq_params(W), N, xas, bt, rp, (uint16_t*)Y, hs);
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W, const void* A,
+                     const void* B, int32_t r, float s, void* dX, void* dA, void* dB, void* ws, int64_t ws_bytes,
+                     void* stream) {
+  static const char* fn = "qlora_linear_bwd";
+  int st = check_linear_shape(W, M, r, fn);
+  if (st) return st;
+  if ((st = check_ptr(dA, "dA", fn)) || (st = check_ptr(dB, "dB", fn))) return st;
+  const int64_t N = W->rows, K = W->cols, rp = round_up(r, 64);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  if (M == 0) {
+    if ((e = launch_fill_zero_u16((uint16_t*)dA, K * r, hs)) != hipSuccess) return hip_fail(e, fn);
+    if ((e = launch_fill_zero_u16((uint16_t*)dB, (int64_t)r * N, hs)) != hipSuccess) return hip_fail(e, fn);
+    return QLORA_OK;
+  }
+  if ((st = check_ptr(dY, "dY", fn)) || (st = check_ptr(X, "X", fn)) || (st = check_ptr(XA, "XA", fn)) ||
+      (st = check_ptr(A, "A", fn)) || (st = check_ptr(B, "B", fn)))
+    return st;
+  if (dX && !aligned16(dX)) return fail(QLORA_ERR_MISALIGNED, "%s: dX not 16-byte aligned", fn);
+  const BwdWs L = bwd_ws(M, N, K, r);
+  if (ws_bytes < L.total) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)L.total);
+  if ((st = check_ptr(ws, "ws", fn))) return st;
+  char* base = (char*)ws;
+  uint16_t* ts = (uint16_t*)(base + L.ts);
+  uint16_t* ap = (uint16_t*)(base + L.ap);
+  uint16_t* xap = (uint16_t*)(base + L.xap);
+  float* part = (float*)(base + L.part);
+  // s*T = s * dY B^T  [M, rp]
+  if ((e = launch_gemm_nt((const uint16_t*)dY, (const uint16_t*)B, M, r, N, nullptr, ts, rp, s, hs)) != hipSuccess)
+    return hip_fail(e, fn);
+  if ((e = launch_pad_copy((const uint16_t*)A, K, r, ap, rp, hs)) != hipSuccess) return hip_fail(e, fn);
+  if ((e = launch_pad_copy((const uint16_t*)XA, M, r, xap, rp, hs)) != hipSuccess) return hip_fail(e, fn);
+  if (dX) {
+    {
+      ProfScope ps(QLORA_KERNEL_BWD_DX, hs);
+      e = launch_bwd_dx((const uint16_t*)dY, M, N, W->codes, dq_params(W), K, ts, ap, rp, (uint16_t*)dX, hs);
+    }
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  // dA = X^T (s T)   [K, r]
+  if ((e = launch_gemm_tn((const uint16_t*)X, ts, M, K, rp, part, L.splits_a, (uint16_t*)dA, K, r, 1.0f, hs)) !=
+      hipSuccess)
+    return hip_fail(e, fn);
+  // dB = s XA^T dY   [r, N]
+  if ((e = launch_gemm_tn(xap, (const uint16_t*)dY, M, rp, N, part, L.splits_b, (uint16_t*)dB, r, N, s, hs)) !=
+      hipSuccess)
+    return hip_fail(e, fn);
+  return QLORA_OK;
+}
+
+}  // extern "C"

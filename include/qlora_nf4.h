@@ -1,0 +1,238 @@
+/*
+ * qlora_nf4.h - C ABI of the MI355X (gfx950) QLoRA frozen-NF4 linear library.
+ *
+ * The library implements the storage and compute types of "QLoRA: Efficient
+ * Finetuning of Quantized LLMs" (Dettmers et al., arXiv 2305.14314; cited
+ * below as QLoRA, by section and equation):
+ *   - blockwise 4-bit NormalFloat quantisation of a weight (section 2
+ *     "Block-wise k-bit Quantization", Eq. 1; section 3 "4-bit NormalFloat
+ *     Quantization"; Appendix E for the 16 values);
+ *   - double quantisation of the per-block constants (section 3 "Double
+ *     Quantization");
+ *   - dequantisation to fp32 or bf16 (Eq. 2 read as multiplication by the
+ *     block absmax, and Eq. 6);
+ *   - the forward and backward of one linear layer with a LoRA adapter over
+ *     the frozen NF4 weight (section 2 "Low-rank Adapters", Eq. 3; section 3
+ *     "QLoRA", Eq. 5 and the paragraph after Eq. 6: gradients for the
+ *     adapter and the input only, none for the weight).
+ *
+ * Conventions shared by every entry point
+ *   Pointers.   Every buffer pointer is a DEVICE pointer into memory the
+ *               caller allocated and owns; the library never allocates,
+ *               frees, or keeps a pointer after a call returns.  Host-only
+ *               outputs (sizes, the codebook) are host pointers and say so.
+ *   Streams.    `stream` is a hipStream_t passed as void* (NULL = the null
+ *               stream).  Every device entry point only enqueues kernels on
+ *               that stream and returns without synchronising; results are
+ *               ready when the stream reaches that point.
+ *   Layouts.    Matrices are dense row-major with no padding between rows.
+ *               The weight is [rows, cols] = [N, K] = [out, in]; its
+ *               elements are taken in that flattened order for blocking.
+ *   Types.      bf16 tensors are IEEE bfloat16 bit patterns (uint16).
+ *   Alignment.  Every tensor pointer must be 16-byte aligned.
+ *   Errors.     Every function returns QLORA_OK (0) or a negative
+ *               qlora_status.  Arguments are validated on the host before
+ *               anything is enqueued; on any validation failure nothing is
+ *               enqueued and no buffer is touched.  QLORA_ERR_HIP reports a
+ *               failed kernel launch (the HIP error text is kept).
+ *               qlora_last_error() returns a message for the calling
+ *               thread's most recent failure.
+ *   Threads.    Calls on different streams are independent; the library
+ *               holds no mutable global state besides the per-thread error
+ *               message.
+ *   Non-finite weights give undefined (but in-range) codes.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1,        /* null pointer, bad size, shape or flag   */
+  QLORA_ERR_UNSUPPORTED_DTYPE = -2,  /* dtype code not accepted by this call     */
+  QLORA_ERR_WORKSPACE_TOO_SMALL = -3,/* ws_bytes below what the call needs        */
+  QLORA_ERR_MISALIGNED = -4,         /* a tensor pointer not 16-byte aligned      */
+  QLORA_ERR_HIP = -5                 /* a kernel launch failed                     */
+} qlora_status;
+
+typedef enum {
+  QLORA_DTYPE_F32 = 0,
+  QLORA_DTYPE_BF16 = 1
+} qlora_dtype;
+
+/* Block sizes fixed by QLoRA section 3 ("QLoRA": block size 64 for W,
+ * 256 for the first-level constants). */
+#define QLORA_NF4_BLOCKSIZE 64
+#define QLORA_NF4_BLOCKSIZE2 256
+/* Largest LoRA rank accepted by the linear entry points. */
+#define QLORA_MAX_RANK 256
+
+/*
+ * Descriptor of one NF4-quantised weight (the quantisation state).  Plain
+ * data: the caller fills it and owns every buffer it points to.
+ *
+ *   rows, cols     weight shape [N, K]; numel = rows*cols, 0 < numel < 2^37.
+ *   blocksize      must be 64;  nb = ceil(numel / 64) blocks, a short last
+ *                  block takes its absmax over the elements that exist.
+ *   blocksize2     must be 256; ng = ceil(nb / 256) groups of constants.
+ *   double_quant   1: constants stored double-quantised (absmax_q, scale2,
+ *                  offset used, absmax ignored); 0: absmax used.
+ *   codes          u8[ceil(numel/2)]: two NF4 codes per byte, element 2j in
+ *                  the low nibble, element 2j+1 in the high nibble; an odd
+ *                  last element leaves the high nibble 0.  Code i stands for
+ *                  the i-th Appendix E value (0 = -1.0, 7 = 0.0, 15 = 1.0).
+ *   absmax_q       u8[nb]: OCP FP8 E4M3FN byte of (c2_b - mu) * 448 / c1_g,
+ *                  nearest-even, saturating (QLoRA c2^FP8).
+ *   absmax         f32[nb]: the block absmax c2_b (no double quantisation).
+ *   scale2         f32[ng]: c1_g / 448 with c1_g = max |c2_b - mu| over the
+ *                  group (QLoRA's second-level constant c1^FP32); 0 when the
+ *                  group is constant.
+ *   offset         f32[1]: mu, the mean of all c2_b, exact and rounded once
+ *                  to fp32 (nearest-even).
+ */
+typedef struct qlora_nf4 {
+  int64_t rows;
+  int64_t cols;
+  int32_t blocksize;
+  int32_t blocksize2;
+  int32_t double_quant;
+  int32_t reserved;  /* set to 0 */
+  uint8_t* codes;
+  uint8_t* absmax_q;
+  float* absmax;
+  float* scale2;
+  float* offset;
+} qlora_nf4_t;
+
+/* ------------------------------------------------------------- host queries */
+
+/* Host only.  Bytes of each buffer of the descriptor for `numel` weights:
+ * bytes[0] codes, [1] absmax_q, [2] absmax, [3] scale2, [4] offset (entries
+ * not used by the chosen double_quant are 0).  `bytes` is a host array of 5.
+ * The total is the storage cost QLoRA section 3 "Double Quantization"
+ * accounts: 4 + 32/64 bits per weight without double quantisation,
+ * 4 + 8/64 + 32/(64*256) (+32/numel for mu) with it. */
+int qlora_nf4_storage_bytes(int64_t numel, int32_t double_quant, int64_t* bytes);
+
+/* Host only.  Workspace bytes qlora_nf4_quantize needs (0 without double
+ * quantisation).  Written to the host pointer *ws_bytes. */
+int qlora_nf4_quantize_workspace(int64_t numel, int32_t double_quant, int64_t* ws_bytes);
+
+/* Host only.  Workspace bytes qlora_linear_fwd / qlora_linear_bwd need for
+ * an [M, K] x [N, K]^T layer of LoRA rank r (host pointers; either may be
+ * NULL). */
+int qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r,
+                           int64_t* fwd_bytes, int64_t* bwd_bytes);
+
+/* Host only.  Copies the 16 NF4 values the library quantises against
+ * (QLoRA Appendix E, code order) into the host array out[16]. */
+int qlora_nf4_codebook(float* out);
+
+/* Text for a status code; never NULL. */
+const char* qlora_status_string(int32_t status);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* qlora_last_error(void);
+
+/* ----------------------------------------------------------- quantisation */
+
+/*
+ * qlora_nf4_quantize - NF4-quantise a weight, optionally double-quantising
+ * the block constants (QLoRA section 2 Eq. 1 and chunking; section 3
+ * "4-bit NormalFloat Quantization" steps (1)-(3); section 3 "Double
+ * Quantization").
+ *
+ *   w        device, [q->rows, q->cols] row-major, dtype w_dtype
+ *            (QLORA_DTYPE_F32 or QLORA_DTYPE_BF16).
+ *   q        host pointer to a filled descriptor; writes q->codes and either
+ *            q->absmax (double_quant = 0) or q->absmax_q, q->scale2,
+ *            q->offset (double_quant = 1).
+ *   ws       device workspace of ws_bytes >= qlora_nf4_quantize_workspace
+ *            (may be NULL when that is 0); contents on entry are ignored.
+ *
+ * Per block b of 64 flattened weights: c2_b = max |w| (exact); each weight
+ * x = fp32(w * fp32(1/c2_b)) gets the index of the nearest Appendix E value,
+ * ties to the lower index; an all-zero block gets code 7 throughout.  With
+ * double quantisation, mu = mean(c2) and each group of 256 constants is
+ * stored as described for qlora_nf4_t.
+ */
+int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q,
+                       void* ws, int64_t ws_bytes, void* stream);
+
+/*
+ * qlora_nf4_dequantize - doubleDequant of QLoRA Eq. 6 (or the single
+ * dequant of Eq. 2 without double quantisation).
+ *
+ *   q        host pointer to a descriptor whose buffers hold a quantised
+ *            weight.
+ *   out      device, [rows, cols] row-major, dtype out_dtype (F32 or BF16).
+ *
+ * c2_hat_b = fp32(fp32(fp8(absmax_q_b) * scale2_g) + mu) (two roundings,
+ * no fused multiply-add), or absmax_b; w_hat = fp32(NF4[code] * c2_hat_b);
+ * bf16 output is w_hat rounded to nearest-even.
+ */
+int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, void* stream);
+
+/* ----------------------------------------------------------- linear layer */
+
+/*
+ * qlora_linear_fwd - QLoRA Eq. 5 with the adapter scale of Eq. 3:
+ *     Y = X * W_bf16^T + s * (X * A) * B
+ * where W_bf16 is exactly what qlora_nf4_dequantize writes as BF16.
+ *
+ *   X        device bf16 [M, K]; M >= 0 (M = 0 enqueues nothing).
+ *   W        host pointer to the descriptor of the frozen weight [N, K];
+ *            K % 64 == 0 and N % 64 == 0.
+ *   A        device bf16 [K, r]  (QLoRA L1).
+ *   B        device bf16 [r, N]  (QLoRA L2).
+ *   r        LoRA rank, 1 <= r <= QLORA_MAX_RANK.
+ *   s        adapter scale (alpha / r).
+ *   Y        device bf16 [M, N], written.
+ *   XA       device bf16 [M, r] or NULL; when given, receives X * A (fp32
+ *            accumulation rounded to bf16) for the backward.
+ *   ws       device workspace, ws_bytes >= the fwd figure of
+ *            qlora_linear_workspace.
+ * Products accumulate in fp32; the adapter term runs through bf16(s*X*A).
+ */
+int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W,
+                     const void* A, const void* B, int32_t r, float s,
+                     void* Y, void* XA, void* ws, int64_t ws_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd - gradients of qlora_linear_fwd for an upstream dY
+ * (QLoRA section 3 "QLoRA", paragraph after Eq. 6: only the adapter
+ * gradients are needed, not dE/dW, and the input gradient goes through the
+ * weight dequantised to BF16):
+ *     T  = dY * B^T
+ *     dX = dY * W_bf16 + s * T * A^T
+ *     dA = s * X^T * T
+ *     dB = s * XA^T * dY
+ *
+ *   dY       device bf16 [M, N].
+ *   X        device bf16 [M, K] (the forward input).
+ *   XA       device bf16 [M, r], as written by qlora_linear_fwd.
+ *   W, A, B, r, s, M   as for qlora_linear_fwd.
+ *   dX       device bf16 [M, K] or NULL (input gradient not wanted).
+ *   dA       device bf16 [K, r], written.
+ *   dB       device bf16 [r, N], written.
+ *   ws       device workspace, ws_bytes >= the bwd figure of
+ *            qlora_linear_workspace.
+ * With M = 0, dA and dB are set to zero.  Products accumulate in fp32; T
+ * enters the products as bf16(s * T).
+ */
+int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M,
+                     const qlora_nf4_t* W, const void* A, const void* B,
+                     int32_t r, float s, void* dX, void* dA, void* dB,
+                     void* ws, int64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, answers host queries, and rejects bad arguments on the
+host before anything is enqueued (the pointers passed here are never
+dereferenced because validation fails first)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_quantize_amd import binding as B
+from oracle import blockwise, codebook
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("qlora_nf4.h", "qlora_nf4_profile.h")]
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+FAKE_MIS = 0x10004      # misaligned
+
+
+def header_functions():
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qlora_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = B.lib()
+    names = header_functions()
+    assert len(names) == 11, names
+    assert sorted(B.EXPORTED) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_storage_bytes_match_closed_form():
+    for numel in (1, 63, 64, 65, 4096 * 4096, 11008 * 4096, 22016 * 8192):
+        for dq in (True, False):
+            got = B.qlora_nf4_storage_bytes(numel, dq)
+            want = blockwise.storage_bytes(numel, dq)
+            assert {k: v for k, v in got.items() if v} == want
+    numel = 4096 * 4096
+    bits = 8 * sum(B.qlora_nf4_storage_bytes(numel, True).values()) / numel
+    assert bits == 4 + 8 / 64 + 32 / (64 * 256) + 32 / numel
+
+
+def test_library_codebook_is_appendix_e():
+    assert np.array_equal(np.array(B.qlora_nf4_codebook(), np.float32).view(np.uint32),
+                          codebook.NF4.view(np.uint32))
+
+
+def test_status_strings():
+    L = B.lib()
+    for s in range(-5, 1):
+        assert L.qlora_status_string(s).decode()
+    assert L.qlora_status_string(-99).decode() == "unknown status"
+
+
+def _desc(rows=256, cols=256, dq=1, codes=FAKE, bs=64, bs2=256):
+    d = B.qlora_nf4_t()
+    d.rows, d.cols, d.blocksize, d.blocksize2, d.double_quant = rows, cols, bs, bs2, dq
+    d.codes, d.absmax_q, d.scale2, d.offset, d.absmax = codes, FAKE, FAKE, FAKE, FAKE
+    return d
+
+
+def _quant(d, w=FAKE, dtype=0, ws=FAKE, nws=1 << 30):
+    return B.lib().qlora_nf4_quantize(w, dtype, ctypes.byref(d) if d is not None else None, ws, nws, None)
+
+
+def test_quantize_validation():
+    L = B.lib()
+    assert _quant(None) == B.QLORA_ERR_INVALID_ARG
+    assert "descriptor" in L.qlora_last_error().decode()
+    assert _quant(_desc(bs=32)) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(bs2=128)) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(dq=2)) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(rows=-1)) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(rows=1 << 20, cols=1 << 20)) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(codes=None)) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(codes=FAKE_MIS)) == B.QLORA_ERR_MISALIGNED
+    assert _quant(_desc(), dtype=7) == B.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert _quant(_desc(), w=None) == B.QLORA_ERR_INVALID_ARG
+    assert _quant(_desc(), w=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert _quant(_desc(), nws=16) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert _quant(_desc(), ws=None) == B.QLORA_ERR_INVALID_ARG
+    d = _desc(dq=1)
+    d.offset = None
+    assert _quant(d) == B.QLORA_ERR_INVALID_ARG
+    d = _desc(dq=0)
+    d.absmax = None
+    assert _quant(d) == B.QLORA_ERR_INVALID_ARG
+    # an empty weight is a successful no-op
+    assert _quant(_desc(rows=0), w=None, ws=None, nws=0) == B.QLORA_OK
+
+
+def test_dequantize_validation():
+    L = B.lib()
+    d = _desc()
+    assert L.qlora_nf4_dequantize(ctypes.byref(d), FAKE, 5, None) == B.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert L.qlora_nf4_dequantize(ctypes.byref(d), None, 0, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_nf4_dequantize(ctypes.byref(d), FAKE_MIS, 0, None) == B.QLORA_ERR_MISALIGNED
+    assert L.qlora_nf4_dequantize(None, FAKE, 0, None) == B.QLORA_ERR_INVALID_ARG
+
+
+def test_workspace_queries():
+    assert B.qlora_nf4_quantize_workspace(4096 * 4096, False) == 0
+    assert B.qlora_nf4_quantize_workspace(4096 * 4096, True) >= 4 * 4096 * 4096 // 64
+    f, b = B.qlora_linear_workspace(4096, 4096, 4096, 64)
+    assert f >= 2 * 4096 * 64 * 3 and b >= 2 * 4096 * 64 * 3
+    with pytest.raises(B.QLoraError):
+        B.qlora_linear_workspace(16, 100, 256, 8)
+    with pytest.raises(B.QLoraError):
+        B.qlora_linear_workspace(16, 256, 256, 0)
+
+
+def _fwd(d, M=16, r=8, X=FAKE, A=FAKE, Bp=FAKE, Y=FAKE, XA=FAKE, ws=FAKE, nws=1 << 30):
+    return B.lib().qlora_linear_fwd(X, M, ctypes.byref(d), A, Bp, r, 2.0, Y, XA, ws, nws, None)
+
+
+def _bwd(d, M=16, r=8, dY=FAKE, X=FAKE, XA=FAKE, A=FAKE, Bp=FAKE, dX=FAKE, dA=FAKE, dB=FAKE, ws=FAKE, nws=1 << 30):
+    return B.lib().qlora_linear_bwd(dY, X, XA, M, ctypes.byref(d), A, Bp, r, 2.0, dX, dA, dB, ws, nws, None)
+
+
+def test_linear_validation():
+    assert _fwd(_desc(cols=200)) == B.QLORA_ERR_INVALID_ARG       # K % 64
+    assert _fwd(_desc(rows=100)) == B.QLORA_ERR_INVALID_ARG       # N % 64
+    assert _fwd(_desc(), r=0) == B.QLORA_ERR_INVALID_ARG
+    assert _fwd(_desc(), r=257) == B.QLORA_ERR_INVALID_ARG
+    assert _fwd(_desc(), M=-1) == B.QLORA_ERR_INVALID_ARG
+    assert _fwd(_desc(), X=None) == B.QLORA_ERR_INVALID_ARG
+    assert _fwd(_desc(), Y=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert _fwd(_desc(), XA=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert _fwd(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd(_desc(bs=128)) == B.QLORA_ERR_INVALID_ARG
+    # M = 0: nothing to compute, nothing enqueued
+    assert _fwd(_desc(), M=0, X=None, Y=None, ws=None, nws=0) == B.QLORA_OK
+    assert _bwd(_desc(cols=100)) == B.QLORA_ERR_INVALID_ARG
+    assert _bwd(_desc(), dA=None) == B.QLORA_ERR_INVALID_ARG
+    assert _bwd(_desc(), XA=None) == B.QLORA_ERR_INVALID_ARG
+    assert _bwd(_desc(), dX=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert _bwd(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert _bwd(_desc(), r=300) == B.QLORA_ERR_INVALID_ARG
+
+
+def test_profile_hook_validation():
+    L = B.lib()
+    assert L.qlora_profile_events(9, None, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_profile_events(0, FAKE, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_profile_events(0, None, None) == B.QLORA_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        B.qlora_nf4_quantize(torch.zeros(64))

@@ -1,0 +1,184 @@
+"""GPU parity: NF4 quantisation, double quantisation and dequantisation
+through the C ABI, bit-exact against the CPU oracle on the same inputs."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import blockwise, codebook
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_nf4_quantized_quantize_amd import binding
+    binding.lib()
+    return binding
+
+
+def _check_state(B, qw, st):
+    h = qw.host()
+    assert np.array_equal(h["codes"], st.packed), "packed codes differ"
+    if st.double_quant:
+        assert np.array_equal(h["absmax_q"], st.absmax_q), "FP8 constants differ"
+        assert np.array_equal(h["scale2"].view(np.uint32), st.scale2.view(np.uint32)), "scale2 differs"
+        assert h["offset"].view(np.uint32)[0] == np.array([st.mu], F32).view(np.uint32)[0], "mean differs"
+    else:
+        assert np.array_equal(h["absmax"].view(np.uint32), st.c2.view(np.uint32)), "absmax differs"
+
+
+def _check_dequant(B, qw, st):
+    ref = st.dequantize().reshape(-1)
+    out32 = B.qlora_nf4_dequantize(qw, torch.float32).reshape(-1).cpu().numpy()
+    assert np.array_equal(out32.view(np.uint32), ref.view(np.uint32)), "fp32 dequant differs"
+    out16 = B.qlora_nf4_dequantize(qw, torch.bfloat16).reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(out16, blockwise.bf16_bits(ref)), "bf16 dequant differs"
+
+
+def _roundtrip(B, w_t, dq):
+    """Quantise w_t on the GPU and compare everything with the oracle."""
+    w_np = w_t.float().cpu().numpy()
+    qw = B.qlora_nf4_quantize(w_t.cuda(), double_quant=dq)
+    torch.cuda.synchronize()
+    st = blockwise.quantize(w_np, double_quant=dq)
+    _check_state(B, qw, st)
+    _check_dequant(B, qw, st)
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_tiny_workload_weight(B, dq):
+    from bit_nf4_quantized_quantize_amd import synth
+    _log(f"quant tiny 256x256 dq={dq}")
+    w = synth.weight((256, 256), "normal", synth.seed_of(1, 0, "W"), "cuda")
+    _roundtrip(B, w, dq)
+
+
+@pytest.mark.parametrize("numel", [1, 3, 63, 64, 65, 127, 1000, 4097, 64 * 257 + 5, 64 * 256 * 3])
+@pytest.mark.parametrize("dq", [True, False])
+def test_ragged_sizes(B, numel, dq):
+    _log(f"quant ragged numel={numel} dq={dq}")
+    g = torch.Generator().manual_seed(numel)
+    w = torch.randn(numel, generator=g) * 0.02
+    _roundtrip(B, w, dq)
+
+
+def _special_blocks():
+    nf4 = codebook.NF4
+    q = [float(v) for v in nf4]
+    mids = [(q[i] + q[i + 1]) / 2 for i in range(15)]
+    blocks = []
+    blocks.append(np.zeros(64, F32))                                    # all-zero block
+    blocks.append(-np.zeros(64, F32))                                   # negative zeros
+    blocks.append(np.tile(nf4, 4).astype(F32))                          # codebook, absmax 1
+    blocks.append((np.tile(nf4, 4) * F32(0.25)).astype(F32))            # scaled by 2^-2
+    ties = np.array([mids[i] for i in (2, 6, 7, 9, 11, 13)], F32)       # exact fp32 midpoints
+    b = np.zeros(64, F32)
+    b[0] = 1.0
+    b[1:7] = ties
+    b[7:13] = -ties
+    b[13:19] = np.nextafter(ties, F32(2))
+    b[19:25] = np.nextafter(ties, F32(-2))
+    blocks.append(b)                                                     # ties -> lower code
+    blocks.append((np.linspace(-1, 1, 64) * 1e-40).astype(F32))         # subnormal block
+    blocks.append((np.linspace(-1, 1, 64) * 3e-38).astype(F32))         # near the normal edge
+    blocks.append((np.linspace(-3, 2, 64) * 1e30).astype(F32))          # huge
+    blocks.append(np.full(64, 7.0, F32))                                 # constant block
+    rng = np.random.default_rng(0)
+    blocks.append((rng.standard_t(3, 64) * 0.02).astype(F32))
+    return np.concatenate(blocks)
+
+
+@pytest.mark.parametrize("dq", [True, False])
+def test_special_values(B, dq):
+    _log(f"quant special blocks dq={dq}")
+    w = _special_blocks()
+    _roundtrip(B, torch.from_numpy(w), dq)
+    # the same blocks repeated over several 256-groups, with a ragged tail
+    rep = np.concatenate([w] * 60 + [w[:100]])
+    _roundtrip(B, torch.from_numpy(rep), dq)
+
+
+def test_bf16_input(B):
+    _log("quant bf16 input 512x1024")
+    g = torch.Generator().manual_seed(7)
+    w = (torch.randn(512, 1024, generator=g) * 0.02).to(torch.bfloat16)
+    _roundtrip(B, w, True)
+
+
+def test_shared_absmax_round_trip_exact(B):
+    _log("quant shared-absmax round trip")
+    block = np.tile(codebook.NF4, 4).astype(F32) * F32(0.125)
+    rng = np.random.default_rng(4)
+    w = np.concatenate([rng.permutation(block) for _ in range(700)]).astype(F32)
+    qw = B.qlora_nf4_quantize(torch.from_numpy(w).cuda(), double_quant=True)
+    out = B.qlora_nf4_dequantize(qw, torch.float32).reshape(-1).cpu().numpy()
+    assert np.array_equal(out, w)
+
+
+def test_attention_projection_full(B):
+    """7B attention projection 4096x4096, every code and constant."""
+    from bit_nf4_quantized_quantize_amd import synth
+    _log("quant 4096x4096 full")
+    w = synth.weight((4096, 4096), "normal", synth.seed_of(2, 0, "W"), "cuda")
+    _roundtrip(B, w, True)
+
+
+def test_65b_mlp_weight_sampled(B):
+    """65B-shaped 22016x8192 Student-t weight: all constants exactly, codes on
+    sampled blocks (every block is quantised independently)."""
+    from bit_nf4_quantized_quantize_amd import synth
+    _log("quant 22016x8192 t5 sampled")
+    w = synth.weight((22016, 8192), "t5", synth.seed_of(4, 0, "W"), "cuda")
+    qw = B.qlora_nf4_quantize(w, double_quant=True)
+    torch.cuda.synchronize()
+    w_np = w.cpu().numpy().reshape(-1, 64)
+    del w
+    c2 = blockwise.block_absmax(w_np.reshape(-1))
+    q, s2, mu = blockwise.double_quantize(c2)
+    h = qw.host()
+    assert np.array_equal(h["absmax_q"], q)
+    assert np.array_equal(h["scale2"].view(np.uint32), s2.view(np.uint32))
+    assert h["offset"][0] == mu
+    rng = np.random.default_rng(1)
+    sel = np.unique(np.concatenate([rng.integers(0, w_np.shape[0], 20000), [0, w_np.shape[0] - 1]]))
+    codes, _ = blockwise.quantize_nf4(w_np[sel].reshape(-1))
+    packed = blockwise.pack_nibbles(codes).reshape(-1, 32)
+    assert np.array_equal(h["codes"].reshape(-1, 32)[sel], packed)
+    # dequantised values of the sampled blocks
+    chat = blockwise.dq_reconstruct(q, s2, mu)[sel]
+    ref = blockwise.dequantize(codes, chat).reshape(-1, 64)
+    out = B.qlora_nf4_dequantize(qw, torch.float32).reshape(-1, 64)[torch.from_numpy(sel).cuda()].cpu().numpy()
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_nonfinite_input_is_defined(B):
+    """Non-finite weights give undefined codes, but the call completes and
+    codes stay in range."""
+    _log("quant non-finite input")
+    w = torch.randn(64 * 300) * 0.02
+    w[5] = float("inf")
+    w[70] = float("nan")
+    w[64 * 200 + 3] = -float("inf")
+    qw = B.qlora_nf4_quantize(w.cuda(), double_quant=True)
+    torch.cuda.synchronize()
+    h = qw.host()
+    assert h["codes"].size == w.numel() // 2
+
+
+def test_empty_weight(B):
+    _log("quant empty")
+    qw = B.qlora_nf4_quantize(torch.zeros(0, 64).cuda(), double_quant=True)
+    torch.cuda.synchronize()
+    assert qw.numel == 0
