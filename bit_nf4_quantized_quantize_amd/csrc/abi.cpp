@@ -101,32 +101,34 @@ int64_t quant_ws(int64_t numel, int dq) {
 }
 
 struct FwdWs {
-  int64_t at, bt, xas, total;  // byte offsets: A^T [r, K], B^T [N, rp], s*XA [M, rp]
+  int64_t part, xas, total;  // byte offsets: fp32 partials of X A, bf16 s*XA [M, rp]
+  int splits;
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = round_up(r, 64);
   FwdWs w;
-  w.at = 0;
-  w.bt = w.at + round_up(r * K * 2, kAlign);
-  w.xas = w.bt + round_up(N * rp * 2, kAlign);
+  w.splits = skinny_splits(M, r, K);
+  w.part = 0;
+  w.xas = w.part + round_up((int64_t)w.splits * M * rp * 4, kAlign);
   w.total = w.xas + round_up(M * rp * 2, kAlign);
+  (void)N;
   return w;
 }
 
 struct BwdWs {
-  int64_t ts, ap, xap, part, total;  // s*T [M, rp], A [K, rp], XA [M, rp], fp32 partials
-  int splits_a, splits_b;
+  int64_t part_t, ts, part, total;  // fp32 partials of dY B^T, bf16 s*T [M, rp], fp32 token partials
+  int splits_t, splits_a, splits_b;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = round_up(r, 64);
   BwdWs w;
-  w.splits_a = tn_splits(M, K, rp);
-  w.splits_b = tn_splits(M, rp, N);
-  const int64_t pa = (int64_t)w.splits_a * K * rp, pb = (int64_t)w.splits_b * rp * N;
-  w.ts = 0;
-  w.ap = w.ts + round_up(M * rp * 2, kAlign);
-  w.xap = w.ap + round_up(K * rp * 2, kAlign);
-  w.part = w.xap + round_up(M * rp * 2, kAlign);
+  w.splits_t = skinny_splits(M, r, N);
+  w.splits_a = tn_splits(M, K, r);
+  w.splits_b = tn_splits(M, r, N);
+  const int64_t pa = (int64_t)w.splits_a * K * r, pb = (int64_t)w.splits_b * r * N;
+  w.part_t = 0;
+  w.ts = w.part_t + round_up((int64_t)w.splits_t * M * rp * 4, kAlign);
+  w.part = w.ts + round_up(M * rp * 2, kAlign);
   w.total = w.part + round_up((pa > pb ? pa : pb) * 4, kAlign);
   return w;
 }
@@ -279,18 +281,17 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
   if ((st = check_ptr(ws, "ws", fn))) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* base = (char*)ws;
-  uint16_t* at = (uint16_t*)(base + L.at);
-  uint16_t* bt = (uint16_t*)(base + L.bt);
+  float* part = (float*)(base + L.part);
   uint16_t* xas = (uint16_t*)(base + L.xas);
   hipError_t e;
-  // A^T [r, K] (no padding: the NT product masks rows >= r)
-  if ((e = launch_transpose_pad((const uint16_t*)A, K, r, at, K, hs)) != hipSuccess) return hip_fail(e, fn);
-  if ((e = launch_transpose_pad((const uint16_t*)B, r, N, bt, rp, hs)) != hipSuccess) return hip_fail(e, fn);
-  if ((e = launch_gemm_nt((const uint16_t*)X, at, M, r, K, (uint16_t*)XA, xas, rp, s, hs)) != hipSuccess)
+  // XA = X A [M, r]: bf16 copy for the backward, bf16(s XA) padded to rp for the adapter steps
+  if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, (uint16_t*)XA, xas, rp,
+                         s, hs)) != hipSuccess)
     return hip_fail(e, fn);
   {
     ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
-    e = launch_fwd_main((const uint16_t*)X, M, K, W->codes, dq_params(W), N, xas, bt, rp, (uint16_t*)Y, hs);
+    e = launch_fwd_main((const uint16_t*)X, M, K, W->codes, dq_params(W), N, xas, (const uint16_t*)B, r, rp,
+                        (uint16_t*)Y, hs);
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
@@ -319,29 +320,28 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, c
   if (ws_bytes < L.total) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)L.total);
   if ((st = check_ptr(ws, "ws", fn))) return st;
   char* base = (char*)ws;
+  float* part_t = (float*)(base + L.part_t);
   uint16_t* ts = (uint16_t*)(base + L.ts);
-  uint16_t* ap = (uint16_t*)(base + L.ap);
-  uint16_t* xap = (uint16_t*)(base + L.xap);
   float* part = (float*)(base + L.part);
   // s*T = s * dY B^T  [M, rp]
-  if ((e = launch_gemm_nt((const uint16_t*)dY, (const uint16_t*)B, M, r, N, nullptr, ts, rp, s, hs)) != hipSuccess)
+  if ((e = launch_skinny((const uint16_t*)dY, (const uint16_t*)B, false, M, r, N, part_t, L.splits_t, nullptr, ts, rp,
+                         s, hs)) != hipSuccess)
     return hip_fail(e, fn);
-  if ((e = launch_pad_copy((const uint16_t*)A, K, r, ap, rp, hs)) != hipSuccess) return hip_fail(e, fn);
-  if ((e = launch_pad_copy((const uint16_t*)XA, M, r, xap, rp, hs)) != hipSuccess) return hip_fail(e, fn);
   if (dX) {
     {
       ProfScope ps(QLORA_KERNEL_BWD_DX, hs);
-      e = launch_bwd_dx((const uint16_t*)dY, M, N, W->codes, dq_params(W), K, ts, ap, rp, (uint16_t*)dX, hs);
+      e = launch_bwd_dx((const uint16_t*)dY, M, N, W->codes, dq_params(W), K, ts, (const uint16_t*)A, r, rp,
+                        (uint16_t*)dX, hs);
     }
     if (e != hipSuccess) return hip_fail(e, fn);
   }
   // dA = X^T (s T)   [K, r]
-  if ((e = launch_gemm_tn((const uint16_t*)X, ts, M, K, rp, part, L.splits_a, (uint16_t*)dA, K, r, 1.0f, hs)) !=
+  if ((e = launch_gemm_tn((const uint16_t*)X, K, K, ts, rp, r, M, part, L.splits_a, (uint16_t*)dA, 1.0f, hs)) !=
       hipSuccess)
     return hip_fail(e, fn);
   // dB = s XA^T dY   [r, N]
-  if ((e = launch_gemm_tn(xap, (const uint16_t*)dY, M, rp, N, part, L.splits_b, (uint16_t*)dB, r, N, s, hs)) !=
-      hipSuccess)
+  if ((e = launch_gemm_tn((const uint16_t*)XA, r, r, (const uint16_t*)dY, N, N, M, part, L.splits_b, (uint16_t*)dB, s,
+                          hs)) != hipSuccess)
     return hip_fail(e, fn);
   return QLORA_OK;
 }

@@ -62,6 +62,73 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// ------------------------------------------------- byte permute (v_perm_b32)
+// Result byte i = byte sel_i of the 64-bit value {s0:s1} (s1 = bytes 0..3);
+// selector 12 gives 0x00 and 13..15 give 0xFF (8..11, sign replication, are
+// not used here).  The host version exists so the lookup below can be
+// checked on the CPU.
+__host__ __device__ __forceinline__ uint32_t perm_b32(uint32_t s0, uint32_t s1, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_perm(s0, s1, sel);
+#else
+  const uint64_t v = ((uint64_t)s0 << 32) | s1;
+  uint32_t out = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t sb = (sel >> (8 * i)) & 0xFF;
+    uint32_t b;
+    if (sb < 8) b = (uint32_t)(v >> (8 * sb)) & 0xFF;
+    else if (sb == 12) b = 0;
+    else b = 0xFF;
+    out |= b << (8 * i);
+  }
+  return out;
+#endif
+}
+
+// ------------------------------------------- per-block bf16 lookup table
+// One NF4 block shares one constant c, so its 16 possible bf16 values
+// bf16(NF4[i] * c) form a table.  The table is kept as two 16-byte planes
+// (low and high bytes of each bf16), four registers each; v_perm_b32 then
+// looks up four codes per instruction from one half-plane, and a bitfield
+// select on code bit 3 picks the half.  Values are exactly those of the
+// dequantisation kernel: fp32 product, nearest-even bf16.
+struct BlockLUT {
+  uint32_t lo[4], hi[4];
+};
+
+// p[j] = bf16(v[2j]) | bf16(v[2j+1]) << 16 for the 16 table values v.
+__host__ __device__ __forceinline__ BlockLUT make_lut(const uint32_t p[8]) {
+  BlockLUT t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = perm_b32(p[2 * q + 1], p[2 * q], 0x06040200u);
+    t.hi[q] = perm_b32(p[2 * q + 1], p[2 * q], 0x07050301u);
+  }
+  return t;
+}
+
+// Eight codes of one 32-bit word (element 0 in the low nibble) -> eight bf16
+// in element order, as four 32-bit words.
+__host__ __device__ __forceinline__ void lut_lookup8(const BlockLUT& t, uint32_t w, uint32_t out[4]) {
+  const uint32_t e7 = w & 0x07070707u;                 // even elements, code & 7
+  const uint32_t o7 = (w >> 4) & 0x07070707u;          // odd elements
+  const uint32_t t3 = w >> 3;
+  const uint32_t me = (t3 & 0x01010101u) * 0xFFu;       // 0xFF where code >= 8
+  const uint32_t mo = ((t3 >> 4) & 0x01010101u) * 0xFFu;
+  const uint32_t loE = (me & perm_b32(t.lo[3], t.lo[2], e7)) | (~me & perm_b32(t.lo[1], t.lo[0], e7));
+  const uint32_t hiE = (me & perm_b32(t.hi[3], t.hi[2], e7)) | (~me & perm_b32(t.hi[1], t.hi[0], e7));
+  const uint32_t loO = (mo & perm_b32(t.lo[3], t.lo[2], o7)) | (~mo & perm_b32(t.lo[1], t.lo[0], o7));
+  const uint32_t hiO = (mo & perm_b32(t.hi[3], t.hi[2], o7)) | (~mo & perm_b32(t.hi[1], t.hi[0], o7));
+  const uint32_t e01 = perm_b32(hiE, loE, 0x05010400u);  // bf16 of elements 0, 2
+  const uint32_t o01 = perm_b32(hiO, loO, 0x05010400u);  // elements 1, 3
+  const uint32_t e23 = perm_b32(hiE, loE, 0x07030602u);  // elements 4, 6
+  const uint32_t o23 = perm_b32(hiO, loO, 0x07030602u);  // elements 5, 7
+  out[0] = perm_b32(o01, e01, 0x05040100u);
+  out[1] = perm_b32(o01, e01, 0x07060302u);
+  out[2] = perm_b32(o23, e23, 0x05040100u);
+  out[3] = perm_b32(o23, e23, 0x07060302u);
+}
+
 // --------------------------------------------------------- wave reductions
 
 // Max over each row of 16 lanes (every lane of the row gets the result).
@@ -91,58 +158,50 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// ------------------------------------------------------------- MFMA tile
-// Block tile 128 x 128, k-step 64, 256 threads = 4 waves in a 2 x 2 grid,
-// each wave 64 x 64 = 2 x 2 MFMA 32x32x16 bf16 tiles.
-//
+// ------------------------------------------------------- MFMA fragments
 // v_mfma_f32_32x32x16_bf16 operand layout (lane l of 64):
 //   A (32 x 16): row l % 32, k = 8 * (l / 32) .. +7
 //   B (16 x 32): col l % 32, k = 8 * (l / 32) .. +7
 //   D (32 x 32): col l % 32, register j -> row 8*(j/4) + 4*(l/32) + j%4
-// Both LDS tiles hold 8 consecutive k per row segment ("k-contiguous"), so
-// an operand fragment is one 16-byte LDS read.
-constexpr int TM = 128, TN = 128, TK = 64;
-constexpr int LDK = TK + 8;  // row pitch in bf16: 144 B keeps 8-lane groups conflict-free
+// Both operands want 8 consecutive reduction indices per lane.  Tiles in LDS
+// come in two orders:
+//   KC  [rows][red]  reduction contiguous: a fragment is one 16-byte read;
+//   RC  [red][rows]  rows contiguous: a fragment is two ds_read_b64_tr_b16.
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group receives
+// element (i & 3) of the 8-byte chunk read by lane 4j + (i >> 2), for
+// j = 0..3.  Pointing lane q of the group at reduction row base + q/4,
+// column c0 + 4*(q%4) therefore hands lane q the four reduction values
+// base..base+3 of column c0 + q.
 
-struct Acc22 {
-  floatx16 c[2][2];
-};
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-__device__ __forceinline__ void acc_zero(Acc22& a) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a.c[i][j][r] = 0.0f;
+__device__ __forceinline__ bf16x8 frag_kc(const __bf16* s, int pitch, int r0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(s + (r0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
 }
 
-__device__ __forceinline__ void mma_128x128x64(const __bf16* sA, const __bf16* sB, Acc22& acc,
-                                               int wm, int wn, int lane) {
-  const int lr = lane & 31, lk = 8 * (lane >> 5);
-#pragma unroll
-  for (int kk = 0; kk < TK; kk += 16) {
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 32 + lr) * LDK + kk + lk);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + j * 32 + lr) * LDK + kk + lk);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
-  }
+__device__ __forceinline__ short4_t ds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((__attribute__((address_space(3))) __bf16*)p));
 }
 
-// Row / column of accumulator element (i, j, reg) for a lane.
-__device__ __forceinline__ int acc_row(int wm, int i, int reg, int lane) {
-  return wm * 64 + i * 32 + 8 * (reg >> 2) + 4 * (lane >> 5) + (reg & 3);
+__device__ __forceinline__ bf16x8 frag_rc(const __bf16* s, int pitch, int r0, int k0, int lane) {
+  const int g = lane >> 4, q = lane & 15;
+  const int col = r0 + 16 * (g & 1) + 4 * (q & 3);
+  const int red = k0 + 8 * (g >> 1) + (q >> 2);
+  const short4_t lo = ds_read_tr16(s + red * pitch + col);
+  const short4_t hi = ds_read_tr16(s + (red + 4) * pitch + col);
+  const short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * 64 + j * 32 + (lane & 31);
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of accumulator register j of a 32x32 tile for a lane (column: lane % 32).
+__device__ __forceinline__ int acc_row32(int j, int lane) {
+  return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
 }
 
 }  // namespace qlora

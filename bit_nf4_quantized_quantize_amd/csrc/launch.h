@@ -46,30 +46,29 @@ struct DQParams {
 };
 
 // Linear-layer building blocks (all bf16 matrices row-major).
-hipError_t launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst,
-                           int64_t cols_pad, hipStream_t stream);
-hipError_t launch_transpose_pad(const uint16_t* src, int64_t src_rows, int64_t src_cols,
-                                uint16_t* dst, int64_t cols_pad, hipStream_t stream);
-// C[M, Q] = U[M, L] * V[Q, L]^T; out1 (ld1 = Q, optional) = bf16(C),
-// out2 (ld2) = bf16(alpha * C) with zeros in columns [Q, ld2).
-hipError_t launch_gemm_nt(const uint16_t* U, const uint16_t* V, int64_t M, int64_t Q, int64_t L,
-                          uint16_t* out1, uint16_t* out2, int64_t ld2, float alpha,
-                          hipStream_t stream);
-// Fused forward: Y = X * What^T + XAs * Bt^T (XAs [M, rp], Bt [N, rp]).
+//
+// Skinny product C[M, Q] = U[M, L] * V, V either [L, Q] (v_is_lq) or
+// [Q, L]; the reduction is split into `splits` chunks of fp32 partials
+// part[splits][M][QP], then out1 [M, Q] = bf16(C) (optional) and
+// out2 [M, QP] = bf16(alpha * C), zero in columns [Q, QP).
+int skinny_splits(int64_t M, int64_t Q, int64_t L);
+hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
+                         float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
+                         hipStream_t stream);
+// Fused forward: Y = X * W_bf16^T + XAs * B_pad (XAs [M, rp]; B [r, N], rows >= r as zero).
 hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
-                           const DQParams& dq, int64_t N, const uint16_t* XAs, const uint16_t* Bt,
-                           int64_t rp, uint16_t* Y, hipStream_t stream);
-// Fused input gradient: dX = dY * What + Ts * Ap^T (Ts [M, rp], Ap [K, rp]).
+                           const DQParams& dq, int64_t N, const uint16_t* XAs, const uint16_t* B,
+                           int64_t r, int64_t rp, uint16_t* Y, hipStream_t stream);
+// Fused input gradient: dX = dY * W_bf16 + Ts * A_pad^T (Ts [M, rp]; A [K, r]).
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
-                         const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* Ap,
-                         int64_t rp, uint16_t* dX, hipStream_t stream);
-// Split-M reduction C[P, Q] = U[M, P]^T * V[M, Q]: fp32 partials then
-// out (bf16 [P, Q]) = bf16(alpha * sum of partials).
+                         const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* A,
+                         int64_t r, int64_t rp, uint16_t* dX, hipStream_t stream);
+// Token reduction C[P, Q] = U[M, P]^T * V[M, Q] (leading dimensions ldu, ldv):
+// fp32 partials [splits][P][Q] then out [P, Q] = bf16(alpha * sum).
 int tn_splits(int64_t M, int64_t P, int64_t Q);
-// Only out[p][q] for p < Pout, q < Qout (ld Qout) is written.
-hipError_t launch_gemm_tn(const uint16_t* U, const uint16_t* V, int64_t M, int64_t P, int64_t Q,
-                          float* partials, int splits, uint16_t* out, int64_t Pout, int64_t Qout,
-                          float alpha, hipStream_t stream);
+hipError_t launch_gemm_tn(const uint16_t* U, int64_t ldu, int64_t P, const uint16_t* V, int64_t ldv,
+                          int64_t Q, int64_t M, float* partials, int splits, uint16_t* out, float alpha,
+                          hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);
 
 }  // namespace qlora

@@ -7,13 +7,25 @@
 //   section 3 "QLoRA", paragraph after Eq. 6: only the adapter gradients are
 //     computed (no dE/dW); the input gradient goes through the BF16 weight.
 //
-// The weight is [N, K] = [out, in] with 64-element NF4 blocks along K.  The
-// two large products (Y = X W^T and dX = dY W) dequantise W tile by tile into
-// LDS and run bf16 MFMA 32x32x16 with fp32 accumulation; the rank-r adapter
-// terms ride along as extra reduction steps over zero-padded bf16 operands:
-//   Y  = [X | s XA] [W ; B^T]^T        (reduction K + r)
-//   dX = [dY | s T] [W ; A^T]          (reduction N + r)
-// The skinny adapter products (XA, T, dA, dB) use the same MFMA tile.
+// The weight is [N, K] = [out, in] with 64-element NF4 blocks along K.
+//
+// Main products (bf16 MFMA 32x32x16, fp32 accumulation), 256 threads as a
+// 2 x 2 grid of waves over a BM x BN output tile, k-step 64, two LDS stages:
+//   forward  Y [M, N]  = X [M, K] W^T     + (s XA) [M, rp] B [rp, N]
+//   backward dX [M, K] = dY [M, N] W      + (s T) [M, rp] A^T
+// Each k-step stages the activation tile (X or dY) and dequantises the
+// weight tile: a thread expands whole NF4 blocks through a per-block bf16
+// lookup table (the exact bf16(NF4[code] * c2_hat) values) into LDS.  The
+// forward tile is [n][k] (reduction contiguous); the backward tile is the
+// same natural [n][k] layout, read through LDS transpose loads because there
+// the reduction runs over n.  The rank-r adapter term is r_pad/64 extra
+// reduction steps over bf16 operands (rows of B / A beyond r read as zero).
+//
+// Adapter products: XA = X A and T = dY B^T are skinny (r columns): split
+// over the reduction into fp32 partials, then one pass writes bf16 XA and
+// bf16(s XA) (zero-padded to r_pad).  dA = X^T (s T) and dB = s XA^T dY
+// reduce over tokens: split over M into fp32 partials, then one reduction
+// pass; both operands are read through LDS transpose loads.
 #include "device.h"
 #include "launch.h"
 
@@ -21,315 +33,430 @@ namespace qlora {
 
 namespace {
 
-constexpr int NT = 256;  // threads per workgroup for every GEMM kernel here
+constexpr int NT = 256;
+constexpr int PK = 72;  // pitch (bf16) of a [rows][64] reduction-contiguous tile
 
-// NF4 value of a code times the block constant, in fp32 (Eq. 6 outer
-// dequant); contraction is irrelevant here (one multiply).
-__device__ __forceinline__ float block_scale(const DQParams& dq, int64_t blk, float mu) {
-  if (dq.double_quant) {
-    const float prod = __fmul_rn(e4m3_decode(dq.absmax_q[blk]), dq.scale2[blk >> 8]);
-    return __fadd_rn(prod, mu);  // two roundings, never fused
-  }
-  return dq.absmax[blk];
+// Appendix E of QLoRA as immediates for the lookup-table build.
+constexpr float kNF4c[16] = {
+    -1.0f, -0.6961928009986877f, -0.5250730514526367f, -0.39491748809814453f,
+    -0.28444138169288635f, -0.18477343022823334f, -0.09105003625154495f, 0.0f,
+    0.07958029955625534f, 0.16093020141124725f, 0.24611230194568634f, 0.33791524171829224f,
+    0.44070982933044434f, 0.5626170039176941f, 0.7229568362236023f, 1.0f};
+
+// c2_hat of one block (Eq. 6 inner dequant): two separately rounded fp32
+// operations for double quantisation, or the stored absmax.
+// `f` is the group's scale2 with double quantisation, else the block absmax.
+__device__ __forceinline__ float block_scale(const DQParams& dq, uint32_t qbyte, float f, float mu) {
+  if (dq.double_quant) return __fadd_rn(__fmul_rn(e4m3_decode(qbyte), f), mu);
+  return f;
 }
 
-// 16 bytes of bf16 from global (zero when out of range).
-__device__ __forceinline__ uint4 ld16(const uint16_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-}
-__device__ __forceinline__ void st16(__bf16* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
-
-// Stage a 128 x 64 bf16 tile of a row-major matrix (rows r0.., cols c0..)
-// into LDS [128][LDK]; rows >= nrows read as zero.  Two threads per row.
-__device__ __forceinline__ void stage_rows(__bf16* s, const uint16_t* g, int64_t ld, int64_t r0,
-                                           int64_t nrows, int64_t c0, int tid) {
-  const int row = tid >> 1, half = tid & 1;
-  const bool ok = r0 + row < nrows;
-  const uint16_t* src = g + (ok ? (r0 + row) * ld + c0 + half * 32 : 0);
+__device__ __forceinline__ BlockLUT lut_for(float c) {
+  uint32_t p[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st16(s + row * LDK + half * 32 + i * 8, ld16(src + i * 8, ok));
+  for (int j = 0; j < 8; ++j) p[j] = pack_bf2(kNF4c[2 * j] * c, kNF4c[2 * j + 1] * c);
+  return make_lut(p);
 }
 
-// Expand 8 NF4 codes (one 32-bit word, element 0 in the low nibble) into 8
-// bf16 values of NF4[code] * c, rounded to nearest-even.
-__device__ __forceinline__ uint4 dequant8(uint32_t w, float c, const float* nf4) {
-  uint4 o;
-  o.x = pack_bf2(nf4[w & 0xF] * c, nf4[(w >> 4) & 0xF] * c);
-  o.y = pack_bf2(nf4[(w >> 8) & 0xF] * c, nf4[(w >> 12) & 0xF] * c);
-  o.z = pack_bf2(nf4[(w >> 16) & 0xF] * c, nf4[(w >> 20) & 0xF] * c);
-  o.w = pack_bf2(nf4[(w >> 24) & 0xF] * c, nf4[(w >> 28) & 0xF] * c);
-  return o;
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void sts16(__bf16* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// 8 bf16 of row `row` of a row-major [rows, cols] matrix starting at column
+// c, zero where row >= rows or column >= cols.  Vector load when the whole
+// chunk is inside and 16-byte aligned (cols % 8 == 0), else element-wise.
+__device__ __forceinline__ uint4 load8_masked(const uint16_t* g, int64_t ld, int64_t row, int64_t rows, int64_t c,
+                                              int64_t cols) {
+  if (row >= rows || c >= cols) return make_uint4(0, 0, 0, 0);
+  const uint16_t* p = g + row * ld + c;
+  if ((ld & 7) == 0 && c + 8 <= cols) return ldg16(p);
+  const int64_t n = cols - c;  // 1..7 valid elements, or an unaligned row
+  auto h = [&](int e) -> uint32_t { return e < n ? (uint32_t)p[e] : 0u; };
+  return make_uint4(h(0) | (h(1) << 16), h(2) | (h(3) << 16), h(4) | (h(5) << 16), h(6) | (h(7) << 16));
 }
 
-// ----------------------------------------------------- forward main GEMM
-// Tile 128 (M) x 128 (N); per k-step of 64 the weight tile is 128 rows of one
-// NF4 block each.  Two threads per weight row, 32 codes (16 bytes) each.
-__global__ __launch_bounds__(NT) void fwd_main_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                      const uint8_t* __restrict__ codes, DQParams dq, int64_t N,
-                                                      const uint16_t* __restrict__ XAs,
-                                                      const uint16_t* __restrict__ Bt, int64_t rp,
-                                                      uint16_t* __restrict__ Y, NF4Values nf4v) {
-  __shared__ __bf16 sA[TM * LDK];
-  __shared__ __bf16 sB[TN * LDK];
-  __shared__ float s_nf4[16];
+// ============================================================ main GEMM
+struct MainArgs {
+  const uint16_t* act;      // X [M, K] (fwd) or dY [M, N] (bwd)
+  int64_t M, L;             // rows of act, reduction length (K fwd, N bwd)
+  const uint8_t* codes;     // weight [Nw, Kw], packed NF4
+  DQParams dq;
+  int64_t Nw, Kw;
+  const uint16_t* ext_act;  // s*XA or s*T  [M, rp]
+  const uint16_t* ext_w;    // B [r, Nw] (fwd) or A [Kw, r] (bwd)
+  int64_t r, rp;
+  uint16_t* out;            // [M, ncols]
+  int64_t ncols;            // Nw (fwd) or Kw (bwd)
+};
+
+template <int BM, int BN, bool BWD>
+struct MainCfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
+  static constexpr int TMW = WM / 32, TNW = WN / 32;   // 32x32 MFMA tiles per wave
+  static constexpr int PRC = BN + 16;                  // pitch of a [64][BN] tile
+  static constexpr int SA = BM * PK;
+  static constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
+  static constexpr int XCH = BM * 8 / NT;              // 16-byte activation chunks per thread
+  static constexpr int DQE = BN * 64 / NT;             // weights dequantised per thread per step
+  static constexpr int DQW = DQE / 8;                  // 32-bit code words per thread
+  static constexpr int ECH = BN * 8 / NT;              // 16-byte ext-weight chunks per thread
+  static_assert(DQE == 32 || DQE == 64, "tile");
+};
+
+template <int BM, int BN, bool BWD>
+__global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
+  using C = MainCfg<BM, BN, BWD>;
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][C::SA];
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][C::SB];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
-  if (tid < 16) s_nf4[tid] = nf4v.v[tid];
-  const float mu = dq.double_quant ? *dq.offset : 0.0f;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
+  const float mu = a.dq.double_quant ? *a.dq.offset : 0.0f;
+  const int64_t kblocks = a.Kw >> 6;
+  const int64_t nk = a.L >> 6;
+
+  // --- dequantisation task of this thread (DQE consecutive weights of one block)
+  int t_row, t_col;
+  if (!BWD) {  // tile [BN rows n][64 k]
+    constexpr int TPR = 64 / C::DQE;
+    t_row = tid / TPR;
+    t_col = (tid % TPR) * C::DQE;
+  } else {     // tile [64 rows n][BN k]
+    constexpr int TPR = BN / C::DQE;
+    t_row = tid / TPR;
+    t_col = (tid % TPR) * C::DQE;
+  }
+  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
+
+  floatx16 acc[C::TMW][C::TNW];
+#pragma unroll
+  for (int i = 0; i < C::TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TNW; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  uint4 xr[C::XCH];
+  uint32_t cw[C::DQW];
+  uint32_t qb = 0;
+  float sf = 0.0f;  // scale2 of the group (double quantisation) or the block absmax
+
+  auto load_step = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < C::XCH; ++i) {
+      const int id = tid + NT * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row;
+      xr[i] = (m < a.M) ? ldg16(a.act + m * a.L + kt * 64 + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+    const int64_t n = BWD ? kt * 64 + t_row : c0 + t_row;
+    const int64_t k = BWD ? c0 + t_col : kt * 64 + t_col;
+    if (t_ok) {
+      const uint8_t* src = a.codes + ((n * a.Kw + k) >> 1);
+#pragma unroll
+      for (int w = 0; w < C::DQW; w += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * w);
+        cw[w] = v.x; cw[w + 1] = v.y; cw[w + 2] = v.z; cw[w + 3] = v.w;
+      }
+      const int64_t blk = n * kblocks + (k >> 6);
+      if (a.dq.double_quant) qb = a.dq.absmax_q[blk];
+      sf = a.dq.double_quant ? a.dq.scale2[blk >> 8] : a.dq.absmax[blk];
+    } else {
+#pragma unroll
+      for (int w = 0; w < C::DQW; ++w) cw[w] = 0x77777777u;  // code 7 = 0.0
+      qb = 0; sf = 0.0f;
+    }
+  };
+
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::XCH; ++i) {
+      const int id = tid + NT * i, row = id >> 3, ch = id & 7;
+      sts16(&sA[buf][row * PK + ch * 8], xr[i]);
+    }
+    const float c = t_ok ? block_scale(a.dq, qb, sf, mu) : 0.0f;
+    const BlockLUT lut = lut_for(c);
+    __bf16* dst = BWD ? &sB[buf][t_row * C::PRC + t_col] : &sB[buf][t_row * PK + t_col];
+#pragma unroll
+    for (int w = 0; w < C::DQW; ++w) {
+      uint32_t o[4];
+      lut_lookup8(lut, cw[w], o);
+      sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  };
+
+  auto mma_step = [&](int buf, bool b_rc, int pitch_b) {
+#pragma unroll
+    for (int kk = 0; kk < 64; kk += 16) {
+      bf16x8 af[C::TMW], bfr[C::TNW];
+#pragma unroll
+      for (int i = 0; i < C::TMW; ++i) af[i] = frag_kc(sA[buf], PK, wm * C::WM + 32 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < C::TNW; ++j)
+        bfr[j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * C::WN + 32 * j, kk, lane)
+                      : frag_kc(sB[buf], pitch_b, wn * C::WN + 32 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < C::TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TNW; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // ---- main reduction over the quantised weight, two LDS stages
+  load_step(0);
+  store_step(0);
   __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt & 1);
+    if (kt + 1 < nk) load_step(kt + 1);
+    mma_step(cur, BWD, BWD ? C::PRC : PK);
+    if (kt + 1 < nk) store_step(cur ^ 1);
+    __syncthreads();
+  }
 
-  Acc22 acc;
-  acc_zero(acc);
-  const int wrow = tid >> 1, whalf = tid & 1;
-  const int64_t n = n0 + wrow;
-  const bool nok = n < N;
-  const int64_t kblocks = K >> 6;
-
-  for (int64_t kt = 0; kt < kblocks; ++kt) {
-    stage_rows(sA, X, K, m0, M, kt * 64, tid);
-    {
-      uint4 cw = make_uint4(0, 0, 0, 0);
-      float c = 0.0f;
-      if (nok) {
-        cw = *reinterpret_cast<const uint4*>(codes + ((n * K + kt * 64 + whalf * 32) >> 1));
-        c = block_scale(dq, n * kblocks + kt, mu);
-      }
-      __bf16* dst = sB + wrow * LDK + whalf * 32;
-      st16(dst + 0, dequant8(cw.x, c, s_nf4));
-      st16(dst + 8, dequant8(cw.y, c, s_nf4));
-      st16(dst + 16, dequant8(cw.z, c, s_nf4));
-      st16(dst + 24, dequant8(cw.w, c, s_nf4));
+  // ---- adapter term: rp/64 extra reduction steps over bf16 operands
+  for (int64_t jt = 0; jt < a.rp; jt += 64) {
+#pragma unroll
+    for (int i = 0; i < C::XCH; ++i) {
+      const int id = tid + NT * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row;
+      sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
     }
-    __syncthreads();
-    mma_128x128x64(sA, sB, acc, wm, wn, lane);
-    __syncthreads();
-  }
-  for (int64_t jt = 0; jt < rp; jt += 64) {
-    stage_rows(sA, XAs, rp, m0, M, jt, tid);
-    stage_rows(sB, Bt, rp, n0, N, jt, tid);
-    __syncthreads();
-    mma_128x128x64(sA, sB, acc, wm, wn, lane);
-    __syncthreads();
-  }
+    if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < C::ECH; ++i) {
+        const int id = tid + NT * i, row = id / (BN / 8), ch = id % (BN / 8);
+        sts16(&sB[0][row * C::PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
+      }
+    } else {     // A [Kw, r]: tile [BN k][64 j]
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + acc_col(wn, j, lane);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + acc_row(wm, i, r, lane);
-        if (row < M && col < N) Y[row * N + col] = f2bf(acc.c[i][j][r]);
+      for (int i = 0; i < C::ECH; ++i) {
+        const int id = tid + NT * i, row = id >> 3, ch = id & 7;
+        sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
       }
     }
-}
-
-// ------------------------------------------------- input-gradient GEMM
-// dX[m, k] = sum_n dY[m, n] W[n, k].  Tile 128 (M) x 128 (K); per step of 64
-// rows n the weight tile covers two NF4 blocks per row.  Four threads per
-// row, 32 codes each, written transposed into LDS as [k][n].
-__global__ __launch_bounds__(NT) void bwd_dx_kernel(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
-                                                    const uint8_t* __restrict__ codes, DQParams dq, int64_t K,
-                                                    const uint16_t* __restrict__ Ts,
-                                                    const uint16_t* __restrict__ Ap, int64_t rp,
-                                                    uint16_t* __restrict__ dX, NF4Values nf4v) {
-  __shared__ __bf16 sA[TM * LDK];
-  __shared__ __bf16 sB[TN * LDK];
-  __shared__ float s_nf4[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * TM, k0 = (int64_t)blockIdx.x * TN;
-  if (tid < 16) s_nf4[tid] = nf4v.v[tid];
-  const float mu = dq.double_quant ? *dq.offset : 0.0f;
-  __syncthreads();
-
-  Acc22 acc;
-  acc_zero(acc);
-  const int nrow = tid >> 2, quarter = tid & 3;
-  const int64_t kcol = k0 + quarter * 32;
-  const bool kok = kcol < K;
-  const int64_t kblocks = K >> 6;
-
-  for (int64_t nt = 0; nt < N; nt += 64) {
-    stage_rows(sA, dY, N, m0, M, nt, tid);
-    {
-      const int64_t n = nt + nrow;
-      uint4 cw = make_uint4(0, 0, 0, 0);
-      float c = 0.0f;
-      if (kok) {
-        cw = *reinterpret_cast<const uint4*>(codes + ((n * K + kcol) >> 1));
-        c = block_scale(dq, n * kblocks + (kcol >> 6), mu);
-      }
-      const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = s_nf4[(words[wv] >> (4 * e)) & 0xF] * c;
-          sB[(quarter * 32 + wv * 8 + e) * LDK + nrow] = (__bf16)v;
-        }
-    }
     __syncthreads();
-    mma_128x128x64(sA, sB, acc, wm, wn, lane);
+    mma_step(0, !BWD, BWD ? PK : C::PRC);
     __syncthreads();
   }
-  for (int64_t jt = 0; jt < rp; jt += 64) {
-    stage_rows(sA, Ts, rp, m0, M, jt, tid);
-    stage_rows(sB, Ap, rp, k0, K, jt, tid);
-    __syncthreads();
-    mma_128x128x64(sA, sB, acc, wm, wn, lane);
-    __syncthreads();
-  }
+
+  // ---- epilogue: bf16 output
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::TMW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = k0 + acc_col(wn, j, lane);
+    for (int j = 0; j < C::TNW; ++j) {
+      const int64_t col = c0 + wn * C::WN + 32 * j + (lane & 31);
+      if (col >= a.ncols) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + acc_row(wm, i, r, lane);
-        if (row < M && col < K) dX[row * K + col] = f2bf(acc.c[i][j][r]);
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * C::WM + 32 * i + acc_row32(e, lane);
+        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
       }
     }
 }
 
-// ------------------------------------------------------- NT small GEMM
-// C[M, Q] = U[M, L] V[Q, L]^T, L % 64 == 0.  Used for XA = X (A^T)^T and
-// T = dY B^T.  Epilogue: out1 = bf16(C) (ld Q), out2 = bf16(alpha C) (ld ld2,
-// zero in columns [Q, ld2)).
-__global__ __launch_bounds__(NT) void gemm_nt_kernel(const uint16_t* __restrict__ U, const uint16_t* __restrict__ V,
-                                                     int64_t M, int64_t Q, int64_t L, uint16_t* __restrict__ out1,
-                                                     uint16_t* __restrict__ out2, int64_t ld2, float alpha) {
-  __shared__ __bf16 sA[TM * LDK];
-  __shared__ __bf16 sB[TN * LDK];
+// ====================================================== skinny products
+// part[s][m][q] = sum over the s-th reduction chunk of U[m, l] * V(l, q),
+// tile 64 (M) x 64 (Q), waves 2 x 2 of one 32x32 MFMA tile each, 128
+// reduction indices per iteration with the next iteration's loads in flight.
+//   NN: V(l, q) = V[l * Q + q]   (A [K, r] for XA)   -> tile [128 l][64 q], transposed reads
+//   NT: V(l, q) = V[q * L + l]   (B [r, N] for dY B^T) -> tile [64 q][128 l]
+constexpr int SK_BK = 128;
+constexpr int SK_PU = SK_BK + 8;   // [64][128] reduction-contiguous pitch
+constexpr int SK_PV = 64 + 16;     // [128][64] transposed-read pitch
+
+template <bool NN>
+__global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__ U, int64_t M, int64_t L,
+                                                    const uint16_t* __restrict__ V, int64_t Q, int64_t chunk,
+                                                    float* __restrict__ part, int64_t QP) {
+  constexpr int SV = NN ? SK_BK * SK_PV : 64 * SK_PU;
+  __shared__ __attribute__((aligned(16))) __bf16 sU[64 * SK_PU];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[SV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * TM, q0 = (int64_t)blockIdx.x * TN;
-  Acc22 acc;
-  acc_zero(acc);
-  for (int64_t lt = 0; lt < L; lt += 64) {
-    stage_rows(sA, U, L, m0, M, lt, tid);
-    stage_rows(sB, V, L, q0, Q, lt, tid);
-    __syncthreads();
-    mma_128x128x64(sA, sB, acc, wm, wn, lane);
-    __syncthreads();
-  }
+  const int64_t q0 = (int64_t)blockIdx.x * 64, m0 = (int64_t)blockIdx.y * 64;
+  const int64_t lbeg = (int64_t)blockIdx.z * chunk;
+  const int64_t lend = lbeg + chunk < L ? lbeg + chunk : L;
+  floatx16 acc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  uint4 ru[4], rv[4];
+  auto load = [&](int64_t lt) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = q0 + acc_col(wn, j, lane);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + acc_row(wm, i, r, lane);
-        if (row >= M) continue;
-        const float v = acc.c[i][j][r];
-        if (col < Q) {
-          if (out1) out1[row * Q + col] = f2bf(v);
-          if (out2) out2[row * ld2 + col] = f2bf(alpha * v);
-        } else if (out2 && col < ld2) {
-          out2[row * ld2 + col] = 0;
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + NT * i;
+      {  // U tile [64 m][128 l]
+        const int row = id >> 4, ch = id & 15;
+        const int64_t m = m0 + row, l = lt + ch * 8;
+        ru[i] = (m < M && l < lend) ? ldg16(U + m * L + l) : make_uint4(0, 0, 0, 0);
+      }
+      if (NN) {  // V tile [128 l][64 q]
+        const int row = id >> 3, ch = id & 7;
+        rv[i] = (lt + row < lend) ? load8_masked(V, Q, lt + row, L, q0 + ch * 8, Q) : make_uint4(0, 0, 0, 0);
+      } else {   // V tile [64 q][128 l]
+        const int row = id >> 4, ch = id & 15;
+        rv[i] = (lt + ch * 8 < lend) ? load8_masked(V, L, q0 + row, Q, lt + ch * 8, L) : make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  if (lbeg < lend) load(lbeg);
+  for (int64_t lt = lbeg; lt < lend; lt += SK_BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + NT * i;
+      sts16(&sU[(id >> 4) * SK_PU + (id & 15) * 8], ru[i]);
+      if (NN) sts16(&sV[(id >> 3) * SK_PV + (id & 7) * 8], rv[i]);
+      else sts16(&sV[(id >> 4) * SK_PU + (id & 15) * 8], rv[i]);
+    }
+    __syncthreads();
+    if (lt + SK_BK < lend) load(lt + SK_BK);
+#pragma unroll
+    for (int kk = 0; kk < SK_BK; kk += 16) {
+      const bf16x8 af = frag_kc(sU, SK_PU, wm * 32, kk, lane);
+      const bf16x8 bv = NN ? frag_rc(sV, SK_PV, wn * 32, kk, lane) : frag_kc(sV, SK_PU, wn * 32, kk, lane);
+      acc = mfma32(af, bv, acc);
+    }
+    __syncthreads();
+  }
+  float* out = part + (int64_t)blockIdx.z * M * QP;
+  const int64_t col = q0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t row = m0 + wm * 32 + acc_row32(e, lane);
+    if (row < M) out[row * QP + col] = acc[e];
+  }
 }
 
-// --------------------------------------------------- TN split-M GEMM
-// partial[s][p][q] = sum_{m in chunk s} U[m, p] V[m, q]; U [M, P], V [M, Q]
-// row-major with P % 64 == 0 and Q % 64 == 0 (callers pass padded operands).
-// Tiles 128 (P) x 128 (Q); each step stages 64 rows m, transposed into LDS.
-__global__ __launch_bounds__(NT) void gemm_tn_partial_kernel(const uint16_t* __restrict__ U,
-                                                             const uint16_t* __restrict__ V, int64_t M,
-                                                             int64_t P, int64_t Q, int64_t chunk,
-                                                             float* __restrict__ partials) {
-  __shared__ __bf16 sA[TM * LDK];
-  __shared__ __bf16 sB[TN * LDK];
+// out1[m][q] = bf16(sum_s part) for q < Q (optional); out2[m][q] =
+// bf16(alpha * sum_s part) for q < QP (columns >= Q are zero partials).
+__global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ part, int S, int64_t M,
+                                                              int64_t Q, int64_t QP, uint16_t* __restrict__ out1,
+                                                              uint16_t* __restrict__ out2, float alpha) {
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (idx >= M * QP) return;
+  float4 s = *reinterpret_cast<const float4*>(part + idx);
+  for (int k = 1; k < S; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * M * QP + idx);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const int64_t m = idx / QP, q = idx - m * QP;
+  const float sv[4] = {s.x, s.y, s.z, s.w};
+  uint2 o;
+  o.x = pack_bf2(alpha * sv[0], alpha * sv[1]);
+  o.y = pack_bf2(alpha * sv[2], alpha * sv[3]);
+  *reinterpret_cast<uint2*>(out2 + idx) = o;
+  if (out1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (q + e < Q) out1[m * Q + q + e] = f2bf(sv[e]);
+  }
+}
+
+// ============================================== token-reduction products
+// part[s][p][q] = sum over tokens m of chunk s of U[m, p] * V[m, q]
+// (U [M, P] and V [M, Q] row-major, leading dimensions ldu, ldv).  Tile
+// BP x BQ, waves 2 x 2; 128 tokens per iteration, next iteration's loads in
+// flight; both tiles are staged as [128 m][cols] and read transposed.
+constexpr int TN_BK = 128;
+
+template <int BP, int BQ>
+__global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, int64_t ldu, int64_t P,
+                                                const uint16_t* __restrict__ V, int64_t ldv, int64_t Q, int64_t M,
+                                                int64_t chunk, float* __restrict__ part) {
+  constexpr int PU = BP + 16, PV = BQ + 16;
+  constexpr int TMW = BP / 64, TNW = BQ / 64;
+  constexpr int CU_ = TN_BK * BP / 8 / NT, CV_ = TN_BK * BQ / 8 / NT;  // chunks per thread
+  __shared__ __attribute__((aligned(16))) __bf16 sU[TN_BK * PU];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[TN_BK * PV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t p0 = (int64_t)blockIdx.x * TM, q0 = (int64_t)blockIdx.y * TN;
+  const int64_t p0 = (int64_t)blockIdx.x * BP, q0 = (int64_t)blockIdx.y * BQ;
   const int64_t mbeg = (int64_t)blockIdx.z * chunk;
   const int64_t mend = mbeg + chunk < M ? mbeg + chunk : M;
-  Acc22 acc;
-  acc_zero(acc);
-  const int mrow = tid >> 2, quarter = tid & 3;
-  for (int64_t mt = mbeg; mt < mend; mt += 64) {
-    const int64_t m = mt + mrow;
-    const bool mok = m < mend;
-    {
-      const int64_t pc = p0 + quarter * 32;
-      const bool ok = mok && pc < P;
-      const uint16_t* src = U + (ok ? m * P + pc : 0);
+  floatx16 acc[TMW][TNW];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = ld16(src + i * 8, ok);
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+  for (int i = 0; i < TMW; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sA[(quarter * 32 + i * 8 + e) * LDK + mrow] = __builtin_bit_cast(__bf16, h[e]);
-      }
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  uint4 ru[CU_], rv[CV_];
+  auto load = [&](int64_t mt) {
+#pragma unroll
+    for (int i = 0; i < CU_; ++i) {
+      const int id = tid + NT * i, row = id / (BP / 8), ch = id % (BP / 8);
+      ru[i] = load8_masked(U, ldu, mt + row, mend, p0 + ch * 8, P);
     }
-    {
-      const int64_t qc = q0 + quarter * 32;
-      const bool ok = mok && qc < Q;
-      const uint16_t* src = V + (ok ? m * Q + qc : 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = ld16(src + i * 8, ok);
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+    for (int i = 0; i < CV_; ++i) {
+      const int id = tid + NT * i, row = id / (BQ / 8), ch = id % (BQ / 8);
+      rv[i] = load8_masked(V, ldv, mt + row, mend, q0 + ch * 8, Q);
+    }
+  };
+  if (mbeg < mend) load(mbeg);
+  for (int64_t mt = mbeg; mt < mend; mt += TN_BK) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sB[(quarter * 32 + i * 8 + e) * LDK + mrow] = __builtin_bit_cast(__bf16, h[e]);
-      }
+    for (int i = 0; i < CU_; ++i) {
+      const int id = tid + NT * i;
+      sts16(&sU[(id / (BP / 8)) * PU + (id % (BP / 8)) * 8], ru[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CV_; ++i) {
+      const int id = tid + NT * i;
+      sts16(&sV[(id / (BQ / 8)) * PV + (id % (BQ / 8)) * 8], rv[i]);
     }
     __syncthreads();
-    mma_128x128x64(sA, sB, acc, wm, wn, lane);
+    if (mt + TN_BK < mend) load(mt + TN_BK);
+#pragma unroll
+    for (int kk = 0; kk < TN_BK; kk += 16) {
+      bf16x8 af[TMW], bv[TNW];
+#pragma unroll
+      for (int i = 0; i < TMW; ++i) af[i] = frag_rc(sU, PU, wm * (BP / 2) + 32 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < TNW; ++j) bv[j] = frag_rc(sV, PV, wn * (BQ / 2) + 32 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bv[j], acc[i][j]);
+    }
     __syncthreads();
   }
-  float* out = partials + (int64_t)blockIdx.z * P * Q;
+  float* out = part + (int64_t)blockIdx.z * P * Q;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TMW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = q0 + acc_col(wn, j, lane);
+    for (int j = 0; j < TNW; ++j) {
+      const int64_t col = q0 + wn * (BQ / 2) + 32 * j + (lane & 31);
+      if (col >= Q) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = p0 + acc_row(wm, i, r, lane);
-        if (row < P && col < Q) out[row * Q + col] = acc.c[i][j][r];
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = p0 + wm * (BP / 2) + 32 * i + acc_row32(e, lane);
+        if (row < P) out[row * Q + col] = acc[i][j][e];
       }
     }
 }
 
-// out[p][q] (p < Pout, q < Qout, ld Qout) = bf16(alpha * sum_s partial[s][p][q])
-// with partials [splits][P][Q].
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ partials, int splits,
-                                                              int64_t P, int64_t Q, int64_t Pout, int64_t Qout,
-                                                              uint16_t* __restrict__ out, float alpha) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= Pout * Qout) return;
-  const int64_t p = idx / Qout, q = idx - p * Qout;
-  float s = 0.0f;
-  for (int k = 0; k < splits; ++k) s += partials[(int64_t)k * P * Q + p * Q + q];
-  out[idx] = f2bf(alpha * s);
-}
-
-// dst[i][j] = src[i][j] for j < cols, 0 for cols <= j < cols_pad.
-__global__ __launch_bounds__(256) void pad_copy_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
-                                                       uint16_t* __restrict__ dst, int64_t cols_pad) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= rows * cols_pad) return;
-  const int64_t i = idx / cols_pad, j = idx - i * cols_pad;
-  dst[idx] = j < cols ? src[i * cols + j] : (uint16_t)0;
-}
-
-// dst[i][j] = src[j][i] for j < src_rows, 0 otherwise; dst is [src_cols, cols_pad].
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t src_rows,
-                                                            int64_t src_cols, uint16_t* __restrict__ dst,
-                                                            int64_t cols_pad) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= src_cols * cols_pad) return;
-  const int64_t i = idx / cols_pad, j = idx - i * cols_pad;
-  dst[idx] = j < src_rows ? src[j * src_cols + i] : (uint16_t)0;
+// out[p][q] = bf16(alpha * sum_s part[s][p][q]), part [S][P][Q], out [P][Q].
+__global__ __launch_bounds__(256) void tn_reduce_kernel(const float* __restrict__ part, int S, int64_t PQ,
+                                                        uint16_t* __restrict__ out, float alpha) {
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (idx >= PQ) return;
+  if (idx + 4 <= PQ && (PQ & 3) == 0) {
+    float4 s = *reinterpret_cast<const float4*>(part + idx);
+    for (int k = 1; k < S; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * PQ + idx);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    uint2 o;
+    o.x = pack_bf2(alpha * s.x, alpha * s.y);
+    o.y = pack_bf2(alpha * s.z, alpha * s.w);
+    *reinterpret_cast<uint2*>(out + idx) = o;
+  } else {
+    for (int64_t e = idx; e < idx + 4 && e < PQ; ++e) {
+      float s = 0.0f;
+      for (int k = 0; k < S; ++k) s += part[(int64_t)k * PQ + e];
+      out[e] = f2bf(alpha * s);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ dst, int64_t n) {
@@ -337,79 +464,133 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
   if (idx < n) dst[idx] = 0;
 }
 
-inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+inline unsigned cdiv(int64_t n, int64_t d) { return (unsigned)((n + d - 1) / d); }
+
+// ------------------------------------------------ main-GEMM tile choice
+// Candidate tiles and a rough per-tile cost (relative MFMA time of a tile,
+// inflated for small tiles whose operand traffic per flop is higher).  The
+// grid runs in waves of 256 workgroups (one per CU); pick the tile with the
+// least estimated time.
+enum MainTile { T256x256 = 0, T256x128 = 1, T128x128 = 2 };
+
+MainTile pick_tile(int64_t M, int64_t ncols) {
+  struct Cand { MainTile t; int bm, bn; double cost; };
+  const Cand cands[3] = {{T256x256, 256, 256, 1.00}, {T256x128, 256, 128, 0.56}, {T128x128, 128, 128, 0.30}};
+  MainTile best = T256x256;
+  double best_t = 1e300;
+  for (const Cand& c : cands) {
+    const int64_t tiles = (int64_t)cdiv(M, c.bm) * cdiv(ncols, c.bn);
+    const int per_cu = c.bm * c.bn >= 256 * 256 ? 1 : 2;
+    const double waves = (double)((tiles + 256 * per_cu - 1) / (256 * per_cu));
+    const double t = waves * c.cost * per_cu;
+    if (t < best_t - 1e-9) { best_t = t; best = c.t; }
+  }
+  return best;
+}
+
+template <int BM, int BN, bool BWD>
+hipError_t launch_main(const MainArgs& a, hipStream_t stream) {
+  const dim3 grid(cdiv(a.ncols, BN), cdiv(a.M, BM));
+  hipLaunchKernelGGL((main_gemm_kernel<BM, BN, BWD>), grid, dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BWD>
+hipError_t launch_main_any(const MainArgs& a, hipStream_t stream) {
+  switch (pick_tile(a.M, a.ncols)) {
+    case T256x256: return launch_main<256, 256, BWD>(a, stream);
+    case T256x128: return launch_main<256, 128, BWD>(a, stream);
+    default: return launch_main<128, 128, BWD>(a, stream);
+  }
+}
 
 }  // namespace
 
-hipError_t launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int64_t cols_pad,
-                           hipStream_t stream) {
-  if (rows * cols_pad == 0) return hipSuccess;
-  hipLaunchKernelGGL(pad_copy_kernel, dim3(blocks_for(rows * cols_pad, 256)), dim3(256), 0, stream, src, rows, cols,
-                     dst, cols_pad);
-  return hipGetLastError();
+// ------------------------------------------------------------ launchers
+
+int skinny_splits(int64_t M, int64_t Q, int64_t L) {
+  int64_t tiles = (int64_t)cdiv(M, 64) * cdiv(Q, 64);
+  if (tiles < 1) tiles = 1;
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t max_s = L / SK_BK > 0 ? L / SK_BK : 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
-hipError_t launch_transpose_pad(const uint16_t* src, int64_t src_rows, int64_t src_cols, uint16_t* dst,
-                                int64_t cols_pad, hipStream_t stream) {
-  if (src_cols * cols_pad == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_pad_kernel, dim3(blocks_for(src_cols * cols_pad, 256)), dim3(256), 0, stream, src,
-                     src_rows, src_cols, dst, cols_pad);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_nt(const uint16_t* U, const uint16_t* V, int64_t M, int64_t Q, int64_t L, uint16_t* out1,
-                          uint16_t* out2, int64_t ld2, float alpha, hipStream_t stream) {
-  const int64_t qcols = out2 && ld2 > Q ? ld2 : Q;
-  const dim3 grid(blocks_for(qcols, TN), blocks_for(M, TM));
-  hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(NT), 0, stream, U, V, M, Q, L, out1, out2, ld2, alpha);
-  return hipGetLastError();
-}
-
-hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq,
-                           int64_t N, const uint16_t* XAs, const uint16_t* Bt, int64_t rp, uint16_t* Y,
-                           hipStream_t stream) {
-  const dim3 grid(blocks_for(N, TN), blocks_for(M, TM));
-  hipLaunchKernelGGL(fwd_main_kernel, grid, dim3(NT), 0, stream, X, M, K, codes, dq, N, XAs, Bt, rp, Y, nf4_values());
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes, const DQParams& dq,
-                         int64_t K, const uint16_t* Ts, const uint16_t* Ap, int64_t rp, uint16_t* dX,
+hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
+                         float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
                          hipStream_t stream) {
-  const dim3 grid(blocks_for(K, TN), blocks_for(M, TM));
-  hipLaunchKernelGGL(bwd_dx_kernel, grid, dim3(NT), 0, stream, dY, M, N, codes, dq, K, Ts, Ap, rp, dX, nf4_values());
+  int64_t chunk = (L + splits - 1) / splits;
+  chunk = (chunk + SK_BK - 1) / SK_BK * SK_BK;
+  const dim3 grid(cdiv(QP, 64), cdiv(M, 64), (unsigned)splits);
+  if (v_is_lq)
+    hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP);
+  else
+    hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(skinny_epilogue_kernel, dim3(cdiv(M * QP / 4, 256)), dim3(256), 0, stream, part, splits, M, Q,
+                     QP, out1, out2, alpha);
   return hipGetLastError();
 }
 
-// Enough M-chunks that the grid has about 1024 workgroups, each chunk a
-// multiple of 64 rows.
 int tn_splits(int64_t M, int64_t P, int64_t Q) {
-  const int64_t tiles = ((P + TM - 1) / TM) * ((Q + TN - 1) / TN);
-  int64_t s = (1024 + tiles - 1) / tiles;
-  const int64_t max_s = (M + 63) / 64;
+  const bool wide = Q > P;
+  int64_t tiles = wide ? (int64_t)cdiv(P, 64) * cdiv(Q, 128) : (int64_t)cdiv(P, 128) * cdiv(Q, 64);
+  if (tiles < 1) tiles = 1;
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t max_s = M / TN_BK > 0 ? M / TN_BK : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
   return (int)s;
 }
 
-hipError_t launch_gemm_tn(const uint16_t* U, const uint16_t* V, int64_t M, int64_t P, int64_t Q, float* partials,
-                          int splits, uint16_t* out, int64_t Pout, int64_t Qout, float alpha, hipStream_t stream) {
+hipError_t launch_gemm_tn(const uint16_t* U, int64_t ldu, int64_t P, const uint16_t* V, int64_t ldv, int64_t Q,
+                          int64_t M, float* partials, int splits, uint16_t* out, float alpha, hipStream_t stream) {
   int64_t chunk = (M + splits - 1) / splits;
-  chunk = (chunk + 63) / 64 * 64;
-  const dim3 grid(blocks_for(P, TM), blocks_for(Q, TN), (unsigned)splits);
-  hipLaunchKernelGGL(gemm_tn_partial_kernel, grid, dim3(NT), 0, stream, U, V, M, P, Q, chunk, partials);
+  chunk = (chunk + TN_BK - 1) / TN_BK * TN_BK;
+  if (Q > P) {
+    const dim3 grid(cdiv(P, 64), cdiv(Q, 128), (unsigned)splits);
+    hipLaunchKernelGGL((tn_kernel<64, 128>), grid, dim3(NT), 0, stream, U, ldu, P, V, ldv, Q, M, chunk, partials);
+  } else {
+    const dim3 grid(cdiv(P, 128), cdiv(Q, 64), (unsigned)splits);
+    hipLaunchKernelGGL((tn_kernel<128, 64>), grid, dim3(NT), 0, stream, U, ldu, P, V, ldv, Q, M, chunk, partials);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3(blocks_for(Pout * Qout, 256)), dim3(256), 0, stream, partials,
-                     splits, P, Q, Pout, Qout, out, alpha);
+  hipLaunchKernelGGL(tn_reduce_kernel, dim3(cdiv(P * Q / 4 + 1, 256)), dim3(256), 0, stream, partials, splits, P * Q,
+                     out, alpha);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, stream, dst, n);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(cdiv(n, 256)), dim3(256), 0, stream, dst, n);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq,
+                           int64_t N, const uint16_t* XAs, const uint16_t* B, int64_t r, int64_t rp, uint16_t* Y,
+                           hipStream_t stream) {
+  MainArgs a;
+  a.act = X; a.M = M; a.L = K;
+  a.codes = codes; a.dq = dq; a.Nw = N; a.Kw = K;
+  a.ext_act = XAs; a.ext_w = B; a.r = r; a.rp = rp;
+  a.out = Y; a.ncols = N;
+  return launch_main_any<false>(a, stream);
+}
+
+hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes, const DQParams& dq,
+                         int64_t K, const uint16_t* Ts, const uint16_t* A, int64_t r, int64_t rp, uint16_t* dX,
+                         hipStream_t stream) {
+  MainArgs a;
+  a.act = dY; a.M = M; a.L = N;
+  a.codes = codes; a.dq = dq; a.Nw = N; a.Kw = K;
+  a.ext_act = Ts; a.ext_w = A; a.r = r; a.rp = rp;
+  a.out = dX; a.ncols = K;
+  return launch_main_any<true>(a, stream);
 }
 
 }  // namespace qlora

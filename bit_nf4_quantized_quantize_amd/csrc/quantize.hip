@@ -264,14 +264,26 @@ __global__ __launch_bounds__(MEAN_THREADS) void dq_mean_partial_kernel(const flo
 // (ties to even).  The fp32 bit pattern of a value v < 2^-125 is v / 2^-149
 // itself; above that the pattern is (shift << 23) + mantissa for a 24-bit
 // mantissa scaled by 2^shift, which also absorbs a rounding carry.
-__global__ void dq_mean_final_kernel(const uint64_t* __restrict__ partials, int parts, int64_t nb,
-                                     float* __restrict__ mu_out) {
+__global__ __launch_bounds__(256) void dq_mean_final_kernel(const uint64_t* __restrict__ partials, int parts,
+                                                             int64_t nb, float* __restrict__ mu_out) {
+  // every thread sums a strided subset of the partials, digit by digit
+  uint64_t acc[kMeanDigits];
+#pragma unroll
+  for (int k = 0; k < kMeanDigits; ++k) acc[k] = 0;
+  for (int p = threadIdx.x; p < parts; p += 256)
+#pragma unroll
+    for (int k = 0; k < kMeanDigits; ++k) acc[k] += partials[(int64_t)p * kMeanDigits + k];
+  __shared__ uint64_t s_part[4][kMeanDigits];
   __shared__ uint64_t s_sum[kMeanDigits];
-  if (threadIdx.x < kMeanDigits) {
-    uint64_t t = 0;
-    for (int p = 0; p < parts; ++p) t += partials[(int64_t)p * kMeanDigits + threadIdx.x];
-    s_sum[threadIdx.x] = t;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < kMeanDigits; ++k) {
+    const uint64_t t = wave_sum_u64(acc[k]);
+    if (lane == 0) s_part[wave][k] = t;
   }
+  __syncthreads();
+  if (threadIdx.x < kMeanDigits)
+    s_sum[threadIdx.x] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x] + s_part[2][threadIdx.x] + s_part[3][threadIdx.x];
   __syncthreads();
   if (threadIdx.x != 0) return;
   uint32_t dig[kMeanDigits];
@@ -364,7 +376,7 @@ hipError_t launch_double_quant(const float* c2, int64_t nb, uint64_t* partials, 
   hipLaunchKernelGGL(dq_mean_partial_kernel, dim3(parts), dim3(MEAN_THREADS), 0, stream, c2, nb, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dq_mean_final_kernel, dim3(1), dim3(64), 0, stream, partials, parts, nb, offset);
+  hipLaunchKernelGGL(dq_mean_final_kernel, dim3(1), dim3(256), 0, stream, partials, parts, nb, offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ng = (nb + 255) / 256;

@@ -110,6 +110,12 @@ def test_workspace_queries():
     assert B.qlora_nf4_quantize_workspace(4096 * 4096, True) >= 4 * 4096 * 4096 // 64
     f, b = B.qlora_linear_workspace(4096, 4096, 4096, 64)
     assert f >= 2 * 4096 * 64 * 3 and b >= 2 * 4096 * 64 * 3
+    # every token count, including none, has a defined workspace
+    for M in (0, 1, 15, 4096, 1 << 20):
+        for r in (1, 8, 64, 100, 256):
+            f, b = B.qlora_linear_workspace(M, 256, 512, r)
+            assert f >= 0 and b >= 0
+    assert B.qlora_nf4_quantize_workspace(0, True) == 0
     with pytest.raises(B.QLoraError):
         B.qlora_linear_workspace(16, 100, 256, 8)
     with pytest.raises(B.QLoraError):
