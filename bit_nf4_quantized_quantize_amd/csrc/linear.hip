@@ -254,6 +254,206 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
     }
 }
 
+// ============================================ main GEMM, 256 x 256, 8 waves
+// Two waves per SIMD so one wave's dequantisation and memory work overlaps
+// the other's MFMAs.  Waves form a 2 (M) x 4 (N) grid of 128 x 64 wave
+// tiles.  Pipeline per k-step kt (one barrier):
+//   registers hold X(kt+1) (issued one step earlier) and the codes of kt+1
+//   (issued two steps earlier);
+//   the codes of kt+2 are issued, then the MFMAs of kt run on LDS stage
+//   kt%2 while the weight tile of kt+1 is dequantised into the other stage;
+//   X(kt+1) is copied to that stage and X(kt+2) is issued.
+#ifndef V3_WAVES
+#define V3_WAVES 8
+#endif
+template <bool BWD, bool DQ, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void main_v3_kernel(const MainArgs a) {
+  constexpr int V3_T = NW * 64;
+  constexpr int BM = 256, BN = 256;
+  constexpr int WTN = NW == 8 ? 64 : 128;   // wave tile 128 x WTN
+  constexpr int TNW = WTN / 32;
+  constexpr int DQE = 256 * 64 / V3_T;       // weights per thread per step (32 or 64)
+  constexpr int PRC = BN + 16;
+  constexpr int SA = BM * PK;
+  constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
+  constexpr int XCH = BM * 8 / V3_T;  // 4 chunks of 16 bytes per thread
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][SA];
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][SB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
+  const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
+  const float mu = DQ ? *a.dq.offset : 0.0f;
+  const int64_t kblocks = a.Kw >> 6;
+  const int nk = (int)(a.L >> 6);
+
+  // dequantisation task: 32 consecutive weights (half a block) per thread.
+  // Every load below is issued unconditionally from a clamped, in-bounds
+  // address (rows past the end feed outputs that are never stored, and a
+  // weight task past the end gets scale 0), so the number of loads in flight
+  // is the same on every path and waits stay precise.
+  const int t_row = BWD ? tid / (BN / DQE) : tid / (64 / DQE);
+  const int t_col = BWD ? (tid % (BN / DQE)) * DQE : (tid % (64 / DQE)) * DQE;
+  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
+  const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);   // fwd: fixed weight row
+  const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - DQE) : 0;  // bwd: fixed weight column
+
+  floatx16 acc[4][TNW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  uint4 xr[XCH];
+  // two register sets for the codes: the loop is unrolled by two so the set
+  // being filled is never copied (a copy would wait for its loads)
+  constexpr int CW = DQE / 32;  // 16-byte code chunks per thread
+  uint4 cwA[CW], cwB[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) cwA[i] = cwB[i] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+  uint8_t qbA = 0, qbB = 0;
+  float sfA = 0.0f, sfB = 0.0f;
+
+  auto load_x = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+      xr[i] = ldg16(a.act + m * a.L + (int64_t)kt * 64 + ch * 8);
+    }
+  };
+  auto load_codes = [&](int kt, uint4* c, uint8_t& q, float& f) {
+    const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
+    const int64_t k = BWD ? t_k : (int64_t)kt * 64 + t_col;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) c[i] = *reinterpret_cast<const uint4*>(a.codes + ((n * a.Kw + k) >> 1) + 16 * i);
+    const int64_t blk = n * kblocks + (k >> 6);
+    if (DQ) {
+      q = a.dq.absmax_q[blk];
+      f = a.dq.scale2[blk >> 8];
+    } else {
+      f = a.dq.absmax[blk];
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
+      sts16(&sA[buf][row * PK + ch * 8], xr[i]);
+    }
+  };
+  auto dequant = [&](int buf, const uint4* c, uint8_t q, float f) {
+    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(q), f), mu) : f;
+    const float sc = t_ok ? bs : 0.0f;
+    const BlockLUT lut = lut_for(sc);
+    __bf16* dst = BWD ? &sB[buf][t_row * PRC + t_col] : &sB[buf][t_row * PK + t_col];
+#pragma unroll
+    for (int w = 0; w < 4 * CW; ++w) {
+      const uint32_t word = (w & 3) == 0 ? c[w >> 2].x : (w & 3) == 1 ? c[w >> 2].y : (w & 3) == 2 ? c[w >> 2].z : c[w >> 2].w;
+      uint32_t o[4];
+      lut_lookup8(lut, word, o);
+      sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  };
+  auto mma = [&](int buf, bool b_rc, int pitch_b) {
+#pragma unroll
+    for (int kk = 0; kk < 64; kk += 16) {
+      bf16x8 af[4], bfr[TNW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < TNW; ++j)
+        bfr[j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * WTN + 32 * j, kk, lane)
+                      : frag_kc(sB[buf], pitch_b, wn * WTN + 32 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+  // one k-step: codes(kt+1) are in (cu, qu, fu); codes(kt+2) go to (cl, ql, fl)
+  // `cur` is a literal at both call sites, so LDS reads of one stage and
+  // writes of the other are provably disjoint and may be interleaved.
+  auto step = [&](int kt, const int cur, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql, float& fl) {
+    const int nxt = cur ^ 1;
+    const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
+    load_codes(k2, cl, ql, fl);
+    mma(cur, BWD, BWD ? PRC : PK);
+    // On the last step this fills a stage nobody reads again: harmless, and
+    // it keeps the whole step one basic block so the scheduler can interleave
+    // the dequantisation VALU work with the MFMAs.
+    dequant(nxt, cu, qu, fu);
+    store_x(nxt);
+    load_x(k2);
+#pragma unroll
+    for (int g = 0; g < 4 * TNW; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- prologue: stage 0 filled; X(1) and codes(1) in flight
+  load_codes(0, cwB, qbB, sfB);
+  load_x(0);
+  store_x(0);
+  dequant(0, cwB, qbB, sfB);
+  load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
+  load_x(nk > 1 ? 1 : 0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
+    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
+  }
+
+  // ---- adapter term over bf16 operands (stage 0 is free)
+  for (int64_t jt = 0; jt < a.rp; jt += 64) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row;
+      sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
+    }
+    if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
+#pragma unroll
+      for (int i = 0; i < BN * 8 / V3_T; ++i) {
+        const int id = tid + V3_T * i, row = id / (BN / 8), ch = id % (BN / 8);
+        sts16(&sB[0][row * PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
+      }
+    } else {     // A [Kw, r]: tile [BN k][64 j]
+#pragma unroll
+      for (int i = 0; i < BN * 8 / V3_T; ++i) {
+        const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
+        sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
+      }
+    }
+    __syncthreads();
+    mma(0, !BWD, BWD ? PK : PRC);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      const int64_t col = c0 + wn * WTN + 32 * j + (lane & 31);
+      if (col >= a.ncols) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
+        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
+      }
+    }
+}
+
 // ====================================================== skinny products
 // part[s][m][q] = sum over the s-th reduction chunk of U[m, l] * V(l, q),
 // tile 64 (M) x 64 (Q), waves 2 x 2 of one 32x32 MFMA tile each, 128
@@ -498,7 +698,14 @@ hipError_t launch_main(const MainArgs& a, hipStream_t stream) {
 template <bool BWD>
 hipError_t launch_main_any(const MainArgs& a, hipStream_t stream) {
   switch (pick_tile(a.M, a.ncols)) {
-    case T256x256: return launch_main<256, 256, BWD>(a, stream);
+    case T256x256: {
+      const dim3 grid(cdiv(a.ncols, 256), cdiv(a.M, 256));
+      if (a.dq.double_quant)
+        hipLaunchKernelGGL((main_v3_kernel<BWD, true, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((main_v3_kernel<BWD, false, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
+      return hipGetLastError();
+    }
     case T256x128: return launch_main<256, 128, BWD>(a, stream);
     default: return launch_main<128, 128, BWD>(a, stream);
   }
