@@ -454,6 +454,434 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void main_v3_kernel(const MainArgs
     }
 }
 
+// ================================= main GEMM, 256 x 256, warp-specialised
+// 12 waves: 8 consumer waves (two per SIMD, a 2 (M) x 4 (N) grid of 128 x 64
+// tiles) only read LDS and issue MFMAs; 4 producer waves (one per SIMD)
+// stage the activation tile and dequantise the weight tile (one whole NF4
+// block per thread) into the other LDS stage.  The MFMA work of consumers and
+// the VALU / memory work of producers run on the same SIMDs concurrently;
+// one workgroup barrier per k-step swaps the stages.  Producers keep codes
+// two steps ahead and activations one step ahead in registers.
+constexpr int WS_T = 768;
+
+template <bool BWD, bool DQ>
+__global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int PRC = BN + 16;
+  constexpr int SA = BM * PK;
+  constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
+  constexpr int NP = 256;          // producer threads
+  constexpr int XCH = BM * 8 / NP; // 8 activation chunks of 16 bytes per producer thread
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][SA];
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][SB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool producer = wave >= 8;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
+  const int nk = (int)(a.L >> 6);
+  const int64_t kblocks = a.Kw >> 6;
+
+  // ---------------- producer state
+  const int pt = tid - 512;
+  const int t_row = BWD ? (pt >> 2) : pt;
+  const int t_col = BWD ? (pt & 3) * 64 : 0;
+  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
+  const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);
+  const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - 64) : 0;
+  const float mu = (DQ && producer) ? *a.dq.offset : 0.0f;
+  uint4 xr[XCH];
+  uint4 cwA[2], cwB[2];
+  uint8_t qbA = 0, qbB = 0;
+  float sfA = 0.0f, sfB = 0.0f;
+
+  auto load_x = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = pt + NP * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+      xr[i] = ldg16(a.act + m * a.L + (int64_t)kt * 64 + ch * 8);
+    }
+  };
+  auto load_codes = [&](int kt, uint4* c, uint8_t& q, float& f) {
+    const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
+    const int64_t k = BWD ? t_k : (int64_t)kt * 64;
+    const uint8_t* src = a.codes + ((n * a.Kw + k) >> 1);
+    c[0] = *reinterpret_cast<const uint4*>(src);
+    c[1] = *reinterpret_cast<const uint4*>(src + 16);
+    const int64_t blk = n * kblocks + (k >> 6);
+    if (DQ) {
+      q = a.dq.absmax_q[blk];
+      f = a.dq.scale2[blk >> 8];
+    } else {
+      f = a.dq.absmax[blk];
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = pt + NP * i, row = id >> 3, ch = id & 7;
+      sts16(&sA[buf][row * PK + ch * 8], xr[i]);
+    }
+  };
+  auto dequant = [&](int buf, const uint4* c, uint8_t q, float f) {
+    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(q), f), mu) : f;
+    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f);
+    __bf16* dst = BWD ? &sB[buf][t_row * PRC + t_col] : &sB[buf][t_row * PK + t_col];
+    const uint32_t words[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t o[4];
+      lut_lookup8(lut, words[w], o);
+      sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  };
+  auto produce = [&](int kt, const int nxt, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql,
+                     float& fl) {
+    const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
+    load_codes(k2, cl, ql, fl);
+    dequant(nxt, cu, qu, fu);
+    store_x(nxt);
+    load_x(k2);
+  };
+
+  // ---------------- consumer state
+  const int cw_ = wave & 7;
+  const int wm = cw_ >> 2, wn = cw_ & 3;
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mma = [&](int buf, bool b_rc, int pitch_b) {
+#pragma unroll
+    for (int kk = 0; kk < 64; kk += 16) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane)
+                      : frag_kc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // The two roles run separate loops with the same number of barriers, so
+  // producer registers and consumer accumulators are never live together.
+  if (producer) {
+    load_codes(0, cwB, qbB, sfB);
+    load_x(0);
+    store_x(0);
+    dequant(0, cwB, qbB, sfB);
+    load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
+    load_x(nk > 1 ? 1 : 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      produce(kt, 1, cwA, qbA, sfA, cwB, qbB, sfB);
+      __syncthreads();
+      if (kt + 1 < nk) {
+        produce(kt + 1, 0, cwB, qbB, sfB, cwA, qbA, sfA);
+        __syncthreads();
+      }
+    }
+    // adapter term operands
+    for (int64_t jt = 0; jt < a.rp; jt += 64) {
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) {
+        const int id = pt + NP * i, row = id >> 3, ch = id & 7;
+        const int64_t m = m0 + row;
+        sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
+      }
+      if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
+#pragma unroll
+        for (int i = 0; i < BN * 8 / NP; ++i) {
+          const int id = pt + NP * i, row = id / (BN / 8), ch = id % (BN / 8);
+          sts16(&sB[0][row * PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
+        }
+      } else {     // A [Kw, r]: tile [BN k][64 j]
+#pragma unroll
+        for (int i = 0; i < BN * 8 / NP; ++i) {
+          const int id = pt + NP * i, row = id >> 3, ch = id & 7;
+          sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
+        }
+      }
+      __syncthreads();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- consumers
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    mma(0, BWD, BWD ? PRC : PK);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      mma(1, BWD, BWD ? PRC : PK);
+      __syncthreads();
+    }
+  }
+  for (int64_t jt = 0; jt < a.rp; jt += 64) {
+    __syncthreads();
+    mma(0, !BWD, BWD ? PK : PRC);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = c0 + wn * 64 + 32 * j + (lane & 31);
+      if (col >= a.ncols) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
+        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
+      }
+    }
+}
+
+// ================================== main GEMM, 256 x 256, 4 waves, v5
+// One wave per SIMD, each owning a 128 x 128 output tile (256 fp32
+// accumulators), so every LDS fragment feeds four MFMAs.  The next k-step's
+// weight tile is dequantised by the same waves, but its instructions are
+// spread between the MFMAs by hand: after each MFMA one small item (a few
+// VALU operations, one LDS store or one global load) is issued, and
+// scheduling barriers keep that order, so the VALU work fills the MFMA
+// shadow instead of running after it.  Fragment reads for sub-step kk+1 are
+// issued while sub-step kk multiplies.
+constexpr int V5_T = 256;
+
+struct WordState {
+  uint32_t e7, o7, me, mo, loE, hiE, loO, hiO;
+};
+
+template <bool BWD, bool DQ>
+__global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int PRC = BN + 16;
+  constexpr int SA = BM * PK;
+  constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
+  constexpr int XCH = BM * 8 / V5_T;  // 8 activation chunks per thread
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][SA];
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][SB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // XCD-aware order: consecutive workgroups go to different XCDs, so give
+  // each XCD a contiguous run of tiles (row-major over the tile grid).
+  const int tn = (int)((a.ncols + BN - 1) / BN), tm = (int)((a.M + BM - 1) / BM);
+  const int T = tn * tm, pid = blockIdx.x;
+  const int lid = (T % 8 == 0) ? (pid % 8) * (T / 8) + pid / 8 : pid;
+  const int64_t m0 = (int64_t)(lid / tn) * BM, c0 = (int64_t)(lid % tn) * BN;
+  const int nk = (int)(a.L >> 6);
+  const int64_t kblocks = a.Kw >> 6;
+  const float mu = DQ ? *a.dq.offset : 0.0f;
+
+  // dequantisation task: one whole NF4 block (64 weights) per thread
+  const int t_row = BWD ? (tid >> 2) : tid;
+  const int t_col = BWD ? (tid & 3) * 64 : 0;
+  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
+  const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);
+  const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - 64) : 0;
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  uint4 xr[XCH];
+  uint4 cwA[2], cwB[2];
+  uint8_t qbA = 0, qbB = 0;
+  float sfA = 0.0f, sfB = 0.0f;
+
+  auto x_src = [&](int i, int kt) -> const uint16_t* {
+    const int id = tid + V5_T * i, row = id >> 3, ch = id & 7;
+    const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+    return a.act + m * a.L + (int64_t)kt * 64 + ch * 8;
+  };
+  auto x_dst = [&](int i, int buf) -> __bf16* {
+    const int id = tid + V5_T * i, row = id >> 3, ch = id & 7;
+    return &sA[buf][row * PK + ch * 8];
+  };
+  auto load_codes = [&](int kt, uint4* c, uint8_t& q, float& f) {
+    const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
+    const int64_t k = BWD ? t_k : (int64_t)kt * 64;
+    const uint8_t* src = a.codes + ((n * a.Kw + k) >> 1);
+    c[0] = *reinterpret_cast<const uint4*>(src);
+    c[1] = *reinterpret_cast<const uint4*>(src + 16);
+    const int64_t blk = n * kblocks + (k >> 6);
+    if (DQ) {
+      q = a.dq.absmax_q[blk];
+      f = a.dq.scale2[blk >> 8];
+    } else {
+      f = a.dq.absmax[blk];
+    }
+  };
+  auto wdst = [&](int buf, int w) -> __bf16* {
+    return BWD ? &sB[buf][t_row * PRC + t_col + 8 * w] : &sB[buf][t_row * PK + t_col + 8 * w];
+  };
+
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](int buf, int kk, int slot, bool b_rc, int pitch_b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[slot][j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * 128 + 32 * j, kk, lane)
+                         : frag_kc(sB[buf], pitch_b, wn * 128 + 32 * j, kk, lane);
+  };
+
+  // ---- one k-step: multiply stage `cur` while producing stage `nxt`
+  auto step = [&](int kt, const int cur, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql, float& fl) {
+    const int nxt = cur ^ 1;
+    const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
+    const uint32_t words[8] = {cu[0].x, cu[0].y, cu[0].z, cu[0].w, cu[1].x, cu[1].y, cu[1].z, cu[1].w};
+    float sc = 0.0f;
+    uint32_t pw[8];
+    BlockLUT lut;
+    WordState ws[8];
+    load_codes(k2, cl, ql, fl);
+    read_frags(cur, 0, 0, BWD, BWD ? PRC : PK);
+    // items interleaved with the 64 MFMAs, in order
+    auto item = [&](int it) {
+      if (it == 0) {
+        const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
+        sc = t_ok ? bs : 0.0f;
+        pw[0] = pack_bf2(kNF4c[0] * sc, kNF4c[1] * sc);
+      } else if (it <= 7) {
+        pw[it] = pack_bf2(kNF4c[2 * it] * sc, kNF4c[2 * it + 1] * sc);
+      } else if (it == 8) {
+        lut = make_lut(pw);
+      } else if (it < 9 + 32) {
+        const int w = (it - 9) >> 2, stg = (it - 9) & 3;
+        WordState& st = ws[w];
+        const uint32_t wd = words[w];
+        if (stg == 0) {
+          st.e7 = wd & 0x07070707u;
+          st.o7 = (wd >> 4) & 0x07070707u;
+          const uint32_t t3 = wd >> 3;
+          st.me = (t3 & 0x01010101u) * 0xFFu;
+          st.mo = ((t3 >> 4) & 0x01010101u) * 0xFFu;
+        } else if (stg == 1) {
+          st.loE = (st.me & perm_b32(lut.lo[3], lut.lo[2], st.e7)) | (~st.me & perm_b32(lut.lo[1], lut.lo[0], st.e7));
+          st.hiE = (st.me & perm_b32(lut.hi[3], lut.hi[2], st.e7)) | (~st.me & perm_b32(lut.hi[1], lut.hi[0], st.e7));
+        } else if (stg == 2) {
+          st.loO = (st.mo & perm_b32(lut.lo[3], lut.lo[2], st.o7)) | (~st.mo & perm_b32(lut.lo[1], lut.lo[0], st.o7));
+          st.hiO = (st.mo & perm_b32(lut.hi[3], lut.hi[2], st.o7)) | (~st.mo & perm_b32(lut.hi[1], lut.hi[0], st.o7));
+        } else {
+          const uint32_t e01 = perm_b32(st.hiE, st.loE, 0x05010400u);
+          const uint32_t o01 = perm_b32(st.hiO, st.loO, 0x05010400u);
+          const uint32_t e23 = perm_b32(st.hiE, st.loE, 0x07030602u);
+          const uint32_t o23 = perm_b32(st.hiO, st.loO, 0x07030602u);
+          sts16(wdst(nxt, w), make_uint4(perm_b32(o01, e01, 0x05040100u), perm_b32(o01, e01, 0x07060302u),
+                                         perm_b32(o23, e23, 0x05040100u), perm_b32(o23, e23, 0x07060302u)));
+        }
+      } else if (it < 41 + XCH) {
+        const int i = it - 41;
+        sts16(x_dst(i, nxt), xr[i]);
+      } else if (it < 41 + 2 * XCH) {
+        const int i = it - 41 - XCH;
+        xr[i] = ldg16(x_src(i, k2));
+      }
+    };
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int slot = kk & 1;
+#pragma unroll
+      for (int ij = 0; ij < 16; ++ij) {
+        const int i = ij >> 2, j = ij & 3;
+        acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
+        if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
+        item(kk * 16 + ij);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- prologue: stage 0 filled; X(1) and codes(1) in flight
+  load_codes(0, cwB, qbB, sfB);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, 0));
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
+  {
+    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
+    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f);
+    const uint32_t words[8] = {cwB[0].x, cwB[0].y, cwB[0].z, cwB[0].w, cwB[1].x, cwB[1].y, cwB[1].z, cwB[1].w};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t o[4];
+      lut_lookup8(lut, words[w], o);
+      sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
+  load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, nk > 1 ? 1 : 0));
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
+    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
+  }
+
+  // ---- adapter term over bf16 operands (stage 0 is free)
+  for (int64_t jt = 0; jt < a.rp; jt += 64) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + V5_T * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row;
+      sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
+    }
+    if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
+#pragma unroll
+      for (int i = 0; i < BN * 8 / V5_T; ++i) {
+        const int id = tid + V5_T * i, row = id / (BN / 8), ch = id % (BN / 8);
+        sts16(&sB[0][row * PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
+      }
+    } else {     // A [Kw, r]: tile [BN k][64 j]
+#pragma unroll
+      for (int i = 0; i < BN * 8 / V5_T; ++i) {
+        const int id = tid + V5_T * i, row = id >> 3, ch = id & 7;
+        sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 64; kk += 16) {
+      read_frags(0, kk, 0, !BWD, BWD ? PK : PRC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[0][i], fb[0][j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = c0 + wn * 128 + 32 * j + (lane & 31);
+      if (col >= a.ncols) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
+        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
+      }
+    }
+}
+
 // ====================================================== skinny products
 // part[s][m][q] = sum over the s-th reduction chunk of U[m, l] * V(l, q),
 // tile 64 (M) x 64 (Q), waves 2 x 2 of one 32x32 MFMA tile each, 128
@@ -700,10 +1128,23 @@ hipError_t launch_main_any(const MainArgs& a, hipStream_t stream) {
   switch (pick_tile(a.M, a.ncols)) {
     case T256x256: {
       const dim3 grid(cdiv(a.ncols, 256), cdiv(a.M, 256));
+#ifdef QLORA_MAIN_V3
       if (a.dq.double_quant)
         hipLaunchKernelGGL((main_v3_kernel<BWD, true, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
       else
         hipLaunchKernelGGL((main_v3_kernel<BWD, false, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
+#elif defined(QLORA_MAIN_WS)
+      if (a.dq.double_quant)
+        hipLaunchKernelGGL((main_ws_kernel<BWD, true>), grid, dim3(WS_T), 0, stream, a);
+      else
+        hipLaunchKernelGGL((main_ws_kernel<BWD, false>), grid, dim3(WS_T), 0, stream, a);
+#else
+      const dim3 grid1(cdiv(a.ncols, 256) * cdiv(a.M, 256));
+      if (a.dq.double_quant)
+        hipLaunchKernelGGL((main_v5_kernel<BWD, true>), grid1, dim3(V5_T), 0, stream, a);
+      else
+        hipLaunchKernelGGL((main_v5_kernel<BWD, false>), grid1, dim3(V5_T), 0, stream, a);
+#endif
       return hipGetLastError();
     }
     case T256x128: return launch_main<256, 128, BWD>(a, stream);
