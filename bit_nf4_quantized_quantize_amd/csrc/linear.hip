@@ -477,7 +477,12 @@ __global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool producer = wave >= 8;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
+  // XCD-aware order: consecutive workgroups go to different XCDs, so give
+  // each XCD a contiguous run of tiles (row-major over the tile grid).
+  const int tn = (int)((a.ncols + BN - 1) / BN), tm = (int)((a.M + BM - 1) / BM);
+  const int T = tn * tm, pid = blockIdx.x;
+  const int lid = (T % 8 == 0) ? (pid % 8) * (T / 8) + pid / 8 : pid;
+  const int64_t m0 = (int64_t)(lid / tn) * BM, c0 = (int64_t)(lid % tn) * BN;
   const int nk = (int)(a.L >> 6);
   const int64_t kblocks = a.Kw >> 6;
 
@@ -489,12 +494,12 @@ __global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
   const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);
   const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - 64) : 0;
   const float mu = (DQ && producer) ? *a.dq.offset : 0.0f;
-  uint4 xr[XCH];
+  uint4 xr0[XCH], xr1[XCH];  // activations two steps ahead, alternating sets
   uint4 cwA[2], cwB[2];
   uint8_t qbA = 0, qbB = 0;
   float sfA = 0.0f, sfB = 0.0f;
 
-  auto load_x = [&](int kt) {
+  auto load_x = [&](int kt, uint4* xr) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int id = pt + NP * i, row = id >> 3, ch = id & 7;
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
       f = a.dq.absmax[blk];
     }
   };
-  auto store_x = [&](int buf) {
+  auto store_x = [&](int buf, const uint4* xr) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int id = pt + NP * i, row = id >> 3, ch = id & 7;
@@ -535,13 +540,16 @@ __global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
       sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
+  // produce step kt: stage nxt gets X(kt+1) (from xs, loaded two steps
+  // earlier) and the dequantised weights of kt+1; then X(kt+3) goes into xs
   auto produce = [&](int kt, const int nxt, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql,
-                     float& fl) {
+                     float& fl, uint4* xs) {
     const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
+    const int k3 = kt + 3 < nk ? kt + 3 : nk - 1;
     load_codes(k2, cl, ql, fl);
     dequant(nxt, cu, qu, fu);
-    store_x(nxt);
-    load_x(k2);
+    store_x(nxt, xs);
+    load_x(k3, xs);
   };
 
   // ---------------- consumer state
@@ -575,17 +583,18 @@ __global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
   // producer registers and consumer accumulators are never live together.
   if (producer) {
     load_codes(0, cwB, qbB, sfB);
-    load_x(0);
-    store_x(0);
+    load_x(0, xr0);
+    store_x(0, xr0);
     dequant(0, cwB, qbB, sfB);
     load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
-    load_x(nk > 1 ? 1 : 0);
+    load_x(nk > 1 ? 1 : 0, xr1);
+    load_x(nk > 2 ? 2 : nk - 1, xr0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
-      produce(kt, 1, cwA, qbA, sfA, cwB, qbB, sfB);
+      produce(kt, 1, cwA, qbA, sfA, cwB, qbB, sfB, xr1);
       __syncthreads();
       if (kt + 1 < nk) {
-        produce(kt + 1, 0, cwB, qbB, sfB, cwA, qbA, sfA);
+        produce(kt + 1, 0, cwB, qbB, sfB, cwA, qbA, sfA, xr0);
         __syncthreads();
       }
     }
@@ -1134,10 +1143,11 @@ hipError_t launch_main_any(const MainArgs& a, hipStream_t stream) {
       else
         hipLaunchKernelGGL((main_v3_kernel<BWD, false, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
 #elif defined(QLORA_MAIN_WS)
+      const dim3 grid1(cdiv(a.ncols, 256) * cdiv(a.M, 256));
       if (a.dq.double_quant)
-        hipLaunchKernelGGL((main_ws_kernel<BWD, true>), grid, dim3(WS_T), 0, stream, a);
+        hipLaunchKernelGGL((main_ws_kernel<BWD, true>), grid1, dim3(WS_T), 0, stream, a);
       else
-        hipLaunchKernelGGL((main_ws_kernel<BWD, false>), grid, dim3(WS_T), 0, stream, a);
+        hipLaunchKernelGGL((main_ws_kernel<BWD, false>), grid1, dim3(WS_T), 0, stream, a);
 #else
       const dim3 grid1(cdiv(a.ncols, 256) * cdiv(a.M, 256));
       if (a.dq.double_quant)
