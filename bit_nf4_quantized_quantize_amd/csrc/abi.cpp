@@ -101,17 +101,20 @@ int64_t quant_ws(int64_t numel, int dq) {
 }
 
 struct FwdWs {
-  int64_t part, xas, total;  // byte offsets: fp32 partials of X A, bf16 s*XA [M, rp]
-  int splits;
+  // byte offsets: fp32 partials of X A, bf16 s*XA [M, rp], and for the
+  // small-token path fp32 partials of X W^T [gemv_splits][M][N]
+  int64_t part, xas, gv, total;
+  int splits, gemv_splits;
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = round_up(r, 64);
   FwdWs w;
   w.splits = skinny_splits(M, r, K);
+  w.gemv_splits = (M >= 1 && M <= kGemvMaxM) ? gemv_splits(M, N, K) : 0;
   w.part = 0;
   w.xas = w.part + round_up((int64_t)w.splits * M * rp * 4, kAlign);
-  w.total = w.xas + round_up(M * rp * 2, kAlign);
-  (void)N;
+  w.gv = w.xas + round_up(M * rp * 2, kAlign);
+  w.total = w.gv + round_up((int64_t)w.gemv_splits * M * N * 4, kAlign);
   return w;
 }
 
@@ -288,6 +291,17 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
   if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, (uint16_t*)XA, xas, rp,
                          s, hs)) != hipSuccess)
     return hip_fail(e, fn);
+  if (L.gemv_splits > 0) {  // few tokens: weight-streaming product, then partial sums + adapter term
+    float* gv = (float*)(base + L.gv);
+    {
+      ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
+      e = launch_gemv((const uint16_t*)X, M, K, W->codes, dq_params(W), N, gv, L.gemv_splits, hs);
+    }
+    if (e != hipSuccess) return hip_fail(e, fn);
+    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, xas, rp, (const uint16_t*)B, r, (uint16_t*)Y, hs);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return QLORA_OK;
+  }
   {
     ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
     e = launch_fwd_main((const uint16_t*)X, M, K, W->codes, dq_params(W), N, xas, (const uint16_t*)B, r, rp,

@@ -199,6 +199,13 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16 (lane l of 64): A (16 x 32) row l % 16 and B
+// (32 x 16) column l % 16, each with reduction slots 8 * (l / 16) .. +7;
+// D (16 x 16) column l % 16, register j -> row 4 * (l / 16) + j.
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Row of accumulator register j of a 32x32 tile for a lane (column: lane % 32).
 __device__ __forceinline__ int acc_row32(int j, int lane) {
   return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);

@@ -59,6 +59,15 @@ hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int
 hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            const DQParams& dq, int64_t N, const uint16_t* XAs, const uint16_t* B,
                            int64_t r, int64_t rp, uint16_t* Y, hipStream_t stream);
+// Small-token forward (1 <= M <= kGemvMaxM): launch_gemv writes fp32
+// partials part[splits][M][N] of X * W_bf16^T over reduction splits, then
+// launch_gemv_reduce writes Y = bf16(sum + XAs * B).
+constexpr int kGemvMaxM = 16;
+int gemv_splits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
+                       float* part, int splits, hipStream_t stream);
+hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const uint16_t* XAs, int64_t rp,
+                              const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t stream);
 // Fused input gradient: dX = dY * W_bf16 + Ts * A_pad^T (Ts [M, rp]; A [K, r]).
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                          const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* A,

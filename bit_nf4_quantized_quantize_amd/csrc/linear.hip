@@ -965,16 +965,64 @@ __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__
 
 // out1[m][q] = bf16(sum_s part) for q < Q (optional); out2[m][q] =
 // bf16(alpha * sum_s part) for q < QP (columns >= Q are zero partials).
+// ------------------------------------------------- split-sum reductions
+// Both adapter reductions add S fp32 partial slices element by element.  A
+// chunk is 4 consecutive elements; T threads share a chunk (thread t adds
+// slices t, t + T, ...), and their T partial sums are then added in LDS in a
+// fixed order, so the result does not depend on timing.  T grows when there
+// are few chunks and many slices (few tokens), keeping the latency chain of
+// one thread short.
+
+// 4 elements of slice k at idx (elements beyond n read as 0).
+__device__ __forceinline__ float4 slice4(const float* part, int64_t k, int64_t n, int64_t idx) {
+  const float* p = part + k * n + idx;
+  if ((n & 3) == 0) return *reinterpret_cast<const float4*>(p);
+  float4 v;
+  v.x = p[0];
+  v.y = idx + 1 < n ? p[1] : 0.0f;
+  v.z = idx + 2 < n ? p[2] : 0.0f;
+  v.w = idx + 3 < n ? p[3] : 0.0f;
+  return v;
+}
+
+// Sum over the S slices of the chunk at idx; the total is valid in t == 0.
+template <int T>
+__device__ __forceinline__ float4 split_sum4(const float* part, int S, int64_t n, int64_t idx, bool ok, int t,
+                                             float4* red) {
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (ok) {
+#pragma unroll 4
+    for (int k = t; k < S; k += T) {
+      const float4 v = slice4(part, k, n, idx);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+  }
+  if (T == 1) return s;
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (t == 0) {
+    constexpr int CPW = 256 / T;
+    for (int u = 1; u < T; ++u) {
+      const float4 v = red[threadIdx.x + u * CPW];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+  }
+  return s;
+}
+
+// XA-style epilogue: out2 [M, QP] = bf16(alpha * C) (C zero in columns
+// >= Q), out1 [M, Q] = bf16(C) when given.  part is [S][M][QP], QP % 64 == 0.
+template <int T>
 __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ part, int S, int64_t M,
                                                               int64_t Q, int64_t QP, uint16_t* __restrict__ out1,
                                                               uint16_t* __restrict__ out2, float alpha) {
-  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (idx >= M * QP) return;
-  float4 s = *reinterpret_cast<const float4*>(part + idx);
-  for (int k = 1; k < S; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * M * QP + idx);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-  }
+  __shared__ float4 red[T > 1 ? 256 : 1];
+  constexpr int CPW = 256 / T;
+  const int t = threadIdx.x / CPW;
+  const int64_t idx = ((int64_t)blockIdx.x * CPW + threadIdx.x % CPW) * 4;
+  const bool ok = idx < M * QP;
+  const float4 s = split_sum4<T>(part, S, M * QP, idx, ok, t, red);
+  if (!ok || t != 0) return;
   const int64_t m = idx / QP, q = idx - m * QP;
   const float sv[4] = {s.x, s.y, s.z, s.w};
   uint2 o;
@@ -1073,26 +1121,25 @@ __global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, 
 }
 
 // out[p][q] = bf16(alpha * sum_s part[s][p][q]), part [S][P][Q], out [P][Q].
+// out [PQ] = bf16(alpha * sum of the S slices of part [S][PQ]).
+template <int T>
 __global__ __launch_bounds__(256) void tn_reduce_kernel(const float* __restrict__ part, int S, int64_t PQ,
                                                         uint16_t* __restrict__ out, float alpha) {
-  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (idx >= PQ) return;
+  __shared__ float4 red[T > 1 ? 256 : 1];
+  constexpr int CPW = 256 / T;
+  const int t = threadIdx.x / CPW;
+  const int64_t idx = ((int64_t)blockIdx.x * CPW + threadIdx.x % CPW) * 4;
+  const bool ok = idx < PQ;
+  const float4 s = split_sum4<T>(part, S, PQ, idx, ok, t, red);
+  if (!ok || t != 0) return;
   if (idx + 4 <= PQ && (PQ & 3) == 0) {
-    float4 s = *reinterpret_cast<const float4*>(part + idx);
-    for (int k = 1; k < S; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * PQ + idx);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
     uint2 o;
     o.x = pack_bf2(alpha * s.x, alpha * s.y);
     o.y = pack_bf2(alpha * s.z, alpha * s.w);
     *reinterpret_cast<uint2*>(out + idx) = o;
   } else {
-    for (int64_t e = idx; e < idx + 4 && e < PQ; ++e) {
-      float s = 0.0f;
-      for (int k = 0; k < S; ++k) s += part[(int64_t)k * PQ + e];
-      out[e] = f2bf(alpha * s);
-    }
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+    for (int e = 0; e < 4 && idx + e < PQ; ++e) out[idx + e] = f2bf(alpha * sv[e]);
   }
 }
 
@@ -1101,7 +1148,210 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
   if (idx < n) dst[idx] = 0;
 }
 
+// ================================ small-token forward (M <= kGemvMaxM)
+// With a handful of tokens the forward is a stream over the packed weight
+// (0.516 bytes per parameter) and every weight is used M times, so the
+// per-block bf16 table of the large kernels (about 4 VALU operations per
+// weight) would cost more than the weight's HBM time.  Here the weight is
+// expanded through one constant table in LDS: entry b (a code byte) holds
+// bf16(NF4[b & 15]) | bf16(NF4[b >> 4]) << 16, the two unscaled codebook
+// values of that byte in element order, so 8 codes are 4 LDS reads.  A
+// block's 64-term partial product comes from two 16x16x32 MFMAs (tokens as
+// rows, weight rows as columns) and is then scaled by the block constant
+// c2_hat in fp32.  The codebook value, not its product with c2_hat, is
+// rounded to bf16 here, an error of the same size as the bf16 rounding of
+// the product.
+//
+// Reduction order inside a block: lane group g = lane / 16 holds the 16
+// consecutive codes k0 + 16g .. +15 of its row (one 8-byte load); MFMA s of
+// the block takes codes 16g + 8s .. +7 from every group, and the activation
+// fragment is loaded with the same assignment.
+//
+// Grid: 64-row weight tiles x S reduction splits of at most GV_MAXB blocks.
+// The workgroup first decodes the block constants of its rows over its split
+// into LDS (coalesced reads of the E4M3 bytes; zero past the split's end).
+// Each of the 8 waves then takes a contiguous run of the split's blocks and
+// covers all four 16-row column tiles of the workgroup (one shared
+// activation fragment), keeping the loads of the next two blocks in flight
+// while it multiplies one.  The waves' partial tiles are added in LDS,
+// giving fp32 partials part[S][M][N].
+constexpr int GV_WAVES = 8;
+constexpr int GV_T = GV_WAVES * 64;
+constexpr int GV_ROWS = 64;
+constexpr int GV_CT = GV_ROWS / 16;    // 16-row column tiles per wave
+constexpr int GV_DEPTH = 3;            // blocks held in registers per wave
+constexpr int GV_QUANT = GV_WAVES * GV_DEPTH;  // blocks per split: a multiple of this
+constexpr int GV_MAXB = 5 * GV_QUANT;  // at most 120 blocks per split
+constexpr int GV_SMEM = (GV_ROWS * (GV_MAXB + 1) > GV_WAVES * kGemvMaxM * (GV_ROWS + 1))
+                            ? GV_ROWS * (GV_MAXB + 1)
+                            : GV_WAVES * kGemvMaxM * (GV_ROWS + 1);
+
+struct GvBlock {
+  uint2 cw[GV_CT];  // 16 codes of each row n_t: k0 + 16g .. +15
+  uint4 x[2];       // X[m, k0 + 16g .. +15]
+};
+
+__device__ __forceinline__ bf16x8 tab_lookup8(const uint32_t* tab, uint32_t w) {
+  const uint4 v = make_uint4(tab[w & 0xFF], tab[(w >> 8) & 0xFF], tab[(w >> 16) & 0xFF], tab[w >> 24]);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool DQ>
+__global__ __launch_bounds__(GV_T, 4) void gemv_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
+                                                      const uint8_t* __restrict__ codes, const DQParams dq, int64_t N,
+                                                      int bps, float* __restrict__ part) {
+  __shared__ uint32_t tab[256];
+  // block constants cs[row][j] during the main loop, then the partial tiles
+  // red[wave][m][row] of the waves
+  __shared__ float smem[GV_SMEM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const int64_t nbk = K >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * GV_ROWS;
+  const int64_t b_lo = (int64_t)blockIdx.y * bps;
+  const int nbs = (int)(nbk - b_lo < bps ? nbk - b_lo : bps);  // blocks in this split, >= 1
+  const int cpitch = bps + 1;
+  {
+    // thread -> row tid / 8, blocks j = tid % 8 + 8u: all loads are issued
+    // before any is used (the pass count is at most GV_MAXB / 8)
+    constexpr int TPR = GV_T / GV_ROWS, PASSES = GV_MAXB / TPR;
+    const int r = tid / TPR, j0c = tid % TPR;
+    const bool row_ok = n0 + r < N;
+    const int64_t blk0 = (row_ok ? n0 + r : 0) * nbk + b_lo;
+    uint32_t qv[PASSES];
+    float fv[PASSES];
+#pragma unroll
+    for (int u = 0; u < PASSES; ++u) {
+      const int j = j0c + TPR * u;
+      const int64_t blk = blk0 + (j < nbs ? j : 0);
+      if (DQ) {
+        qv[u] = dq.absmax_q[blk];
+        fv[u] = dq.scale2[blk >> 8];
+      } else {
+        qv[u] = 0;
+        fv[u] = dq.absmax[blk];
+      }
+    }
+    const float mu = DQ ? *dq.offset : 0.0f;
+    if (tid < 256) tab[tid] = pack_bf2(kNF4c[tid & 15], kNF4c[tid >> 4]);
+#pragma unroll
+    for (int u = 0; u < PASSES; ++u) {
+      const int j = j0c + TPR * u;
+      if (j < bps) {
+        const float c = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qv[u]), fv[u]), mu) : fv[u];
+        smem[r * cpitch + j] = (row_ok && j < nbs) ? c : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int col = lane & 15, g = lane >> 4;
+  // rows beyond N read row N - 1 (their constants are zero)
+  const uint8_t* cbase = codes + ((n0 * K) >> 1);
+  uint32_t coff[GV_CT];
+#pragma unroll
+  for (int t = 0; t < GV_CT; ++t) {
+    const int64_t rr = n0 + 16 * t + col < N ? 16 * t + col : N - 1 - n0;
+    coff[t] = (uint32_t)((rr * K + 16 * g) >> 1);
+  }
+  // MFMA row = token index; rows M..15 repeat token M-1 and are never stored
+  const uint16_t* xp = X + (int64_t)(col < M ? col : M - 1) * K + 16 * g;
+  const int bpw = bps / GV_WAVES;    // blocks per wave, a multiple of GV_DEPTH
+  const int j0 = wave * bpw;         // first block of this wave, relative to b_lo
+  const int64_t blast = b_lo + nbs - 1;
+
+  auto load = [&](int j, GvBlock& d) {
+    const int64_t b = b_lo + j <= blast ? b_lo + j : blast;  // past the end: weighted by zero
+#pragma unroll
+    for (int t = 0; t < GV_CT; ++t) d.cw[t] = *reinterpret_cast<const uint2*>(cbase + coff[t] + b * 32);
+    d.x[0] = ldg16(xp + b * 64);
+    d.x[1] = ldg16(xp + b * 64 + 8);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the math that follows
+  };
+  floatx4 acc[GV_CT];
+#pragma unroll
+  for (int t = 0; t < GV_CT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][e] = 0.0f;
+  auto compute = [&](int j, const GvBlock& d) {
+    const bf16x8 x0 = __builtin_bit_cast(bf16x8, d.x[0]), x1 = __builtin_bit_cast(bf16x8, d.x[1]);
+#pragma unroll
+    for (int t = 0; t < GV_CT; ++t) {
+      const float c = smem[(16 * t + col) * cpitch + j];
+      floatx4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+      p = mfma16(x0, tab_lookup8(tab, d.cw[t].x), p);
+      p = mfma16(x1, tab_lookup8(tab, d.cw[t].y), p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] = __builtin_fmaf(c, p[e], acc[t][e]);
+    }
+  };
+
+  GvBlock A, B, C;
+  load(j0, A);
+  load(j0 + 1, B);
+  for (int i = 0; i < bpw; i += GV_DEPTH) {
+    const int j = j0 + i;
+    load(j + 2, C);
+    compute(j, A);
+    load(j + 3, A);  // past this wave's run on the last pass: unused
+    compute(j + 1, B);
+    load(j + 4, B);
+    compute(j + 2, C);
+  }
+  __syncthreads();  // constants no longer needed: smem becomes red
+
+  float* red = smem;  // [wave][m][GV_ROWS + 1]
+#pragma unroll
+  for (int t = 0; t < GV_CT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(wave * kGemvMaxM + 4 * g + e) * (GV_ROWS + 1) + 16 * t + col] = acc[t][e];
+  __syncthreads();
+  for (int o = tid; o < M * GV_ROWS; o += GV_T) {
+    const int m = o / GV_ROWS, c = o % GV_ROWS;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; ++w) v += red[(w * kGemvMaxM + m) * (GV_ROWS + 1) + c];
+    if (n0 + c < N) part[((int64_t)blockIdx.y * M + m) * N + n0 + c] = v;
+  }
+}
+
+// Y[m, n] = bf16(sum_s part[s][m][n] + sum_j XAs[m, j] B[j, n]); one token
+// row per blockIdx.y, 4 columns per thread (N % 4 == 0).
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int S, int M, int64_t N,
+                                                          const uint16_t* __restrict__ XAs, int64_t rp,
+                                                          const uint16_t* __restrict__ B, int r,
+                                                          uint16_t* __restrict__ Y) {
+  const int64_t nc = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int m = blockIdx.y;
+  if (nc >= N) return;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + m) * N + nc);
+    a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
+  }
+  const uint16_t* xa = XAs + (int64_t)m * rp;
+#pragma unroll 8
+  for (int j = 0; j < r; ++j) {
+    const float x = bf2f(xa[j]);
+    const uint2 bv = *reinterpret_cast<const uint2*>(B + (int64_t)j * N + nc);
+    a0 = __builtin_fmaf(x, __uint_as_float(bv.x << 16), a0);
+    a1 = __builtin_fmaf(x, __uint_as_float(bv.x & 0xFFFF0000u), a1);
+    a2 = __builtin_fmaf(x, __uint_as_float(bv.y << 16), a2);
+    a3 = __builtin_fmaf(x, __uint_as_float(bv.y & 0xFFFF0000u), a3);
+  }
+  *reinterpret_cast<uint2*>(Y + (int64_t)m * N + nc) = make_uint2(pack_bf2(a0, a1), pack_bf2(a2, a3));
+}
+
 inline unsigned cdiv(int64_t n, int64_t d) { return (unsigned)((n + d - 1) / d); }
+
+// Threads per chunk for the split-sum reductions: double while the grid has
+// fewer than 64K threads and each thread would still add several slices.
+int split_sum_threads(int64_t chunks, int S) {
+  int T = 1;
+  while (T < 64 && chunks * T < 65536 && 4 * T < S) T *= 2;
+  return T;
+}
 
 // ------------------------------------------------ main-GEMM tile choice
 // Candidate tiles and a rough per-tile cost (relative MFMA time of a tile,
@@ -1188,8 +1438,14 @@ hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int
     hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(skinny_epilogue_kernel, dim3(cdiv(M * QP / 4, 256)), dim3(256), 0, stream, part, splits, M, Q,
-                     QP, out1, out2, alpha);
+  const int T = split_sum_threads(cdiv(M * QP, 4), splits);
+#define QLORA_EPI(TT)                                                                                        \
+  case TT:                                                                                                   \
+    hipLaunchKernelGGL(skinny_epilogue_kernel<TT>, dim3(cdiv(cdiv(M * QP, 4), 256 / TT)), dim3(256), 0, stream, \
+                       part, splits, M, Q, QP, out1, out2, alpha);                                           \
+    break;
+  switch (T) { QLORA_EPI(1) QLORA_EPI(2) QLORA_EPI(4) QLORA_EPI(8) QLORA_EPI(16) QLORA_EPI(32) default: QLORA_EPI(64) }
+#undef QLORA_EPI
   return hipGetLastError();
 }
 
@@ -1218,8 +1474,14 @@ hipError_t launch_gemm_tn(const uint16_t* U, int64_t ldu, int64_t P, const uint1
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tn_reduce_kernel, dim3(cdiv(P * Q / 4 + 1, 256)), dim3(256), 0, stream, partials, splits, P * Q,
-                     out, alpha);
+  const int T = split_sum_threads(cdiv(P * Q, 4), splits);
+#define QLORA_RED(TT)                                                                                           \
+  case TT:                                                                                                      \
+    hipLaunchKernelGGL(tn_reduce_kernel<TT>, dim3(cdiv(cdiv(P * Q, 4), 256 / TT)), dim3(256), 0, stream, partials, \
+                       splits, P * Q, out, alpha);                                                              \
+    break;
+  switch (T) { QLORA_RED(1) QLORA_RED(2) QLORA_RED(4) QLORA_RED(8) QLORA_RED(16) QLORA_RED(32) default: QLORA_RED(64) }
+#undef QLORA_RED
   return hipGetLastError();
 }
 
@@ -1238,6 +1500,54 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
   a.ext_act = XAs; a.ext_w = B; a.r = r; a.rp = rp;
   a.out = Y; a.ncols = N;
   return launch_main_any<false>(a, stream);
+}
+
+// Blocks per split: a multiple of GV_QUANT (GV_DEPTH per loop pass for each
+// wave), at most GV_MAXB.
+int64_t gemv_blocks_per_split(int64_t nbk, int64_t splits) {
+  return ((nbk + splits - 1) / splits + GV_QUANT - 1) / GV_QUANT * GV_QUANT;
+}
+
+int gemv_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = (int64_t)cdiv(N, GV_ROWS), nbk = K >> 6;
+  // about 16 waves per CU over the whole grid
+  int64_t s = (512 + tiles - 1) / tiles;
+  // keep the fp32 partials (S * M * N * 4 bytes, written and read once)
+  // below about 1/16 of the packed weight (N * K / 2 bytes)
+  const int64_t by_bytes = K / (128 * (M > 0 ? M : 1));
+  if (s > by_bytes) s = by_bytes;
+  const int64_t by_blocks = nbk / GV_QUANT;  // a full pass for every wave
+  if (s > by_blocks) s = by_blocks;
+  const int64_t min_s = (nbk + GV_MAXB - 1) / GV_MAXB;  // the constants must fit in LDS
+  if (s < min_s) s = min_s;
+  if (s < 1) s = 1;
+  // the split count that the rounded block count actually gives; every
+  // split then holds at least one block
+  const int64_t bps = gemv_blocks_per_split(nbk, s);
+  return (int)((nbk + bps - 1) / bps);
+}
+
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
+                       float* part, int splits, hipStream_t stream) {
+  if (M < 1 || M > kGemvMaxM || splits < 1) return hipErrorInvalidValue;
+  const int64_t nbk = K >> 6;
+  const int bps = (int)gemv_blocks_per_split(nbk, splits);
+  if ((int64_t)(splits - 1) * bps >= nbk || bps > GV_MAXB || (int64_t)splits * bps < nbk)
+    return hipErrorInvalidValue;  // an empty split, or constants beyond the LDS table
+  const dim3 grid(cdiv(N, GV_ROWS), (unsigned)splits);
+  if (dq.double_quant)
+    hipLaunchKernelGGL((gemv_kernel<true>), grid, dim3(GV_T), 0, stream, X, (int)M, K, codes, dq, N, bps, part);
+  else
+    hipLaunchKernelGGL((gemv_kernel<false>), grid, dim3(GV_T), 0, stream, X, (int)M, K, codes, dq, N, bps, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const uint16_t* XAs, int64_t rp,
+                              const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t stream) {
+  if (N % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemv_reduce_kernel, dim3(cdiv(N, 1024), (unsigned)M), dim3(256), 0, stream, part, splits, (int)M,
+                     N, XAs, rp, B, (int)r, Y);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes, const DQParams& dq,

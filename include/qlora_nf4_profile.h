@@ -25,7 +25,7 @@ extern "C" {
 typedef enum {
   QLORA_KERNEL_QUANTIZE = 0,   /* NF4 codes + block absmax (qlora_nf4_quantize)   */
   QLORA_KERNEL_DEQUANTIZE = 1, /* qlora_nf4_dequantize                            */
-  QLORA_KERNEL_FWD_MAIN = 2,   /* fused dequant GEMM of qlora_linear_fwd          */
+  QLORA_KERNEL_FWD_MAIN = 2,   /* weight product of qlora_linear_fwd: the fused dequant GEMM, or for M <= 16 the weight-streaming kernel */
   QLORA_KERNEL_BWD_DX = 3,     /* fused dequant GEMM for dX in qlora_linear_bwd   */
   QLORA_KERNEL_COUNT = 4
 } qlora_kernel_id;

@@ -143,6 +143,16 @@ def test_ragged_shapes(B, M, N, K, r):
     _full_check(B, M, N, K, r, 16.0 / r, seed=M * 7 + N + K + r)
 
 
+@pytest.mark.parametrize("M,N,K,dq", [(1, 64, 192, True), (2, 128, 64 * 37, True), (5, 192, 64 * 130, True),
+                                        (16, 256, 64 * 9, True), (16, 1024, 4096, True), (3, 320, 64 * 21, False),
+                                        (17, 128, 64 * 11, True)])
+def test_small_token_path(B, M, N, K, dq):
+    """1..16 tokens take the weight-streaming forward (split reduction with
+    a ragged last split); 17 tokens the tiled kernel."""
+    _log(f"linear small-token M={M} N={N} K={K} dq={dq}")
+    _full_check(B, M, N, K, 64, 0.25, seed=M * 1000 + K // 64, dq=dq)
+
+
 def test_no_double_quant(B):
     _log("linear without double quantisation")
     _full_check(B, 96, 256, 256, 16, 1.0, seed=5, dq=False)
