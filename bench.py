@@ -6,13 +6,23 @@ workload: NF4 quantisation with double quantisation of the fp32 weight,
 dequantisation to bf16, the fused forward, and the backward (dX, dA, dB).
 Inputs are drawn once and stay resident in HBM; the weight is rotated over
 several copies (> 256 MB in total) so the quantiser does not read it from the
-Infinity Cache.
+Infinity Cache.  Workload 5 (small batch) times only the forward at 1, 4 and
+16 tokens against one NF4 weight (rotated copies) and reports GB/s.
+
+Measurement:
+  1. W untimed warm-up steps;
+  2. a breakdown pass of a few steps with HIP events around every library
+     kernel of interest and every phase (these events cost a few us each, so
+     this pass is not used for `value`);
+  3. the timed region: K steps bracketed by synchronisation, with events
+     only around the dominant kernel (found in pass 2), recorded by the
+     library on the kernel's own launch stream; its mean duration over the
+     K launches gives `roofline.achieved`.
 
 Prints one JSON line.  `value` is the step's algorithmic fwd+bwd flops
-(4MNK + 6Mr(K+N) per linear) over the measured step time, in TFLOP/s.
-`roofline` describes the dominant kernel, timed with HIP events recorded on
-its launch stream around every launch inside the timed region.
-`cpu_baseline` times the CPU oracle on the same workload (rank 0, N = 1).
+(4MNK + 6Mr(K+N) per linear) over the measured step time, in TFLOP/s (GB/s
+of algorithmic bytes for workload 5).  `cpu_baseline` times the CPU oracle
+on a bounded sample of the same workload (rank 0, N = 1).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload 2]
 """
@@ -24,6 +34,7 @@ import sys
 import time
 
 METRIC = "QLoRA linear fwd+bwd TFLOP/s and quantize GB/s (fraction of roofline), 1 GPU"
+SMALL_METRIC = "QLoRA small-batch forward GB/s (fraction of HBM roofline), 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
@@ -38,6 +49,7 @@ WORKLOAD_NAMES = {
     2: "7B attention projection: W 4096x4096 NF4+DQ, X 4096x4096 bf16 (4 x 1024 tokens), r=64, alpha=16",
     3: "7B MLP block: gate/up 11008x4096 + down 4096x11008 NF4+DQ, 2048 tokens, r=64, alpha=16",
     4: "65B-shaped MLP: gate/up 22016x8192 + down 8192x22016 NF4+DQ (Student-t), 8192 tokens, r=64, alpha=16",
+    5: "small batch: 1, 4 and 16 tokens against the 8192x22016 NF4+DQ weight (Student-t), r=64, alpha=16, fwd only",
 }
 
 
@@ -89,33 +101,97 @@ def linear_flops(lin):
     return 4 * lin.M * lin.N * lin.K + 6 * lin.M * lin.r * (lin.K + lin.N)
 
 
-def cpu_baseline(lin, tensors):
-    """Time the CPU oracle on one full step of one linear: quantise with double
-    quantisation, dequantise, forward and backward in fp64."""
-    import numpy as np
+def _blas_threads():
     from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
 
+
+def cpu_baseline(lin, tensors, min_s=10.0, max_steps=20):
+    """Time the CPU oracle on full steps of one linear (quantise with double
+    quantisation, dequantise, forward and backward in fp64), repeated until
+    about min_s seconds of CPU work have run."""
     from oracle import blockwise, linear
 
     W = tensors["W"].cpu().numpy()
     X, A, Bm, dY = (tensors[k].float().cpu().numpy() for k in ("X", "A", "B", "dY"))
     t0 = time.perf_counter()
-    st = blockwise.quantize(W, double_quant=True)
-    Wb = blockwise.bf16_round(st.dequantize())
-    Y, XA = linear.forward(X, Wb, A, Bm, lin.s)
-    dX, dA, dB = linear.backward(dY, X, Wb, A, Bm, lin.s)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    del Y, XA, dX, dA, dB, np
+    n = 0
+    while n < max_steps and (n == 0 or time.perf_counter() - t0 < min_s):
+        st = blockwise.quantize(W, double_quant=True)
+        Wb = blockwise.bf16_round(st.dequantize())
+        Y, XA = linear.forward(X, Wb, A, Bm, lin.s)
+        dX, dA, dB = linear.backward(dY, X, Wb, A, Bm, lin.s)
+        del st, Wb, Y, XA, dX, dA, dB
+        n += 1
+    dt = (time.perf_counter() - t0) / n
+    threads = _blas_threads()
     return {
         "value": linear_flops(lin) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"one full step of the {lin.name} linear ({lin.N}x{lin.K} weight, {lin.M} tokens, r={lin.r}): "
-                   f"oracle quantise+DQ, dequantise, fwd and bwd in fp64 numpy; {dt:.2f} s; "
+        "sample": (f"{n} full steps of the {lin.name} linear ({lin.N}x{lin.K} weight, {lin.M} tokens, r={lin.r}): "
+                   f"oracle quantise+DQ, dequantise, fwd and bwd in fp64 numpy; {dt:.2f} s per step; "
                    f"BLAS threads {threads}, os.cpu_count() {os.cpu_count()}"),
     }
+
+
+def cpu_baseline_small(L, rows=1024, min_s=10.0, max_reps=50):
+    """Time the CPU oracle's forward at the largest token count on a slice of
+    the weight's rows (dequantise the slice from its stored state, then the
+    fp64 product), repeated for about min_s seconds; GB/s over the same
+    algorithmic bytes per weight as the GPU figure."""
+    import torch
+
+    from oracle import blockwise, linear
+
+    lin = L["lin"]
+    g = torch.Generator().manual_seed(1234)
+    Wr = (torch.randn(rows, lin.K, generator=g) * 0.02).numpy()
+    st = blockwise.quantize(Wr, double_quant=True)
+    X = L["X"].float().cpu().numpy()
+    A = L["A"].float().cpu().numpy()
+    Bm = L["B"].float().cpu().numpy()[:, :rows]
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_reps and (n == 0 or time.perf_counter() - t0 < min_s):
+        Wb = blockwise.bf16_round(st.dequantize())
+        Y, XA = linear.forward(X, Wb, A, Bm, lin.s)
+        del Wb, Y, XA
+        n += 1
+    dt = (time.perf_counter() - t0) / n
+    gb = STORED_BYTES_PER_PARAM * rows * lin.K + 2 * lin.M * (lin.K + rows) + 2 * lin.r * (lin.K + rows)
+    threads = _blas_threads()
+    return {
+        "value": gb / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n} forwards of {lin.M} tokens against a {rows}x{lin.K} slice of the weight (oracle "
+                   f"dequantise from the stored NF4+DQ state, fp64 product); {dt * 1e3:.1f} ms each; "
+                   f"BLAS threads {threads}, os.cpu_count() {os.cpu_count()}"),
+    }
+
+
+def _dominant(per, layers, small):
+    """(kernel, bound, algorithmic work, mean us, linear index) of the kernel
+    with the largest share of the step, from a per-linear kernel breakdown.
+    The small-token forward kernel streams the packed weight (HBM-bound)."""
+    best = None
+    for li, (kt, _) in enumerate(per):
+        lin = layers[li]["lin"]
+        p = lin.N * lin.K
+        cands = [
+            ("fwd_main", "hbm", STORED_BYTES_PER_PARAM * p) if small else
+            ("fwd_main", "mfma", 2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * lin.N),
+            ("bwd_dx", "mfma", 2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * lin.K),
+            ("quantize", "hbm", QUANT_BYTES_PER_PARAM * p),
+            ("dequantize", "hbm", DEQUANT_BYTES_PER_PARAM * p),
+        ]
+        for name, bound, work in cands:
+            if name in kt and (best is None or kt[name] > best[3]):
+                best = (name, bound, work, kt[name], li)
+    return best
 
 
 def main():
@@ -138,150 +214,175 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     bf = torch.bfloat16
+    small = args.workload == 5
 
     lins = synth.workload(args.workload)
-    wbytes = sum(l.N * l.K * 4 for l in lins)
-    rotate = args.rotate or max(1, -(-(300 << 20) // wbytes))
-    layers = []
-    for lin in lins:
-        t = lin.draw(dev)
-        st = {
-            "lin": lin, "t": t,
-            "W": [t["W"]] + [t["W"].clone() for _ in range(rotate - 1)],
-            "qw": B.NF4Weight(lin.N, lin.K, True, dev),
-            "Wd": torch.empty(lin.N, lin.K, dtype=bf, device=dev),
-            "Y": torch.empty(lin.M, lin.N, dtype=bf, device=dev),
-            "XA": torch.empty(lin.M, lin.r, dtype=bf, device=dev),
-            "dX": torch.empty(lin.M, lin.K, dtype=bf, device=dev),
-            "dA": torch.empty(lin.K, lin.r, dtype=bf, device=dev),
-            "dB": torch.empty(lin.r, lin.N, dtype=bf, device=dev),
-            "ws": B.Workspace(),
-            "qws": torch.empty(max(B.qlora_nf4_quantize_workspace(lin.N * lin.K, True), 16),
-                               dtype=torch.uint8, device=dev),
-        }
-        layers.append(st)
+    if small:
+        # the three token counts share one weight (rows drawn for the largest)
+        base = lins[-1]
+        t0 = base.draw(dev, with_grad=False)
+        wbytes = base.N * base.K * 0.516
+        rotate = args.rotate or max(1, -(-(300 << 20) // int(wbytes)))
+        qws = [B.qlora_nf4_quantize(t0["W"] * (1.0 + 1e-3 * i)) for i in range(rotate)]
+        del t0["W"]
+        layers = []
+        for lin in lins:
+            layers.append({"lin": lin, "X": t0["X"][:lin.M].contiguous(), "A": t0["A"], "B": t0["B"],
+                           "Y": torch.empty(lin.M, lin.N, dtype=bf, device=dev),
+                           "XA": torch.empty(lin.M, lin.r, dtype=bf, device=dev), "ws": B.Workspace()})
+        kernels = ("fwd_main",)
+        phases = ("fwd",)
+    else:
+        wbytes = sum(l.N * l.K * 4 for l in lins)
+        rotate = args.rotate or max(1, -(-(300 << 20) // wbytes))
+        layers = []
+        for lin in lins:
+            t = lin.draw(dev)
+            layers.append({
+                "lin": lin, "t": t,
+                "W": [t["W"]] + [t["W"].clone() for _ in range(rotate - 1)],
+                "qw": B.NF4Weight(lin.N, lin.K, True, dev),
+                "Wd": torch.empty(lin.N, lin.K, dtype=bf, device=dev),
+                "Y": torch.empty(lin.M, lin.N, dtype=bf, device=dev),
+                "XA": torch.empty(lin.M, lin.r, dtype=bf, device=dev),
+                "dX": torch.empty(lin.M, lin.K, dtype=bf, device=dev),
+                "dA": torch.empty(lin.K, lin.r, dtype=bf, device=dev),
+                "dB": torch.empty(lin.r, lin.N, dtype=bf, device=dev),
+                "ws": B.Workspace(),
+                "qws": torch.empty(max(B.qlora_nf4_quantize_workspace(lin.N * lin.K, True), 16),
+                                   dtype=torch.uint8, device=dev),
+            })
+        kernels = ("quantize", "dequantize", "fwd_main", "bwd_dx")
+        phases = ("quantize", "dequantize", "fwd", "bwd")
 
-    kernels = ("quantize", "dequantize", "fwd_main", "bwd_dx")
-    phases = ("quantize", "dequantize", "fwd", "bwd")
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     hev = HipEvents()
-    # one event pair per (timed step, linear, kernel), created before timing
-    kpool = [[{k: (hev.create(), hev.create()) for k in kernels} for _ in layers] for _ in range(args.steps)]
+    tev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(i, rec):
+    def run_step(i, kev=None, pe=None):
+        """One step.  kev[li][kernel] = (start, stop) hipEvents attached to
+        library kernels; pe[li] = torch events between the phases."""
         for li, L in enumerate(layers):
-            lin, t = L["lin"], L["t"]
-            kev = kpool[i][li] if rec is not None else None
-            if kev:
-                for k in kernels:
-                    B.lib().qlora_profile_events(B.QLORA_KERNEL[k], kev[k][0], kev[k][1])
-            pe = [ev() for _ in range(5)] if rec is not None else None
-            if pe:
-                pe[0].record()
-            B.qlora_nf4_quantize(L["W"][i % rotate], double_quant=True, out=L["qw"], workspace=L["qws"])
-            if pe:
-                pe[1].record()
-            B.qlora_nf4_dequantize(L["qw"], bf, out=L["Wd"])
-            if pe:
-                pe[2].record()
-            B.qlora_linear_fwd(t["X"], L["qw"], t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
-            if pe:
-                pe[3].record()
-            B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], L["qw"], t["A"], t["B"], lin.s,
-                               dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
-            if pe:
-                pe[4].record()
-                rec.append((li, kev, pe))
-        if rec is not None:
+            lin = L["lin"]
+            if kev is not None:
+                for k, (e0, e1) in kev[li].items():
+                    B.lib().qlora_profile_events(B.QLORA_KERNEL[k], e0, e1)
+            marks = pe[li] if pe is not None else None
+            if marks:
+                marks[0].record()
+            if small:
+                B.qlora_linear_fwd(L["X"], qws[i % rotate], L["A"], L["B"], lin.s, Y=L["Y"], XA=L["XA"],
+                                   workspace=L["ws"])
+                if marks:
+                    marks[1].record()
+            else:
+                t = L["t"]
+                B.qlora_nf4_quantize(L["W"][i % rotate], double_quant=True, out=L["qw"], workspace=L["qws"])
+                if marks:
+                    marks[1].record()
+                B.qlora_nf4_dequantize(L["qw"], bf, out=L["Wd"])
+                if marks:
+                    marks[2].record()
+                B.qlora_linear_fwd(t["X"], L["qw"], t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
+                if marks:
+                    marks[3].record()
+                B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], L["qw"], t["A"], t["B"], lin.s,
+                                   dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
+                if marks:
+                    marks[4].record()
+        if kev is not None:
             for k in kernels:
                 B.lib().qlora_profile_events(B.QLORA_KERNEL[k], None, None)
 
     for i in range(args.warmup):
-        step(i, None)
+        run_step(i)
     torch.cuda.synchronize()
-    rec = []
-    start, stop = ev(), ev()
+
+    # 1) breakdown pass (untimed for `value`): events around every kernel and phase
+    nprof = max(3, min(args.steps, 10))
+    kev_all = [[{k: (hev.create(), hev.create()) for k in kernels} for _ in layers] for _ in range(nprof)]
+    pe_all = [[[tev() for _ in range(len(phases) + 1)] for _ in layers] for _ in range(nprof)]
+    for i in range(nprof):
+        run_step(args.warmup + i, kev_all[i], pe_all[i])
+    torch.cuda.synchronize()
+    per = []
+    for li in range(len(layers)):
+        kt = {k: sum(hev.elapsed_ms(*kev_all[i][li][k]) for i in range(nprof)) * 1e3 / nprof for k in kernels}
+        pt = {p: sum(pe_all[i][li][j].elapsed_time(pe_all[i][li][j + 1]) for i in range(nprof)) * 1e3 / nprof
+              for j, p in enumerate(phases)}
+        per.append((kt, pt))
+    name, bound, work, _, dli = _dominant(per, layers, small)
+
+    # 2) timed region: K steps, events only around the dominant kernel
+    kev_t = [[{name: (hev.create(), hev.create())} if li == dli else {} for li in range(len(layers))]
+             for _ in range(args.steps)]
+    start, stop = tev(), tev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(i, rec)
+        run_step(args.warmup + nprof + i, kev_t[i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(stop) / args.steps
-
-    # per-kernel and per-phase averages (microseconds), per linear
-    per = []
-    for li, L in enumerate(layers):
-        kt = {k: [] for k in kernels}
-        pt = {p: [] for p in phases}
-        for (lj, kev, pe) in rec:
-            if lj != li:
-                continue
-            for k in kernels:
-                kt[k].append(hev.elapsed_ms(kev[k][0], kev[k][1]) * 1e3)
-            for j, p in enumerate(phases):
-                pt[p].append(pe[j].elapsed_time(pe[j + 1]) * 1e3)
-        per.append(({k: sum(v) / len(v) for k, v in kt.items()}, {p: sum(v) / len(v) for p, v in pt.items()}))
-
+    us = sum(hev.elapsed_ms(*kev_t[i][dli][name]) for i in range(args.steps)) * 1e3 / args.steps
     hev.close()
+
+    if bound == "mfma":
+        achieved = work / us / 1e6
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        achieved = work / us / 1e3
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof.update({"kernel": name, "linear": layers[dli]["lin"].name, "algorithmic_per_launch": work,
+                 "avg_launch_us": us})
+
     breakdown = []
-    dominant = None
     for (kt, pt), L in zip(per, layers):
         lin = L["lin"]
         p = lin.N * lin.K
-        fwd_main_flops = 2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * lin.N
-        bwd_dx_flops = 2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * lin.K
-        rows = {
-            "linear": lin.name, "M": lin.M, "N": lin.N, "K": lin.K, "r": lin.r,
-            "quantize_call_us": pt["quantize"], "quantize_kernel_us": kt["quantize"],
-            "quantize_GBps": QUANT_BYTES_PER_PARAM * p / pt["quantize"] / 1e3,
-            "dequantize_us": kt["dequantize"],
-            "dequantize_GBps": DEQUANT_BYTES_PER_PARAM * p / kt["dequantize"] / 1e3,
-            "fwd_us": pt["fwd"], "fwd_main_kernel_us": kt["fwd_main"],
-            "fwd_TFLOPs": (2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * (lin.K + lin.N)) / pt["fwd"] / 1e6,
-            "bwd_us": pt["bwd"], "bwd_dx_kernel_us": kt["bwd_dx"],
-            "bwd_TFLOPs": (2 * lin.M * lin.N * lin.K + 4 * lin.M * lin.r * (lin.K + lin.N)) / pt["bwd"] / 1e6,
-        }
-        breakdown.append(rows)
-        cands = [
-            ("fwd_main", "mfma", fwd_main_flops, kt["fwd_main"]),
-            ("bwd_dx", "mfma", bwd_dx_flops, kt["bwd_dx"]),
-            ("quantize", "hbm", (4.0 + 0.5) * p + 4.0 * (p // 64), kt["quantize"]),
-            ("dequantize", "hbm", DEQUANT_BYTES_PER_PARAM * p, kt["dequantize"]),
-        ]
-        for c in cands:
-            if dominant is None or c[3] > dominant[3]:
-                dominant = c + (lin.name,)
-
-    name, bound, work, us, lname = dominant
-    if bound == "mfma":
-        achieved = work / us / 1e6
-        roof = {"kernel": name, "linear": lname, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
-                "algorithmic_per_launch": work, "avg_launch_us": us}
-    else:
-        achieved = work / us / 1e3
-        roof = {"kernel": name, "linear": lname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "algorithmic_per_launch": work, "avg_launch_us": us}
-
-    flops = sum(linear_flops(L["lin"]) for L in layers)
-    value = flops / (ms_per_step / 1e3) / 1e12
-    q_bytes = sum(QUANT_BYTES_PER_PARAM * L["lin"].N * L["lin"].K for L in layers)
-    q_us = sum(b["quantize_call_us"] for b in breakdown)
+        row = {"linear": lin.name, "M": lin.M, "N": lin.N, "K": lin.K, "r": lin.r}
+        if small:
+            gb = STORED_BYTES_PER_PARAM * p + 2 * lin.M * (lin.K + lin.N) + 2 * lin.r * (lin.K + lin.N)
+            row.update({"fwd_us": pt["fwd"], "fwd_GBps": gb / pt["fwd"] / 1e3,
+                        "weight_kernel_us": kt["fwd_main"],
+                        "weight_kernel_GBps": STORED_BYTES_PER_PARAM * p / kt["fwd_main"] / 1e3})
+        else:
+            row.update({
+                "quantize_call_us": pt["quantize"], "quantize_kernel_us": kt["quantize"],
+                "quantize_GBps": QUANT_BYTES_PER_PARAM * p / pt["quantize"] / 1e3,
+                "dequantize_us": kt["dequantize"],
+                "dequantize_GBps": DEQUANT_BYTES_PER_PARAM * p / kt["dequantize"] / 1e3,
+                "fwd_us": pt["fwd"], "fwd_main_kernel_us": kt["fwd_main"],
+                "fwd_TFLOPs": (2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * (lin.K + lin.N)) / pt["fwd"] / 1e6,
+                "bwd_us": pt["bwd"], "bwd_dx_kernel_us": kt["bwd_dx"],
+                "bwd_TFLOPs": (2 * lin.M * lin.N * lin.K + 4 * lin.M * lin.r * (lin.K + lin.N)) / pt["bwd"] / 1e6,
+                "fwd_bwd_TFLOPs": linear_flops(lin) / (pt["fwd"] + pt["bwd"]) / 1e6,
+            })
+        breakdown.append(row)
 
     cpu = None
     if not args.no_cpu_baseline:
-        L0 = layers[0]
-        cpu = cpu_baseline(L0["lin"], L0["t"])
+        cpu = cpu_baseline_small(layers[-1]) if small else cpu_baseline(layers[0]["lin"], layers[0]["t"])
 
     lin0 = layers[0]["lin"]
+    if small:
+        total_bytes = sum(STORED_BYTES_PER_PARAM * L["lin"].N * L["lin"].K
+                          + 2 * L["lin"].M * (L["lin"].K + L["lin"].N) + 2 * L["lin"].r * (L["lin"].K + L["lin"].N)
+                          for L in layers)
+        metric, unit = SMALL_METRIC, "GB/s"
+        value = total_bytes / (ms_per_step / 1e3) / 1e9
+        step_desc = "forward (fused small-token path) at 1, 4 and 16 tokens against one rotated NF4+DQ weight"
+    else:
+        metric, unit = METRIC, "TFLOP/s"
+        value = sum(linear_flops(L["lin"]) for L in layers) / (ms_per_step / 1e3) / 1e12
+        step_desc = "quantize+DQ, dequantize->bf16, fwd, bwd (dX, dA, dB) per linear"
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": value,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -295,16 +396,22 @@ def main():
             "workload": WORKLOAD_NAMES[args.workload],
             "linears": [{"name": L["lin"].name, "M": L["lin"].M, "N": L["lin"].N, "K": L["lin"].K,
                          "r": L["lin"].r, "alpha": L["lin"].alpha} for L in layers],
-            "global_batch": lin0.M, "weight_copies_rotated": rotate,
-            "step": "quantize+DQ, dequantize->bf16, fwd, bwd (dX, dA, dB) per linear",
+            "global_batch": lin0.M, "weight_copies_rotated": rotate, "step": step_desc,
         },
-        "quantize": {"GB/s": q_bytes / q_us / 1e3, "frac_hbm": q_bytes / q_us / 1e3 / HBM_PEAK_GBS,
-                     "bytes_per_param": QUANT_BYTES_PER_PARAM},
         "roofline": roof,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "breakdown_steps": nprof,
         "wall_s_timed": wall,
     }
+    if not small:
+        q_us = sum(b["quantize_call_us"] for b in breakdown)
+        q_bytes = sum(QUANT_BYTES_PER_PARAM * L["lin"].N * L["lin"].K for L in layers)
+        out["quantize"] = {"GB/s": q_bytes / q_us / 1e3, "frac_hbm": q_bytes / q_us / 1e3 / HBM_PEAK_GBS,
+                           "bytes_per_param": QUANT_BYTES_PER_PARAM}
+        fb_us = sum(b["fwd_us"] + b["bwd_us"] for b in breakdown)
+        fb = sum(linear_flops(L["lin"]) for L in layers) / fb_us / 1e6
+        out["fwd_bwd"] = {"TFLOP/s": fb, "frac_mfma": fb / BF16_PEAK_TFLOPS}
     print(json.dumps(out), flush=True)
 
 

@@ -97,7 +97,7 @@ DQParams dq_params(const qlora_nf4_t* q) {
 int64_t quant_ws(int64_t numel, int dq) {
   if (!dq || numel == 0) return 0;
   const int64_t nb = nblocks(numel);
-  return round_up(nb * 4, kAlign) + round_up((int64_t)dq_mean_parts(nb) * kMeanDigits * 8, kAlign);
+  return round_up(nb * 4, kAlign) + round_up((int64_t)quantize_parts(numel) * kMeanDigits * 8, kAlign);
 }
 
 struct FwdWs {
@@ -235,15 +235,15 @@ int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q, voi
   hipStream_t s = (hipStream_t)stream;
   const int64_t nb = nblocks(numel);
   float* c2 = q->double_quant ? (float*)ws : q->absmax;
+  uint64_t* parts = q->double_quant ? (uint64_t*)((char*)ws + round_up(nb * 4, kAlign)) : nullptr;
   hipError_t e;
   {
     ProfScope ps(QLORA_KERNEL_QUANTIZE, s);
-    e = launch_quantize(w, w_dtype == QLORA_DTYPE_BF16, numel, q->codes, c2, s);
+    e = launch_quantize(w, w_dtype == QLORA_DTYPE_BF16, numel, q->codes, c2, parts, s);
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   if (q->double_quant) {
-    uint64_t* parts = (uint64_t*)((char*)ws + round_up(nb * 4, kAlign));
-    e = launch_double_quant(c2, nb, parts, q->absmax_q, q->scale2, q->offset, s);
+    e = launch_double_quant(c2, nb, parts, quantize_parts(numel), q->absmax_q, q->scale2, q->offset, s);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
   return QLORA_OK;

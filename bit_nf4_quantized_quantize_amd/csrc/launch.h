@@ -24,14 +24,18 @@ struct NF4Values {
 const NF4Values& nf4_values();
 const QuantTable& quant_table();
 
-// Number of partial sums the exact-mean reduction uses for nb constants.
-int dq_mean_parts(int64_t nb);
+// Quantisation writes the codes and the fp32 block absmax c2; with
+// `partials` it also writes, per workgroup, the exact sum of its c2 as
+// kMeanDigits 32-bit digits in 64-bit counters (quantize_parts(numel)
+// workgroups).  Double quantisation then divides the total by nb for the mean
+// and encodes the constants.
+int quantize_parts(int64_t numel);
 constexpr int kMeanDigits = 10;  // 32-bit digits of the exact fixed-point sum
 
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2,
-                           hipStream_t stream);
-hipError_t launch_double_quant(const float* c2, int64_t nb, uint64_t* partials, uint8_t* absmax_q,
-                               float* scale2, float* offset, hipStream_t stream);
+                           uint64_t* partials, hipStream_t stream);
+hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts,
+                               uint8_t* absmax_q, float* scale2, float* offset, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, bool dq, const uint8_t* absmax_q,
                              const float* absmax, const float* scale2, const float* offset,
                              void* out, bool out_bf16, hipStream_t stream);

@@ -1162,33 +1162,36 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
 // rounded to bf16 here, an error of the same size as the bf16 rounding of
 // the product.
 //
-// Reduction order inside a block: lane group g = lane / 16 holds the 16
-// consecutive codes k0 + 16g .. +15 of its row (one 8-byte load); MFMA s of
-// the block takes codes 16g + 8s .. +7 from every group, and the activation
-// fragment is loaded with the same assignment.
+// Lane layout: lane (c, g) = (lane % 16, lane / 16) loads 16 bytes = 32
+// codes of weight row n0 + 16t + c for each of the wave's four 16-row tiles
+// t, covering a pair of blocks (b, b + 1) with the four lane groups: groups
+// 0, 1 hold the two halves of block b, groups 2, 3 those of block b + 1.
+// Word s of a lane (8 codes) goes to MFMA sub-step s.  A 16x16x32 MFMA sums
+// over all four groups, so each block gets its own MFMAs, with the
+// activation fragment zeroed in the other block's groups; the block's
+// constant then scales that block's product.  Activations are loaded with
+// the same code-to-lane assignment (token c in the MFMA rows).
 //
 // Grid: 64-row weight tiles x S reduction splits of at most GV_MAXB blocks.
 // The workgroup first decodes the block constants of its rows over its split
 // into LDS (coalesced reads of the E4M3 bytes; zero past the split's end).
-// Each of the 8 waves then takes a contiguous run of the split's blocks and
-// covers all four 16-row column tiles of the workgroup (one shared
-// activation fragment), keeping the loads of the next two blocks in flight
-// while it multiplies one.  The waves' partial tiles are added in LDS,
-// giving fp32 partials part[S][M][N].
+// Each of the 8 waves then takes a contiguous run of the split's block
+// pairs, keeping the next pair's loads in flight while it multiplies one.
+// The waves' partial tiles are added in LDS, giving fp32 partials
+// part[S][M][N].
 constexpr int GV_WAVES = 8;
 constexpr int GV_T = GV_WAVES * 64;
 constexpr int GV_ROWS = 64;
-constexpr int GV_CT = GV_ROWS / 16;    // 16-row column tiles per wave
-constexpr int GV_DEPTH = 3;            // blocks held in registers per wave
-constexpr int GV_QUANT = GV_WAVES * GV_DEPTH;  // blocks per split: a multiple of this
-constexpr int GV_MAXB = 5 * GV_QUANT;  // at most 120 blocks per split
+constexpr int GV_CT = GV_ROWS / 16;        // 16-row column tiles per wave
+constexpr int GV_QUANT = GV_WAVES * 4;     // blocks per split: a multiple of this (two pairs per pass)
+constexpr int GV_MAXB = 4 * GV_QUANT;      // at most 128 blocks per split
 constexpr int GV_SMEM = (GV_ROWS * (GV_MAXB + 1) > GV_WAVES * kGemvMaxM * (GV_ROWS + 1))
                             ? GV_ROWS * (GV_MAXB + 1)
                             : GV_WAVES * kGemvMaxM * (GV_ROWS + 1);
 
-struct GvBlock {
-  uint2 cw[GV_CT];  // 16 codes of each row n_t: k0 + 16g .. +15
-  uint4 x[2];       // X[m, k0 + 16g .. +15]
+struct GvPair {
+  uint4 cw[GV_CT];  // 32 codes of each row n_t
+  uint4 x[4];       // the matching 32 activations of token c
 };
 
 __device__ __forceinline__ bf16x8 tab_lookup8(const uint32_t* tab, uint32_t w) {
@@ -1246,26 +1249,32 @@ __global__ __launch_bounds__(GV_T, 4) void gemv_kernel(const uint16_t* __restric
   __syncthreads();
 
   const int col = lane & 15, g = lane >> 4;
+  const int gb = g >> 1;  // block of the pair this lane group holds
   // rows beyond N read row N - 1 (their constants are zero)
   const uint8_t* cbase = codes + ((n0 * K) >> 1);
   uint32_t coff[GV_CT];
 #pragma unroll
   for (int t = 0; t < GV_CT; ++t) {
     const int64_t rr = n0 + 16 * t + col < N ? 16 * t + col : N - 1 - n0;
-    coff[t] = (uint32_t)((rr * K + 16 * g) >> 1);
+    coff[t] = (uint32_t)((rr * K) >> 1);
   }
   // MFMA row = token index; rows M..15 repeat token M-1 and are never stored
-  const uint16_t* xp = X + (int64_t)(col < M ? col : M - 1) * K + 16 * g;
-  const int bpw = bps / GV_WAVES;    // blocks per wave, a multiple of GV_DEPTH
-  const int j0 = wave * bpw;         // first block of this wave, relative to b_lo
+  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K;
+  const int bpw = bps / GV_WAVES;  // blocks per wave, a multiple of 4
+  const int j0 = wave * bpw;       // first block of this wave, relative to b_lo
   const int64_t blast = b_lo + nbs - 1;
 
-  auto load = [&](int j, GvBlock& d) {
-    const int64_t b = b_lo + j <= blast ? b_lo + j : blast;  // past the end: weighted by zero
+  // Pair starting at block b_lo + j (j even).  A block past the split's end
+  // is replaced by the split's last block (its constant is zero).
+  auto load = [&](int j, GvPair& d) {
+    int64_t b = b_lo + j + gb;
+    b = b <= blast ? b : blast;
+    const uint32_t boff = (uint32_t)(b * 32 + 16 * (g & 1));
 #pragma unroll
-    for (int t = 0; t < GV_CT; ++t) d.cw[t] = *reinterpret_cast<const uint2*>(cbase + coff[t] + b * 32);
-    d.x[0] = ldg16(xp + b * 64);
-    d.x[1] = ldg16(xp + b * 64 + 8);
+    for (int t = 0; t < GV_CT; ++t) d.cw[t] = *reinterpret_cast<const uint4*>(cbase + coff[t] + boff);
+    const uint16_t* xp = xrow + b * 64 + 32 * (g & 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) d.x[s] = ldg16(xp + 8 * s);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the math that follows
   };
   floatx4 acc[GV_CT];
@@ -1273,30 +1282,39 @@ __global__ __launch_bounds__(GV_T, 4) void gemv_kernel(const uint16_t* __restric
   for (int t = 0; t < GV_CT; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.0f;
-  auto compute = [&](int j, const GvBlock& d) {
-    const bf16x8 x0 = __builtin_bit_cast(bf16x8, d.x[0]), x1 = __builtin_bit_cast(bf16x8, d.x[1]);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  auto compute = [&](int j, const GvPair& d) {
+    bf16x8 xa[4], xb[4];  // activations of block j (groups 0, 1) and block j + 1 (groups 2, 3)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      xa[s] = __builtin_bit_cast(bf16x8, gb == 0 ? d.x[s] : z);
+      xb[s] = __builtin_bit_cast(bf16x8, gb == 0 ? z : d.x[s]);
+    }
 #pragma unroll
     for (int t = 0; t < GV_CT; ++t) {
-      const float c = smem[(16 * t + col) * cpitch + j];
-      floatx4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-      p = mfma16(x0, tab_lookup8(tab, d.cw[t].x), p);
-      p = mfma16(x1, tab_lookup8(tab, d.cw[t].y), p);
+      const float* cr = &smem[(16 * t + col) * cpitch + j];
+      const float ca = cr[0], cb = cr[1];
+      const uint32_t w[4] = {d.cw[t].x, d.cw[t].y, d.cw[t].z, d.cw[t].w};
+      floatx4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = __builtin_fmaf(c, p[e], acc[t][e]);
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 wv = tab_lookup8(tab, w[s]);
+        pa = mfma16(xa[s], wv, pa);
+        pb = mfma16(xb[s], wv, pb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] = __builtin_fmaf(cb, pb[e], __builtin_fmaf(ca, pa[e], acc[t][e]));
     }
   };
 
-  GvBlock A, B, C;
+  GvPair A, B;
   load(j0, A);
-  load(j0 + 1, B);
-  for (int i = 0; i < bpw; i += GV_DEPTH) {
+  for (int i = 0; i < bpw; i += 4) {
     const int j = j0 + i;
-    load(j + 2, C);
+    load(j + 2, B);
     compute(j, A);
-    load(j + 3, A);  // past this wave's run on the last pass: unused
-    compute(j + 1, B);
-    load(j + 4, B);
-    compute(j + 2, C);
+    load(j + 4, A);  // past this wave's run on the last pass: unused
+    compute(j + 2, B);
   }
   __syncthreads();  // constants no longer needed: smem becomes red
 
@@ -1502,8 +1520,8 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
   return launch_main_any<false>(a, stream);
 }
 
-// Blocks per split: a multiple of GV_QUANT (GV_DEPTH per loop pass for each
-// wave), at most GV_MAXB.
+// Blocks per split: a multiple of GV_QUANT (two block pairs per loop pass for
+// each wave), at most GV_MAXB.
 int64_t gemv_blocks_per_split(int64_t nbk, int64_t splits) {
   return ((nbk + splits - 1) / splits + GV_QUANT - 1) / GV_QUANT * GV_QUANT;
 }

@@ -100,16 +100,50 @@ const QuantTable& quant_table() {
   return t;
 }
 
+// --------------------------------------------------- exact mean of c2
+// The mean mu is the exact sum of all c2 divided by their count, rounded
+// once to fp32.  Every non-negative fp32 value is an integer multiple of
+// 2^-149, so the sum is accumulated as an integer in units of 2^-149 split
+// into 32-bit digits held in 64-bit counters (no carries are needed while
+// summing: each addend is below 2^32 and there are fewer than 2^31 of them
+// per counter).  The result is order-independent and bit-reproducible.
+// The quantisation kernel adds the constants it produces into per-workgroup
+// counters; one small kernel then adds the workgroups' counters and divides.
+
+// Digit index and the two 32-bit digit addends of c (|c| finite or not).
+__device__ __forceinline__ void c2_digits(float c, uint32_t& d, uint32_t& lo, uint32_t& hi) {
+  const uint32_t bits = __float_as_uint(c) & 0x7FFFFFFFu;
+  uint32_t e = bits >> 23, m = bits & 0x7FFFFFu;
+  if (e == 0xFF) { e = 0xFE; m = 0x7FFFFFu; }  // non-finite input: result undefined, stay in range
+  const uint32_t shift = e ? e - 1 : 0;
+  m |= e ? 0x800000u : 0u;
+  const uint64_t v = (uint64_t)m << (shift & 31);
+  d = shift >> 5;  // 0..7
+  lo = (uint32_t)v;
+  hi = (uint32_t)(v >> 32);
+}
+
 // ------------------------------------------------------- quantise kernel
-// One workgroup = 256 threads = 4 waves covers 4096 consecutive weights
-// (64 blocks).  In each of 4 steps a wave covers 256 weights = 4 blocks; a
-// lane holds 4 consecutive weights, so a block is one row of 16 lanes and its
-// absmax is a 16-lane DPP reduction.  Each lane writes its 4 codes as one
-// 16-bit store; lane 0 of each row writes the block's absmax.
+// A workgroup of 256 threads = 4 waves handles chunks of 4096 consecutive
+// weights (64 blocks), striding over the tensor by the grid size.  In each of
+// 4 steps of a chunk a wave covers 256 weights = 4 blocks; a lane holds 4
+// consecutive weights, so a block is one row of 16 lanes and its absmax is a
+// 16-lane DPP reduction.  Each lane writes its 4 codes as one 16-bit store;
+// lane 0 of each row writes the block's absmax and, with double
+// quantisation, adds it to the workgroup's exact-sum counters in LDS.  The
+// next chunk's weights are loaded before the current one is coded (two
+// register sets; a chunk past the end re-reads the current one).  A final
+// partial chunk is coded by the workgroup that owns it, with bounds checks.
 
 constexpr int QZ_THREADS = 256;
 constexpr int QZ_STEPS = 4;
 constexpr int QZ_PER_WG = QZ_THREADS * 4 * QZ_STEPS;  // 4096 weights
+constexpr int QZ_MAX_WG = 1024;
+
+int quantize_parts(int64_t numel) {
+  const int64_t chunks = (numel + QZ_PER_WG - 1) / QZ_PER_WG;
+  return (int)(chunks < 1 ? 1 : (chunks > QZ_MAX_WG ? QZ_MAX_WG : chunks));
+}
 
 template <bool BF16_IN>
 __device__ __forceinline__ void load4(const void* w, int64_t e0, int64_t numel, float v[4]) {
@@ -136,51 +170,63 @@ __device__ __forceinline__ void load4(const void* w, int64_t e0, int64_t numel, 
   }
 }
 
+// 4 weights of a full chunk (no bounds checks).
+template <bool BF16_IN>
+__device__ __forceinline__ void load4_full(const void* w, int64_t e0, float v[4]) {
+  if (BF16_IN) {
+    const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(w) + e0);
+    v[0] = __uint_as_float(p.x << 16);
+    v[1] = __uint_as_float(p.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(p.y << 16);
+    v[3] = __uint_as_float(p.y & 0xFFFF0000u);
+  } else {
+    const float4 p = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + e0);
+    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+  }
+}
+
 template <bool BF16_IN>
 __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
                                                                   uint8_t* __restrict__ codes,
-                                                                  float* __restrict__ c2out, QuantTable tab) {
+                                                                  float* __restrict__ c2out,
+                                                                  uint64_t* __restrict__ partials, QuantTable tab) {
   __shared__ uint2 s_tab[32];  // {threshold bits, base code}
+  __shared__ unsigned long long s_acc[kMeanDigits];
   const int tid = threadIdx.x;
   if (tid < 32) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
+  if (tid < kMeanDigits) s_acc[tid] = 0;
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
-  const int64_t wg0 = (int64_t)blockIdx.x * QZ_PER_WG;
   const int64_t nb = (numel + 63) >> 6;
+  const int64_t nfull = numel / QZ_PER_WG;
+  const int64_t G = gridDim.x;
+  const bool sums = partials != nullptr;
 
-  float v[QZ_STEPS][4];
-#pragma unroll
-  for (int s = 0; s < QZ_STEPS; ++s) {
-    const int64_t e0 = wg0 + (int64_t)(s * 4 + wave) * 256 + lane * 4;
-    load4<BF16_IN>(w, e0, numel, v[s]);
-  }
-
-#pragma unroll
-  for (int s = 0; s < QZ_STEPS; ++s) {
-    const int64_t e0 = wg0 + (int64_t)(s * 4 + wave) * 256 + lane * 4;
-    float m = fmaxf(fmaxf(fabsf(v[s][0]), fabsf(v[s][1])), fmaxf(fabsf(v[s][2]), fabsf(v[s][3])));
+  // code one step (4 weights per lane) starting at element e0
+  auto code_step = [&](int64_t e0, float v[4], bool full) {
+    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
     const float c2 = row16_max(m);
     float cs = c2;
     const bool tiny = c2 > 0.0f && c2 < kTiny;
     if (__builtin_amdgcn_ballot_w64(tiny)) {  // rare, wave-uniform branch
       const float sc = tiny ? kPrescale : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[s][i] *= sc;
+      for (int i = 0; i < 4; ++i) v[i] *= sc;
       cs = c2 * sc;
     }
     const float inv = cs > 0.0f ? 1.0f / cs : 0.0f;  // correctly rounded division
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x = v[s][i] * inv;                  // in [-1, 1]
+      const float x = v[i] * inv;                     // in [-1, 1]
       int b = (int)__builtin_fmaf(x, 16.0f, 16.0f);   // bucket 0..32 (x*16 is exact)
       b = b < 0 ? 0 : (b > 31 ? 31 : b);
       const uint2 t = s_tab[b];
       const uint32_t code = t.y + (x > __uint_as_float(t.x) ? 1u : 0u);
       packed |= code << (4 * i);
     }
-    if (e0 + 3 < numel) {
+    if (full) {
       *reinterpret_cast<uint16_t*>(codes + (e0 >> 1)) = (uint16_t)packed;
     } else {
       // past the end: the nibble of a missing element is 0
@@ -190,74 +236,63 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
       if (e0 + 2 < numel) codes[(e0 >> 1) + 1] = (uint8_t)(packed >> 8);
     }
     const int64_t blk = e0 >> 6;
-    if ((lane & 15) == 0 && blk < nb) c2out[blk] = c2;
+    if ((lane & 15) == 0 && blk < nb) {
+      c2out[blk] = c2;
+      if (sums && c2 > 0.0f) {
+        uint32_t d, lo, hi;
+        c2_digits(c2, d, lo, hi);
+        atomicAdd(&s_acc[d], (unsigned long long)lo);
+        if (hi) atomicAdd(&s_acc[d + 1], (unsigned long long)hi);
+      }
+    }
+  };
+  auto elem = [&](int64_t c, int s) { return c * QZ_PER_WG + (int64_t)(s * 4 + wave) * 256 + lane * 4; };
+
+  float va[QZ_STEPS][4], vb[QZ_STEPS][4];
+  int64_t c = blockIdx.x;
+  if (c < nfull) {
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) load4_full<BF16_IN>(w, elem(c, s), va[s]);
+  }
+  while (c < nfull) {
+    const int64_t c1 = c + G;
+    const int64_t l1 = c1 < nfull ? c1 : c;  // past the end: re-read the current chunk (cached)
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) load4_full<BF16_IN>(w, elem(l1, s), vb[s]);
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) code_step(elem(c, s), va[s], true);
+    if (c1 >= nfull) break;
+    const int64_t c2i = c1 + G;
+    const int64_t l2 = c2i < nfull ? c2i : c1;
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) load4_full<BF16_IN>(w, elem(l2, s), va[s]);
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) code_step(elem(c1, s), vb[s], true);
+    c = c2i;
+  }
+  // the partial last chunk, if any
+  if (nfull * QZ_PER_WG < numel && (nfull % G) == blockIdx.x) {
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) load4<BF16_IN>(w, elem(nfull, s), numel, va[s]);
+#pragma unroll
+    for (int s = 0; s < QZ_STEPS; ++s) code_step(elem(nfull, s), va[s], elem(nfull, s) + 3 < numel);
+  }
+  if (sums) {
+    __syncthreads();
+    if (tid < kMeanDigits) partials[(int64_t)blockIdx.x * kMeanDigits + tid] = s_acc[tid];
   }
 }
 
-hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2,
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2, uint64_t* partials,
                            hipStream_t stream) {
-  const int64_t grid = (numel + QZ_PER_WG - 1) / QZ_PER_WG;
+  const int grid = quantize_parts(numel);
   if (w_bf16)
     hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, w,
-                       numel, codes, c2, quant_table());
+                       numel, codes, c2, partials, quant_table());
   else
     hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, w,
-                       numel, codes, c2, quant_table());
+                       numel, codes, c2, partials, quant_table());
   return hipGetLastError();
-}
-
-// --------------------------------------------------- exact mean of c2
-// The mean mu is the exact sum of all c2 divided by their count, rounded
-// once to fp32.  Every non-negative fp32 value is an integer multiple of
-// 2^-149, so the sum is accumulated as an integer in units of 2^-149 split
-// into 32-bit digits held in 64-bit counters (no carries are needed while
-// summing: each addend is below 2^32 and there are fewer than 2^31 of them
-// per counter).  The result is order-independent and bit-reproducible.
-
-constexpr int MEAN_THREADS = 256;
-constexpr int MEAN_MAX_PARTS = 512;
-
-int dq_mean_parts(int64_t nb) {
-  int64_t p = (nb + 4 * MEAN_THREADS - 1) / (4 * MEAN_THREADS);
-  if (p < 1) p = 1;
-  if (p > MEAN_MAX_PARTS) p = MEAN_MAX_PARTS;
-  return (int)p;
-}
-
-__global__ __launch_bounds__(MEAN_THREADS) void dq_mean_partial_kernel(const float* __restrict__ c2, int64_t nb,
-                                                                       uint64_t* __restrict__ partials) {
-  uint64_t acc[kMeanDigits];
-#pragma unroll
-  for (int k = 0; k < kMeanDigits; ++k) acc[k] = 0;
-  const int64_t stride = (int64_t)gridDim.x * MEAN_THREADS;
-  for (int64_t i = (int64_t)blockIdx.x * MEAN_THREADS + threadIdx.x; i < nb; i += stride) {
-    const uint32_t bits = __float_as_uint(c2[i]) & 0x7FFFFFFFu;
-    uint32_t e = bits >> 23, m = bits & 0x7FFFFFu;
-    if (e == 0xFF) { e = 0xFE; m = 0x7FFFFFu; }  // non-finite input: result undefined, stay in range
-    const uint32_t shift = e ? e - 1 : 0;
-    m |= e ? 0x800000u : 0u;
-    const uint64_t v = (uint64_t)m << (shift & 31);
-    const uint32_t d = shift >> 5;  // 0..7
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-#pragma unroll
-    for (int k = 0; k < kMeanDigits - 1; ++k) {
-      acc[k] += (d == (uint32_t)k) ? lo : 0u;
-      acc[k] += (d + 1 == (uint32_t)k) ? hi : 0u;
-    }
-  }
-  __shared__ uint64_t s_part[MEAN_THREADS / 64][kMeanDigits];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 0; k < kMeanDigits; ++k) {
-    const uint64_t t = wave_sum_u64(acc[k]);
-    if (lane == 0) s_part[wave][k] = t;
-  }
-  __syncthreads();
-  if (threadIdx.x < kMeanDigits) {
-    uint64_t t = 0;
-    for (int w = 0; w < MEAN_THREADS / 64; ++w) t += s_part[w][threadIdx.x];
-    partials[(int64_t)blockIdx.x * kMeanDigits + threadIdx.x] = t;
-  }
 }
 
 // Round the rational (sum / nb) in units of 2^-149 to the nearest fp32
@@ -286,42 +321,67 @@ __global__ __launch_bounds__(256) void dq_mean_final_kernel(const uint64_t* __re
     s_sum[threadIdx.x] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x] + s_part[2][threadIdx.x] + s_part[3][threadIdx.x];
   __syncthreads();
   if (threadIdx.x != 0) return;
-  uint32_t dig[kMeanDigits];
+  // carry-propagate into 32-bit digits: S = sum_k dig[k] 2^(32k)
+  constexpr int ND = kMeanDigits + 1;
+  uint32_t dig[ND];
   uint64_t carry = 0;
+#pragma unroll
   for (int k = 0; k < kMeanDigits; ++k) {
     const uint64_t t = (s_sum[k] & 0xFFFFFFFFull) + carry;
     dig[k] = (uint32_t)t;
     carry = (t >> 32) + (s_sum[k] >> 32);
   }
-  // quotient digits and remainder of the long division by nb (nb < 2^32)
-  uint32_t q[kMeanDigits];
-  uint64_t rem = 0;
+  dig[kMeanDigits] = (uint32_t)carry;
+  int h = -1;  // highest nonzero digit
+#pragma unroll
+  for (int k = ND - 1; k >= 0; --k)
+    if (h < 0 && dig[k]) h = k;
   const uint64_t den = (uint64_t)nb;
-  for (int k = kMeanDigits - 1; k >= 0; --k) {
-    const uint64_t cur = (rem << 32) | dig[k];
-    q[k] = (uint32_t)(cur / den);
-    rem = cur % den;
-  }
-  int top = -1;  // highest set bit of the quotient
-  for (int k = kMeanDigits - 1; k >= 0 && top < 0; --k)
-    if (q[k]) top = 32 * k + 31 - __builtin_clz(q[k]);
-  auto bit = [&](int p) -> uint32_t { return (p < 0) ? 0u : ((q[p >> 5] >> (p & 31)) & 1u); };
-  uint32_t result;
-  if (top < 24) {
-    // value below 2^24 units: the integer part is the bit pattern already
-    uint32_t ip = (top < 0) ? 0u : q[0];
-    const uint64_t twice = 2 * rem;
-    const bool up = twice > den || (twice == den && (ip & 1u));
-    result = ip + (up ? 1u : 0u);
+  // S / nb = q * 2^E + f with 0 <= f < 2^E; `rest` is set when f's exact
+  // value is nonzero beyond what the remainder r of q shows (bits of S below
+  // 2^E).  With S < 2^64, E = 0 and q, r are exact; otherwise q = floor(T /
+  // nb) for the top 64 bits T of S, which has at least 31 significant bits,
+  // so the bits of the result that fp32 rounding looks at all lie in q.
+  uint64_t q, r;
+  int E = 0;
+  bool rest = false;
+  if (h <= 1) {
+    const uint64_t S = ((uint64_t)dig[1] << 32) | dig[0];
+    q = S / den;
+    r = S - q * den;
   } else {
-    const int shift = top - 23;
-    uint32_t mant = 0;
-    for (int p = top; p >= shift; --p) mant = (mant << 1) | bit(p);
-    const uint32_t rbit = bit(shift - 1);
-    bool sticky = rem != 0;
-    for (int p = shift - 2; p >= 0 && !sticky; --p) sticky = bit(p) != 0;
+    uint32_t a = 0, b = 0, c = 0;
+    bool below = false;  // any nonzero digit under the top three
+#pragma unroll
+    for (int k = 0; k < ND; ++k) {
+      if (k == h) a = dig[k];
+      if (k == h - 1) b = dig[k];
+      if (k == h - 2) c = dig[k];
+      if (k < h - 2) below = below || dig[k] != 0;
+    }
+    const int lz = __builtin_clz(a);
+    const uint64_t ab = ((uint64_t)a << 32) | b;
+    const uint64_t T = lz ? (ab << lz) | (c >> (32 - lz)) : ab;
+    const uint32_t cmask = lz ? (1u << (32 - lz)) - 1u : 0xFFFFFFFFu;  // bits of c under 2^E
+    rest = below || (c & cmask) != 0;
+    E = 32 * (h - 1) - lz;
+    q = T / den;
+    r = T - q * den;
+  }
+  uint32_t result;
+  const int t = q ? 63 - __builtin_clzll(q) : -1;  // highest set bit of q
+  if (E == 0 && t < 24) {
+    // value below 2^24 units: the integer part is the bit pattern already
+    const uint64_t twice = 2 * r;
+    const bool up = twice > den || (twice == den && (q & 1u));
+    result = (uint32_t)q + (up ? 1u : 0u);
+  } else {
+    const int sh = t - 23;  // >= 1 (E > 0 implies t >= 31)
+    const uint32_t mant = (uint32_t)(q >> sh);
+    const uint32_t rbit = (uint32_t)(q >> (sh - 1)) & 1u;
+    const bool sticky = (q & ((1ull << (sh - 1)) - 1ull)) != 0 || r != 0 || rest;
     const bool up = rbit && (sticky || (mant & 1u));
-    result = ((uint32_t)shift << 23) + mant + (up ? 1u : 0u);
+    result = ((uint32_t)(sh + E) << 23) + mant + (up ? 1u : 0u);
   }
   *mu_out = __uint_as_float(result);
 }
@@ -370,14 +430,10 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
   if (lane == 0) scale2[g] = c1 / 448.0f;
 }
 
-hipError_t launch_double_quant(const float* c2, int64_t nb, uint64_t* partials, uint8_t* absmax_q,
+hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts, uint8_t* absmax_q,
                                float* scale2, float* offset, hipStream_t stream) {
-  const int parts = dq_mean_parts(nb);
-  hipLaunchKernelGGL(dq_mean_partial_kernel, dim3(parts), dim3(MEAN_THREADS), 0, stream, c2, nb, partials);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dq_mean_final_kernel, dim3(1), dim3(256), 0, stream, partials, parts, nb, offset);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ng = (nb + 255) / 256;
   hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, stream, c2, nb, offset,

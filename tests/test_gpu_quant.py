@@ -110,6 +110,17 @@ def test_special_values(B, dq):
     _roundtrip(B, torch.from_numpy(rep), dq)
 
 
+@pytest.mark.parametrize("scale", [1e-44, 1e-41, 1e-38, 1e-36, 1e-20, 1.0, 1e20, 1e37])
+def test_mean_rounding_across_magnitudes(B, scale):
+    """The exact mean of the block absmax is rounded once to fp32 at every
+    magnitude: sums below 2^64 units of 2^-149 (exact quotient), subnormal
+    and normal results, and sums spanning many 32-bit digits."""
+    _log(f"quant mean rounding scale={scale:g}")
+    g = torch.Generator().manual_seed(int(abs(np.log10(scale))) + 7)
+    w = (torch.randn(64 * 1037, generator=g, dtype=torch.float64) * scale).float()
+    _roundtrip(B, w, True)
+
+
 def test_bf16_input(B):
     _log("quant bf16 input 512x1024")
     g = torch.Generator().manual_seed(7)
