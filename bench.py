@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0: enough for > 256 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="first run a plain device copy of this many MiB three times (a known-size kernel that "
+                        "calibrates hardware byte counters taken over the same run)")
     return p.parse_args()
 
 
@@ -215,6 +218,13 @@ def main():
     torch.cuda.set_device(dev)
     bf = torch.bfloat16
     small = args.workload == 5
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     lins = synth.workload(args.workload)
     if small:

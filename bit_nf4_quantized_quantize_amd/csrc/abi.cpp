@@ -103,6 +103,7 @@ int64_t quant_ws(int64_t numel, int dq) {
 struct FwdWs {
   // byte offsets: fp32 partials of X A, bf16 s*XA [M, rp], and for the
   // small-token path fp32 partials of X W^T [gemv_splits][M][N]
+  // small-token path and the main product's split tiles share one region
   int64_t part, xas, gv, total;
   int splits, gemv_splits;
 };
@@ -114,12 +115,15 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   w.part = 0;
   w.xas = w.part + round_up((int64_t)w.splits * M * rp * 4, kAlign);
   w.gv = w.xas + round_up(M * rp * 2, kAlign);
-  w.total = w.gv + round_up((int64_t)w.gemv_splits * M * N * 4, kAlign);
+  const int64_t gv_bytes = w.gemv_splits > 0 ? (int64_t)w.gemv_splits * M * N * 4 : main_split_bytes(M, N, K);
+  w.total = w.gv + round_up(gv_bytes, kAlign);
   return w;
 }
 
 struct BwdWs {
-  int64_t part_t, ts, part, total;  // fp32 partials of dY B^T, bf16 s*T [M, rp], fp32 token partials
+  // fp32 partials of dY B^T, bf16 s*T [M, rp], fp32 partials of the token
+  // reductions and of the main product's split tiles (one region, used in turn)
+  int64_t part_t, ts, part, total;
   int splits_t, splits_a, splits_b;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -128,11 +132,14 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   w.splits_t = skinny_splits(M, r, N);
   w.splits_a = tn_splits(M, K, r);
   w.splits_b = tn_splits(M, r, N);
-  const int64_t pa = (int64_t)w.splits_a * K * r, pb = (int64_t)w.splits_b * r * N;
+  int64_t pbytes = (int64_t)w.splits_a * K * r * 4;
+  const int64_t pb = (int64_t)w.splits_b * r * N * 4, pm = main_split_bytes(M, K, N);
+  if (pb > pbytes) pbytes = pb;
+  if (pm > pbytes) pbytes = pm;
   w.part_t = 0;
   w.ts = w.part_t + round_up((int64_t)w.splits_t * M * rp * 4, kAlign);
   w.part = w.ts + round_up(M * rp * 2, kAlign);
-  w.total = w.part + round_up((pa > pb ? pa : pb) * 4, kAlign);
+  w.total = w.part + round_up(pbytes, kAlign);
   return w;
 }
 
@@ -305,7 +312,7 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
   {
     ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
     e = launch_fwd_main((const uint16_t*)X, M, K, W->codes, dq_params(W), N, xas, (const uint16_t*)B, r, rp,
-                        (uint16_t*)Y, hs);
+                        (uint16_t*)Y, (float*)(base + L.gv), hs);
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
@@ -345,7 +352,7 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, c
     {
       ProfScope ps(QLORA_KERNEL_BWD_DX, hs);
       e = launch_bwd_dx((const uint16_t*)dY, M, N, W->codes, dq_params(W), K, ts, (const uint16_t*)A, r, rp,
-                        (uint16_t*)dX, hs);
+                        (uint16_t*)dX, part, hs);
     }
     if (e != hipSuccess) return hip_fail(e, fn);
   }

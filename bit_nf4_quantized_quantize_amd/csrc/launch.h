@@ -59,10 +59,13 @@ int skinny_splits(int64_t M, int64_t Q, int64_t L);
 hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
                          float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
                          hipStream_t stream);
+// Workspace bytes of the fp32 partial tiles a main product [M, ncols] with
+// reduction length L uses (0 when no tile is split).
+int64_t main_split_bytes(int64_t M, int64_t ncols, int64_t L);
 // Fused forward: Y = X * W_bf16^T + XAs * B_pad (XAs [M, rp]; B [r, N], rows >= r as zero).
 hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            const DQParams& dq, int64_t N, const uint16_t* XAs, const uint16_t* B,
-                           int64_t r, int64_t rp, uint16_t* Y, hipStream_t stream);
+                           int64_t r, int64_t rp, uint16_t* Y, float* split_ws, hipStream_t stream);
 // Small-token forward (1 <= M <= kGemvMaxM): launch_gemv writes fp32
 // partials part[splits][M][N] of X * W_bf16^T over reduction splits, then
 // launch_gemv_reduce writes Y = bf16(sum + XAs * B).
@@ -75,7 +78,7 @@ hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t 
 // Fused input gradient: dX = dY * W_bf16 + Ts * A_pad^T (Ts [M, rp]; A [K, r]).
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                          const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* A,
-                         int64_t r, int64_t rp, uint16_t* dX, hipStream_t stream);
+                         int64_t r, int64_t rp, uint16_t* dX, float* split_ws, hipStream_t stream);
 // Token reduction C[P, Q] = U[M, P]^T * V[M, Q] (leading dimensions ldu, ldv):
 // fp32 partials [splits][P][Q] then out [P, Q] = bf16(alpha * sum).
 int tn_splits(int64_t M, int64_t P, int64_t Q);

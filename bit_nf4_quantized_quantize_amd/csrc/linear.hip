@@ -86,6 +86,11 @@ struct MainArgs {
   int64_t r, rp;
   uint16_t* out;            // [M, ncols]
   int64_t ncols;            // Nw (fwd) or Kw (bwd)
+  // split reduction of the last tiles (256 x 256 kernel only): tiles
+  // [full_tiles, T) are each cut into `split` reduction ranges whose fp32
+  // partial tiles go to part[unit][256][256]; a fixup pass adds them.
+  int full_tiles, split;
+  float* part;
 };
 
 template <int BM, int BN, bool BWD>
@@ -681,13 +686,25 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // XCD-aware order: consecutive workgroups go to different XCDs, so give
-  // each XCD a contiguous run of tiles (row-major over the tile grid).
-  const int tn = (int)((a.ncols + BN - 1) / BN), tm = (int)((a.M + BM - 1) / BM);
-  const int T = tn * tm, pid = blockIdx.x;
-  const int lid = (T % 8 == 0) ? (pid % 8) * (T / 8) + pid / 8 : pid;
+  const int tn = (int)((a.ncols + BN - 1) / BN);
+  const int nkt = (int)(a.L >> 6);  // k-steps of the whole reduction
+  const int F = a.full_tiles, pid = blockIdx.x;
+  // Work unit -> tile and reduction range.  Whole tiles first, in XCD-aware
+  // order (consecutive workgroups go to different XCDs, so each XCD gets a
+  // contiguous run of tiles); then the split units of the last tiles.
+  int lid, ks = 0, ke = nkt, unit = -1;
+  if (pid < F) {
+    lid = (F % 8 == 0) ? (pid % 8) * (F / 8) + pid / 8 : pid;
+  } else {
+    unit = pid - F;
+    const int sp = unit % a.split;
+    lid = F + unit / a.split;
+    ks = (int)((int64_t)sp * nkt / a.split);
+    ke = (int)((int64_t)(sp + 1) * nkt / a.split);
+  }
+  const bool last_range = ke == nkt;  // the range that also adds the adapter term
   const int64_t m0 = (int64_t)(lid / tn) * BM, c0 = (int64_t)(lid % tn) * BN;
-  const int nk = (int)(a.L >> 6);
+  const int nk = ke;
   const int64_t kblocks = a.Kw >> 6;
   const float mu = DQ ? *a.dq.offset : 0.0f;
 
@@ -816,10 +833,10 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     __syncthreads();
   };
 
-  // ---- prologue: stage 0 filled; X(1) and codes(1) in flight
-  load_codes(0, cwB, qbB, sfB);
+  // ---- prologue: stage 0 filled; X(ks+1) and codes(ks+1) in flight
+  load_codes(ks, cwB, qbB, sfB);
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, 0));
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks));
 #pragma unroll
   for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
   {
@@ -833,18 +850,18 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
       sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
     }
   }
-  load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
+  load_codes(ks + 1 < nk ? ks + 1 : ks, cwA, qbA, sfA);
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, nk > 1 ? 1 : 0));
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks + 1 < nk ? ks + 1 : ks));
   __syncthreads();
 
-  for (int kt = 0; kt < nk; kt += 2) {
+  for (int kt = ks; kt < nk; kt += 2) {
     step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
     if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
   }
 
   // ---- adapter term over bf16 operands (stage 0 is free)
-  for (int64_t jt = 0; jt < a.rp; jt += 64) {
+  for (int64_t jt = 0; last_range && jt < a.rp; jt += 64) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int id = tid + V5_T * i, row = id >> 3, ch = id & 7;
@@ -876,7 +893,19 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue
+  // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
+  if (unit >= 0) {
+    float* pt = a.part + (int64_t)unit * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cl = wn * 128 + 32 * j + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pt[(wm * 128 + 32 * i + acc_row32(e, lane)) * BN + cl] = acc[i][j][e];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -889,6 +918,31 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
         if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
       }
     }
+}
+
+// Adds the `split` fp32 partial tiles of each split tile (fixed order) and
+// writes the bf16 result.  Thread: 4 consecutive columns of one tile row.
+__global__ __launch_bounds__(256) void main_fixup_kernel(const float* __restrict__ part, int split, int full_tiles,
+                                                         int tn, int64_t M, int64_t ncols, uint16_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over R * 256 * 64
+  const int64_t t = idx >> 14, rem = idx & 16383;
+  const int r = (int)(rem >> 6), c = (int)(rem & 63) * 4;
+  const int lid = full_tiles + (int)t;
+  const int64_t row = (int64_t)(lid / tn) * 256 + r, col0 = (int64_t)(lid % tn) * 256 + c;
+  float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int sp = 0; sp < split; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((t * split + sp) << 16) + r * 256 + c);
+    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+  }
+  if (row >= M) return;
+  const float sv[4] = {sum.x, sum.y, sum.z, sum.w};
+  if (col0 + 4 <= ncols && (ncols & 3) == 0) {
+    *reinterpret_cast<uint2*>(out + row * ncols + col0) = make_uint2(pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col0 + e < ncols) out[row * ncols + col0 + e] = f2bf(sv[e]);
+  }
 }
 
 // ====================================================== skinny products
@@ -1372,22 +1426,50 @@ int split_sum_threads(int64_t chunks, int S) {
 }
 
 // ------------------------------------------------ main-GEMM tile choice
-// Candidate tiles and a rough per-tile cost (relative MFMA time of a tile,
-// inflated for small tiles whose operand traffic per flop is higher).  The
-// grid runs in waves of 256 workgroups (one per CU); pick the tile with the
-// least estimated time.
+// The 256 x 256 kernel runs one workgroup per CU.  Its tiles go in rounds of
+// kCUs; when the last round would leave CUs idle, its R tiles are cut along
+// the reduction into `split` ranges (split * R <= kCUs), whose fp32 partial
+// tiles a fixup pass adds.  The older 128-wide kernels remain for shapes
+// where even that leaves most of the chip idle.
+constexpr int kCUs = 256;  // MI355X compute units
+
+struct SplitPlan {
+  int tiles, full, split;  // split == 1: no split units
+  int64_t units() const { return full + (int64_t)(tiles - full) * split; }
+  int64_t part_floats() const { return split > 1 ? (int64_t)(tiles - full) * split * 65536 : 0; }
+};
+
+SplitPlan plan_256(int64_t M, int64_t ncols, int64_t L) {
+  SplitPlan p;
+  p.tiles = (int)(cdiv(M, 256) * cdiv(ncols, 256));
+  const int nkt = (int)(L >> 6);
+  const int R = p.tiles % kCUs;
+  int split = R > 0 ? kCUs / R : 1;
+  if (split > nkt / 2) split = nkt / 2;  // at least two k-steps per range
+  if (split < 2) {
+    p.full = p.tiles;
+    p.split = 1;
+  } else {
+    p.full = p.tiles - R;
+    p.split = split;
+  }
+  return p;
+}
+
 enum MainTile { T256x256 = 0, T256x128 = 1, T128x128 = 2 };
 
-MainTile pick_tile(int64_t M, int64_t ncols) {
-  struct Cand { MainTile t; int bm, bn; double cost; };
-  const Cand cands[3] = {{T256x256, 256, 256, 1.00}, {T256x128, 256, 128, 0.56}, {T128x128, 128, 128, 0.30}};
+// Rough time in units of one 256 x 256 tile on a CU.
+MainTile pick_tile(int64_t M, int64_t ncols, int64_t L) {
+  const SplitPlan p = plan_256(M, ncols, L);
+  double best_t = (double)(p.full / kCUs) + (p.full % kCUs ? 1.0 : 0.0) +
+                  (p.split > 1 ? 1.0 / p.split + 0.05 : 0.0);
   MainTile best = T256x256;
-  double best_t = 1e300;
+  struct Cand { MainTile t; int bm, bn; double cost; };
+  const Cand cands[2] = {{T256x128, 256, 128, 0.56}, {T128x128, 128, 128, 0.30}};
   for (const Cand& c : cands) {
     const int64_t tiles = (int64_t)cdiv(M, c.bm) * cdiv(ncols, c.bn);
-    const int per_cu = c.bm * c.bn >= 256 * 256 ? 1 : 2;
-    const double waves = (double)((tiles + 256 * per_cu - 1) / (256 * per_cu));
-    const double t = waves * c.cost * per_cu;
+    const double waves = (double)((tiles + 2 * kCUs - 1) / (2 * kCUs));
+    const double t = waves * c.cost * 2;
     if (t < best_t - 1e-9) { best_t = t; best = c.t; }
   }
   return best;
@@ -1401,28 +1483,25 @@ hipError_t launch_main(const MainArgs& a, hipStream_t stream) {
 }
 
 template <bool BWD>
-hipError_t launch_main_any(const MainArgs& a, hipStream_t stream) {
-  switch (pick_tile(a.M, a.ncols)) {
+hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
+  switch (pick_tile(a.M, a.ncols, a.L)) {
     case T256x256: {
-      const dim3 grid(cdiv(a.ncols, 256), cdiv(a.M, 256));
-#ifdef QLORA_MAIN_V3
-      if (a.dq.double_quant)
-        hipLaunchKernelGGL((main_v3_kernel<BWD, true, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
-      else
-        hipLaunchKernelGGL((main_v3_kernel<BWD, false, V3_WAVES>), grid, dim3(V3_WAVES * 64), 0, stream, a);
-#elif defined(QLORA_MAIN_WS)
-      const dim3 grid1(cdiv(a.ncols, 256) * cdiv(a.M, 256));
-      if (a.dq.double_quant)
-        hipLaunchKernelGGL((main_ws_kernel<BWD, true>), grid1, dim3(WS_T), 0, stream, a);
-      else
-        hipLaunchKernelGGL((main_ws_kernel<BWD, false>), grid1, dim3(WS_T), 0, stream, a);
-#else
-      const dim3 grid1(cdiv(a.ncols, 256) * cdiv(a.M, 256));
+      const SplitPlan p = plan_256(a.M, a.ncols, a.L);
+      a.full_tiles = p.full;
+      a.split = p.split;
+      a.part = split_ws;
+      if (p.split > 1 && !split_ws) return hipErrorInvalidValue;
+      const dim3 grid1((unsigned)p.units());
       if (a.dq.double_quant)
         hipLaunchKernelGGL((main_v5_kernel<BWD, true>), grid1, dim3(V5_T), 0, stream, a);
       else
         hipLaunchKernelGGL((main_v5_kernel<BWD, false>), grid1, dim3(V5_T), 0, stream, a);
-#endif
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || p.split == 1) return e;
+      const int tn = (int)cdiv(a.ncols, 256);
+      const int64_t threads = (int64_t)(p.tiles - p.full) * 256 * 64;
+      hipLaunchKernelGGL(main_fixup_kernel, dim3(cdiv(threads, 256)), dim3(256), 0, stream, split_ws, p.split,
+                         p.full, tn, a.M, a.ncols, a.out);
       return hipGetLastError();
     }
     case T256x128: return launch_main<256, 128, BWD>(a, stream);
@@ -1509,15 +1588,21 @@ hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int64_t main_split_bytes(int64_t M, int64_t ncols, int64_t L) {
+  if (pick_tile(M, ncols, L) != T256x256) return 0;
+  return plan_256(M, ncols, L).part_floats() * 4;
+}
+
 hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq,
                            int64_t N, const uint16_t* XAs, const uint16_t* B, int64_t r, int64_t rp, uint16_t* Y,
-                           hipStream_t stream) {
+                           float* split_ws, hipStream_t stream) {
   MainArgs a;
   a.act = X; a.M = M; a.L = K;
   a.codes = codes; a.dq = dq; a.Nw = N; a.Kw = K;
   a.ext_act = XAs; a.ext_w = B; a.r = r; a.rp = rp;
   a.out = Y; a.ncols = N;
-  return launch_main_any<false>(a, stream);
+  a.full_tiles = 0; a.split = 1; a.part = nullptr;
+  return launch_main_any<false>(a, split_ws, stream);
 }
 
 // Blocks per split: a multiple of GV_QUANT (two block pairs per loop pass for
@@ -1570,13 +1655,14 @@ hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t 
 
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes, const DQParams& dq,
                          int64_t K, const uint16_t* Ts, const uint16_t* A, int64_t r, int64_t rp, uint16_t* dX,
-                         hipStream_t stream) {
+                         float* split_ws, hipStream_t stream) {
   MainArgs a;
   a.act = dY; a.M = M; a.L = N;
   a.codes = codes; a.dq = dq; a.Nw = N; a.Kw = K;
   a.ext_act = Ts; a.ext_w = A; a.r = r; a.rp = rp;
   a.out = dX; a.ncols = K;
-  return launch_main_any<true>(a, stream);
+  a.full_tiles = 0; a.split = 1; a.part = nullptr;
+  return launch_main_any<true>(a, split_ws, stream);
 }
 
 }  // namespace qlora

@@ -301,13 +301,23 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* c
 // mantissa scaled by 2^shift, which also absorbs a rounding carry.
 __global__ __launch_bounds__(256) void dq_mean_final_kernel(const uint64_t* __restrict__ partials, int parts,
                                                              int64_t nb, float* __restrict__ mu_out) {
-  // every thread sums a strided subset of the partials, digit by digit
+  // every thread sums a strided subset of the partials (parts <= 4 * 256),
+  // digit by digit, with all of its loads issued before the additions
+  constexpr int PER = (QZ_MAX_WG + 255) / 256;
+  uint64_t v[PER][kMeanDigits];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int p = threadIdx.x + 256 * u;
+#pragma unroll
+    for (int k = 0; k < kMeanDigits; ++k) v[u][k] = p < parts ? partials[(int64_t)p * kMeanDigits + k] : 0;
+  }
   uint64_t acc[kMeanDigits];
 #pragma unroll
-  for (int k = 0; k < kMeanDigits; ++k) acc[k] = 0;
-  for (int p = threadIdx.x; p < parts; p += 256)
+  for (int k = 0; k < kMeanDigits; ++k) {
+    acc[k] = 0;
 #pragma unroll
-    for (int k = 0; k < kMeanDigits; ++k) acc[k] += partials[(int64_t)p * kMeanDigits + k];
+    for (int u = 0; u < PER; ++u) acc[k] += v[u][k];
+  }
   __shared__ uint64_t s_part[4][kMeanDigits];
   __shared__ uint64_t s_sum[kMeanDigits];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -432,6 +442,7 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
 
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts, uint8_t* absmax_q,
                                float* scale2, float* offset, hipStream_t stream) {
+  if (parts < 1 || parts > QZ_MAX_WG) return hipErrorInvalidValue;
   hipLaunchKernelGGL(dq_mean_final_kernel, dim3(1), dim3(256), 0, stream, partials, parts, nb, offset);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -199,6 +199,10 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, voi
  *   ws       device workspace, ws_bytes >= the fwd figure of
  *            qlora_linear_workspace.
  * Products accumulate in fp32; the adapter term runs through bf16(s*X*A).
+ * For 1 <= M <= 16 the weight term is computed by a weight-streaming kernel
+ * that rounds the codebook value (not its product with c2_hat) to bf16 and
+ * applies c2_hat in fp32 to each 64-term block product: the same size of
+ * error, but not bit-identical to the product with W_bf16.
  */
 int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W,
                      const void* A, const void* B, int32_t r, float s,
