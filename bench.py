@@ -11,9 +11,10 @@ Infinity Cache.  Workload 5 (small batch) times only the forward at 1, 4 and
 
 Measurement:
   1. W untimed warm-up steps;
-  2. a breakdown pass of a few steps with HIP events around every library
-     kernel of interest and every phase (these events cost a few us each, so
-     this pass is not used for `value`);
+  2. a breakdown pass: a few steps with HIP events around every library
+     kernel of interest (each event costs the stream a few us, so this pass
+     is not used for `value`), then each phase timed as a run of back-to-back
+     calls between two events;
   3. the timed region: K steps bracketed by synchronisation, with events
      only around the dominant kernel (found in pass 2), recorded by the
      library on the kernel's own launch stream; its mean duration over the
@@ -268,37 +269,34 @@ def main():
     hev = HipEvents()
     tev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def run_step(i, kev=None, pe=None):
-        """One step.  kev[li][kernel] = (start, stop) hipEvents attached to
-        library kernels; pe[li] = torch events between the phases."""
-        for li, L in enumerate(layers):
-            lin = L["lin"]
+    def run_phase(li, p, i):
+        """One call of phase p for linear li (rotation index i)."""
+        L = layers[li]
+        lin = L["lin"]
+        if small:
+            B.qlora_linear_fwd(L["X"], qws[i % rotate], L["A"], L["B"], lin.s, Y=L["Y"], XA=L["XA"],
+                               workspace=L["ws"])
+            return
+        t = L["t"]
+        if p == "quantize":
+            B.qlora_nf4_quantize(L["W"][i % rotate], double_quant=True, out=L["qw"], workspace=L["qws"])
+        elif p == "dequantize":
+            B.qlora_nf4_dequantize(L["qw"], bf, out=L["Wd"])
+        elif p == "fwd":
+            B.qlora_linear_fwd(t["X"], L["qw"], t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
+        else:
+            B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], L["qw"], t["A"], t["B"], lin.s,
+                               dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
+
+    def run_step(i, kev=None):
+        """One step; kev[li][kernel] = (start, stop) hipEvents the library
+        records around its kernels."""
+        for li in range(len(layers)):
             if kev is not None:
                 for k, (e0, e1) in kev[li].items():
                     B.lib().qlora_profile_events(B.QLORA_KERNEL[k], e0, e1)
-            marks = pe[li] if pe is not None else None
-            if marks:
-                marks[0].record()
-            if small:
-                B.qlora_linear_fwd(L["X"], qws[i % rotate], L["A"], L["B"], lin.s, Y=L["Y"], XA=L["XA"],
-                                   workspace=L["ws"])
-                if marks:
-                    marks[1].record()
-            else:
-                t = L["t"]
-                B.qlora_nf4_quantize(L["W"][i % rotate], double_quant=True, out=L["qw"], workspace=L["qws"])
-                if marks:
-                    marks[1].record()
-                B.qlora_nf4_dequantize(L["qw"], bf, out=L["Wd"])
-                if marks:
-                    marks[2].record()
-                B.qlora_linear_fwd(t["X"], L["qw"], t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
-                if marks:
-                    marks[3].record()
-                B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], L["qw"], t["A"], t["B"], lin.s,
-                                   dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
-                if marks:
-                    marks[4].record()
+            for p in phases:
+                run_phase(li, p, i)
         if kev is not None:
             for k in kernels:
                 B.lib().qlora_profile_events(B.QLORA_KERNEL[k], None, None)
@@ -307,18 +305,26 @@ def main():
         run_step(i)
     torch.cuda.synchronize()
 
-    # 1) breakdown pass (untimed for `value`): events around every kernel and phase
+    # 1) breakdown (untimed for `value`): kernel durations from events around
+    # each library kernel; phase durations from nprof back-to-back calls of
+    # each phase between two events (no events inside the calls)
     nprof = max(3, min(args.steps, 10))
     kev_all = [[{k: (hev.create(), hev.create()) for k in kernels} for _ in layers] for _ in range(nprof)]
-    pe_all = [[[tev() for _ in range(len(phases) + 1)] for _ in layers] for _ in range(nprof)]
     for i in range(nprof):
-        run_step(args.warmup + i, kev_all[i], pe_all[i])
+        run_step(args.warmup + i, kev_all[i])
     torch.cuda.synchronize()
     per = []
     for li in range(len(layers)):
         kt = {k: sum(hev.elapsed_ms(*kev_all[i][li][k]) for i in range(nprof)) * 1e3 / nprof for k in kernels}
-        pt = {p: sum(pe_all[i][li][j].elapsed_time(pe_all[i][li][j + 1]) for i in range(nprof)) * 1e3 / nprof
-              for j, p in enumerate(phases)}
+        pt = {}
+        for p in phases:
+            e0, e1 = tev(), tev()
+            e0.record()
+            for i in range(nprof):
+                run_phase(li, p, args.warmup + i)
+            e1.record()
+            torch.cuda.synchronize()
+            pt[p] = e0.elapsed_time(e1) * 1e3 / nprof
         per.append((kt, pt))
     name, bound, work, _, dli = _dominant(per, layers, small)
 

@@ -1210,40 +1210,40 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
 // expanded through one constant table in LDS: entry b (a code byte) holds
 // bf16(NF4[b & 15]) | bf16(NF4[b >> 4]) << 16, the two unscaled codebook
 // values of that byte in element order, so 8 codes are 4 LDS reads.  A
-// block's 64-term partial product comes from two 16x16x32 MFMAs (tokens as
+// block's 64-term partial product comes from four 32x32x16 MFMAs (tokens as
 // rows, weight rows as columns) and is then scaled by the block constant
 // c2_hat in fp32.  The codebook value, not its product with c2_hat, is
 // rounded to bf16 here, an error of the same size as the bf16 rounding of
 // the product.
 //
-// Lane layout: lane (c, g) = (lane % 16, lane / 16) loads 16 bytes = 32
-// codes of weight row n0 + 16t + c for each of the wave's four 16-row tiles
-// t, covering a pair of blocks (b, b + 1) with the four lane groups: groups
-// 0, 1 hold the two halves of block b, groups 2, 3 those of block b + 1.
-// Word s of a lane (8 codes) goes to MFMA sub-step s.  A 16x16x32 MFMA sums
-// over all four groups, so each block gets its own MFMAs, with the
-// activation fragment zeroed in the other block's groups; the block's
-// constant then scales that block's product.  Activations are loaded with
-// the same code-to-lane assignment (token c in the MFMA rows).
+// Lane layout (32x32x16 MFMA; tokens are rows 0..M-1 of the 32-row A
+// operand, the rest repeat token M-1 and are never stored): lane (c, h) =
+// (lane % 32, lane / 32) loads the 16 bytes = 32 codes k0 + 32h .. +31 of
+// weight row n0 + 32t + c, for each of the wave's two 32-row column tiles t,
+// so one load instruction reads 32 bytes of each of 32 rows.  Word s of a
+// lane (8 codes) goes to MFMA sub-step s; the activation fragment uses the
+// same code-to-lane assignment, so the four sub-steps of a block sum exactly
+// that block's 64 products before its constant scales them.
 //
 // Grid: 64-row weight tiles x S reduction splits of at most GV_MAXB blocks.
 // The workgroup first decodes the block constants of its rows over its split
 // into LDS (coalesced reads of the E4M3 bytes; zero past the split's end).
-// Each of the 8 waves then takes a contiguous run of the split's block
-// pairs, keeping the next pair's loads in flight while it multiplies one.
-// The waves' partial tiles are added in LDS, giving fp32 partials
-// part[S][M][N].
+// Each of the 8 waves then takes a contiguous run of the split's blocks,
+// keeping the loads of the next two blocks in flight while it multiplies
+// one.  The
+// waves' partial tiles are added in LDS, giving fp32 partials part[S][M][N].
 constexpr int GV_WAVES = 8;
 constexpr int GV_T = GV_WAVES * 64;
 constexpr int GV_ROWS = 64;
-constexpr int GV_CT = GV_ROWS / 16;        // 16-row column tiles per wave
-constexpr int GV_QUANT = GV_WAVES * 4;     // blocks per split: a multiple of this (two pairs per pass)
-constexpr int GV_MAXB = 4 * GV_QUANT;      // at most 128 blocks per split
+constexpr int GV_CT = GV_ROWS / 32;        // 32-row column tiles per wave
+constexpr int GV_DEPTH = 3;                // blocks held in registers per wave
+constexpr int GV_QUANT = GV_WAVES * GV_DEPTH;  // blocks per split: a multiple of this
+constexpr int GV_MAXB = 5 * GV_QUANT;      // at most 120 blocks per split
 constexpr int GV_SMEM = (GV_ROWS * (GV_MAXB + 1) > GV_WAVES * kGemvMaxM * (GV_ROWS + 1))
                             ? GV_ROWS * (GV_MAXB + 1)
                             : GV_WAVES * kGemvMaxM * (GV_ROWS + 1);
 
-struct GvPair {
+struct GvBlock {
   uint4 cw[GV_CT];  // 32 codes of each row n_t
   uint4 x[4];       // the matching 32 activations of token c
 };
@@ -1302,73 +1302,66 @@ __global__ __launch_bounds__(GV_T, 4) void gemv_kernel(const uint16_t* __restric
   }
   __syncthreads();
 
-  const int col = lane & 15, g = lane >> 4;
-  const int gb = g >> 1;  // block of the pair this lane group holds
+  const int col = lane & 31, h = lane >> 5;
   // rows beyond N read row N - 1 (their constants are zero)
-  const uint8_t* cbase = codes + ((n0 * K) >> 1);
+  const uint8_t* cbase = codes + ((n0 * K) >> 1) + 16 * h;
   uint32_t coff[GV_CT];
 #pragma unroll
   for (int t = 0; t < GV_CT; ++t) {
-    const int64_t rr = n0 + 16 * t + col < N ? 16 * t + col : N - 1 - n0;
+    const int64_t rr = n0 + 32 * t + col < N ? 32 * t + col : N - 1 - n0;
     coff[t] = (uint32_t)((rr * K) >> 1);
   }
-  // MFMA row = token index; rows M..15 repeat token M-1 and are never stored
-  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K;
-  const int bpw = bps / GV_WAVES;  // blocks per wave, a multiple of 4
+  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K + 32 * h;
+  const int bpw = bps / GV_WAVES;  // blocks per wave, a multiple of GV_DEPTH
   const int j0 = wave * bpw;       // first block of this wave, relative to b_lo
   const int64_t blast = b_lo + nbs - 1;
 
-  // Pair starting at block b_lo + j (j even).  A block past the split's end
-  // is replaced by the split's last block (its constant is zero).
-  auto load = [&](int j, GvPair& d) {
-    int64_t b = b_lo + j + gb;
-    b = b <= blast ? b : blast;
-    const uint32_t boff = (uint32_t)(b * 32 + 16 * (g & 1));
+  // Block b_lo + j; past the split's end the split's last block is loaded
+  // again (its constant is zero).  Loads run two blocks ahead: all of a
+  // block's loads (codes and activations) are issued together, since the
+  // memory counter retires loads in issue order.
+  auto load = [&](int j, GvBlock& d) {
+    const int64_t b = b_lo + j <= blast ? b_lo + j : blast;
 #pragma unroll
-    for (int t = 0; t < GV_CT; ++t) d.cw[t] = *reinterpret_cast<const uint4*>(cbase + coff[t] + boff);
-    const uint16_t* xp = xrow + b * 64 + 32 * (g & 1);
+    for (int t = 0; t < GV_CT; ++t) d.cw[t] = *reinterpret_cast<const uint4*>(cbase + coff[t] + b * 32);
+    const uint16_t* xp = xrow + b * 64;
 #pragma unroll
     for (int s = 0; s < 4; ++s) d.x[s] = ldg16(xp + 8 * s);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the math that follows
   };
-  floatx4 acc[GV_CT];
+  float acc[GV_CT][8];
 #pragma unroll
   for (int t = 0; t < GV_CT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[t][e] = 0.0f;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  auto compute = [&](int j, const GvPair& d) {
-    bf16x8 xa[4], xb[4];  // activations of block j (groups 0, 1) and block j + 1 (groups 2, 3)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      xa[s] = __builtin_bit_cast(bf16x8, gb == 0 ? d.x[s] : z);
-      xb[s] = __builtin_bit_cast(bf16x8, gb == 0 ? z : d.x[s]);
-    }
+    for (int e = 0; e < 8; ++e) acc[t][e] = 0.0f;
+  auto compute = [&](int j, const GvBlock& d) {
 #pragma unroll
     for (int t = 0; t < GV_CT; ++t) {
-      const float* cr = &smem[(16 * t + col) * cpitch + j];
-      const float ca = cr[0], cb = cr[1];
+      const float c = smem[(32 * t + col) * cpitch + j];
       const uint32_t w[4] = {d.cw[t].x, d.cw[t].y, d.cw[t].z, d.cw[t].w};
-      floatx4 pa = {0.0f, 0.0f, 0.0f, 0.0f}, pb = {0.0f, 0.0f, 0.0f, 0.0f};
+      floatx16 p;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 wv = tab_lookup8(tab, w[s]);
-        pa = mfma16(xa[s], wv, pa);
-        pb = mfma16(xb[s], wv, pb);
-      }
+      for (int e = 0; e < 16; ++e) p[e] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = __builtin_fmaf(cb, pb[e], __builtin_fmaf(ca, pa[e], acc[t][e]));
+      for (int s = 0; s < 4; ++s) p = mfma32(__builtin_bit_cast(bf16x8, d.x[s]), tab_lookup8(tab, w[s]), p);
+      // token rows 0..15 of the 32-row tile are registers 0..7
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[t][e] = __builtin_fmaf(c, p[e], acc[t][e]);
     }
   };
 
-  GvPair A, B;
+  // bpw is a multiple of GV_DEPTH: three register sets in rotation
+  GvBlock A, B, C;
   load(j0, A);
-  for (int i = 0; i < bpw; i += 4) {
+  load(j0 + 1, B);
+  for (int i = 0; i < bpw; i += 3) {
     const int j = j0 + i;
-    load(j + 2, B);
+    load(j + 2, C);
     compute(j, A);
-    load(j + 4, A);  // past this wave's run on the last pass: unused
-    compute(j + 2, B);
+    load(j + 3, A);  // past this wave's run on the last pass: unused
+    compute(j + 1, B);
+    load(j + 4, B);
+    compute(j + 2, C);
   }
   __syncthreads();  // constants no longer needed: smem becomes red
 
@@ -1376,7 +1369,8 @@ __global__ __launch_bounds__(GV_T, 4) void gemv_kernel(const uint16_t* __restric
 #pragma unroll
   for (int t = 0; t < GV_CT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[(wave * kGemvMaxM + 4 * g + e) * (GV_ROWS + 1) + 16 * t + col] = acc[t][e];
+    for (int e = 0; e < 8; ++e)
+      red[(wave * kGemvMaxM + acc_row32(e, lane)) * (GV_ROWS + 1) + 32 * t + col] = acc[t][e];
   __syncthreads();
   for (int o = tid; o < M * GV_ROWS; o += GV_T) {
     const int m = o / GV_ROWS, c = o % GV_ROWS;
@@ -1605,8 +1599,8 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
   return launch_main_any<false>(a, split_ws, stream);
 }
 
-// Blocks per split: a multiple of GV_QUANT (two block pairs per loop pass for
-// each wave), at most GV_MAXB.
+// Blocks per split: a multiple of GV_QUANT (GV_DEPTH blocks per loop pass
+// for each wave), at most GV_MAXB.
 int64_t gemv_blocks_per_split(int64_t nbk, int64_t splits) {
   return ((nbk + splits - 1) / splits + GV_QUANT - 1) / GV_QUANT * GV_QUANT;
 }
