@@ -28,17 +28,11 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
 // OCP E4M3FN: sign, 4-bit exponent with bias 7, 3-bit mantissa; exponent
 // field 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN; largest finite 448.
 
+// Exact decode of the low byte of b with gfx950's native conversion
+// (v_cvt_f32_fp8 reads the OCP E4M3FN format on this target).  One
+// instruction and no branches, which matters where it sits between MFMAs.
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xF, m = b & 0x7;
-  float v;
-  if (e == 0) {
-    v = (float)m * 0x1p-9f;  // exact
-  } else if (e == 0xF && m == 0x7) {
-    v = __uint_as_float(0x7FC00000u);
-  } else {
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
-  }
-  return (b & 0x80) ? -v : v;
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
 // Nearest-even encode of y with |y| <= 448 (callers clamp first); the sign

@@ -121,6 +121,44 @@ def test_mean_rounding_across_magnitudes(B, scale):
     _roundtrip(B, w, True)
 
 
+def test_fp8_constant_decode_all_bytes(B):
+    """Every E4M3 byte as a stored block constant: with codes all 15 (+1.0),
+    scale2 = 1 and mu = 0, dequantisation returns exactly the decoded byte,
+    through both the dequantiser and the fused forward (Y = X W^T with X = e0
+    picks row 0 of the bf16 weight)."""
+    _log("quant fp8 decode, all 256 bytes")
+    nb = 256
+    qw = B.NF4Weight(1, nb * 64, True)
+    qw.codes.fill_(0xFF)
+    q = np.arange(256, dtype=np.uint8)
+    qw.absmax_q[:nb].copy_(torch.from_numpy(q))
+    qw.scale2.fill_(1.0)
+    qw.offset.fill_(0.0)
+    chat = blockwise.dq_reconstruct(q, np.ones(1, F32), F32(0.0))
+    ref = blockwise.dequantize(np.full(nb * 64, 15, np.uint8), chat)
+    out = B.qlora_nf4_dequantize(qw, torch.float32).reshape(-1).cpu().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan), "NaN bytes differ"
+    assert np.array_equal(out[~nan].view(np.uint32), ref[~nan].view(np.uint32)), "decoded constants differ"
+    # the same constants through the forward: W [64, 256] (4 blocks per row);
+    # token m selects column 64m, so Y[m, n] = bf16(c2_hat of block 4n + m)
+    qf = B.NF4Weight(64, 256, True)
+    for name in ("codes", "absmax_q", "scale2", "offset"):
+        getattr(qf, name).copy_(getattr(qw, name)[:getattr(qf, name).numel()])
+    finite = np.where(np.isnan(chat), F32(0.0), chat)  # NaN bytes replaced by 0x00
+    qf.absmax_q[:nb].copy_(torch.from_numpy(np.where(np.isnan(chat), 0, q).astype(np.uint8)))
+    want = blockwise.bf16_bits(finite.reshape(64, 4).T.copy())
+    for M in (4, 40):  # the small-token kernel and the tiled kernel
+        X = torch.zeros(M, 256, dtype=torch.bfloat16, device="cuda")
+        for m in range(4):
+            X[m, 64 * m] = 1.0
+        A = torch.zeros(256, 8, dtype=torch.bfloat16, device="cuda")
+        Bm = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
+        Y, _ = B.qlora_linear_fwd(X, qf, A, Bm, 1.0)
+        got = Y[:4].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), f"forward with M={M} decodes constants differently"
+
+
 def test_bf16_input(B):
     _log("quant bf16 input 512x1024")
     g = torch.Generator().manual_seed(7)
