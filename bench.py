@@ -45,6 +45,33 @@ STORED_BYTES_PER_PARAM = 0.5 + 1.0 / 64 + 4.0 / 16384
 QUANT_BYTES_PER_PARAM = 4.0 + STORED_BYTES_PER_PARAM      # fp32 in
 DEQUANT_BYTES_PER_PARAM = STORED_BYTES_PER_PARAM + 2.0    # bf16 out
 
+# HBM bytes per launch of the dominant kernels, from two rocprofv3 counter
+# runs (FETCH_SIZE, WRITE_SIZE; each scaled by what it reads for a plain copy
+# of known size; profiles/*_hbm_bytes.md give the commands and tables).  Valid
+# only for the kernel sources they were taken on: `traffic` is null when the
+# digest of those sources differs.
+KERNEL_SOURCES = ("csrc/linear.hip", "csrc/quantize.hip", "csrc/device.h")
+TRAFFIC_DIGEST = "01d1d125412fdde2"
+TRAFFIC_BYTES = {
+    (2, "bwd_dx"): 108.8e6 + 34.1e6,
+    (2, "fwd_main"): 108.3e6 + 33.8e6,
+    (2, "quantize"): 67.2e6 + 9.5e6,
+    (2, "dequantize"): 8.8e6 + 33.6e6,
+    (5, "fwd_main"): 124.6e6 + 0.9e6,
+}
+
+
+def kernel_digest():
+    import hashlib
+    from bit_nf4_quantized_quantize_amd import binding
+    root = os.path.dirname(os.path.abspath(binding.__file__))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 WORKLOAD_NAMES = {
     1: "tiny: W 256x256 NF4+DQ, X 16x256 bf16, r=8, alpha=16",
     2: "7B attention projection: W 4096x4096 NF4+DQ, X 4096x4096 bf16 (4 x 1024 tokens), r=64, alpha=16",
@@ -354,6 +381,9 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
     roof.update({"kernel": name, "linear": layers[dli]["lin"].name, "algorithmic_per_launch": work,
                  "avg_launch_us": us})
+    if kernel_digest() == TRAFFIC_DIGEST and (args.workload, name) in TRAFFIC_BYTES:
+        roof["traffic"] = TRAFFIC_BYTES[(args.workload, name)]
+        roof["traffic_unit"] = "bytes per launch (HBM read + write)"
 
     breakdown = []
     for (kt, pt), L in zip(per, layers):
