@@ -385,6 +385,12 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
   __shared__ uint64_t s_part[4][kMeanDigits];
   __shared__ uint64_t s_sum[kMeanDigits];
   __shared__ float s_mu;
+  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t i0 = g * 256 + lane * 4;
+  // this wave's constants do not depend on mu: their loads go out first
+  float cv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cv[i] = i0 + i < nb ? c2[i0 + i] : 0.0f;
   {
     uint64_t v[kMeanDigits];
     const int p = threadIdx.x;
@@ -407,15 +413,13 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
     __syncthreads();
   }
   const float mu = s_mu;
-  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t i0 = g * 256 + lane * 4;
   if (g * 256 >= nb) return;  // whole wave exits together
   float d[4];
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t idx = i0 + i;
-    d[i] = idx < nb ? c2[idx] - mu : 0.0f;
+    d[i] = idx < nb ? cv[i] - mu : 0.0f;
     if (idx < nb) m = fmaxf(m, fabsf(d[i]));
   }
   const float c1 = wave_max(m);
