@@ -10,7 +10,9 @@
 // The weight is [N, K] = [out, in] with 64-element NF4 blocks along K.
 //
 // Main products (bf16 MFMA 32x32x16, fp32 accumulation), 256 threads as a
-// 2 x 2 grid of waves over a BM x BN output tile, k-step 64, two LDS stages:
+// 2 x 2 grid of waves over a 256 x 256 output tile (128 x 128 per wave), or
+// over 256 x 128 / 128 x 128 tiles for very short reductions, k-step 64,
+// two LDS stages:
 //   forward  Y [M, N]  = X [M, K] W^T     + (s XA) [M, rp] B [rp, N]
 //   backward dX [M, K] = dY [M, N] W      + (s T) [M, rp] A^T
 // Each k-step stages the activation tile (X or dY) and dequantises the
@@ -20,6 +22,9 @@
 // same natural [n][k] layout, read through LDS transpose loads because there
 // the reduction runs over n.  The rank-r adapter term is r_pad/64 extra
 // reduction steps over bf16 operands (rows of B / A beyond r read as zero).
+//
+// With 1 <= M <= 16 tokens the forward instead streams the packed weight
+// through a dedicated kernel (see the small-token section).
 //
 // Adapter products: XA = X A and T = dY B^T are skinny (r columns): split
 // over the reduction into fp32 partials, then one pass writes bf16 XA and
@@ -254,406 +259,6 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * C::WM + 32 * i + acc_row32(e, lane);
-        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
-      }
-    }
-}
-
-// ============================================ main GEMM, 256 x 256, 8 waves
-// Two waves per SIMD so one wave's dequantisation and memory work overlaps
-// the other's MFMAs.  Waves form a 2 (M) x 4 (N) grid of 128 x 64 wave
-// tiles.  Pipeline per k-step kt (one barrier):
-//   registers hold X(kt+1) (issued one step earlier) and the codes of kt+1
-//   (issued two steps earlier);
-//   the codes of kt+2 are issued, then the MFMAs of kt run on LDS stage
-//   kt%2 while the weight tile of kt+1 is dequantised into the other stage;
-//   X(kt+1) is copied to that stage and X(kt+2) is issued.
-#ifndef V3_WAVES
-#define V3_WAVES 8
-#endif
-template <bool BWD, bool DQ, int NW>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void main_v3_kernel(const MainArgs a) {
-  constexpr int V3_T = NW * 64;
-  constexpr int BM = 256, BN = 256;
-  constexpr int WTN = NW == 8 ? 64 : 128;   // wave tile 128 x WTN
-  constexpr int TNW = WTN / 32;
-  constexpr int DQE = 256 * 64 / V3_T;       // weights per thread per step (32 or 64)
-  constexpr int PRC = BN + 16;
-  constexpr int SA = BM * PK;
-  constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
-  constexpr int XCH = BM * 8 / V3_T;  // 4 chunks of 16 bytes per thread
-  __shared__ __attribute__((aligned(16))) __bf16 sA[2][SA];
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][SB];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
-  const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
-  const float mu = DQ ? *a.dq.offset : 0.0f;
-  const int64_t kblocks = a.Kw >> 6;
-  const int nk = (int)(a.L >> 6);
-
-  // dequantisation task: 32 consecutive weights (half a block) per thread.
-  // Every load below is issued unconditionally from a clamped, in-bounds
-  // address (rows past the end feed outputs that are never stored, and a
-  // weight task past the end gets scale 0), so the number of loads in flight
-  // is the same on every path and waits stay precise.
-  const int t_row = BWD ? tid / (BN / DQE) : tid / (64 / DQE);
-  const int t_col = BWD ? (tid % (BN / DQE)) * DQE : (tid % (64 / DQE)) * DQE;
-  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
-  const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);   // fwd: fixed weight row
-  const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - DQE) : 0;  // bwd: fixed weight column
-
-  floatx16 acc[4][TNW];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TNW; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  uint4 xr[XCH];
-  // two register sets for the codes: the loop is unrolled by two so the set
-  // being filled is never copied (a copy would wait for its loads)
-  constexpr int CW = DQE / 32;  // 16-byte code chunks per thread
-  uint4 cwA[CW], cwB[CW];
-#pragma unroll
-  for (int i = 0; i < CW; ++i) cwA[i] = cwB[i] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-  uint8_t qbA = 0, qbB = 0;
-  float sfA = 0.0f, sfB = 0.0f;
-
-  auto load_x = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
-      const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
-      xr[i] = ldg16(a.act + m * a.L + (int64_t)kt * 64 + ch * 8);
-    }
-  };
-  auto load_codes = [&](int kt, uint4* c, uint8_t& q, float& f) {
-    const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
-    const int64_t k = BWD ? t_k : (int64_t)kt * 64 + t_col;
-#pragma unroll
-    for (int i = 0; i < CW; ++i) c[i] = *reinterpret_cast<const uint4*>(a.codes + ((n * a.Kw + k) >> 1) + 16 * i);
-    const int64_t blk = n * kblocks + (k >> 6);
-    if (DQ) {
-      q = a.dq.absmax_q[blk];
-      f = a.dq.scale2[blk >> 8];
-    } else {
-      f = a.dq.absmax[blk];
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
-      sts16(&sA[buf][row * PK + ch * 8], xr[i]);
-    }
-  };
-  auto dequant = [&](int buf, const uint4* c, uint8_t q, float f) {
-    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(q), f), mu) : f;
-    const float sc = t_ok ? bs : 0.0f;
-    const BlockLUT lut = lut_for(sc);
-    __bf16* dst = BWD ? &sB[buf][t_row * PRC + t_col] : &sB[buf][t_row * PK + t_col];
-#pragma unroll
-    for (int w = 0; w < 4 * CW; ++w) {
-      const uint32_t word = (w & 3) == 0 ? c[w >> 2].x : (w & 3) == 1 ? c[w >> 2].y : (w & 3) == 2 ? c[w >> 2].z : c[w >> 2].w;
-      uint32_t o[4];
-      lut_lookup8(lut, word, o);
-      sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
-    }
-  };
-  auto mma = [&](int buf, bool b_rc, int pitch_b) {
-#pragma unroll
-    for (int kk = 0; kk < 64; kk += 16) {
-      bf16x8 af[4], bfr[TNW];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
-#pragma unroll
-      for (int j = 0; j < TNW; ++j)
-        bfr[j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * WTN + 32 * j, kk, lane)
-                      : frag_kc(sB[buf], pitch_b, wn * WTN + 32 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-  };
-  // one k-step: codes(kt+1) are in (cu, qu, fu); codes(kt+2) go to (cl, ql, fl)
-  // `cur` is a literal at both call sites, so LDS reads of one stage and
-  // writes of the other are provably disjoint and may be interleaved.
-  auto step = [&](int kt, const int cur, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql, float& fl) {
-    const int nxt = cur ^ 1;
-    const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
-    load_codes(k2, cl, ql, fl);
-    mma(cur, BWD, BWD ? PRC : PK);
-    // On the last step this fills a stage nobody reads again: harmless, and
-    // it keeps the whole step one basic block so the scheduler can interleave
-    // the dequantisation VALU work with the MFMAs.
-    dequant(nxt, cu, qu, fu);
-    store_x(nxt);
-    load_x(k2);
-#pragma unroll
-    for (int g = 0; g < 4 * TNW; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-      }
-    }
-    __syncthreads();
-  };
-
-  // ---- prologue: stage 0 filled; X(1) and codes(1) in flight
-  load_codes(0, cwB, qbB, sfB);
-  load_x(0);
-  store_x(0);
-  dequant(0, cwB, qbB, sfB);
-  load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
-  load_x(nk > 1 ? 1 : 0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
-    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
-  }
-
-  // ---- adapter term over bf16 operands (stage 0 is free)
-  for (int64_t jt = 0; jt < a.rp; jt += 64) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
-      const int64_t m = m0 + row;
-      sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
-    }
-    if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
-#pragma unroll
-      for (int i = 0; i < BN * 8 / V3_T; ++i) {
-        const int id = tid + V3_T * i, row = id / (BN / 8), ch = id % (BN / 8);
-        sts16(&sB[0][row * PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
-      }
-    } else {     // A [Kw, r]: tile [BN k][64 j]
-#pragma unroll
-      for (int i = 0; i < BN * 8 / V3_T; ++i) {
-        const int id = tid + V3_T * i, row = id >> 3, ch = id & 7;
-        sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
-      }
-    }
-    __syncthreads();
-    mma(0, !BWD, BWD ? PK : PRC);
-    __syncthreads();
-  }
-
-  // ---- epilogue
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TNW; ++j) {
-      const int64_t col = c0 + wn * WTN + 32 * j + (lane & 31);
-      if (col >= a.ncols) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
-        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
-      }
-    }
-}
-
-// ================================= main GEMM, 256 x 256, warp-specialised
-// 12 waves: 8 consumer waves (two per SIMD, a 2 (M) x 4 (N) grid of 128 x 64
-// tiles) only read LDS and issue MFMAs; 4 producer waves (one per SIMD)
-// stage the activation tile and dequantise the weight tile (one whole NF4
-// block per thread) into the other LDS stage.  The MFMA work of consumers and
-// the VALU / memory work of producers run on the same SIMDs concurrently;
-// one workgroup barrier per k-step swaps the stages.  Producers keep codes
-// two steps ahead and activations one step ahead in registers.
-constexpr int WS_T = 768;
-
-template <bool BWD, bool DQ>
-__global__ __launch_bounds__(WS_T) void main_ws_kernel(const MainArgs a) {
-  constexpr int BM = 256, BN = 256;
-  constexpr int PRC = BN + 16;
-  constexpr int SA = BM * PK;
-  constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
-  constexpr int NP = 256;          // producer threads
-  constexpr int XCH = BM * 8 / NP; // 8 activation chunks of 16 bytes per producer thread
-  __shared__ __attribute__((aligned(16))) __bf16 sA[2][SA];
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][SB];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool producer = wave >= 8;
-  // XCD-aware order: consecutive workgroups go to different XCDs, so give
-  // each XCD a contiguous run of tiles (row-major over the tile grid).
-  const int tn = (int)((a.ncols + BN - 1) / BN), tm = (int)((a.M + BM - 1) / BM);
-  const int T = tn * tm, pid = blockIdx.x;
-  const int lid = (T % 8 == 0) ? (pid % 8) * (T / 8) + pid / 8 : pid;
-  const int64_t m0 = (int64_t)(lid / tn) * BM, c0 = (int64_t)(lid % tn) * BN;
-  const int nk = (int)(a.L >> 6);
-  const int64_t kblocks = a.Kw >> 6;
-
-  // ---------------- producer state
-  const int pt = tid - 512;
-  const int t_row = BWD ? (pt >> 2) : pt;
-  const int t_col = BWD ? (pt & 3) * 64 : 0;
-  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
-  const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);
-  const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - 64) : 0;
-  const float mu = (DQ && producer) ? *a.dq.offset : 0.0f;
-  uint4 xr0[XCH], xr1[XCH];  // activations two steps ahead, alternating sets
-  uint4 cwA[2], cwB[2];
-  uint8_t qbA = 0, qbB = 0;
-  float sfA = 0.0f, sfB = 0.0f;
-
-  auto load_x = [&](int kt, uint4* xr) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = pt + NP * i, row = id >> 3, ch = id & 7;
-      const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
-      xr[i] = ldg16(a.act + m * a.L + (int64_t)kt * 64 + ch * 8);
-    }
-  };
-  auto load_codes = [&](int kt, uint4* c, uint8_t& q, float& f) {
-    const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
-    const int64_t k = BWD ? t_k : (int64_t)kt * 64;
-    const uint8_t* src = a.codes + ((n * a.Kw + k) >> 1);
-    c[0] = *reinterpret_cast<const uint4*>(src);
-    c[1] = *reinterpret_cast<const uint4*>(src + 16);
-    const int64_t blk = n * kblocks + (k >> 6);
-    if (DQ) {
-      q = a.dq.absmax_q[blk];
-      f = a.dq.scale2[blk >> 8];
-    } else {
-      f = a.dq.absmax[blk];
-    }
-  };
-  auto store_x = [&](int buf, const uint4* xr) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = pt + NP * i, row = id >> 3, ch = id & 7;
-      sts16(&sA[buf][row * PK + ch * 8], xr[i]);
-    }
-  };
-  auto dequant = [&](int buf, const uint4* c, uint8_t q, float f) {
-    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(q), f), mu) : f;
-    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f);
-    __bf16* dst = BWD ? &sB[buf][t_row * PRC + t_col] : &sB[buf][t_row * PK + t_col];
-    const uint32_t words[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      uint32_t o[4];
-      lut_lookup8(lut, words[w], o);
-      sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
-    }
-  };
-  // produce step kt: stage nxt gets X(kt+1) (from xs, loaded two steps
-  // earlier) and the dequantised weights of kt+1; then X(kt+3) goes into xs
-  auto produce = [&](int kt, const int nxt, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql,
-                     float& fl, uint4* xs) {
-    const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
-    const int k3 = kt + 3 < nk ? kt + 3 : nk - 1;
-    load_codes(k2, cl, ql, fl);
-    dequant(nxt, cu, qu, fu);
-    store_x(nxt, xs);
-    load_x(k3, xs);
-  };
-
-  // ---------------- consumer state
-  const int cw_ = wave & 7;
-  const int wm = cw_ >> 2, wn = cw_ & 3;
-  floatx16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  auto mma = [&](int buf, bool b_rc, int pitch_b) {
-#pragma unroll
-    for (int kk = 0; kk < 64; kk += 16) {
-      bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane)
-                      : frag_kc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-  };
-
-  // The two roles run separate loops with the same number of barriers, so
-  // producer registers and consumer accumulators are never live together.
-  if (producer) {
-    load_codes(0, cwB, qbB, sfB);
-    load_x(0, xr0);
-    store_x(0, xr0);
-    dequant(0, cwB, qbB, sfB);
-    load_codes(nk > 1 ? 1 : 0, cwA, qbA, sfA);
-    load_x(nk > 1 ? 1 : 0, xr1);
-    load_x(nk > 2 ? 2 : nk - 1, xr0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      produce(kt, 1, cwA, qbA, sfA, cwB, qbB, sfB, xr1);
-      __syncthreads();
-      if (kt + 1 < nk) {
-        produce(kt + 1, 0, cwB, qbB, sfB, cwA, qbA, sfA, xr0);
-        __syncthreads();
-      }
-    }
-    // adapter term operands
-    for (int64_t jt = 0; jt < a.rp; jt += 64) {
-#pragma unroll
-      for (int i = 0; i < XCH; ++i) {
-        const int id = pt + NP * i, row = id >> 3, ch = id & 7;
-        const int64_t m = m0 + row;
-        sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
-      }
-      if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
-#pragma unroll
-        for (int i = 0; i < BN * 8 / NP; ++i) {
-          const int id = pt + NP * i, row = id / (BN / 8), ch = id % (BN / 8);
-          sts16(&sB[0][row * PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
-        }
-      } else {     // A [Kw, r]: tile [BN k][64 j]
-#pragma unroll
-        for (int i = 0; i < BN * 8 / NP; ++i) {
-          const int id = pt + NP * i, row = id >> 3, ch = id & 7;
-          sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
-        }
-      }
-      __syncthreads();
-      __syncthreads();
-    }
-    return;
-  }
-
-  // ---------------- consumers
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    mma(0, BWD, BWD ? PRC : PK);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      mma(1, BWD, BWD ? PRC : PK);
-      __syncthreads();
-    }
-  }
-  for (int64_t jt = 0; jt < a.rp; jt += 64) {
-    __syncthreads();
-    mma(0, !BWD, BWD ? PK : PRC);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = c0 + wn * 64 + 32 * j + (lane & 31);
-      if (col >= a.ncols) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
         if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
       }
     }
