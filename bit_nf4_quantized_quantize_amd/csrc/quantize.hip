@@ -29,8 +29,11 @@ namespace qlora {
 
 // A block (or a group of constants) whose absmax is an fp32 subnormal is
 // first scaled by 2^32, exactly, so that the reciprocal of Eq. 1's constant
-// stays finite; normal blocks are unaffected.
+// stays finite; normal blocks are unaffected.  The second-level constant
+// divides 448 rather than 1, so its threshold is 2^-118 (448 * 2^118 is
+// still below the largest fp32).
 constexpr float kTiny = 0x1p-126f;
+constexpr float kTinyDQ = 0x1p-118f;
 constexpr float kPrescale = 0x1p32f;
 
 // ----------------------------------------------------------------- tables
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
     if (idx < nb) m = fmaxf(m, fabsf(d[i]));
   }
   const float c1 = wave_max(m);
-  const bool tiny = c1 > 0.0f && c1 < kTiny;   // same for the whole wave
+  const bool tiny = c1 > 0.0f && c1 < kTinyDQ;   // same for the whole wave
   const float sc = tiny ? kPrescale : 1.0f;
   const float c1s = c1 * sc;
   const float f = c1s > 0.0f ? 448.0f / c1s : 0.0f;

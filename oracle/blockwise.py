@@ -30,8 +30,10 @@ Readings where the page is silent or garbled (tags match the design notes):
   G13 Eq. (1)'s constant must be finite: for a block whose absmax is an fp32
       subnormal (0 < absmax < 2^-126) the reciprocal would overflow, so the
       block and its absmax are first multiplied by 2^32 (exact for such
-      values) before the reciprocal and the product are taken.  The same
-      rule applies to the second-level constant c1 in double quantisation.
+      values) before the reciprocal and the product are taken.  The
+      second-level constant takes the same rule with its own numerator:
+      fp32(448 / c1) overflows already for c1 below about 1.3e-36, so a
+      256-group whose c1 lies below 2^-118 is scaled by 2^32 first.
       Codes of normal blocks are unaffected, and the rule keeps the codes
       invariant under power-of-two scaling of a block.
 """
@@ -48,6 +50,7 @@ BLOCKSIZE2 = 256    # second-level block (first-level constants per FP8 scale)
 FP8_MAX = np.float32(448.0)
 TINY = np.float32(2.0 ** -126)     # smallest normal fp32
 PRESCALE = np.float32(2.0 ** 32)   # G13
+TINY_DQ = np.float32(2.0 ** -118)  # G13, second level: 448 * 2^118 < FLT_MAX
 
 _F32 = np.float32
 
@@ -209,7 +212,7 @@ def double_quantize(c2, blocksize2=BLOCKSIZE2):
       c1_g        = max |d_b| over group g of 256 constants        (G9 tail)
       absmax_q_b  = E4M3 byte of clamp(fp32(d_b * fp32(448 / c1_g)), +-448),
                     nearest-even; all bytes 0 and scale 0 when c1_g == 0;
-                    when c1_g is subnormal, d_b and c1_g are first
+                    when c1_g < 2^-118, d_b and c1_g are first
                     multiplied by 2^32 (G13)
       scale2_g    = fp32(c1_g / 448)   (the page's second-level constant c1,
                     stored in the multiplicative form dequantisation uses)
@@ -222,7 +225,7 @@ def double_quantize(c2, blocksize2=BLOCKSIZE2):
     grp = np.arange(nb) // blocksize2
     c1 = np.zeros(ng, dtype=_F32)
     np.maximum.at(c1, grp, np.abs(d))
-    tiny = (c1 > 0) & (c1 < TINY)                       # G13
+    tiny = (c1 > 0) & (c1 < TINY_DQ)                    # G13
     sc = np.where(tiny, PRESCALE, _F32(1.0)).astype(_F32)
     c1s = (c1 * sc).astype(_F32)
     ds = (d * sc[grp]).astype(_F32)

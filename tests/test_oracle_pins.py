@@ -306,6 +306,23 @@ def test_double_quant_error_bound_and_monotonicity():
         assert np.all(np.diff(c2h[sel][order]) >= 0)
 
 
+def test_double_quant_power_of_two_invariance():
+    # Scaling every first-level constant by 2^-k scales the mean, the
+    # differences and c1 exactly (the values stay normal fp32 and their
+    # differences are exact), so the FP8 bytes must not change: this holds
+    # through the range where 448 / c1 alone would overflow fp32 (G13).
+    rng = np.random.default_rng(17)
+    base = rng.uniform(0.5, 1.0, 700).astype(F32)
+    q0, s0, mu0 = blockwise.double_quantize(base)
+    for k in (40, 100, 117, 119, 121, 123, 125):
+        sc = F32(2.0 ** -k)
+        with np.errstate(over="raise", divide="raise", invalid="raise", under="ignore"):
+            q, s, mu = blockwise.double_quantize((base * sc).astype(F32))
+        assert np.array_equal(q, q0), k
+        assert float(mu) == float(mu0) * 2.0 ** -k
+        assert np.all(np.isfinite(s)) and np.all(s > 0)
+
+
 def test_bf16_round_matches_torch():
     rng = np.random.default_rng(8)
     x = np.concatenate([rng.standard_normal(10000), rng.standard_normal(1000) * 1e-39,
