@@ -7,7 +7,9 @@ dequantisation to bf16, the fused forward, and the backward (dX, dA, dB).
 Inputs are drawn once and stay resident in HBM; the weight is rotated over
 several copies (> 256 MB in total) so the quantiser does not read it from the
 Infinity Cache.  Workload 5 (small batch) times only the forward at 1, 4 and
-16 tokens against one NF4 weight (rotated copies) and reports GB/s.
+16 tokens against one NF4 weight (rotated copies) and reports GB/s; it then
+times the 32-layer 7B-shaped sweep (quantise+DQ of all 224 fp32 weights, then
+dequantisation of all of them to bf16) and reports it under "sweep".
 
 Measurement:
   1. W untimed warm-up steps;
@@ -89,6 +91,7 @@ def parse():
     p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0: enough for > 256 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="workload 5: skip the 32-layer 7B quantise/dequantise sweep")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="first run a plain device copy of this many MiB three times (a known-size kernel that "
                         "calibrates hardware byte counters taken over the same run)")
@@ -201,6 +204,59 @@ def cpu_baseline_small(L, rows=1024, min_s=10.0, max_reps=50):
         "sample": (f"{n} forwards of {lin.M} tokens against a {rows}x{lin.K} slice of the weight (oracle "
                    f"dequantise from the stored NF4+DQ state, fp64 product); {dt * 1e3:.1f} ms each; "
                    f"BLAS threads {threads}, os.cpu_count() {os.cpu_count()}"),
+    }
+
+
+def run_sweep(B, synth, dev, reps=3):
+    """The 32-layer 7B-shaped sweep: every fp32 weight (224 matrices, 6.48e9
+    parameters, each drawn with its own seed and resident in HBM) is quantised
+    with double quantisation, then every stored weight is dequantised to its
+    own bf16 output.  Each pass (224 back-to-back calls) is timed between two
+    events, `reps` times after a warm-up pass; the median pass is reported,
+    with the host time to enqueue a pass (the GPU time is only meaningful
+    while that stays below it)."""
+    import torch
+
+    shapes = synth.sweep_7b_shapes()
+    ws_bytes = max(B.qlora_nf4_quantize_workspace(n * k, True) for n, k in shapes)
+    qws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    W, Q, D = [], [], []
+    for i, (n, k) in enumerate(shapes):
+        W.append(synth.sweep_weight(i, dev))
+        Q.append(B.NF4Weight(n, k, True, dev))
+        D.append(torch.empty(n, k, dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        times, enq = [], 0.0
+        for p in range(reps + 1):                 # the first pass is a warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record()
+            for i in range(len(shapes)):
+                fn(i)
+            e1.record()
+            t1 = time.perf_counter()
+            torch.cuda.synchronize()
+            if p > 0:
+                times.append(e0.elapsed_time(e1))
+                enq = max(enq, (t1 - t0) * 1e3)
+        return sorted(times)[len(times) // 2], enq
+
+    q_ms, q_enq = timed(lambda i: B.qlora_nf4_quantize(W[i], double_quant=True, out=Q[i], workspace=qws))
+    d_ms, d_enq = timed(lambda i: B.qlora_nf4_dequantize(Q[i], torch.bfloat16, out=D[i]))
+    params = sum(n * k for n, k in shapes)
+    qb, db = QUANT_BYTES_PER_PARAM * params, DEQUANT_BYTES_PER_PARAM * params
+    del W, Q, D, qws
+    torch.cuda.empty_cache()
+    return {
+        "matrices": len(shapes), "params": params, "passes": reps,
+        "quantize_ms": q_ms, "quantize_GBps": qb / q_ms / 1e6, "quantize_frac_hbm": qb / q_ms / 1e6 / HBM_PEAK_GBS,
+        "dequantize_ms": d_ms, "dequantize_GBps": db / d_ms / 1e6,
+        "dequantize_frac_hbm": db / d_ms / 1e6 / HBM_PEAK_GBS,
+        "host_enqueue_ms": {"quantize": q_enq, "dequantize": d_enq},
+        "bytes_per_param": {"quantize": QUANT_BYTES_PER_PARAM, "dequantize": DEQUANT_BYTES_PER_PARAM},
     }
 
 
@@ -458,6 +514,10 @@ def main():
         fb_us = sum(b["fwd_us"] + b["bwd_us"] for b in breakdown)
         fb = sum(linear_flops(L["lin"]) for L in layers) / fb_us / 1e6
         out["fwd_bwd"] = {"TFLOP/s": fb, "frac_mfma": fb / BF16_PEAK_TFLOPS}
+    elif not args.no_sweep:
+        del layers, qws
+        torch.cuda.empty_cache()
+        out["sweep"] = run_sweep(B, synth, dev)
     print(json.dumps(out), flush=True)
 
 

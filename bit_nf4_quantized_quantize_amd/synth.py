@@ -117,3 +117,9 @@ def sweep_7b_shapes():
     and down 4096x11008."""
     layer = [(4096, 4096)] * 4 + [(11008, 4096), (11008, 4096), (4096, 11008)]
     return [shape for _ in range(32) for shape in layer]
+
+
+def sweep_weight(i, device="cpu"):
+    """fp32 weight i (0..223) of the sweep, N(0, 0.02^2), seed of workload 5
+    with layer slot 1 + i (slot 0 is the small-batch weight)."""
+    return weight(sweep_7b_shapes()[i], "normal", seed_of(5, 1 + i, "W"), device)

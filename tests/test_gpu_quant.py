@@ -212,6 +212,43 @@ def test_65b_mlp_weight_sampled(B):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
+def test_7b_sweep_layer_sampled(B):
+    """One 7B-shaped layer of the quantise/dequantise sweep, run as the sweep
+    runs it: the seven fp32 weights quantised back to back through one shared
+    workspace into preallocated states, then each dequantised to its own bf16
+    output.  Constants exactly for every matrix; codes and bf16 weights on
+    sampled blocks."""
+    from bit_nf4_quantized_quantize_amd import synth
+    shapes = synth.sweep_7b_shapes()[:7]
+    ws = torch.empty(max(B.qlora_nf4_quantize_workspace(n * k, True) for n, k in shapes), dtype=torch.uint8,
+                     device="cuda")
+    W = [synth.sweep_weight(i, "cuda") for i in range(7)]
+    Q = [B.NF4Weight(n, k, True, torch.device("cuda")) for n, k in shapes]
+    D = [torch.empty(n, k, dtype=torch.bfloat16, device="cuda") for n, k in shapes]
+    _log("sweep layer: quantise 7 matrices, then dequantise")
+    for i in range(7):
+        B.qlora_nf4_quantize(W[i], double_quant=True, out=Q[i], workspace=ws)
+    for i in range(7):
+        B.qlora_nf4_dequantize(Q[i], torch.bfloat16, out=D[i])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for i, (n, k) in enumerate(shapes):
+        _log(f"sweep layer: check matrix {i} ({n}x{k})")
+        w_np = W[i].cpu().numpy().reshape(-1, 64)
+        c2 = blockwise.block_absmax(w_np.reshape(-1))
+        q, s2, mu = blockwise.double_quantize(c2)
+        h = Q[i].host()
+        assert np.array_equal(h["absmax_q"], q), i
+        assert np.array_equal(h["scale2"].view(np.uint32), s2.view(np.uint32)), i
+        assert h["offset"][0] == mu, i
+        sel = np.unique(np.concatenate([rng.integers(0, w_np.shape[0], 4000), [0, w_np.shape[0] - 1]]))
+        codes, _ = blockwise.quantize_nf4(w_np[sel].reshape(-1))
+        assert np.array_equal(h["codes"].reshape(-1, 32)[sel], blockwise.pack_nibbles(codes).reshape(-1, 32)), i
+        ref = blockwise.dequantize(codes, blockwise.dq_reconstruct(q, s2, mu)[sel])
+        out = D[i].reshape(-1, 64)[torch.from_numpy(sel).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(out.reshape(-1), blockwise.bf16_bits(ref).reshape(-1)), i
+
+
 def test_nonfinite_input_is_defined(B):
     """Non-finite weights give undefined codes, but the call completes and
     codes stay in range."""
