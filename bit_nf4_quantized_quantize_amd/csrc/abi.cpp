@@ -110,8 +110,9 @@ struct FwdWs {
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = round_up(r, 64);
   FwdWs w;
+  const bool small = M >= 1 && M <= kGemvMaxM && N % 4 == 0 && r <= 256;
+  w.gemv_splits = small ? gemv_splits(M, N, K) : 0;
   w.splits = skinny_splits(M, r, K);
-  w.gemv_splits = (M >= 1 && M <= kGemvMaxM) ? gemv_splits(M, N, K) : 0;
   w.part = 0;
   w.xas = w.part + round_up((int64_t)w.splits * M * rp * 4, kAlign);
   w.gv = w.xas + round_up(M * rp * 2, kAlign);
@@ -294,21 +295,27 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
   float* part = (float*)(base + L.part);
   uint16_t* xas = (uint16_t*)(base + L.xas);
   hipError_t e;
-  // XA = X A [M, r]: bf16 copy for the backward, bf16(s XA) padded to rp for the adapter steps
-  if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, (uint16_t*)XA, xas, rp,
-                         s, hs)) != hipSuccess)
-    return hip_fail(e, fn);
-  if (L.gemv_splits > 0) {  // few tokens: weight-streaming product, then partial sums + adapter term
+  if (L.gemv_splits > 0) {
+    // few tokens: partials of X A, the weight-streaming product, then one
+    // kernel that adds both sets of partials and the adapter term
+    if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, nullptr, nullptr,
+                           rp, s, hs)) != hipSuccess)
+      return hip_fail(e, fn);
     float* gv = (float*)(base + L.gv);
     {
       ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
       e = launch_gemv((const uint16_t*)X, M, K, W->codes, dq_params(W), N, gv, L.gemv_splits, hs);
     }
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, xas, rp, (const uint16_t*)B, r, (uint16_t*)Y, hs);
+    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, part, L.splits, rp, s, (const uint16_t*)B, r, (uint16_t*)Y,
+                           (uint16_t*)XA, hs);
     if (e != hipSuccess) return hip_fail(e, fn);
     return QLORA_OK;
   }
+  // XA = X A [M, r]: bf16 copy for the backward, bf16(s XA) padded to rp for the adapter steps
+  if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, (uint16_t*)XA, xas, rp,
+                         s, hs)) != hipSuccess)
+    return hip_fail(e, fn);
   {
     ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
     e = launch_fwd_main((const uint16_t*)X, M, K, W->codes, dq_params(W), N, xas, (const uint16_t*)B, r, rp,

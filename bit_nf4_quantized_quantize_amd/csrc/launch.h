@@ -54,7 +54,8 @@ struct DQParams {
 // Skinny product C[M, Q] = U[M, L] * V, V either [L, Q] (v_is_lq) or
 // [Q, L]; the reduction is split into `splits` chunks of fp32 partials
 // part[splits][M][QP], then out1 [M, Q] = bf16(C) (optional) and
-// out2 [M, QP] = bf16(alpha * C), zero in columns [Q, QP).
+// out2 [M, QP] = bf16(alpha * C), zero in columns [Q, QP).  With out1 and
+// out2 both null only the partials are written.
 int skinny_splits(int64_t M, int64_t Q, int64_t L);
 hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
                          float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
@@ -66,15 +67,18 @@ int64_t main_split_bytes(int64_t M, int64_t ncols, int64_t L);
 hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            const DQParams& dq, int64_t N, const uint16_t* XAs, const uint16_t* B,
                            int64_t r, int64_t rp, uint16_t* Y, float* split_ws, hipStream_t stream);
-// Small-token forward (1 <= M <= kGemvMaxM): launch_gemv writes fp32
-// partials part[splits][M][N] of X * W_bf16^T over reduction splits, then
-// launch_gemv_reduce writes Y = bf16(sum + XAs * B).
+// Small-token forward (1 <= M <= kGemvMaxM, N % 4 == 0): launch_gemv writes
+// fp32 partials part[splits][M][N] of X * W_bf16^T over reduction splits;
+// launch_gemv_reduce adds them, forms C = X A from the skinny partials
+// xpart[xsplits][M][rp] (rp <= 256), and writes Y = bf16(sum + bf16(alpha C) * B)
+// and, when XA is given, XA = bf16(C) [M, r].
 constexpr int kGemvMaxM = 16;
 int gemv_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
                        float* part, int splits, hipStream_t stream);
-hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const uint16_t* XAs, int64_t rp,
-                              const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t stream);
+hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const float* xpart, int xsplits,
+                              int64_t rp, float alpha, const uint16_t* B, int64_t r, uint16_t* Y, uint16_t* XA,
+                              hipStream_t stream);
 // Fused input gradient: dX = dY * W_bf16 + Ts * A_pad^T (Ts [M, rp]; A [K, r]).
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                          const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* A,

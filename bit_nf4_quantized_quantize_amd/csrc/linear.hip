@@ -809,202 +809,278 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
 
 // ================================ small-token forward (M <= kGemvMaxM)
 // With a handful of tokens the forward is a stream over the packed weight
-// (0.516 bytes per parameter) and every weight is used M times, so the
-// per-block bf16 table of the large kernels (about 4 VALU operations per
-// weight) would cost more than the weight's HBM time.  Here the weight is
-// expanded through one constant table in LDS: entry b (a code byte) holds
-// bf16(NF4[b & 15]) | bf16(NF4[b >> 4]) << 16, the two unscaled codebook
-// values of that byte in element order, so 8 codes are 4 LDS reads.  A
-// block's 64-term partial product comes from four 32x32x16 MFMAs (tokens as
-// rows, weight rows as columns) and is then scaled by the block constant
-// c2_hat in fp32.  The codebook value, not its product with c2_hat, is
-// rounded to bf16 here, an error of the same size as the bf16 rounding of
-// the product.
+// (0.516 bytes per parameter), and the per-block scaled bf16 table of the
+// large kernels (about 4 VALU operations per weight) would cost more than
+// the weight's HBM time: the codes are looked up unscaled and each block's
+// constant scales the fp32 MFMA result instead.
 //
-// Lane layout (32x32x16 MFMA; tokens are rows 0..M-1 of the 32-row A
-// operand, the rest repeat token M-1 and are never stored): lane (c, h) =
-// (lane % 32, lane / 32) loads the 16 bytes = 32 codes k0 + 32h .. +31 of
-// weight row n0 + 32t + c, for each of the wave's two 32-row column tiles t,
-// so one load instruction reads 32 bytes of each of 32 rows.  Word s of a
-// lane (8 codes) goes to MFMA sub-step s; the activation fragment uses the
-// same code-to-lane assignment, so the four sub-steps of a block sum exactly
-// that block's 64 products before its constant scales them.
+// Staged small-token forward.  The packed weight is read in full 128-byte
+// lines: a workgroup owns 256 weight rows and walks its reduction split in
+// chunks of 4 blocks (128 bytes of every row); each thread loads 16-byte
+// pieces, so one load instruction covers 8 rows x 128 bytes.  The chunk goes
+// to LDS with the 16-byte pieces of row r XOR-permuted by (r / 2) % 8, so the
+// MFMA-layout reads below (16 rows x 8 bytes per half wave) hit 64 distinct
+// banks.  The chunk's block constants travel with it (one row and two
+// blocks per thread, decoded to fp32 as they are stored).  Three chunks are in
+// flight in registers (a set's codes are reloaded as soon as they are in LDS,
+// its activations once they have been used), LDS is double buffered, and one
+// barrier per chunk orders the two.
 //
-// Grid: 64-row weight tiles x S reduction splits of at most GV_MAXB blocks.
-// The workgroup first decodes the block constants of its rows over its split
-// into LDS (coalesced reads of the E4M3 bytes; zero past the split's end).
-// Each of the 8 waves then takes a contiguous run of the split's blocks,
-// keeping the loads of the next two blocks in flight while it multiplies
-// one.  The
-// waves' partial tiles are added in LDS, giving fp32 partials part[S][M][N].
-constexpr int GV_WAVES = 8;
-constexpr int GV_T = GV_WAVES * 64;
-constexpr int GV_ROWS = 64;
-constexpr int GV_CT = GV_ROWS / 32;        // 32-row column tiles per wave
-constexpr int GV_DEPTH = 3;                // blocks held in registers per wave
-constexpr int GV_QUANT = GV_WAVES * GV_DEPTH;  // blocks per split: a multiple of this
-constexpr int GV_MAXB = 5 * GV_QUANT;      // at most 120 blocks per split
-constexpr int GV_SMEM = (GV_ROWS * (GV_MAXB + 1) > GV_WAVES * kGemvMaxM * (GV_ROWS + 1))
-                            ? GV_ROWS * (GV_MAXB + 1)
-                            : GV_WAVES * kGemvMaxM * (GV_ROWS + 1);
+// Code lookup: a byte (two codes) indexes a table of the two unscaled bf16
+// codebook values.  The table is held once per LDS bank (entry e of copy l at
+// word 64e + l) and lane l reads copy l % 64, so a lookup instruction never
+// has a bank conflict; one v_perm_b32 builds its address from the code byte
+// and the lane.
+//
+// Product (16x16x32 MFMA, tokens = the 16 rows of the A operand, rows >= M
+// repeat token M-1 and are never stored): wave w takes block w % 4 of every
+// chunk for rows 128 (w / 4) .. +127.  Lane (c, g) = (lane % 16, lane / 16)
+// holds the codes 16g .. 16g+15 of its row's block (8 bytes); MFMA s of a
+// block takes codes 16g + 8s .. +7 in reduction slots 8g .. 8g+7, so two MFMAs
+// sum exactly that block's 64 products before its constant scales them.  The
+// activation fragment of lane (t, g) is X[t][64b + 16g + 8s .. +7].  The
+// codebook value, not its product with c2_hat, is rounded to bf16; the error
+// is of the same size as rounding the product.  The partial tiles of the four
+// waves that share rows are added in LDS at the end, giving fp32 partials
+// part[S][M][N].
+constexpr int G3_WAVES = 8;
+constexpr int G3_T = G3_WAVES * 64;
+constexpr int G3_ROWS = 256;                     // weight rows per workgroup
+constexpr int G3_CB = 4;                         // blocks per chunk
+constexpr int G3_RT = G3_ROWS * G3_CB / (16 * G3_WAVES);  // 16-row tiles per wave (8)
+constexpr int G3_CHUNK16 = G3_ROWS * 2 * G3_CB;  // 16-byte pieces per chunk (2048)
+constexpr int G3_LPT = G3_CHUNK16 / G3_T;        // piece loads per thread per chunk (4)
+constexpr int G3_D = 3;                          // chunks in flight in registers
+static_assert(G3_T == 2 * G3_ROWS, "one thread per (row, block pair) for the constants");
+static_assert(G3_CB * kGemvMaxM * G3_ROWS * 4 <= 2 * G3_CHUNK16 * 16, "reduction buffer aliases the stages");
 
-struct GvBlock {
-  uint4 cw[GV_CT];  // 32 codes of each row n_t
-  uint4 x[4];       // the matching 32 activations of token c
+// Native 4 x u32 vectors (not HIP's uint4 struct), so that copies between
+// global memory, registers and LDS stay plain vector loads and stores.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct G3Set {
+  u32x4 c[G3_LPT];  // this thread's code pieces of one chunk
+  u32x4 x[2];       // the activations of this wave's block of the chunk
+  float f[2];       // constants of this thread's row and block pair: fp32 absmax, or the
+                    // second-level scales of the E4M3 bytes in q (double quantisation)
+  uint8_t q[2];
 };
 
-__device__ __forceinline__ bf16x8 tab_lookup8(const uint32_t* tab, uint32_t w) {
-  const uint4 v = make_uint4(tab[w & 0xFF], tab[(w >> 8) & 0xFF], tab[(w >> 16) & 0xFF], tab[w >> 24]);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 template <bool DQ>
-__global__ __launch_bounds__(GV_T, 4) void gemv_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
-                                                      const uint8_t* __restrict__ codes, const DQParams dq, int64_t N,
-                                                      int bps, float* __restrict__ part) {
-  __shared__ uint32_t tab[256];
-  // block constants cs[row][j] during the main loop, then the partial tiles
-  // red[wave][m][row] of the waves
-  __shared__ float smem[GV_SMEM];
+__global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
+                                                       const uint8_t* __restrict__ codes, const DQParams dq,
+                                                       int64_t N, int S, float* __restrict__ part) {
+  __shared__ uint32_t tab[256 * 64];
+  __shared__ u32x4 stage[2][G3_CHUNK16];  // code chunks; the partial tiles at the end
+  __shared__ float2 cst[2][G3_ROWS * G3_CB / 2];  // block constants cst[buf][row][block]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  const int64_t nbk = K >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * GV_ROWS;
-  const int64_t b_lo = (int64_t)blockIdx.y * bps;
-  const int nbs = (int)(nbk - b_lo < bps ? nbk - b_lo : bps);  // blocks in this split, >= 1
-  const int cpitch = bps + 1;
+  const int64_t nbk = K >> 6, half_k = K >> 1;
+  const int64_t n0 = (int64_t)blockIdx.x * G3_ROWS;
+  const int nchunks = (int)((nbk + G3_CB - 1) / G3_CB);
+  const int c_lo = (int)((int64_t)blockIdx.y * nchunks / S);
+  const int c_hi = (int)((int64_t)(blockIdx.y + 1) * nchunks / S);  // c_hi > c_lo (S <= nchunks)
+  const float mu = DQ ? *dq.offset : 0.0f;
+
+  // code pieces: load u of thread tid fills LDS slot P = u * G3_T + tid, i.e.
+  // row P / 8, slot P % 8, with the row's piece (P % 8) ^ ((row / 2) % 8)
+  const uint8_t* gsrc[G3_LPT];
+  int gblk[G3_LPT];
+#pragma unroll
+  for (int u = 0; u < G3_LPT; ++u) {
+    const int P = u * G3_T + tid, r = P >> 3;
+    const int piece = (P & 7) ^ ((r >> 1) & 7);
+    const int64_t row = n0 + r < N ? n0 + r : N - 1;  // rows past N: their constants are zero
+    gblk[u] = piece >> 1;
+    gsrc[u] = codes + row * half_k + 16 * (piece & 1);
+  }
+  // constants: thread -> row tid / 2, blocks 2 (tid % 2) + {0, 1} of the chunk
+  const bool crow_ok = n0 + (tid >> 1) < N;
+  const int64_t cbase = (crow_ok ? n0 + (tid >> 1) : N - 1) * nbk;
+  const int cpair = 2 * (tid & 1);
+  // activations: lane (t, g) of wave w, block w % 4 of the chunk
+  const int t = lane & 15, g = lane >> 4, q = wave & 3, hrow = 128 * (wave >> 2);
+  const uint16_t* xrow = X + (int64_t)(t < M ? t : M - 1) * K + 16 * g;
+
   {
-    // thread -> row tid / 8, blocks j = tid % 8 + 8u: all loads are issued
-    // before any is used (the pass count is at most GV_MAXB / 8)
-    constexpr int TPR = GV_T / GV_ROWS, PASSES = GV_MAXB / TPR;
-    const int r = tid / TPR, j0c = tid % TPR;
-    const bool row_ok = n0 + r < N;
-    const int64_t blk0 = (row_ok ? n0 + r : 0) * nbk + b_lo;
-    uint32_t qv[PASSES];
-    float fv[PASSES];
+    // table: entry e (a code byte) = the bf16 pair (NF4[e % 16], NF4[e / 16]),
+    // 64 copies side by side
+    u32x4* tv = reinterpret_cast<u32x4*>(tab);
 #pragma unroll
-    for (int u = 0; u < PASSES; ++u) {
-      const int j = j0c + TPR * u;
-      const int64_t blk = blk0 + (j < nbs ? j : 0);
+    for (int k = 0; k < 256 * 64 / 4 / G3_T; ++k) {
+      const int i = k * G3_T + tid, e = i >> 4;
+      const uint32_t v = pack_bf2(kNF4c[e & 15], kNF4c[e >> 4]);
+      tv[i] = u32x4{v, v, v, v};
+    }
+  }
+
+  // chunk kc >= c_hi (the pipeline's run-out) reloads chunk c_hi - 1, which
+  // is still in L2; blocks past the weight's end reload its last block
+  // (their constants are zero)
+  auto blk = [&](int kc, int j) -> int64_t {
+    const int64_t b = (int64_t)G3_CB * (kc < c_hi ? kc : c_hi - 1) + j;
+    return b < nbk ? b : nbk - 1;
+  };
+  // loads of chunk kc into register set d: the code pieces and constants,
+  // then (separately, once the set's activations have been used) the
+  // activations
+  auto issue_codes = [&](int kc, G3Set& d) {
+#pragma unroll
+    for (int u = 0; u < G3_LPT; ++u) d.c[u] = *reinterpret_cast<const u32x4*>(gsrc[u] + blk(kc, gblk[u]) * 32);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t fb = cbase + blk(kc, cpair + j);
       if (DQ) {
-        qv[u] = dq.absmax_q[blk];
-        fv[u] = dq.scale2[blk >> 8];
+        d.q[j] = dq.absmax_q[fb];
+        d.f[j] = dq.scale2[fb >> 8];
       } else {
-        qv[u] = 0;
-        fv[u] = dq.absmax[blk];
+        d.q[j] = 0;
+        d.f[j] = dq.absmax[fb];
       }
     }
-    const float mu = DQ ? *dq.offset : 0.0f;
-    if (tid < 256) tab[tid] = pack_bf2(kNF4c[tid & 15], kNF4c[tid >> 4]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_x = [&](int kc, G3Set& d) {
+    const uint16_t* xp = xrow + blk(kc, q) * 64;
+    d.x[0] = *reinterpret_cast<const u32x4*>(xp);
+    d.x[1] = *reinterpret_cast<const u32x4*>(xp + 8);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  floatx4 acc[G3_RT];
 #pragma unroll
-    for (int u = 0; u < PASSES; ++u) {
-      const int j = j0c + TPR * u;
-      if (j < bps) {
-        const float c = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qv[u]), fv[u]), mu) : fv[u];
-        smem[r * cpitch + j] = (row_ok && j < nbs) ? c : 0.0f;
+  for (int rt = 0; rt < G3_RT; ++rt) acc[rt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t lane4 = (uint32_t)lane << 2;
+
+  // one chunk: codes and constants of register set d (chunk kc) to LDS
+  // buffer kc & 1, the set refilled with the codes of chunk kc + G3_D,
+  // barrier, then this wave's block of the chunk for its 128 rows, and the
+  // set's activations refilled last
+  auto step = [&](int kc, G3Set& d) {
+    const int sbuf = kc & 1;
+#pragma unroll
+    for (int u = 0; u < G3_LPT; ++u) stage[sbuf][u * G3_T + tid] = d.c[u];
+    {
+      float c[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool ok = crow_ok && (int64_t)G3_CB * kc + cpair + j < nbk;
+        const float v = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(d.q[j]), d.f[j]), mu) : d.f[j];
+        c[j] = ok ? v : 0.0f;
       }
+      cst[sbuf][tid] = make_float2(c[0], c[1]);
     }
-  }
-  __syncthreads();
-
-  const int col = lane & 31, h = lane >> 5;
-  // rows beyond N read row N - 1 (their constants are zero)
-  const uint8_t* cbase = codes + ((n0 * K) >> 1) + 16 * h;
-  uint32_t coff[GV_CT];
+    issue_codes(kc + G3_D, d);
+    __syncthreads();
+    const bf16x8 x0 = __builtin_bit_cast(bf16x8, d.x[0]);
+    const bf16x8 x1 = __builtin_bit_cast(bf16x8, d.x[1]);
+    const int piece = 2 * q + (g >> 1);
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage[sbuf]);
+    const float* cs = reinterpret_cast<const float*>(cst[sbuf]);
+    uint2 cw[G3_RT];
 #pragma unroll
-  for (int t = 0; t < GV_CT; ++t) {
-    const int64_t rr = n0 + 32 * t + col < N ? 32 * t + col : N - 1 - n0;
-    coff[t] = (uint32_t)((rr * K) >> 1);
-  }
-  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K + 32 * h;
-  const int bpw = bps / GV_WAVES;  // blocks per wave, a multiple of GV_DEPTH
-  const int j0 = wave * bpw;       // first block of this wave, relative to b_lo
-  const int64_t blast = b_lo + nbs - 1;
-
-  // Block b_lo + j; past the split's end the split's last block is loaded
-  // again (its constant is zero).  Loads run two blocks ahead: all of a
-  // block's loads (codes and activations) are issued together, since the
-  // memory counter retires loads in issue order.
-  auto load = [&](int j, GvBlock& d) {
-    const int64_t b = b_lo + j <= blast ? b_lo + j : blast;
-#pragma unroll
-    for (int t = 0; t < GV_CT; ++t) d.cw[t] = *reinterpret_cast<const uint4*>(cbase + coff[t] + b * 32);
-    const uint16_t* xp = xrow + b * 64;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) d.x[s] = ldg16(xp + 8 * s);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the math that follows
-  };
-  float acc[GV_CT][8];
-#pragma unroll
-  for (int t = 0; t < GV_CT; ++t)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[t][e] = 0.0f;
-  auto compute = [&](int j, const GvBlock& d) {
-#pragma unroll
-    for (int t = 0; t < GV_CT; ++t) {
-      const float c = smem[(32 * t + col) * cpitch + j];
-      const uint32_t w[4] = {d.cw[t].x, d.cw[t].y, d.cw[t].z, d.cw[t].w};
-      floatx16 p;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) p[e] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) p = mfma32(__builtin_bit_cast(bf16x8, d.x[s]), tab_lookup8(tab, w[s]), p);
-      // token rows 0..15 of the 32-row tile are registers 0..7
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[t][e] = __builtin_fmaf(c, p[e], acc[t][e]);
+    for (int rt = 0; rt < G3_RT; ++rt) {
+      const int r = hrow + 16 * rt + t;
+      cw[rt] = *reinterpret_cast<const uint2*>(sb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)) + 8 * (g & 1));
     }
+    const char* tb = reinterpret_cast<const char*>(tab);
+    auto look8 = [&](uint32_t w) -> bf16x8 {
+      u32x4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(w, lane4, 0x0C0C0400u + (k << 8)));
+      return __builtin_bit_cast(bf16x8, v);
+    };
+#pragma unroll
+    for (int rt = 0; rt < G3_RT; ++rt) {
+      const int r = hrow + 16 * rt + t;
+      floatx4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+      p = mfma16(x0, look8(cw[rt].x), p);
+      p = mfma16(x1, look8(cw[rt].y), p);
+      const float c = cs[r * G3_CB + q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rt][i] = __builtin_fmaf(c, p[i], acc[rt][i]);
+    }
+    issue_x(kc + G3_D, d);
   };
 
-  // bpw is a multiple of GV_DEPTH: three register sets in rotation
-  GvBlock A, B, C;
-  load(j0, A);
-  load(j0 + 1, B);
-  for (int i = 0; i < bpw; i += 3) {
-    const int j = j0 + i;
-    load(j + 2, C);
-    compute(j, A);
-    load(j + 3, A);  // past this wave's run on the last pass: unused
-    compute(j + 1, B);
-    load(j + 4, B);
-    compute(j + 2, C);
+  G3Set A, B, C;  // G3_D register sets in rotation
+  issue_codes(c_lo, A);
+  issue_x(c_lo, A);
+  issue_codes(c_lo + 1, B);
+  issue_x(c_lo + 1, B);
+  issue_codes(c_lo + 2, C);
+  issue_x(c_lo + 2, C);
+  int kc = c_lo;
+  for (; kc + G3_D <= c_hi; kc += G3_D) {
+    step(kc, A);
+    step(kc + 1, B);
+    step(kc + 2, C);
   }
-  __syncthreads();  // constants no longer needed: smem becomes red
+  if (kc < c_hi) step(kc, A);  // the remaining 0..2 chunks (uniform branches)
+  if (kc + 1 < c_hi) step(kc + 1, B);
+  __syncthreads();  // the stages are free: they hold the partial tiles now
 
-  float* red = smem;  // [wave][m][GV_ROWS + 1]
+  float* red = reinterpret_cast<float*>(stage);  // [block q][m][G3_ROWS]
 #pragma unroll
-  for (int t = 0; t < GV_CT; ++t)
+  for (int rt = 0; rt < G3_RT; ++rt)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      red[(wave * kGemvMaxM + acc_row32(e, lane)) * (GV_ROWS + 1) + 32 * t + col] = acc[t][e];
+    for (int i = 0; i < 4; ++i) red[(q * kGemvMaxM + 4 * g + i) * G3_ROWS + hrow + 16 * rt + t] = acc[rt][i];
   __syncthreads();
-  for (int o = tid; o < M * GV_ROWS; o += GV_T) {
-    const int m = o / GV_ROWS, c = o % GV_ROWS;
+  for (int o = tid; o < M * G3_ROWS; o += G3_T) {
+    const int m = o / G3_ROWS, c = o % G3_ROWS;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < GV_WAVES; ++w) v += red[(w * kGemvMaxM + m) * (GV_ROWS + 1) + c];
+    for (int w = 0; w < G3_CB; ++w) v += red[(w * kGemvMaxM + m) * G3_ROWS + c];
     if (n0 + c < N) part[((int64_t)blockIdx.y * M + m) * N + n0 + c] = v;
   }
 }
 
-// Y[m, n] = bf16(sum_s part[s][m][n] + sum_j XAs[m, j] B[j, n]); one token
-// row per blockIdx.y, 4 columns per thread (N % 4 == 0).
+// Y[m, n] = bf16(sum_s part[s][m][n] + sum_j XAs[m, j] B[j, n]), with the
+// adapter input formed here from the fp32 partials of X A, xpart[SX][M][rp]:
+// C = sum of the slices, XAs = bf16(alpha C) (columns >= r are zero
+// partials), and XA = bf16(C) [M, r] written by the blocks with
+// blockIdx.x == 0 when XA is given.  One token row per blockIdx.y, 4 columns
+// per thread (N % 4 == 0), rp <= 256.
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int S, int M, int64_t N,
-                                                          const uint16_t* __restrict__ XAs, int64_t rp,
-                                                          const uint16_t* __restrict__ B, int r,
-                                                          uint16_t* __restrict__ Y) {
-  const int64_t nc = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const int m = blockIdx.y;
+                                                          const float* __restrict__ xpart, int SX, int rp,
+                                                          float alpha, const uint16_t* __restrict__ B, int r,
+                                                          uint16_t* __restrict__ Y, uint16_t* __restrict__ XA) {
+  __shared__ float4 xsum[256];  // [group][rp / 4]
+  __shared__ float xas[256];
+  const int tid = threadIdx.x, m = blockIdx.y;
+  // thread (group u, column quad c4): the slices u, u + G, ... of 4 columns;
+  // the G group sums are then added in a fixed order
+  const int nq = rp >> 2, G = 256 / nq, c4 = tid % nq, u = tid / nq;
+  {
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+    for (int k = u; k < SX; k += G) {
+      const float4 v = *reinterpret_cast<const float4*>(xpart + ((int64_t)k * M + m) * rp + 4 * c4);
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    xsum[tid] = a;  // tid = u * nq + c4
+  }
+  __syncthreads();
+  for (int j = tid; j < rp; j += 256) {
+    const float* xs = reinterpret_cast<const float*>(xsum);
+    float c = 0.0f;
+    for (int w = 0; w < G; ++w) c += xs[w * rp + j];
+    xas[j] = bf2f(f2bf(alpha * c));
+    if (XA != nullptr && blockIdx.x == 0 && j < r) XA[(int64_t)m * r + j] = f2bf(c);
+  }
+  __syncthreads();
+  const int64_t nc = ((int64_t)blockIdx.x * 256 + tid) * 4;
   if (nc >= N) return;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll 4
-  for (int s = 0; s < S; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + m) * N + nc);
+  for (int k = 0; k < S; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)k * M + m) * N + nc);
     a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
   }
-  const uint16_t* xa = XAs + (int64_t)m * rp;
 #pragma unroll 8
   for (int j = 0; j < r; ++j) {
-    const float x = bf2f(xa[j]);
+    const float x = xas[j];
     const uint2 bv = *reinterpret_cast<const uint2*>(B + (int64_t)j * N + nc);
     a0 = __builtin_fmaf(x, __uint_as_float(bv.x << 16), a0);
     a1 = __builtin_fmaf(x, __uint_as_float(bv.x & 0xFFFF0000u), a1);
@@ -1133,7 +1209,7 @@ hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int
   else
     hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || (out1 == nullptr && out2 == nullptr)) return e;  // partials only
   const int T = split_sum_threads(cdiv(M * QP, 4), splits);
 #define QLORA_EPI(TT)                                                                                        \
   case TT:                                                                                                   \
@@ -1204,51 +1280,36 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
   return launch_main_any<false>(a, split_ws, stream);
 }
 
-// Blocks per split: a multiple of GV_QUANT (GV_DEPTH blocks per loop pass
-// for each wave), at most GV_MAXB.
-int64_t gemv_blocks_per_split(int64_t nbk, int64_t splits) {
-  return ((nbk + splits - 1) / splits + GV_QUANT - 1) / GV_QUANT * GV_QUANT;
-}
-
 int gemv_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = (int64_t)cdiv(N, GV_ROWS), nbk = K >> 6;
-  // about 16 waves per CU over the whole grid
-  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t tiles = (int64_t)cdiv(N, G3_ROWS), nchunks = ((K >> 6) + G3_CB - 1) / G3_CB;
+  // one workgroup per CU over the whole grid
+  int64_t s = (kCUs + tiles - 1) / tiles;
   // keep the fp32 partials (S * M * N * 4 bytes, written and read once)
-  // below about 1/16 of the packed weight (N * K / 2 bytes)
-  const int64_t by_bytes = K / (128 * (M > 0 ? M : 1));
+  // below about 1/4 of the packed weight (N * K / 2 bytes)
+  const int64_t by_bytes = K / (32 * (M > 0 ? M : 1));
   if (s > by_bytes) s = by_bytes;
-  const int64_t by_blocks = nbk / GV_QUANT;  // a full pass for every wave
-  if (s > by_blocks) s = by_blocks;
-  const int64_t min_s = (nbk + GV_MAXB - 1) / GV_MAXB;  // the constants must fit in LDS
-  if (s < min_s) s = min_s;
-  if (s < 1) s = 1;
-  // the split count that the rounded block count actually gives; every
-  // split then holds at least one block
-  const int64_t bps = gemv_blocks_per_split(nbk, s);
-  return (int)((nbk + bps - 1) / bps);
+  if (s > nchunks) s = nchunks;  // every split holds at least one chunk
+  return (int)(s < 1 ? 1 : s);
 }
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
                        float* part, int splits, hipStream_t stream) {
-  if (M < 1 || M > kGemvMaxM || splits < 1) return hipErrorInvalidValue;
-  const int64_t nbk = K >> 6;
-  const int bps = (int)gemv_blocks_per_split(nbk, splits);
-  if ((int64_t)(splits - 1) * bps >= nbk || bps > GV_MAXB || (int64_t)splits * bps < nbk)
-    return hipErrorInvalidValue;  // an empty split, or constants beyond the LDS table
-  const dim3 grid(cdiv(N, GV_ROWS), (unsigned)splits);
+  if (M < 1 || M > kGemvMaxM || splits < 1 || K < 64 || N < 1) return hipErrorInvalidValue;
+  if (splits > ((K >> 6) + G3_CB - 1) / G3_CB) return hipErrorInvalidValue;  // an empty split
+  const dim3 grid(cdiv(N, G3_ROWS), (unsigned)splits);
   if (dq.double_quant)
-    hipLaunchKernelGGL((gemv_kernel<true>), grid, dim3(GV_T), 0, stream, X, (int)M, K, codes, dq, N, bps, part);
+    hipLaunchKernelGGL((gemv3_kernel<true>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part);
   else
-    hipLaunchKernelGGL((gemv_kernel<false>), grid, dim3(GV_T), 0, stream, X, (int)M, K, codes, dq, N, bps, part);
+    hipLaunchKernelGGL((gemv3_kernel<false>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const uint16_t* XAs, int64_t rp,
-                              const uint16_t* B, int64_t r, uint16_t* Y, hipStream_t stream) {
-  if (N % 4) return hipErrorInvalidValue;
+hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const float* xpart, int xsplits,
+                              int64_t rp, float alpha, const uint16_t* B, int64_t r, uint16_t* Y, uint16_t* XA,
+                              hipStream_t stream) {
+  if (N % 4 || rp % 64 || rp > 256 || r > rp || xsplits < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3(cdiv(N, 1024), (unsigned)M), dim3(256), 0, stream, part, splits, (int)M,
-                     N, XAs, rp, B, (int)r, Y);
+                     N, xpart, xsplits, (int)rp, alpha, B, (int)r, Y, XA);
   return hipGetLastError();
 }
 

@@ -153,6 +153,22 @@ def test_small_token_path(B, M, N, K, dq):
     _full_check(B, M, N, K, 64, 0.25, seed=M * 1000 + K // 64, dq=dq)
 
 
+@pytest.mark.parametrize("M,N,K,r", [(4, 192, 64 * 40, 8), (9, 256, 64 * 66, 100), (16, 128, 64 * 13, 256),
+                                     (1, 64, 64 * 3, 17)])
+def test_small_token_ranks(B, M, N, K, r):
+    """The small-token forward forms X A itself from split partials: ranks
+    below and above the 64-column padding, and r = 256."""
+    _log(f"linear small-token rank M={M} N={N} K={K} r={r}")
+    _full_check(B, M, N, K, r, 16.0 / r, seed=M * 31 + N + K + r)
+
+
+def test_small_token_zero_weight(B):
+    """W = 0 on the small-token path: Y = s X A B through the final kernel alone."""
+    _log("linear small-token W=0")
+    Y, Yr = _full_check(B, 8, 256, 64 * 20, 64, 0.25, seed=13, w_zero=True)
+    assert np.linalg.norm(Yr) > 0
+
+
 def test_no_double_quant(B):
     _log("linear without double quantisation")
     _full_check(B, 96, 256, 256, 16, 1.0, seed=5, dq=False)
