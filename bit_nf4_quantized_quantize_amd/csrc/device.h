@@ -83,8 +83,8 @@ __host__ __device__ __forceinline__ uint32_t perm_b32(uint32_t s0, uint32_t s1, 
 // One NF4 block shares one constant c, so its 16 possible bf16 values
 // bf16(NF4[i] * c) form a table.  The table is kept as two 16-byte planes
 // (low and high bytes of each bf16), four registers each; v_perm_b32 then
-// looks up four codes per instruction from one half-plane, and a bitfield
-// select on code bit 3 picks the half.  Values are exactly those of the
+// looks up four codes per instruction from one half-plane, and a third
+// v_perm_b32, with a selector made from code bit 3, picks the half.  Values are exactly those of the
 // dequantisation kernel: fp32 product, nearest-even bf16.
 struct BlockLUT {
   uint32_t lo[4], hi[4];
@@ -101,18 +101,25 @@ __host__ __device__ __forceinline__ BlockLUT make_lut(const uint32_t p[8]) {
   return t;
 }
 
+// Selector that picks, per byte, byte i of the second v_perm_b32 operand
+// (the table half for codes 0..7) when bit 0 of byte i of t is 0 and byte i
+// of the first operand (codes 8..15) when it is 1.
+__host__ __device__ __forceinline__ uint32_t lut_half_sel(uint32_t t) {
+  return ((t & 0x01010101u) << 2) + 0x03020100u;
+}
+
 // Eight codes of one 32-bit word (element 0 in the low nibble) -> eight bf16
 // in element order, as four 32-bit words.
 __host__ __device__ __forceinline__ void lut_lookup8(const BlockLUT& t, uint32_t w, uint32_t out[4]) {
   const uint32_t e7 = w & 0x07070707u;                 // even elements, code & 7
   const uint32_t o7 = (w >> 4) & 0x07070707u;          // odd elements
   const uint32_t t3 = w >> 3;
-  const uint32_t me = (t3 & 0x01010101u) * 0xFFu;       // 0xFF where code >= 8
-  const uint32_t mo = ((t3 >> 4) & 0x01010101u) * 0xFFu;
-  const uint32_t loE = (me & perm_b32(t.lo[3], t.lo[2], e7)) | (~me & perm_b32(t.lo[1], t.lo[0], e7));
-  const uint32_t hiE = (me & perm_b32(t.hi[3], t.hi[2], e7)) | (~me & perm_b32(t.hi[1], t.hi[0], e7));
-  const uint32_t loO = (mo & perm_b32(t.lo[3], t.lo[2], o7)) | (~mo & perm_b32(t.lo[1], t.lo[0], o7));
-  const uint32_t hiO = (mo & perm_b32(t.hi[3], t.hi[2], o7)) | (~mo & perm_b32(t.hi[1], t.hi[0], o7));
+  const uint32_t me = lut_half_sel(t3);                 // code bit 3 of the even elements
+  const uint32_t mo = lut_half_sel(t3 >> 4);            // of the odd elements
+  const uint32_t loE = perm_b32(perm_b32(t.lo[3], t.lo[2], e7), perm_b32(t.lo[1], t.lo[0], e7), me);
+  const uint32_t hiE = perm_b32(perm_b32(t.hi[3], t.hi[2], e7), perm_b32(t.hi[1], t.hi[0], e7), me);
+  const uint32_t loO = perm_b32(perm_b32(t.lo[3], t.lo[2], o7), perm_b32(t.lo[1], t.lo[0], o7), mo);
+  const uint32_t hiO = perm_b32(perm_b32(t.hi[3], t.hi[2], o7), perm_b32(t.hi[1], t.hi[0], o7), mo);
   const uint32_t e01 = perm_b32(hiE, loE, 0x05010400u);  // bf16 of elements 0, 2
   const uint32_t o01 = perm_b32(hiO, loO, 0x05010400u);  // elements 1, 3
   const uint32_t e23 = perm_b32(hiE, loE, 0x07030602u);  // elements 4, 6

@@ -9,14 +9,15 @@
 //
 // The weight is [N, K] = [out, in] with 64-element NF4 blocks along K.
 //
-// Main products (bf16 MFMA 32x32x16, fp32 accumulation), 256 threads as a
-// 2 x 2 grid of waves over a 256 x 256 output tile (128 x 128 per wave), or
-// over 256 x 128 / 128 x 128 tiles for very short reductions, k-step 64,
-// two LDS stages:
+// Main products (bf16 MFMA 32x32x16, fp32 accumulation), 512 threads as a
+// 2 x 4 grid of waves over a 256 x 256 output tile (128 x 64 per wave, two
+// waves per SIMD), or 256 threads over 256 x 128 / 128 x 128 tiles for very
+// short reductions; k-step 64, two LDS stages:
 //   forward  Y [M, N]  = X [M, K] W^T     + (s XA) [M, rp] B [rp, N]
 //   backward dX [M, K] = dY [M, N] W      + (s T) [M, rp] A^T
 // Each k-step stages the activation tile (X or dY) and dequantises the
-// weight tile: a thread expands whole NF4 blocks through a per-block bf16
+// weight tile: a thread expands NF4 blocks (a whole block in the narrow-tile
+// kernel, half a block in the 256 x 256 kernel) through a per-block bf16
 // lookup table (the exact bf16(NF4[code] * c2_hat) values) into LDS.  The
 // forward tile is [n][k] (reduction contiguous); the backward tile is the
 // same natural [n][k] layout, read through LDS transpose loads because there
@@ -40,6 +41,11 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int PK = 72;  // pitch (bf16) of a [rows][64] reduction-contiguous tile
+// Padding (bf16) of a tile read through transpose loads ([red][cols], cols a
+// multiple of 64).  Half a wave of frag_rc reads 4 reduction rows x 64
+// bytes; with the row pitch = 32 or 96 mod 128 bf16 those rows start 16 or 48
+// banks apart and cover all 64 banks once (with +16 they overlapped 2-way).
+constexpr int kRcPad = 32;
 
 // Appendix E of QLoRA as immediates for the lookup-table build.
 constexpr float kNF4c[16] = {
@@ -102,7 +108,7 @@ template <int BM, int BN, bool BWD>
 struct MainCfg {
   static constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
   static constexpr int TMW = WM / 32, TNW = WN / 32;   // 32x32 MFMA tiles per wave
-  static constexpr int PRC = BN + 16;                  // pitch of a [64][BN] tile
+  static constexpr int PRC = BN + kRcPad;              // pitch of a [64][BN] tile
   static constexpr int SA = BM * PK;
   static constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
   static constexpr int XCH = BM * 8 / NT;              // 16-byte activation chunks per thread
@@ -282,7 +288,7 @@ struct WordState {
 template <bool BWD, bool DQ>
 __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
   constexpr int BM = 256, BN = 256;
-  constexpr int PRC = BN + 16;
+  constexpr int PRC = BN + kRcPad;
   constexpr int SA = BM * PK;
   constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
   constexpr int XCH = BM * 8 / V5_T;  // 8 activation chunks per thread
@@ -399,14 +405,14 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
           st.e7 = wd & 0x07070707u;
           st.o7 = (wd >> 4) & 0x07070707u;
           const uint32_t t3 = wd >> 3;
-          st.me = (t3 & 0x01010101u) * 0xFFu;
-          st.mo = ((t3 >> 4) & 0x01010101u) * 0xFFu;
+          st.me = lut_half_sel(t3);
+          st.mo = lut_half_sel(t3 >> 4);
         } else if (stg == 1) {
-          st.loE = (st.me & perm_b32(lut.lo[3], lut.lo[2], st.e7)) | (~st.me & perm_b32(lut.lo[1], lut.lo[0], st.e7));
-          st.hiE = (st.me & perm_b32(lut.hi[3], lut.hi[2], st.e7)) | (~st.me & perm_b32(lut.hi[1], lut.hi[0], st.e7));
+          st.loE = perm_b32(perm_b32(lut.lo[3], lut.lo[2], st.e7), perm_b32(lut.lo[1], lut.lo[0], st.e7), st.me);
+          st.hiE = perm_b32(perm_b32(lut.hi[3], lut.hi[2], st.e7), perm_b32(lut.hi[1], lut.hi[0], st.e7), st.me);
         } else if (stg == 2) {
-          st.loO = (st.mo & perm_b32(lut.lo[3], lut.lo[2], st.o7)) | (~st.mo & perm_b32(lut.lo[1], lut.lo[0], st.o7));
-          st.hiO = (st.mo & perm_b32(lut.hi[3], lut.hi[2], st.o7)) | (~st.mo & perm_b32(lut.hi[1], lut.hi[0], st.o7));
+          st.loO = perm_b32(perm_b32(lut.lo[3], lut.lo[2], st.o7), perm_b32(lut.lo[1], lut.lo[0], st.o7), st.mo);
+          st.hiO = perm_b32(perm_b32(lut.hi[3], lut.hi[2], st.o7), perm_b32(lut.hi[1], lut.hi[0], st.o7), st.mo);
         } else {
           const uint32_t e01 = perm_b32(st.hiE, st.loE, 0x05010400u);
           const uint32_t o01 = perm_b32(st.hiO, st.loO, 0x05010400u);
@@ -525,6 +531,268 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     }
 }
 
+// ================================== main GEMM, 256 x 256, 8 waves, v6
+// Two waves per SIMD, each owning a 128 x 64 output tile (128 fp32
+// accumulators), so that one wave's LDS reads and dequantisation VALU overlap
+// the other wave's MFMAs.  Every thread dequantises half an NF4 block (32
+// weights) of the next k-step; those instructions are spread between the
+// MFMAs by hand as in the 4-wave kernel.  Fragment reads for sub-step kk+1
+// are issued while sub-step kk multiplies.
+constexpr int V6_T = 512;
+
+
+template <bool BWD, bool DQ>
+__global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int PRC = BN + kRcPad;
+  constexpr int SA = BM * PK;
+  constexpr int SB = (BN * PK > 64 * PRC) ? BN * PK : 64 * PRC;
+  constexpr int XCH = BM * 8 / V6_T;  // 4 activation chunks per thread
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][SA];
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][SB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // rows wm * 128 .. +127, columns wn * 64 .. +63
+  const int tn = (int)((a.ncols + BN - 1) / BN);
+  const int nkt = (int)(a.L >> 6);
+  const int F = a.full_tiles, pid = blockIdx.x;
+  int lid, ks = 0, ke = nkt, unit = -1;
+  if (pid < F) {
+    lid = (F % 8 == 0) ? (pid % 8) * (F / 8) + pid / 8 : pid;
+  } else {
+    unit = pid - F;
+    const int sp = unit % a.split;
+    lid = F + unit / a.split;
+    ks = (int)((int64_t)sp * nkt / a.split);
+    ke = (int)((int64_t)(sp + 1) * nkt / a.split);
+  }
+  const bool last_range = ke == nkt;
+  const int64_t m0 = (int64_t)(lid / tn) * BM, c0 = (int64_t)(lid % tn) * BN;
+  const int nk = ke;
+  const int64_t kblocks = a.Kw >> 6;
+  const float mu = DQ ? *a.dq.offset : 0.0f;
+
+  // dequantisation task: half (t_half) of one NF4 block per thread; the 16
+  // lanes of a store group take 16 different rows (fwd) or 4 rows x 4 blocks
+  // (bwd)
+  const int tq = tid & 255, t_half = tid >> 8;
+  const int t_row = BWD ? (tq >> 2) : tq;
+  const int t_col = BWD ? (tq & 3) * 64 : 0;
+  const bool t_ok = BWD ? (c0 + t_col < a.Kw) : (c0 + t_row < a.Nw);
+  const int64_t t_n = BWD ? 0 : (t_ok ? c0 + t_row : a.Nw - 1);
+  const int64_t t_k = BWD ? (t_ok ? c0 + t_col : a.Kw - 64) : 0;
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  uint4 xr[XCH];
+  uint4 cwA, cwB;
+  uint8_t qbA = 0, qbB = 0;
+  float sfA = 0.0f, sfB = 0.0f;
+
+  auto x_src = [&](int i, int kt) -> const uint16_t* {
+    const int id = tid + V6_T * i, row = id >> 3, ch = id & 7;
+    const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+    return a.act + m * a.L + (int64_t)kt * 64 + ch * 8;
+  };
+  auto x_dst = [&](int i, int buf) -> __bf16* {
+    const int id = tid + V6_T * i, row = id >> 3, ch = id & 7;
+    return &sA[buf][row * PK + ch * 8];
+  };
+  auto load_codes = [&](int kt, uint4& c, uint8_t& q, float& f) {
+    const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
+    const int64_t k = BWD ? t_k : (int64_t)kt * 64;
+    c = *reinterpret_cast<const uint4*>(a.codes + ((n * a.Kw + k) >> 1) + 16 * t_half);
+    const int64_t blk = n * kblocks + (k >> 6);
+    if (DQ) {
+      q = a.dq.absmax_q[blk];
+      f = a.dq.scale2[blk >> 8];
+    } else {
+      f = a.dq.absmax[blk];
+    }
+  };
+  auto wdst = [&](int buf, int w) -> __bf16* {
+    const int off = t_col + 32 * t_half + 8 * w;
+    return BWD ? &sB[buf][t_row * PRC + off] : &sB[buf][t_row * PK + off];
+  };
+
+  bf16x8 fa[2][4], fb[2][2];
+  auto read_frags = [&](int buf, int kk, int slot, bool b_rc, int pitch_b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[slot][j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane)
+                         : frag_kc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane);
+  };
+
+  // ---- one k-step: multiply stage `cur` while producing stage `nxt`
+  auto step = [&](int kt, const int cur, const uint4& cu, uint8_t qu, float fu, uint4& cl, uint8_t& ql, float& fl) {
+    const int nxt = cur ^ 1;
+    const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
+    const uint32_t words[4] = {cu.x, cu.y, cu.z, cu.w};
+    float sc = 0.0f;
+    uint32_t pw[8];
+    BlockLUT lut;
+    WordState ws[4];
+    load_codes(k2, cl, ql, fl);
+    read_frags(cur, 0, 0, BWD, BWD ? PRC : PK);
+    // items 0..32 interleaved with the 32 MFMAs, in order (slot 0 takes
+    // items 0 and 1, slot s item s + 1)
+    auto item = [&](int it) {
+      if (it == 0) {
+        const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
+        sc = t_ok ? bs : 0.0f;
+        pw[0] = pack_bf2(kNF4c[0] * sc, kNF4c[1] * sc);
+      } else if (it <= 7) {
+        pw[it] = pack_bf2(kNF4c[2 * it] * sc, kNF4c[2 * it + 1] * sc);
+      } else if (it == 8) {
+        lut = make_lut(pw);
+      } else if (it < 9 + 16) {
+        const int w = (it - 9) >> 2, stg = (it - 9) & 3;
+        WordState& st = ws[w];
+        const uint32_t wd = words[w];
+        if (stg == 0) {
+          st.e7 = wd & 0x07070707u;
+          st.o7 = (wd >> 4) & 0x07070707u;
+          const uint32_t t3 = wd >> 3;
+          st.me = lut_half_sel(t3);
+          st.mo = lut_half_sel(t3 >> 4);
+        } else if (stg == 1) {
+          st.loE = perm_b32(perm_b32(lut.lo[3], lut.lo[2], st.e7), perm_b32(lut.lo[1], lut.lo[0], st.e7), st.me);
+          st.hiE = perm_b32(perm_b32(lut.hi[3], lut.hi[2], st.e7), perm_b32(lut.hi[1], lut.hi[0], st.e7), st.me);
+        } else if (stg == 2) {
+          st.loO = perm_b32(perm_b32(lut.lo[3], lut.lo[2], st.o7), perm_b32(lut.lo[1], lut.lo[0], st.o7), st.mo);
+          st.hiO = perm_b32(perm_b32(lut.hi[3], lut.hi[2], st.o7), perm_b32(lut.hi[1], lut.hi[0], st.o7), st.mo);
+        } else {
+          const uint32_t e01 = perm_b32(st.hiE, st.loE, 0x05010400u);
+          const uint32_t o01 = perm_b32(st.hiO, st.loO, 0x05010400u);
+          const uint32_t e23 = perm_b32(st.hiE, st.loE, 0x07030602u);
+          const uint32_t o23 = perm_b32(st.hiO, st.loO, 0x07030602u);
+          sts16(wdst(nxt, w), make_uint4(perm_b32(o01, e01, 0x05040100u), perm_b32(o01, e01, 0x07060302u),
+                                         perm_b32(o23, e23, 0x05040100u), perm_b32(o23, e23, 0x07060302u)));
+        }
+      } else if (it < 25 + XCH) {
+        const int i = it - 25;
+        sts16(x_dst(i, nxt), xr[i]);
+      } else if (it < 25 + 2 * XCH) {
+        const int i = it - 25 - XCH;
+        xr[i] = ldg16(x_src(i, k2));
+      }
+    };
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int slot = kk & 1;
+#pragma unroll
+      for (int ij = 0; ij < 8; ++ij) {
+        const int i = ij >> 1, j = ij & 1;
+        acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
+        if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
+        const int sl = kk * 8 + ij;
+        if (sl == 0) {
+          item(0);
+          item(1);
+        } else {
+          item(sl + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- prologue: stage 0 filled; X(ks+1) and codes(ks+1) in flight
+  load_codes(ks, cwB, qbB, sfB);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks));
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
+  {
+    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
+    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f);
+    const uint32_t words[4] = {cwB.x, cwB.y, cwB.z, cwB.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o[4];
+      lut_lookup8(lut, words[w], o);
+      sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
+  load_codes(ks + 1 < nk ? ks + 1 : ks, cwA, qbA, sfA);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks + 1 < nk ? ks + 1 : ks));
+  __syncthreads();
+
+  for (int kt = ks; kt < nk; kt += 2) {
+    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
+    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
+  }
+
+  // ---- adapter term over bf16 operands (stage 0 is free)
+  for (int64_t jt = 0; last_range && jt < a.rp; jt += 64) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + V6_T * i, row = id >> 3, ch = id & 7;
+      const int64_t m = m0 + row;
+      sts16(&sA[0][row * PK + ch * 8], (m < a.M) ? ldg16(a.ext_act + m * a.rp + jt + ch * 8) : make_uint4(0, 0, 0, 0));
+    }
+    if (!BWD) {  // B [r, Nw]: tile [64 j][BN n], read transposed
+#pragma unroll
+      for (int i = 0; i < BN * 8 / V6_T; ++i) {
+        const int id = tid + V6_T * i, row = id / (BN / 8), ch = id % (BN / 8);
+        sts16(&sB[0][row * PRC + ch * 8], load8_masked(a.ext_w, a.Nw, jt + row, a.r, c0 + ch * 8, a.Nw));
+      }
+    } else {     // A [Kw, r]: tile [BN k][64 j]
+#pragma unroll
+      for (int i = 0; i < BN * 8 / V6_T; ++i) {
+        const int id = tid + V6_T * i, row = id >> 3, ch = id & 7;
+        sts16(&sB[0][row * PK + ch * 8], load8_masked(a.ext_w, a.r, c0 + row, a.Kw, jt + ch * 8, a.r));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 64; kk += 16) {
+      read_frags(0, kk, 0, !BWD, BWD ? PK : PRC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[0][i], fb[0][j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
+  if (unit >= 0) {
+    float* pt = a.part + (int64_t)unit * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cl = wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pt[(wm * 128 + 32 * i + acc_row32(e, lane)) * BN + cl] = acc[i][j][e];
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = c0 + wn * 64 + 32 * j + (lane & 31);
+      if (col >= a.ncols) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
+        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
+      }
+    }
+}
+
 // Adds the `split` fp32 partial tiles of each split tile (fixed order) and
 // writes the bf16 result.  Thread: 4 consecutive columns of one tile row.
 __global__ __launch_bounds__(256) void main_fixup_kernel(const float* __restrict__ part, int split, int full_tiles,
@@ -558,7 +826,7 @@ __global__ __launch_bounds__(256) void main_fixup_kernel(const float* __restrict
 //   NT: V(l, q) = V[q * L + l]   (B [r, N] for dY B^T) -> tile [64 q][128 l]
 constexpr int SK_BK = 128;
 constexpr int SK_PU = SK_BK + 8;   // [64][128] reduction-contiguous pitch
-constexpr int SK_PV = 64 + 16;     // [128][64] transposed-read pitch
+constexpr int SK_PV = 64 + kRcPad; // [128][64] transposed-read pitch
 
 template <bool NN>
 __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__ U, int64_t M, int64_t L,
@@ -706,7 +974,7 @@ template <int BP, int BQ>
 __global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, int64_t ldu, int64_t P,
                                                 const uint16_t* __restrict__ V, int64_t ldv, int64_t Q, int64_t M,
                                                 int64_t chunk, float* __restrict__ part) {
-  constexpr int PU = BP + 16, PV = BQ + 16;
+  constexpr int PU = BP + kRcPad, PV = BQ + kRcPad;
   constexpr int TMW = BP / 64, TNW = BQ / 64;
   constexpr int CU_ = TN_BK * BP / 8 / NT, CV_ = TN_BK * BQ / 8 / NT;  // chunks per thread
   __shared__ __attribute__((aligned(16))) __bf16 sU[TN_BK * PU];
@@ -1167,10 +1435,20 @@ hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
       a.part = split_ws;
       if (p.split > 1 && !split_ws) return hipErrorInvalidValue;
       const dim3 grid1((unsigned)p.units());
-      if (a.dq.double_quant)
-        hipLaunchKernelGGL((main_v5_kernel<BWD, true>), grid1, dim3(V5_T), 0, stream, a);
-      else
-        hipLaunchKernelGGL((main_v5_kernel<BWD, false>), grid1, dim3(V5_T), 0, stream, a);
+      // forward: one wave per SIMD (128 x 128 wave tiles); backward: two
+      // waves per SIMD (128 x 64), whose transpose-load fragment reads and
+      // dequantisation gain more from a second wave to hide them
+      if (BWD) {
+        if (a.dq.double_quant)
+          hipLaunchKernelGGL((main_v6_kernel<true, true>), grid1, dim3(V6_T), 0, stream, a);
+        else
+          hipLaunchKernelGGL((main_v6_kernel<true, false>), grid1, dim3(V6_T), 0, stream, a);
+      } else {
+        if (a.dq.double_quant)
+          hipLaunchKernelGGL((main_v5_kernel<false, true>), grid1, dim3(V5_T), 0, stream, a);
+        else
+          hipLaunchKernelGGL((main_v5_kernel<false, false>), grid1, dim3(V5_T), 0, stream, a);
+      }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || p.split == 1) return e;
       const int tn = (int)cdiv(a.ncols, 256);
