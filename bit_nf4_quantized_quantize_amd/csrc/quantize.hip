@@ -190,11 +190,13 @@ __device__ __forceinline__ void load4_full(const void* w, int64_t e0, float v[4]
   }
 }
 
+// The quantisation of one workgroup's chunks (grid-stride over 8192-weight
+// chunks); with `partials` it ends by storing the workgroup's exact-sum
+// counters at partials[blockIdx.x].
 template <bool BF16_IN>
-__global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
-                                                                  uint8_t* __restrict__ codes,
-                                                                  float* __restrict__ c2out,
-                                                                  uint64_t* __restrict__ partials, QuantTable tab) {
+__device__ __forceinline__ void quantize_chunks(const void* __restrict__ w, int64_t numel,
+                                                uint8_t* __restrict__ codes, float* __restrict__ c2out,
+                                                uint64_t* __restrict__ partials, const QuantTable& tab) {
   __shared__ uint2 s_tab[32];  // {threshold bits, base code}
   __shared__ unsigned long long s_acc[kMeanDigits];
   const int tid = threadIdx.x;
@@ -288,6 +290,14 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
   }
 }
 
+template <bool BF16_IN>
+__global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  float* __restrict__ c2out,
+                                                                  uint64_t* __restrict__ partials, QuantTable tab) {
+  quantize_chunks<BF16_IN>(w, numel, codes, c2out, partials, tab);
+}
+
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2, uint64_t* partials,
                            hipStream_t stream) {
   const int grid = quantize_parts(numel);
@@ -379,44 +389,52 @@ __device__ float exact_mean(const uint64_t* s_sum, int64_t nb) {
 // counters (at most 256, one per thread) and divides for mu; workgroup 0
 // stores mu.  This costs each workgroup one 20 KB read from L2 instead of a
 // separate single-workgroup launch.
-__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ c2, int64_t nb,
-                                                        const uint64_t* __restrict__ partials, int parts,
-                                                        float* __restrict__ mu_out,
-                                                        uint8_t* __restrict__ absmax_q,
-                                                        float* __restrict__ scale2) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ uint64_t s_part[4][kMeanDigits];
+// mu from the exact-sum counters of `parts` workgroups (at most WAVES * 64,
+// one per thread), reduced across this workgroup; every thread gets it.
+template <int WAVES>
+__device__ __forceinline__ float mean_from_partials(const uint64_t* __restrict__ partials, int parts, int64_t nb) {
+  __shared__ uint64_t s_part[WAVES][kMeanDigits];
   __shared__ uint64_t s_sum[kMeanDigits];
   __shared__ float s_mu;
-  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t v[kMeanDigits];
+  const int p = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < kMeanDigits; ++k) v[k] = p < parts ? partials[(int64_t)p * kMeanDigits + k] : 0;
+#pragma unroll
+  for (int k = 0; k < kMeanDigits; ++k) {
+    const uint64_t t = wave_sum_u64(v[k]);
+    if (lane == 0) s_part[wave][k] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < kMeanDigits) {
+    uint64_t t = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += s_part[w][threadIdx.x];
+    s_sum[threadIdx.x] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) s_mu = exact_mean(s_sum, nb);
+  __syncthreads();
+  return s_mu;
+}
+
+// The constants c2[256 g .. +255] of 256-group g, four per lane (zero past nb).
+__device__ __forceinline__ void load_group(const float* __restrict__ c2, int64_t g, int64_t nb, int lane,
+                                           float cv[4]) {
   const int64_t i0 = g * 256 + lane * 4;
-  // this wave's constants do not depend on mu: their loads go out first
-  float cv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) cv[i] = i0 + i < nb ? c2[i0 + i] : 0.0f;
-  {
-    uint64_t v[kMeanDigits];
-    const int p = threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < kMeanDigits; ++k) v[k] = p < parts ? partials[(int64_t)p * kMeanDigits + k] : 0;
-#pragma unroll
-    for (int k = 0; k < kMeanDigits; ++k) {
-      const uint64_t t = wave_sum_u64(v[k]);
-      if (lane == 0) s_part[wave][k] = t;
-    }
-    __syncthreads();
-    if (threadIdx.x < kMeanDigits)
-      s_sum[threadIdx.x] = s_part[0][threadIdx.x] + s_part[1][threadIdx.x] + s_part[2][threadIdx.x] +
-                           s_part[3][threadIdx.x];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      s_mu = exact_mean(s_sum, nb);
-      if (blockIdx.x == 0) *mu_out = s_mu;
-    }
-    __syncthreads();
-  }
-  const float mu = s_mu;
-  if (g * 256 >= nb) return;  // whole wave exits together
+}
+
+// Double quantisation of 256-group g by one wave (Sec. 3 of the QLoRA paper,
+// reading G4 for mu): d = c2 - mu, c1 = max |d| over the group, byte =
+// E4M3(clamp(d * fp32(448 / c1), +-448)) nearest-even, scale2 = c1 / 448; a
+// group with c1 < 2^-118 is first scaled by 2^32 (reading G13).
+__device__ __forceinline__ void encode_group(const float cv[4], int64_t g, int64_t nb, float mu,
+                                             uint8_t* __restrict__ absmax_q, float* __restrict__ scale2,
+                                             int lane) {
+  const int64_t i0 = g * 256 + lane * 4;
   float d[4];
   float m = 0.0f;
 #pragma unroll
@@ -446,6 +464,24 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
       if (i0 + i < nb) absmax_q[i0 + i] = (uint8_t)(word >> (8 * i));
   }
   if (lane == 0) scale2[g] = c1 / 448.0f;
+}
+
+// Second kernel of the two-launch double quantisation: one wave per 256-group;
+// every workgroup first forms mu from the exact-sum counters (workgroup 0
+// stores it).
+__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ c2, int64_t nb,
+                                                        const uint64_t* __restrict__ partials, int parts,
+                                                        float* __restrict__ mu_out,
+                                                        uint8_t* __restrict__ absmax_q,
+                                                        float* __restrict__ scale2) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
+  float cv[4];
+  load_group(c2, g, nb, lane, cv);  // independent of mu: these loads go out first
+  const float mu = mean_from_partials<4>(partials, parts, nb);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+  if (g * 256 >= nb) return;  // whole wave exits together
+  encode_group(cv, g, nb, mu, absmax_q, scale2, lane);
 }
 
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts, uint8_t* absmax_q,
