@@ -844,7 +844,20 @@ __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
   uint4 ru[4], rv[4];
+  // whole, aligned tiles (the usual case) load without per-element checks, so
+  // that all loads of a tile are in flight together
+  const bool inner = m0 + 64 <= M && q0 + 64 <= Q && (L & 7) == 0 && (Q & 7) == 0;
   auto load = [&](int64_t lt) {
+    if (inner && lt + SK_BK <= lend) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int id = tid + NT * i;
+        ru[i] = ldg16(U + (m0 + (id >> 4)) * L + lt + (id & 15) * 8);
+        rv[i] = NN ? ldg16(V + (lt + (id >> 3)) * Q + q0 + (id & 7) * 8)
+                   : ldg16(V + (q0 + (id >> 4)) * L + lt + (id & 15) * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int id = tid + NT * i;
@@ -992,7 +1005,23 @@ __global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   uint4 ru[CU_], rv[CV_];
+  // whole, aligned tiles (the usual case) load without per-element checks, so
+  // that all loads of a tile are in flight together
+  const bool inner = p0 + BP <= P && q0 + BQ <= Q && (ldu & 7) == 0 && (ldv & 7) == 0;
   auto load = [&](int64_t mt) {
+    if (inner && mt + TN_BK <= mend) {
+#pragma unroll
+      for (int i = 0; i < CU_; ++i) {
+        const int id = tid + NT * i, row = id / (BP / 8), ch = id % (BP / 8);
+        ru[i] = ldg16(U + (mt + row) * ldu + p0 + ch * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < CV_; ++i) {
+        const int id = tid + NT * i, row = id / (BQ / 8), ch = id % (BQ / 8);
+        rv[i] = ldg16(V + (mt + row) * ldv + q0 + ch * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CU_; ++i) {
       const int id = tid + NT * i, row = id / (BP / 8), ch = id % (BP / 8);
