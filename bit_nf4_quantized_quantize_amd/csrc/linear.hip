@@ -1532,7 +1532,7 @@ int tn_splits(int64_t M, int64_t P, int64_t Q) {
   const bool wide = Q > P;
   int64_t tiles = wide ? (int64_t)cdiv(P, 64) * cdiv(Q, 128) : (int64_t)cdiv(P, 128) * cdiv(Q, 64);
   if (tiles < 1) tiles = 1;
-  int64_t s = (512 + tiles - 1) / tiles;
+  int64_t s = (256 + tiles - 1) / tiles;  // about one workgroup per CU
   const int64_t max_s = M / TN_BK > 0 ? M / TN_BK : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
