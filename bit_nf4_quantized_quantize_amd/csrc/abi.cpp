@@ -124,7 +124,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
 struct BwdWs {
   // fp32 partials of dY B^T, bf16 s*T [M, rp], fp32 partials of the token
   // reductions and of the main product's split tiles (one region, used in turn)
-  int64_t part_t, ts, part, total;
+  int64_t part_t, ts, part, part_b, total;
   int splits_t, splits_a, splits_b;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -132,10 +132,13 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   BwdWs w;
   w.splits_t = skinny_splits(M, r, N);
   w.splits_a = tn_splits(M, K, r);
-  w.splits_b = tn_splits(M, r, N);
-  int64_t pbytes = (int64_t)w.splits_a * K * r * 4;
-  const int64_t pb = (int64_t)w.splits_b * r * N * 4, pm = main_split_bytes(M, K, N);
-  if (pb > pbytes) pbytes = pb;
+  w.splits_b = tn_splits(M, N, r);  // dB is formed as dB^T [N, r]
+  // the two token reductions run together (dA partials at part, dB^T
+  // partials at part + part_b); the main product's split tiles use the
+  // same space before them
+  w.part_b = round_up((int64_t)w.splits_a * K * r * 4, kAlign);
+  int64_t pbytes = w.part_b + (int64_t)w.splits_b * N * r * 4;
+  const int64_t pm = main_split_bytes(M, K, N);
   if (pm > pbytes) pbytes = pm;
   w.part_t = 0;
   w.ts = w.part_t + round_up((int64_t)w.splits_t * M * rp * 4, kAlign);
@@ -363,13 +366,10 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, c
     }
     if (e != hipSuccess) return hip_fail(e, fn);
   }
-  // dA = X^T (s T)   [K, r]
-  if ((e = launch_gemm_tn((const uint16_t*)X, K, K, ts, rp, r, M, part, L.splits_a, (uint16_t*)dA, 1.0f, hs)) !=
-      hipSuccess)
-    return hip_fail(e, fn);
-  // dB = s XA^T dY   [r, N]
-  if ((e = launch_gemm_tn((const uint16_t*)XA, r, r, (const uint16_t*)dY, N, N, M, part, L.splits_b, (uint16_t*)dB, s,
-                          hs)) != hipSuccess)
+  // dA = X^T (s T) [K, r] and dB^T = s dY^T XA [N, r] (written as dB [r, N])
+  if ((e = launch_tn_pair((const uint16_t*)X, K, K, ts, rp, r, part, L.splits_a, (uint16_t*)dA, 1.0f,
+                          (const uint16_t*)dY, N, N, (const uint16_t*)XA, r, r,
+                          (float*)((char*)part + L.part_b), L.splits_b, (uint16_t*)dB, s, M, hs)) != hipSuccess)
     return hip_fail(e, fn);
   return QLORA_OK;
 }

@@ -83,12 +83,16 @@ hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t 
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                          const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* A,
                          int64_t r, int64_t rp, uint16_t* dX, float* split_ws, hipStream_t stream);
-// Token reduction C[P, Q] = U[M, P]^T * V[M, Q] (leading dimensions ldu, ldv):
-// fp32 partials [splits][P][Q] then out [P, Q] = bf16(alpha * sum).
+// Two token reductions, one launch for both products and one for both
+// epilogues: C_a [Pa, Qa] = U_a[M, Pa]^T * V_a[M, Qa] and C_b likewise
+// (leading dimensions ld*), fp32 partials part_x [splits_x][P][Q], then
+// out_a [Pa, Qa] = bf16(alpha_a * sum) and out_b = bf16(alpha_b * sum) written
+// transposed, [Qb, Pb].
 int tn_splits(int64_t M, int64_t P, int64_t Q);
-hipError_t launch_gemm_tn(const uint16_t* U, int64_t ldu, int64_t P, const uint16_t* V, int64_t ldv,
-                          int64_t Q, int64_t M, float* partials, int splits, uint16_t* out, float alpha,
-                          hipStream_t stream);
+hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint16_t* Va, int64_t ldva, int64_t Qa,
+                          float* part_a, int splits_a, uint16_t* out_a, float alpha_a, const uint16_t* Ub,
+                          int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb, float* part_b,
+                          int splits_b, uint16_t* out_b, float alpha_b, int64_t M, hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);
 
 }  // namespace qlora

@@ -983,10 +983,24 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
 // flight; both tiles are staged as [128 m][cols] and read transposed.
 constexpr int TN_BK = 128;
 
+struct TnProblem {
+  const uint16_t* U;
+  const uint16_t* V;
+  int64_t ldu, ldv, P, Q, M, chunk;
+  float* part;  // [splits][P][Q]
+};
+
 template <int BP, int BQ>
-__global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, int64_t ldu, int64_t P,
-                                                const uint16_t* __restrict__ V, int64_t ldv, int64_t Q, int64_t M,
-                                                int64_t chunk, float* __restrict__ part) {
+__global__ __launch_bounds__(NT) void tn_kernel(const TnProblem pa, const TnProblem pb, int za) {
+  // grid z below za: the splits of problem pa; from za on: those of pb
+  const bool second = (int)blockIdx.z >= za;
+  const TnProblem& pr = second ? pb : pa;
+  const int64_t bz = second ? blockIdx.z - za : blockIdx.z;
+  const uint16_t* __restrict__ U = pr.U;
+  const uint16_t* __restrict__ V = pr.V;
+  const int64_t ldu = pr.ldu, ldv = pr.ldv, P = pr.P, Q = pr.Q, M = pr.M, chunk = pr.chunk;
+  float* __restrict__ part = pr.part;
+  if ((int64_t)blockIdx.x * BP >= P || (int64_t)blockIdx.y * BQ >= Q) return;  // outside this problem's grid
   constexpr int PU = BP + kRcPad, PV = BQ + kRcPad;
   constexpr int TMW = BP / 64, TNW = BQ / 64;
   constexpr int CU_ = TN_BK * BP / 8 / NT, CV_ = TN_BK * BQ / 8 / NT;  // chunks per thread
@@ -995,7 +1009,7 @@ __global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t p0 = (int64_t)blockIdx.x * BP, q0 = (int64_t)blockIdx.y * BQ;
-  const int64_t mbeg = (int64_t)blockIdx.z * chunk;
+  const int64_t mbeg = bz * chunk;
   const int64_t mend = mbeg + chunk < M ? mbeg + chunk : M;
   floatx16 acc[TMW][TNW];
 #pragma unroll
@@ -1061,7 +1075,7 @@ __global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, 
     }
     __syncthreads();
   }
-  float* out = part + (int64_t)blockIdx.z * P * Q;
+  float* out = part + bz * P * Q;
 #pragma unroll
   for (int i = 0; i < TMW; ++i)
 #pragma unroll
@@ -1078,24 +1092,44 @@ __global__ __launch_bounds__(NT) void tn_kernel(const uint16_t* __restrict__ U, 
 
 // out[p][q] = bf16(alpha * sum_s part[s][p][q]), part [S][P][Q], out [P][Q].
 // out [PQ] = bf16(alpha * sum of the S slices of part [S][PQ]).
+// Token-reduction epilogue for up to two problems (blocks [0, nblk_a) take
+// problem a): out = bf16(alpha * sum of the S partial slices [P][Q]), written
+// as [P][Q], or as [Q][P] when `trans`.
+struct TnOut {
+  const float* part;
+  int S;
+  int64_t P, Q;
+  uint16_t* out;
+  float alpha;
+  int trans;
+};
+
 template <int T>
-__global__ __launch_bounds__(256) void tn_reduce_kernel(const float* __restrict__ part, int S, int64_t PQ,
-                                                        uint16_t* __restrict__ out, float alpha) {
+__global__ __launch_bounds__(256) void tn_reduce_kernel(const TnOut oa, const TnOut ob, int nblk_a) {
   __shared__ float4 red[T > 1 ? 256 : 1];
   constexpr int CPW = 256 / T;
+  const bool second = (int)blockIdx.x >= nblk_a;
+  const TnOut& o = second ? ob : oa;
+  const int64_t bx = second ? blockIdx.x - nblk_a : blockIdx.x;
+  const int64_t PQ = o.P * o.Q;
   const int t = threadIdx.x / CPW;
-  const int64_t idx = ((int64_t)blockIdx.x * CPW + threadIdx.x % CPW) * 4;
+  const int64_t idx = (bx * CPW + threadIdx.x % CPW) * 4;
   const bool ok = idx < PQ;
-  const float4 s = split_sum4<T>(part, S, PQ, idx, ok, t, red);
+  const float4 s = split_sum4<T>(o.part, o.S, PQ, idx, ok, t, red);
   if (!ok || t != 0) return;
-  if (idx + 4 <= PQ && (PQ & 3) == 0) {
-    uint2 o;
-    o.x = pack_bf2(alpha * s.x, alpha * s.y);
-    o.y = pack_bf2(alpha * s.z, alpha * s.w);
-    *reinterpret_cast<uint2*>(out + idx) = o;
+  const float sv[4] = {s.x, s.y, s.z, s.w};
+  if (o.trans) {
+    for (int e = 0; e < 4 && idx + e < PQ; ++e) {
+      const int64_t p = (idx + e) / o.Q, q = (idx + e) - p * o.Q;
+      o.out[q * o.P + p] = f2bf(o.alpha * sv[e]);
+    }
+  } else if (idx + 4 <= PQ && (PQ & 3) == 0) {
+    uint2 w;
+    w.x = pack_bf2(o.alpha * sv[0], o.alpha * sv[1]);
+    w.y = pack_bf2(o.alpha * sv[2], o.alpha * sv[3]);
+    *reinterpret_cast<uint2*>(o.out + idx) = w;
   } else {
-    const float sv[4] = {s.x, s.y, s.z, s.w};
-    for (int e = 0; e < 4 && idx + e < PQ; ++e) out[idx + e] = f2bf(alpha * sv[e]);
+    for (int e = 0; e < 4 && idx + e < PQ; ++e) o.out[idx + e] = f2bf(o.alpha * sv[e]);
   }
 }
 
@@ -1529,8 +1563,7 @@ hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int
 }
 
 int tn_splits(int64_t M, int64_t P, int64_t Q) {
-  const bool wide = Q > P;
-  int64_t tiles = wide ? (int64_t)cdiv(P, 64) * cdiv(Q, 128) : (int64_t)cdiv(P, 128) * cdiv(Q, 64);
+  int64_t tiles = (int64_t)cdiv(P, 128) * cdiv(Q, 64);
   if (tiles < 1) tiles = 1;
   int64_t s = (256 + tiles - 1) / tiles;  // about one workgroup per CU
   const int64_t max_s = M / TN_BK > 0 ? M / TN_BK : 1;
@@ -1540,25 +1573,30 @@ int tn_splits(int64_t M, int64_t P, int64_t Q) {
   return (int)s;
 }
 
-hipError_t launch_gemm_tn(const uint16_t* U, int64_t ldu, int64_t P, const uint16_t* V, int64_t ldv, int64_t Q,
-                          int64_t M, float* partials, int splits, uint16_t* out, float alpha, hipStream_t stream) {
-  int64_t chunk = (M + splits - 1) / splits;
-  chunk = (chunk + TN_BK - 1) / TN_BK * TN_BK;
-  if (Q > P) {
-    const dim3 grid(cdiv(P, 64), cdiv(Q, 128), (unsigned)splits);
-    hipLaunchKernelGGL((tn_kernel<64, 128>), grid, dim3(NT), 0, stream, U, ldu, P, V, ldv, Q, M, chunk, partials);
-  } else {
-    const dim3 grid(cdiv(P, 128), cdiv(Q, 64), (unsigned)splits);
-    hipLaunchKernelGGL((tn_kernel<128, 64>), grid, dim3(NT), 0, stream, U, ldu, P, V, ldv, Q, M, chunk, partials);
-  }
+hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint16_t* Va, int64_t ldva, int64_t Qa,
+                          float* part_a, int splits_a, uint16_t* out_a, float alpha_a, const uint16_t* Ub,
+                          int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb, float* part_b,
+                          int splits_b, uint16_t* out_b, float alpha_b, int64_t M, hipStream_t stream) {
+  auto chunk_of = [&](int splits) {
+    const int64_t c = (M + splits - 1) / splits;
+    return (c + TN_BK - 1) / TN_BK * TN_BK;
+  };
+  const TnProblem pa{Ua, Va, ldua, ldva, Pa, Qa, M, chunk_of(splits_a), part_a};
+  const TnProblem pb{Ub, Vb, ldub, ldvb, Pb, Qb, M, chunk_of(splits_b), part_b};
+  const dim3 grid(cdiv(Pa > Pb ? Pa : Pb, 128), cdiv(Qa > Qb ? Qa : Qb, 64), (unsigned)(splits_a + splits_b));
+  hipLaunchKernelGGL((tn_kernel<128, 64>), grid, dim3(NT), 0, stream, pa, pb, splits_a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int T = split_sum_threads(cdiv(P * Q, 4), splits);
-#define QLORA_RED(TT)                                                                                           \
-  case TT:                                                                                                      \
-    hipLaunchKernelGGL(tn_reduce_kernel<TT>, dim3(cdiv(cdiv(P * Q, 4), 256 / TT)), dim3(256), 0, stream, partials, \
-                       splits, P * Q, out, alpha);                                                              \
-    break;
+  const int64_t ca = cdiv(Pa * Qa, 4), cb = cdiv(Pb * Qb, 4);
+  const int T = split_sum_threads(ca < cb ? ca : cb, splits_a > splits_b ? splits_a : splits_b);
+  const TnOut oa{part_a, splits_a, Pa, Qa, out_a, alpha_a, 0};
+  const TnOut ob{part_b, splits_b, Pb, Qb, out_b, alpha_b, 1};
+#define QLORA_RED(TT)                                                                                       \
+  case TT: {                                                                                                \
+    const int na = (int)cdiv(ca, 256 / TT), nb = (int)cdiv(cb, 256 / TT);                                  \
+    hipLaunchKernelGGL(tn_reduce_kernel<TT>, dim3((unsigned)(na + nb)), dim3(256), 0, stream, oa, ob, na);  \
+    break;                                                                                                  \
+  }
   switch (T) { QLORA_RED(1) QLORA_RED(2) QLORA_RED(4) QLORA_RED(8) QLORA_RED(16) QLORA_RED(32) default: QLORA_RED(64) }
 #undef QLORA_RED
   return hipGetLastError();
