@@ -514,6 +514,45 @@ __global__ __launch_bounds__(DQZ_THREADS) void nf4_dequant_kernel(const uint8_t*
   __syncthreads();
   const float mu = DQ ? *offset : 0.0f;
   const int64_t wg0 = (int64_t)blockIdx.x * DQZ_PER_WG;
+  if (wg0 + DQZ_PER_WG <= numel) {
+    // a whole chunk: every load goes out before the first is used
+    uint32_t word[DQZ_STEPS], qb[DQZ_STEPS];
+    float f[DQZ_STEPS];
+#pragma unroll
+    for (int s = 0; s < DQZ_STEPS; ++s) {
+      const int64_t e0 = wg0 + ((int64_t)s * DQZ_THREADS + threadIdx.x) * 8;
+      const int64_t blk = e0 >> 6;
+      word[s] = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
+      if (DQ) {
+        qb[s] = absmax_q[blk];
+        f[s] = scale2[blk >> 8];
+      } else {
+        qb[s] = 0;
+        f[s] = absmax[blk];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < DQZ_STEPS; ++s) {
+      const int64_t e0 = wg0 + ((int64_t)s * DQZ_THREADS + threadIdx.x) * 8;
+      const float c = DQ ? e4m3_decode(qb[s]) * f[s] + mu : f[s];
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = s_nf4[(word[s] >> (4 * i)) & 0xF] * c;
+      if (BF16_OUT) {
+        uint4 o;
+        o.x = pack_bf2(v[0], v[1]);
+        o.y = pack_bf2(v[2], v[3]);
+        o.z = pack_bf2(v[4], v[5]);
+        o.w = pack_bf2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = o;
+      } else {
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < DQZ_STEPS; ++s) {
     const int64_t e0 = wg0 + ((int64_t)s * DQZ_THREADS + threadIdx.x) * 8;
