@@ -149,14 +149,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+// Sums over the whole 64-lane wave of N values at once (every lane gets the
+// sums); the N exchanges of each butterfly step are in flight together.
+template <int N>
+__device__ __forceinline__ void wave_sum_u64(uint64_t (&v)[N]) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    v += ((uint64_t)hi << 32) | lo;
+    uint32_t lo[N], hi[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      lo[k] = __shfl_xor((uint32_t)v[k], o, 64);
+      hi[k] = __shfl_xor((uint32_t)(v[k] >> 32), o, 64);
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += ((uint64_t)hi[k] << 32) | lo[k];
   }
-  return v;
 }
 
 // ------------------------------------------------------- MFMA fragments

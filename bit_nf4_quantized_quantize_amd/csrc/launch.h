@@ -7,13 +7,15 @@
 
 namespace qlora {
 
-// Quantisation lookup: the [-1, 1] range cut into 32 buckets of width 1/16.
+// Quantisation lookup: x in [-1, 1] goes to bucket b = round(16 x + 16)
+// (0..32, ties to even), which covers [(b - 1/2)/16 - 1, (b + 1/2)/16 - 1].
 // For x in bucket b, code(x) = base[b] + (x > thr[b]); thr[b] is the one
 // decision threshold (midpoint of two adjacent NF4 values, rounded toward
 // -inf to fp32) inside the bucket, or +inf when the bucket holds none.
+constexpr int kBuckets = 33;
 struct QuantTable {
-  float thr[32];
-  uint32_t base[32];
+  float thr[kBuckets];
+  uint32_t base[kBuckets];
 };
 
 struct NF4Values {
@@ -27,7 +29,8 @@ const QuantTable& quant_table();
 // Quantisation writes the codes and the fp32 block absmax c2; with
 // `partials` it also writes, per workgroup, the exact sum of its c2 as
 // kMeanDigits 32-bit digits in 64-bit counters (quantize_parts(numel)
-// workgroups).  Double quantisation then divides the total by nb for the mean
+// workgroups; digit k of workgroup p at partials[k * parts + p]).  Double
+// quantisation then divides the total by nb for the mean
 // and encodes the constants.
 int quantize_parts(int64_t numel);
 constexpr int kMeanDigits = 10;  // 32-bit digits of the exact fixed-point sum

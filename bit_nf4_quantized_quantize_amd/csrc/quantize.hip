@@ -70,10 +70,10 @@ const NF4Values& nf4_values() {
 // Decision thresholds between codes i and i+1 are the exact midpoints
 // (NF4[i] + NF4[i+1]) / 2 (exact in double), rounded toward -inf to fp32 so
 // that "x > thr" equals "x > midpoint" for every fp32 x; a tie (x equal to a
-// midpoint) keeps the lower code.  Buckets [b/16 - 1, (b+1)/16 - 1) each
-// hold at most one midpoint, and none lies within 2^-20 of a bucket edge, so
-// a bucket index computed with one fp32 rounding is off by at most one only
-// where that cannot change the code.
+// midpoint) keeps the lower code.  Each bucket (width 1/16) holds at most one
+// midpoint, since adjacent midpoints are more than 1/16 apart.  The bucket
+// index is computed exactly from x; an x on the edge between two buckets
+// gets the same code from either of them.
 const QuantTable& quant_table() {
   static const QuantTable t = [] {
     QuantTable q;
@@ -85,8 +85,8 @@ const QuantTable& quant_table() {
       if ((double)f > mid[i]) f = nextafterf(f, -INFINITY);
       thr[i] = f;
     }
-    for (int b = 0; b < 32; ++b) {
-      const double lo = b / 16.0 - 1.0, hi = (b + 1) / 16.0 - 1.0;
+    for (int b = 0; b < kBuckets; ++b) {
+      const double lo = (b - 0.5) / 16.0 - 1.0, hi = (b + 0.5) / 16.0 - 1.0;
       uint32_t base = 0;
       float t_in = INFINITY;
       int inside = 0;
@@ -127,175 +127,290 @@ __device__ __forceinline__ void c2_digits(float c, uint32_t& d, uint32_t& lo, ui
 }
 
 // ------------------------------------------------------- quantise kernel
-// A workgroup of 512 threads = 8 waves handles chunks of 8192 consecutive
-// weights (128 blocks), striding over the tensor by the grid size (at most
-// one workgroup per CU).  In each of 4 steps of a chunk a wave covers 256
-// weights = 4 blocks; a lane holds 4
-// consecutive weights, so a block is one row of 16 lanes and its absmax is a
-// 16-lane DPP reduction.  Each lane writes its 4 codes as one 16-bit store;
-// lane 0 of each row writes the block's absmax and, with double
-// quantisation, adds it to the workgroup's exact-sum counters in LDS.  The
-// next chunk's weights are loaded before the current one is coded (two
-// register sets; a chunk past the end re-reads the current one).  A final
-// partial chunk is coded by the workgroup that owns it, with bounds checks.
+// A lane codes 8 consecutive weights, so a block of 64 is one group of 8
+// lanes (an octet) and its absmax is a 3-step DPP reduction.  A workgroup of
+// 512 threads = 8 waves takes chunks of STEPS * 8 * 512 weights (STEPS = 8
+// for bf16 input, 4 for fp32), striding over the tensor by the grid size;
+// step s of a wave is the 512 weights at chunk + (8 s + wave) * 512.  A chunk
+// is coded in three phases:
+//   A. the absmax of every step; lane 8j+k keeps that of block j of step k,
+//      so the wave's blocks end up one per lane;
+//   B. per lane, one block: store c2, add it to the exact-sum counters and
+//      take the correctly rounded reciprocal (one division per lane for up
+//      to 8 blocks, instead of one per block and step);
+//   C. per step, every lane fetches its block's reciprocal from lane 8j+s
+//      (ds_bpermute) and codes its 8 weights into one 32-bit store.
+// The next chunk is loaded while the current one is coded.  A chunk holding
+// a subnormal or non-finite absmax takes a generic per-step path instead
+// (prescaling, clamped bucket index), and so does the final partial chunk,
+// which is spread over the workgroups as 512-weight wave steps with bounds
+// checks.  Each wave has its own exact-sum counters in LDS.
 
 constexpr int QZ_THREADS = 512;
 constexpr int QZ_WAVES = QZ_THREADS / 64;
-constexpr int QZ_STEPS = 4;
-constexpr int QZ_PER_WG = QZ_THREADS * 4 * QZ_STEPS;  // 8192 weights
-constexpr int QZ_MAX_WG = 256;                        // also the number of exact-sum partials
+constexpr int QZ_MAX_WG = 256;       // also the number of exact-sum partials
+constexpr int64_t QZ_GRID_UNIT = 16384;  // weights per workgroup when sizing the grid
+
+typedef uint32_t qz_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short qz_u16x2 __attribute__((ext_vector_type(2)));
+
+template <bool BF16>
+struct QzGeo {
+  static constexpr int STEPS = BF16 ? 8 : 4;   // steps per chunk and wave
+  static constexpr int NV = BF16 ? 1 : 2;      // 16-byte loads per lane and step
+  static constexpr int64_t CH = (int64_t)STEPS * QZ_WAVES * 512;
+};
 
 int quantize_parts(int64_t numel) {
-  const int64_t chunks = (numel + QZ_PER_WG - 1) / QZ_PER_WG;
-  return (int)(chunks < 1 ? 1 : (chunks > QZ_MAX_WG ? QZ_MAX_WG : chunks));
+  const int64_t units = (numel + QZ_GRID_UNIT - 1) / QZ_GRID_UNIT;
+  return (int)(units < 1 ? 1 : (units > QZ_MAX_WG ? QZ_MAX_WG : units));
 }
 
-template <bool BF16_IN>
-__device__ __forceinline__ void load4(const void* w, int64_t e0, int64_t numel, float v[4]) {
-  if (e0 + 3 < numel) {
-    if (BF16_IN) {
-      const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(w) + e0);
-      v[0] = __uint_as_float(p.x << 16);
-      v[1] = __uint_as_float(p.x & 0xFFFF0000u);
-      v[2] = __uint_as_float(p.y << 16);
-      v[3] = __uint_as_float(p.y & 0xFFFF0000u);
-    } else {
-      const float4 p = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + e0);
-      v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
-    }
+// Max over the 8 lanes of each octet (every lane gets its octet's max).
+__device__ __forceinline__ uint32_t octet_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return v;
+}
+
+// fp32 bit pattern of max |w| over a lane's 8 weights.  For values that are
+// not NaN the order of |w| is the unsigned order of its bit pattern.
+template <bool BF16>
+__device__ __forceinline__ uint32_t absmax_bits(const qz_u32x4* r) {
+  if (BF16) {
+    const qz_u16x2 a0 = __builtin_bit_cast(qz_u16x2, r[0].x & 0x7FFF7FFFu);
+    const qz_u16x2 a1 = __builtin_bit_cast(qz_u16x2, r[0].y & 0x7FFF7FFFu);
+    const qz_u16x2 a2 = __builtin_bit_cast(qz_u16x2, r[0].z & 0x7FFF7FFFu);
+    const qz_u16x2 a3 = __builtin_bit_cast(qz_u16x2, r[0].w & 0x7FFF7FFFu);
+    const uint32_t m = __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_max(__builtin_elementwise_max(a0, a1), __builtin_elementwise_max(a2, a3)));
+    return max(m << 16, m & 0xFFFF0000u);
   } else {
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t e = e0 + i;
-      if (e < numel)
-        v[i] = BF16_IN ? bf2f(reinterpret_cast<const uint16_t*>(w)[e]) : reinterpret_cast<const float*>(w)[e];
-      else
-        v[i] = 0.0f;
-    }
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, r[v][i] & 0x7FFFFFFFu);
+    return m;
   }
 }
 
-// 4 weights of a full chunk (no bounds checks).
-template <bool BF16_IN>
-__device__ __forceinline__ void load4_full(const void* w, int64_t e0, float v[4]) {
-  if (BF16_IN) {
-    const uint2 p = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(w) + e0);
-    v[0] = __uint_as_float(p.x << 16);
-    v[1] = __uint_as_float(p.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(p.y << 16);
-    v[3] = __uint_as_float(p.y & 0xFFFF0000u);
-  } else {
-    const float4 p = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + e0);
-    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+// Weight i (0..7) of a lane's 8 as fp32.
+template <bool BF16>
+__device__ __forceinline__ float weight_of(const qz_u32x4* r, int i) {
+  if (BF16) {
+    const uint32_t wd = r[0][i >> 1];
+    return __uint_as_float((i & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+  }
+  return __uint_as_float(r[i >> 2][i & 3]);
+}
+
+// Bucket of x: b = round-to-nearest-even(16 x + 16), 0..32 for x in [-1, 1].
+// One fma lands 16 x + 16 + 1.5 * 2^23 in [2^23, 2^24), where fp32 spacing is
+// 1, so b is the low mantissa field; shifting the bit pattern left by 3 and
+// removing the shifted exponent bits (mod 2^32) gives the table entry's byte
+// offset 8 b.
+constexpr float kBucketMagic = 12582928.0f;  // 1.5 * 2^23 + 16
+constexpr uint32_t kBucketBits = 0x4B400000u; // bit pattern of 1.5 * 2^23
+constexpr uint32_t kBucketBias = 0u - (kBucketBits << 3);
+
+// Codes of a lane's 8 weights (normalised by inv, |x| <= 1), packed
+// low nibble first.
+template <bool BF16>
+__device__ __forceinline__ uint32_t code8_fast(const qz_u32x4* r, float inv, const uint2* s_tab) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = weight_of<BF16>(r, i) * inv;
+    const float y = __builtin_fmaf(x, 16.0f, kBucketMagic);
+    const uint32_t off = (__float_as_uint(y) << 3) + kBucketBias;
+    const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) + off);
+    packed |= (t.y + (x > __uint_as_float(t.x) ? 1u : 0u)) << (4 * i);
+  }
+  return packed;
+}
+
+// As code8_fast with the weights first scaled by sc (exact) and the bucket
+// index clamped, so that any input (NaN included) reads inside the table.
+template <bool BF16>
+__device__ __forceinline__ uint32_t code8_generic(const qz_u32x4* r, float sc, float inv, const uint2* s_tab) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = (weight_of<BF16>(r, i) * sc) * inv;
+    const float y = __builtin_fmaf(x, 16.0f, kBucketMagic);
+    int b = (int)(__float_as_uint(y) - kBucketBits);
+    b = b < 0 ? 0 : (b > kBuckets - 1 ? kBuckets - 1 : b);
+    const uint2 t = s_tab[b];
+    packed |= (t.y + (x > __uint_as_float(t.x) ? 1u : 0u)) << (4 * i);
+  }
+  return packed;
+}
+
+__device__ __forceinline__ void add_c2(unsigned long long* acc, float c2) {
+  uint32_t d, lo, hi;
+  c2_digits(c2, d, lo, hi);
+  atomicAdd(&acc[d], (unsigned long long)lo);
+  if (hi) atomicAdd(&acc[d + 1], (unsigned long long)hi);
+}
+
+// One wave step of 512 weights with every check: the lane's 8 weights start
+// at e0 (zeros past numel); block constants of blocks past nb are not
+// stored, and the nibble of a missing element is 0.
+template <bool BF16>
+__device__ __forceinline__ void generic_step(const qz_u32x4* r, int64_t e0, int64_t numel, int64_t nb,
+                                             uint8_t* __restrict__ codes, float* __restrict__ c2out,
+                                             unsigned long long* acc, const uint2* s_tab, int lane) {
+  const float c2 = __uint_as_float(octet_max(absmax_bits<BF16>(r)));
+  const bool tiny = c2 > 0.0f && c2 < kTiny;
+  const float sc = tiny ? kPrescale : 1.0f;
+  const float cs = c2 * sc;
+  const float inv = cs > 0.0f ? 1.0f / cs : 0.0f;  // correctly rounded division
+  uint32_t packed = code8_generic<BF16>(r, sc, inv, s_tab);
+  if (e0 + 7 < numel) {
+    *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
+  } else if (e0 < numel) {
+    const int have = (int)(numel - e0);  // 1..7
+    packed &= (1u << (4 * have)) - 1u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (2 * j < have) codes[(e0 >> 1) + j] = (uint8_t)(packed >> (8 * j));
+  }
+  const int64_t blk = e0 >> 6;
+  if ((lane & 7) == 0 && blk < nb) {
+    c2out[blk] = c2;
+    if (acc && c2 > 0.0f) add_c2(acc, c2);
   }
 }
 
-// The quantisation of one workgroup's chunks (grid-stride over 8192-weight
-// chunks); with `partials` it ends by storing the workgroup's exact-sum
-// counters at partials[blockIdx.x].
-template <bool BF16_IN>
-__device__ __forceinline__ void quantize_chunks(const void* __restrict__ w, int64_t numel,
-                                                uint8_t* __restrict__ codes, float* __restrict__ c2out,
-                                                uint64_t* __restrict__ partials, const QuantTable& tab) {
-  __shared__ uint2 s_tab[32];  // {threshold bits, base code}
-  __shared__ unsigned long long s_acc[kMeanDigits];
-  const int tid = threadIdx.x;
-  if (tid < 32) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
-  if (tid < kMeanDigits) s_acc[tid] = 0;
-  __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63;
-  const int64_t nb = (numel + 63) >> 6;
-  const int64_t nfull = numel / QZ_PER_WG;
-  const int64_t G = gridDim.x;
-  const bool sums = partials != nullptr;
-
-  // code one step (4 weights per lane) starting at element e0
-  auto code_step = [&](int64_t e0, float v[4], bool full) {
-    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    const float c2 = row16_max(m);
-    float cs = c2;
-    const bool tiny = c2 > 0.0f && c2 < kTiny;
-    if (__builtin_amdgcn_ballot_w64(tiny)) {  // rare, wave-uniform branch
-      const float sc = tiny ? kPrescale : 1.0f;
+// A lane's 8 weights from e0 with bounds checks (zeros past numel).
+template <bool BF16>
+__device__ __forceinline__ void load_partial(const void* __restrict__ w, int64_t e0, int64_t numel, qz_u32x4* r) {
+  if (e0 + 7 < numel) {
+    const qz_u32x4* p = reinterpret_cast<const qz_u32x4*>(BF16 ? (const char*)w + e0 * 2 : (const char*)w + e0 * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= sc;
-      cs = c2 * sc;
-    }
-    const float inv = cs > 0.0f ? 1.0f / cs : 0.0f;  // correctly rounded division
-    uint32_t packed = 0;
+    for (int v = 0; v < QzGeo<BF16>::NV; ++v) r[v] = p[v];
+    return;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = v[i] * inv;                     // in [-1, 1]
-      int b = (int)__builtin_fmaf(x, 16.0f, 16.0f);   // bucket 0..32 (x*16 is exact)
-      b = b < 0 ? 0 : (b > 31 ? 31 : b);
-      const uint2 t = s_tab[b];
-      const uint32_t code = t.y + (x > __uint_as_float(t.x) ? 1u : 0u);
-      packed |= code << (4 * i);
-    }
-    if (full) {
-      *reinterpret_cast<uint16_t*>(codes + (e0 >> 1)) = (uint16_t)packed;
-    } else {
-      // past the end: the nibble of a missing element is 0
-      const int64_t have = numel - e0;  // may be <= 0
-      if (have < 4) packed &= have <= 0 ? 0u : (0xFFFFu >> (4 * (4 - have)));
-      if (e0 < numel) codes[e0 >> 1] = (uint8_t)(packed & 0xFF);
-      if (e0 + 2 < numel) codes[(e0 >> 1) + 1] = (uint8_t)(packed >> 8);
-    }
-    const int64_t blk = e0 >> 6;
-    if ((lane & 15) == 0 && blk < nb) {
-      c2out[blk] = c2;
-      if (sums && c2 > 0.0f) {
-        uint32_t d, lo, hi;
-        c2_digits(c2, d, lo, hi);
-        atomicAdd(&s_acc[d], (unsigned long long)lo);
-        if (hi) atomicAdd(&s_acc[d + 1], (unsigned long long)hi);
+  for (int v = 0; v < QzGeo<BF16>::NV; ++v) r[v] = qz_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t e = e0 + i;
+    if (e < numel) {
+      if (BF16) {
+        const uint32_t h = reinterpret_cast<const uint16_t*>(w)[e];
+        r[0][i >> 1] |= (i & 1) ? (h << 16) : h;
+      } else {
+        r[i >> 2][i & 3] = reinterpret_cast<const uint32_t*>(w)[e];
       }
     }
-  };
-  auto elem = [&](int64_t c, int s) { return c * QZ_PER_WG + (int64_t)(s * QZ_WAVES + wave) * 256 + lane * 4; };
-
-  float va[QZ_STEPS][4], vb[QZ_STEPS][4];
-  int64_t c = blockIdx.x;
-  if (c < nfull) {
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) load4_full<BF16_IN>(w, elem(c, s), va[s]);
-  }
-  while (c < nfull) {
-    const int64_t c1 = c + G;
-    const int64_t l1 = c1 < nfull ? c1 : c;  // past the end: re-read the current chunk (cached)
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) load4_full<BF16_IN>(w, elem(l1, s), vb[s]);
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) code_step(elem(c, s), va[s], true);
-    if (c1 >= nfull) break;
-    const int64_t c2i = c1 + G;
-    const int64_t l2 = c2i < nfull ? c2i : c1;
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) load4_full<BF16_IN>(w, elem(l2, s), va[s]);
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) code_step(elem(c1, s), vb[s], true);
-    c = c2i;
-  }
-  // the partial last chunk, if any
-  if (nfull * QZ_PER_WG < numel && (nfull % G) == blockIdx.x) {
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) load4<BF16_IN>(w, elem(nfull, s), numel, va[s]);
-#pragma unroll
-    for (int s = 0; s < QZ_STEPS; ++s) code_step(elem(nfull, s), va[s], elem(nfull, s) + 3 < numel);
-  }
-  if (sums) {
-    __syncthreads();
-    if (tid < kMeanDigits) partials[(int64_t)blockIdx.x * kMeanDigits + tid] = s_acc[tid];
   }
 }
 
-template <bool BF16_IN>
+template <bool BF16>
 __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
                                                                   uint8_t* __restrict__ codes,
                                                                   float* __restrict__ c2out,
                                                                   uint64_t* __restrict__ partials, QuantTable tab) {
-  quantize_chunks<BF16_IN>(w, numel, codes, c2out, partials, tab);
+  using Geo = QzGeo<BF16>;
+  constexpr int STEPS = Geo::STEPS, NV = Geo::NV;
+  constexpr int64_t CH = Geo::CH;
+  constexpr int ES = BF16 ? 2 : 4;  // bytes per input weight
+  __shared__ uint2 s_tab[kBuckets];  // {threshold bits, base code}
+  __shared__ unsigned long long s_acc[QZ_WAVES][kMeanDigits];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < kBuckets) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
+  if (tid < QZ_WAVES * kMeanDigits) (&s_acc[0][0])[tid] = 0;
+  __syncthreads();
+
+  const int64_t nb = (numel + 63) >> 6;
+  const int64_t nfull = numel / CH;
+  const int64_t G = gridDim.x;
+  unsigned long long* acc = partials ? s_acc[wave] : nullptr;
+  const uint32_t lane_off = (uint32_t)(wave * 512 + lane * 8);  // weights, within a step row
+  const int k = lane & 7;
+
+  auto load_chunk = [&](int64_t c, qz_u32x4 (&r)[STEPS][NV]) {
+    const char* base = (const char*)w + c * CH * ES;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        r[s][v] = *reinterpret_cast<const qz_u32x4*>(base + ((uint32_t)(s * QZ_WAVES * 512) + lane_off) * ES + 16 * v);
+  };
+
+  auto process = [&](int64_t c, qz_u32x4 (&r)[STEPS][NV]) {
+    // A: every step's block absmax; lane 8j+k keeps block j of step k
+    uint32_t comb = 0;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const uint32_t m = octet_max(absmax_bits<BF16>(r[s]));
+      comb = k == s ? m : comb;
+    }
+    const bool mine = k < STEPS;
+    const bool normal = comb == 0u || comb - 0x00800000u < 0x7F000000u;  // zero, or a finite normal
+    if (__builtin_amdgcn_ballot_w64(mine && !normal)) {  // rare, wave-uniform
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s)
+        generic_step<BF16>(r[s], c * CH + s * QZ_WAVES * 512 + lane_off, numel, nb, codes, c2out, acc, s_tab,
+                           lane);
+      return;
+    }
+    // B: one block per lane
+    const float c2 = __uint_as_float(comb);
+    if (mine) {
+      c2out[c * (CH / 64) + (k * QZ_WAVES + wave) * 8 + (lane >> 3)] = c2;
+      if (acc && comb) add_c2(acc, c2);
+    }
+    const float inv = comb ? 1.0f / c2 : 0.0f;  // correctly rounded division
+    // C: code each step with its block's reciprocal
+    const int src = (lane & ~7) << 2;
+    uint8_t* cb = codes + c * (CH / 2);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const float inv_s = __int_as_float(__builtin_amdgcn_ds_bpermute(src + 4 * s, __float_as_int(inv)));
+      *reinterpret_cast<uint32_t*>(cb + (((uint32_t)(s * QZ_WAVES * 512) + lane_off) >> 1)) =
+          code8_fast<BF16>(r[s], inv_s, s_tab);
+    }
+  };
+
+  qz_u32x4 ra[STEPS][NV], rb[STEPS][NV];
+  int64_t c = blockIdx.x;
+  if (c < nfull) load_chunk(c, ra);
+  while (c < nfull) {
+    const int64_t c1 = c + G;
+    if (c1 < nfull) load_chunk(c1, rb);
+    process(c, ra);
+    if (c1 >= nfull) break;
+    const int64_t c2i = c1 + G;
+    if (c2i < nfull) load_chunk(c2i, ra);
+    process(c1, rb);
+    c = c2i;
+  }
+
+  // the final partial chunk, as 512-weight wave steps over all workgroups
+  const int64_t tail0 = nfull * CH;
+  if (tail0 < numel) {
+    const int64_t T = (numel - tail0 + 511) >> 9;
+    const int64_t rot = (blockIdx.x + G - nfull % G) % G;  // workgroups with fewer full chunks first
+    for (int64_t t = rot * QZ_WAVES + wave; t < T; t += G * QZ_WAVES) {
+      const int64_t e0 = tail0 + t * 512 + lane * 8;
+      qz_u32x4 r[NV];
+      load_partial<BF16>(w, e0, numel, r);
+      generic_step<BF16>(r, e0, numel, nb, codes, c2out, acc, s_tab, lane);
+    }
+  }
+  if (partials) {
+    __syncthreads();
+    if (tid < kMeanDigits) {
+      unsigned long long t = 0;
+#pragma unroll
+      for (int v = 0; v < QZ_WAVES; ++v) t += s_acc[v][tid];
+      partials[(int64_t)tid * gridDim.x + blockIdx.x] = t;  // digit-major
+    }
+  }
 }
 
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2, uint64_t* partials,
@@ -400,11 +515,11 @@ __device__ __forceinline__ float mean_from_partials(const uint64_t* __restrict__
   uint64_t v[kMeanDigits];
   const int p = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < kMeanDigits; ++k) v[k] = p < parts ? partials[(int64_t)p * kMeanDigits + k] : 0;
+  for (int k = 0; k < kMeanDigits; ++k) v[k] = p < parts ? partials[(int64_t)k * parts + p] : 0;
+  wave_sum_u64<kMeanDigits>(v);
+  if (lane == 0) {
 #pragma unroll
-  for (int k = 0; k < kMeanDigits; ++k) {
-    const uint64_t t = wave_sum_u64(v[k]);
-    if (lane == 0) s_part[wave][k] = t;
+    for (int k = 0; k < kMeanDigits; ++k) s_part[wave][k] = v[k];
   }
   __syncthreads();
   if (threadIdx.x < kMeanDigits) {
@@ -466,30 +581,41 @@ __device__ __forceinline__ void encode_group(const float cv[4], int64_t g, int64
   if (lane == 0) scale2[g] = c1 / 448.0f;
 }
 
-// Second kernel of the two-launch double quantisation: one wave per 256-group;
-// every workgroup first forms mu from the exact-sum counters (workgroup 0
-// stores it).
+// Second kernel of the double quantisation: every workgroup first forms mu
+// from the exact-sum counters (workgroup 0 stores it), then its waves encode
+// 256-groups in a grid-stride loop (one group per wave at a time, the next
+// group's constants loading while the current one is encoded).  The grid is
+// capped, so mu is formed at most DQE_MAX_WG times.
+constexpr int DQE_MAX_WG = 512;
+
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ c2, int64_t nb,
                                                         const uint64_t* __restrict__ partials, int parts,
                                                         float* __restrict__ mu_out,
                                                         uint8_t* __restrict__ absmax_q,
                                                         float* __restrict__ scale2) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t ng = (nb + 255) >> 8, gstep = (int64_t)gridDim.x * 4;
+  int64_t g = (int64_t)blockIdx.x * 4 + wave;
   float cv[4];
-  load_group(c2, g, nb, lane, cv);  // independent of mu: these loads go out first
+  load_group(c2, g < ng ? g : 0, nb, lane, cv);  // independent of mu: these loads go out first
   const float mu = mean_from_partials<4>(partials, parts, nb);
   if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
-  if (g * 256 >= nb) return;  // whole wave exits together
-  encode_group(cv, g, nb, mu, absmax_q, scale2, lane);
+  for (; g < ng; g += gstep) {  // wave-uniform
+    float cn[4];
+    if (g + gstep < ng) load_group(c2, g + gstep, nb, lane, cn);
+    encode_group(cv, g, nb, mu, absmax_q, scale2, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cv[i] = cn[i];
+  }
 }
 
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts, uint8_t* absmax_q,
                                float* scale2, float* offset, hipStream_t stream) {
   if (parts < 1 || parts > QZ_MAX_WG || QZ_MAX_WG > 256) return hipErrorInvalidValue;
   const int64_t ng = (nb + 255) / 256;
-  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)((ng + 3) / 4)), dim3(256), 0, stream, c2, nb, partials, parts,
-                     offset, absmax_q, scale2);
+  const int64_t wgs = (ng + 3) / 4 < DQE_MAX_WG ? (ng + 3) / 4 : DQE_MAX_WG;
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, c2, nb, partials, parts, offset,
+                     absmax_q, scale2);
   return hipGetLastError();
 }
 
