@@ -219,4 +219,23 @@ __device__ __forceinline__ int acc_row32(int j, int lane) {
   return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
 }
 
+// 4 x 4 transpose inside each quad of lanes.  On entry lane c = lane % 4
+// holds column c of rows 0..3 in v[0..3]; on exit it holds row c, columns
+// 0..3.  Two DPP exchange stages: the off-diagonal 2 x 2 blocks between lanes
+// c and c ^ 2, then the off-diagonal elements of each 2 x 2 block between
+// lanes c and c ^ 1.
+template <int CTRL>
+__device__ __forceinline__ float quad_xchg(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose4(float (&v)[4], int lane) {
+  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+  float x = quad_xchg<0x4E>(b1 ? v[0] : v[2]);  // quad_perm [2,3,0,1]
+  float y = quad_xchg<0x4E>(b1 ? v[1] : v[3]);
+  if (b1) { v[0] = x; v[1] = y; } else { v[2] = x; v[3] = y; }
+  x = quad_xchg<0xB1>(b0 ? v[0] : v[1]);        // quad_perm [1,0,3,2]
+  y = quad_xchg<0xB1>(b0 ? v[2] : v[3]);
+  if (b0) { v[0] = x; v[2] = y; } else { v[1] = x; v[3] = y; }
+}
+
 }  // namespace qlora

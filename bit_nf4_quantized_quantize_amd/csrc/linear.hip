@@ -270,6 +270,30 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
     }
 }
 
+// Stores one 32 x 32 fp32 accumulator tile (MFMA 32x32 layout) at rows r0..,
+// columns c0.. of `out` (bf16, row pitch ncols; rows >= M dropped), or of an
+// fp32 partial tile `pt` (row pitch pitch_pt) when pt is given.  Groups of 4
+// accumulator rows are transposed inside each quad of lanes, so every lane
+// writes 4 consecutive columns of one row (8 or 16 bytes) instead of 4
+// single elements.  Needs ncols % 4 == 0 and c0 + 32 <= ncols.
+__device__ __forceinline__ void store_acc32(const floatx16& acc, int lane, int64_t r0, int64_t c0, int64_t M,
+                                            int64_t ncols, uint16_t* __restrict__ out, float* __restrict__ pt,
+                                            int pitch_pt) {
+  const int col = 4 * ((lane & 31) >> 2);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    quad_transpose4(v, lane);
+    const int rr = 8 * g + 4 * (lane >> 5) + (lane & 3);
+    if (pt) {
+      *reinterpret_cast<float4*>(pt + (int64_t)(r0 + rr) * pitch_pt + c0 + col) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if (r0 + rr < M) {
+      *reinterpret_cast<uint2*>(out + (r0 + rr) * ncols + c0 + col) =
+          make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+    }
+  }
+}
+
 // ================================== main GEMM, 256 x 256, 4 waves, v5
 // One wave per SIMD, each owning a 128 x 128 output tile (256 fp32
 // accumulators), so every LDS fragment feeds four MFMAs.  The next k-step's
@@ -505,28 +529,15 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
   }
 
   // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
-  if (unit >= 0) {
-    float* pt = a.part + (int64_t)unit * (BM * BN);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int cl = wn * 128 + 32 * j + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) pt[(wm * 128 + 32 * i + acc_row32(e, lane)) * BN + cl] = acc[i][j][e];
-      }
-    return;
-  }
+  float* pt = unit >= 0 ? a.part + (int64_t)unit * (BM * BN) : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = c0 + wn * 128 + 32 * j + (lane & 31);
-      if (col >= a.ncols) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
-        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
+      if (pt) {
+        store_acc32(acc[i][j], lane, wm * 128 + 32 * i, wn * 128 + 32 * j, BM, BN, nullptr, pt, BN);
+      } else if (c0 + wn * 128 + 32 * j < a.ncols) {
+        store_acc32(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 128 + 32 * j, a.M, a.ncols, a.out, nullptr, 0);
       }
     }
 }
@@ -767,28 +778,15 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   }
 
   // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
-  if (unit >= 0) {
-    float* pt = a.part + (int64_t)unit * (BM * BN);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int cl = wn * 64 + 32 * j + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) pt[(wm * 128 + 32 * i + acc_row32(e, lane)) * BN + cl] = acc[i][j][e];
-      }
-    return;
-  }
+  float* pt = unit >= 0 ? a.part + (int64_t)unit * (BM * BN) : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t col = c0 + wn * 64 + 32 * j + (lane & 31);
-      if (col >= a.ncols) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + 32 * i + acc_row32(e, lane);
-        if (row < a.M) a.out[row * a.ncols + col] = f2bf(acc[i][j][e]);
+      if (pt) {
+        store_acc32(acc[i][j], lane, wm * 128 + 32 * i, wn * 64 + 32 * j, BM, BN, nullptr, pt, BN);
+      } else if (c0 + wn * 64 + 32 * j < a.ncols) {
+        store_acc32(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 64 + 32 * j, a.M, a.ncols, a.out, nullptr, 0);
       }
     }
 }
