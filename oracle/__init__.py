@@ -32,6 +32,13 @@ is in tests/test_oracle_pins.py):
                                closed form of section 3 and its arithmetic by
                                the round-trip special cases
   blockwise.dequantize         pinned (round trips)
+  codebook.FP4_E2M1 / FP4_E3M0 pinned (format tables), INT4 pinned (two's
+                               complement over 7)
+  blockwise.nearest_level,
+  blockwise.quantize_4bit      pinned (brute force at every decision point,
+                               Eq. 1 rounding for Int4, round trips, equality
+                               with the NF4 quantiser, NF4 lowest error on
+                               normal weights)
   linear.forward / backward    pinned (brute force, finite differences,
                                special cases, torch.autograd in fp64)
 """

@@ -42,7 +42,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from .codebook import NF4, ZERO_CODE
+from .codebook import NF4, ZERO_CODE, CODEBOOKS, CODE_NF4, sorted_levels, zero_code
 from . import fp8_e4m3
 
 BLOCKSIZE = 64      # first-level block (elements of W per constant)
@@ -87,6 +87,15 @@ def nearest_code(x, codebook=NF4):
     return out
 
 
+def nearest_level(x, codebook):
+    """Code of the nearest value of a 16-entry codebook for each fp32 x, ties
+    to the smaller value (G6, G14).  Brute force over the codebook's sorted
+    distinct values in fp64, as nearest_code; for NF4, whose codes are in
+    increasing order, the two agree."""
+    vals, codes = sorted_levels(codebook)
+    return codes[nearest_code(x, vals)]
+
+
 def bf16_round(x):
     """Round fp32 values to bfloat16 (nearest-even), returned as fp32 values.
     The 16 dropped bits decide the rounding; NaN stays NaN."""
@@ -106,6 +115,28 @@ def bf16_bits(x):
 
 
 # ------------------------------------------------- first level: NF4 codes
+
+def quantize_4bit(w, codebook, blocksize=BLOCKSIZE):
+    """quantize_nf4 against any of the 4-bit codebooks of section 3's data
+    type comparison (G14): the same absmax scaling and reciprocal, then the
+    nearest codebook value, ties to the smaller value; an all-zero block gets
+    the code of 0.0.  For NF4 the result equals quantize_nf4's."""
+    flat = np.asarray(w, dtype=_F32).reshape(-1)
+    n = flat.size
+    c2 = block_absmax(flat, blocksize)
+    if not np.all(np.isfinite(c2)):
+        raise ValueError("non-finite input: codes are undefined")
+    blk = np.arange(n) // blocksize
+    tiny = (c2 > 0) & (c2 < TINY)                       # G13
+    sc = np.where(tiny, PRESCALE, _F32(1.0)).astype(_F32)
+    cs = (c2 * sc).astype(_F32)
+    ws = (flat * sc[blk]).astype(_F32)
+    inv = np.where(cs > 0, _F32(1.0) / np.where(cs > 0, cs, _F32(1.0)), _F32(0.0)).astype(_F32)
+    x = (ws * inv[blk]).astype(_F32)
+    codes = nearest_level(x, codebook).astype(np.uint8)
+    codes[c2[blk] == 0] = zero_code(codebook)
+    return codes, c2
+
 
 def quantize_nf4(w, blocksize=BLOCKSIZE, codebook=NF4):
     """NF4-quantise a tensor blockwise (section 3 steps (1)-(3), Eq. (1)).
@@ -262,8 +293,9 @@ def dequantize(codes, c2_hat, blocksize=BLOCKSIZE, codebook=NF4):
 class QuantState:
     """Everything the oracle's quantiser produces for one tensor."""
 
-    def __init__(self, shape, codes, c2, double_quant, absmax_q=None, scale2=None, mu=None):
+    def __init__(self, shape, codes, c2, double_quant, absmax_q=None, scale2=None, mu=None, code_type=CODE_NF4):
         self.shape = tuple(shape)
+        self.code_type = code_type  # which 4-bit codebook the codes index
         self.codes = codes          # uint8 per element
         self.c2 = c2                # fp32 per block (exact first-level constant)
         self.double_quant = double_quant
@@ -281,18 +313,22 @@ class QuantState:
         return self.c2
 
     def dequantize(self):
-        return dequantize(self.codes, self.c2_hat()).reshape(self.shape)
+        return dequantize(self.codes, self.c2_hat(), codebook=CODEBOOKS[self.code_type]).reshape(self.shape)
 
 
-def quantize(w, double_quant=True):
-    """NF4 + (optional) double quantisation of a tensor, as QLoRA section 3
-    defines its storage type."""
+def quantize(w, double_quant=True, code_type=CODE_NF4):
+    """NF4 (or another 4-bit type of section 3's comparison, G14) + optional
+    double quantisation of a tensor, as QLoRA section 3 defines its storage
+    type."""
     w = np.asarray(w, dtype=_F32)
-    codes, c2 = quantize_nf4(w)
+    if code_type == CODE_NF4:
+        codes, c2 = quantize_nf4(w)
+    else:
+        codes, c2 = quantize_4bit(w, CODEBOOKS[code_type])
     if not double_quant:
-        return QuantState(w.shape, codes, c2, False)
+        return QuantState(w.shape, codes, c2, False, code_type=code_type)
     q, s2, mu = double_quantize(c2)
-    return QuantState(w.shape, codes, c2, True, q, s2, mu)
+    return QuantState(w.shape, codes, c2, True, q, s2, mu, code_type=code_type)
 
 
 def storage_bytes(numel, double_quant=True):

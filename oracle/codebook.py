@@ -59,3 +59,75 @@ def derive_from_quantiles():
     neg = -norm.ppf(np.linspace(p_max, 0.5, 8)[:-1])
     vals = np.sort(np.concatenate([neg, [0.0], pos]))
     return vals / vals.max()
+
+
+# ------------------------------------------- the other 4-bit storage types
+# QLoRA section 3 compares NF4 with Int4 and two 4-bit floats, Float4 (E2M1)
+# and Float4 (E3M0) (Table 2, mean perplexity per data type), but prints no
+# values for them.  Readings (G14): each type is taken from its bit-field
+# definition, its largest magnitude normalised to 1 so that x = w / absmax in
+# [-1, 1] is quantised against it exactly as for NF4:
+#   FP4 E2M1  code = s e1 e0 m (the OCP microscaling 4-bit float): magnitude
+#             m / 2 for e = 0 (subnormal), 2^(e-1) * (1 + m/2) otherwise;
+#             the largest, 6, is divided out.
+#   FP4 E3M0  code = s e2 e1 e0: magnitude 0 for e = 0, 2^(e-7) otherwise
+#             (exponent only; the largest, 2^0, is already 1).
+#   INT4      code = two's-complement 4-bit integer k, value k / 7 (Eq. 1's
+#             absmax scaling with 2^(4-1) - 1 = 7 levels per side; k = -8 is
+#             never produced by quantisation).
+# Values are fp32 (m / 6 and k / 7 rounded to nearest).
+
+CODE_NF4, CODE_FP4_E2M1, CODE_FP4_E3M0, CODE_INT4 = 0, 1, 2, 3
+CODE_NAMES = {CODE_NF4: "nf4", CODE_FP4_E2M1: "fp4_e2m1", CODE_FP4_E3M0: "fp4_e3m0", CODE_INT4: "int4"}
+
+
+def _e2m1_magnitude(e, m):
+    return m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+
+
+def _fp4_e2m1():
+    out = []
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        out.append((-1.0 if s else 1.0) * _e2m1_magnitude(e, m) / _e2m1_magnitude(3, 1))
+    return np.array(out, dtype=np.float32)
+
+
+def _fp4_e3m0():
+    out = []
+    for c in range(16):
+        s, e = c >> 3, c & 7
+        mag = 0.0 if e == 0 else 2.0 ** (e - 7)
+        out.append((-1.0 if s else 1.0) * mag)
+    return np.array(out, dtype=np.float32)
+
+
+def _int4():
+    return np.array([(c - 16 if c >= 8 else c) / 7.0 for c in range(16)], dtype=np.float32)
+
+
+FP4_E2M1 = _fp4_e2m1()
+FP4_E3M0 = _fp4_e3m0()
+INT4 = _int4()
+
+CODEBOOKS = {CODE_NF4: NF4, CODE_FP4_E2M1: FP4_E2M1, CODE_FP4_E3M0: FP4_E3M0, CODE_INT4: INT4}
+
+
+def sorted_levels(codebook):
+    """The distinct values of a 16-entry codebook in increasing order, each
+    with the code that stands for it (the smallest such code, so +0 rather
+    than -0 for the float types).  Nearest-value search runs over this list,
+    ties to the smaller value (G6 read per value: for NF4 the smaller value
+    is the lower index)."""
+    cb = np.asarray(codebook, dtype=np.float32)
+    vals, codes = [], []
+    for v in sorted(set(float(x) for x in cb)):
+        vals.append(v)
+        codes.append(min(i for i in range(16) if float(cb[i]) == v))
+    return np.array(vals, dtype=np.float32), np.array(codes, dtype=np.uint8)
+
+
+def zero_code(codebook):
+    """The code an all-zero block gets: the one standing for 0.0."""
+    vals, codes = sorted_levels(codebook)
+    return int(codes[list(vals).index(0.0)])

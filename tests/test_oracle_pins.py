@@ -431,3 +431,114 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     x = F32(float(mids[7]))
     upper = int(np.argmin(np.abs(x - codebook.NF4[::-1].astype(np.float64))))
     assert 15 - upper != 7
+
+
+# ------------------------------------------- other 4-bit storage types (G14)
+
+def _golden_fp4(fmt):
+    for line in _read_golden("fp4_formats.txt"):
+        parts = line.split()
+        if parts[0] == fmt:
+            return np.array([float(v) for v in parts[1:]], dtype=np.float64)
+    raise KeyError(fmt)
+
+
+def test_fp4_codebooks_equal_format_tables():
+    """Codes 0..7 are the format's magnitudes (largest normalised to 1), codes
+    8..15 their negatives; every value is the fp32 rounding of that ratio."""
+    for fmt, cb in (("e2m1", codebook.FP4_E2M1), ("e3m0", codebook.FP4_E3M0)):
+        mags = _golden_fp4(fmt)
+        want = np.concatenate([mags, -mags]) / mags.max()
+        assert np.array_equal(cb, want.astype(F32)), fmt
+        assert cb[7] == 1.0 and cb[15] == -1.0
+
+
+def test_int4_codebook_is_twos_complement_over_7():
+    for c in range(16):
+        k = c - 16 if c & 8 else c
+        assert float(codebook.INT4[c]) == float(F32(k / 7.0))
+        assert round(float(codebook.INT4[c]) * 7) == k
+
+
+def _nearest_bruteforce(x, cb):
+    """Smallest-value code among those at minimal |x - v| (exact in fp64)."""
+    d = [abs(float(x) - float(v)) for v in cb]
+    best = min(d)
+    cands = [c for c in range(16) if d[c] == best]
+    vmin = min(float(cb[c]) for c in cands)
+    return min(c for c in cands if float(cb[c]) == vmin)
+
+
+def test_nearest_level_bruteforce_all_types():
+    rng = np.random.default_rng(21)
+    for ct, cb in codebook.CODEBOOKS.items():
+        vals, _ = codebook.sorted_levels(cb)
+        mids = [(float(a) + float(b)) / 2 for a, b in zip(vals[:-1], vals[1:])]
+        xs = list(rng.uniform(-1, 1, 300).astype(F32))
+        for m in mids:  # at, just below and just above every decision point
+            f = F32(m)
+            xs += [f, np.nextafter(f, F32(-2)), np.nextafter(f, F32(2))]
+        xs += [F32(0.0), F32(-0.0), F32(1.0), F32(-1.0)]
+        xs = np.array(xs, dtype=F32)
+        got = blockwise.nearest_level(xs, cb)
+        want = np.array([_nearest_bruteforce(x, cb) for x in xs])
+        assert np.array_equal(got, want), ct
+    # NF4 codes are in increasing order: the per-value rule is the per-index one
+    x = rng.uniform(-1, 1, 2000).astype(F32)
+    assert np.array_equal(blockwise.nearest_level(x, codebook.NF4), blockwise.nearest_code(x))
+
+
+def test_int4_is_eq1_rounding_to_seven_levels():
+    """For Int4 the nearest level is Eq. 1's absmax rounding with 2^3 - 1 = 7
+    levels per side (ties to the smaller value): k = ceil(7x - 1/2)."""
+    rng = np.random.default_rng(22)
+    x = np.concatenate([rng.uniform(-1, 1, 5000), (np.arange(-7, 7) + 0.5) / 7.0]).astype(F32)
+    k = np.ceil(7.0 * x.astype(np.float64) - 0.5)
+    # the fp32 levels are k/7 rounded, which moves each decision point by
+    # under 1e-7: compare away from the points (the brute-force pin covers
+    # them)
+    t = 7.0 * x.astype(np.float64)
+    clear = np.abs(np.abs(t - np.floor(t)) - 0.5) > 1e-5
+    codes = blockwise.nearest_level(x, codebook.INT4)
+    got_k = np.array([int(c) - 16 if c & 8 else int(c) for c in codes])
+    assert np.array_equal(got_k[clear], k[clear].astype(int))
+
+
+def test_other_types_round_trip_and_zero_block():
+    for ct, cb in codebook.CODEBOOKS.items():
+        vals, codes = codebook.sorted_levels(cb)
+        inside = np.abs(vals) <= 1.0
+        block = np.zeros(64, dtype=F32)
+        block[:inside.sum()] = vals[inside]
+        block[-1] = F32(1.0)  # absmax 1: x = w exactly
+        got, c2 = blockwise.quantize_4bit(block, cb)
+        assert c2[0] == 1.0
+        assert np.array_equal(cb[got], block), ct
+        z, _ = blockwise.quantize_4bit(np.zeros(64, F32), cb)
+        assert np.all(cb[z] == 0.0) and np.all(z == codebook.zero_code(cb))
+    # NF4 through the generic path equals the NF4 quantiser
+    w = (np.random.default_rng(23).standard_normal(64 * 50) * 0.02).astype(F32)
+    assert np.array_equal(blockwise.quantize_4bit(w, codebook.NF4)[0], blockwise.quantize_nf4(w)[0])
+
+
+def test_nf4_has_the_lowest_error_on_normal_weights():
+    """Section 3 motivates NF4 as the information-theoretically optimal 4-bit
+    type for normally distributed weights: on N(0, 0.02^2) blocks its
+    reconstruction error is the smallest of the four types."""
+    w = (np.random.default_rng(24).standard_normal(64 * 4000) * 0.02).astype(F32)
+    err = {}
+    for ct in codebook.CODEBOOKS:
+        q = blockwise.quantize(w, double_quant=False, code_type=ct)
+        err[ct] = float(np.sqrt(np.mean((q.dequantize().astype(np.float64) - w) ** 2)))
+    assert min(err, key=err.get) == codebook.CODE_NF4
+    assert all(err[ct] > 1.1 * err[codebook.CODE_NF4] for ct in err if ct != codebook.CODE_NF4)
+
+
+def test_pins_catch_planted_code_order_tie_rule():
+    """Searching the FP4 codebook in code order (ties to the lower code, not
+    the smaller value) is caught by the brute-force pin at a midpoint."""
+    cb = codebook.FP4_E2M1
+    x = F32((float(cb[9]) + 0.0) / 2)  # between -1/12 (code 9) and 0 (codes 0, 8)
+    wrong = int(np.argmin(np.abs(float(x) - cb.astype(np.float64))))
+    assert wrong != _nearest_bruteforce(x, cb)
+    assert int(blockwise.nearest_level(np.array([x]), cb)[0]) == _nearest_bruteforce(x, cb)
