@@ -25,6 +25,14 @@ QLORA_ERR_MISALIGNED = -4
 QLORA_ERR_HIP = -5
 QLORA_DTYPE_F32 = 0
 QLORA_DTYPE_BF16 = 1
+
+# qlora_code_type: the 4-bit codebook of a quantised weight
+QLORA_CODE_NF4 = 0
+QLORA_CODE_FP4_E2M1 = 1
+QLORA_CODE_FP4_E3M0 = 2
+QLORA_CODE_INT4 = 3
+CODE_TYPES = {"nf4": QLORA_CODE_NF4, "fp4_e2m1": QLORA_CODE_FP4_E2M1, "fp4_e3m0": QLORA_CODE_FP4_E3M0,
+              "int4": QLORA_CODE_INT4}
 BLOCKSIZE = 64
 BLOCKSIZE2 = 256
 MAX_RANK = 256
@@ -32,7 +40,7 @@ MAX_RANK = 256
 # Every function declared in include/qlora_nf4.h.
 EXPORTED = (
     "qlora_nf4_storage_bytes", "qlora_nf4_quantize_workspace", "qlora_linear_workspace",
-    "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
+    "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string", "qlora_last_error",
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_profile_events",
 )
@@ -53,7 +61,7 @@ class qlora_nf4_t(ctypes.Structure):
     _fields_ = [
         ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
         ("blocksize", ctypes.c_int32), ("blocksize2", ctypes.c_int32),
-        ("double_quant", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("double_quant", ctypes.c_int32), ("code_type", ctypes.c_int32),
         ("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
         ("scale2", ctypes.c_void_p), ("offset", ctypes.c_void_p),
     ]
@@ -81,6 +89,7 @@ def lib():
         "qlora_nf4_quantize_workspace": (_i32, [_i64, _i32, ctypes.POINTER(_i64)]),
         "qlora_linear_workspace": (_i32, [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
         "qlora_nf4_codebook": (_i32, [ctypes.POINTER(_f32)]),
+        "qlora_codebook": (_i32, [_i32, ctypes.POINTER(_f32)]),
         "qlora_status_string": (ctypes.c_char_p, [_i32]),
         "qlora_last_error": (ctypes.c_char_p, []),
         "qlora_nf4_quantize": (_i32, [_vp, _i32, _pdesc, _vp, _i64, _vp]),
@@ -145,6 +154,12 @@ def qlora_linear_workspace(M, N, K, r):
     return f.value, b.value
 
 
+def qlora_codebook(code_type):
+    out = (_f32 * 16)()
+    _check(lib().qlora_codebook(int(code_type), out), "qlora_codebook")
+    return list(out)
+
+
 def qlora_nf4_codebook():
     out = (_f32 * 16)()
     _check(lib().qlora_nf4_codebook(out), "qlora_nf4_codebook")
@@ -165,8 +180,9 @@ class NF4Weight:
     """Device buffers of one NF4-quantised weight [rows, cols] plus the C
     descriptor that points at them."""
 
-    def __init__(self, rows, cols, double_quant=True, device=None):
+    def __init__(self, rows, cols, double_quant=True, device=None, code_type=QLORA_CODE_NF4):
         self.rows, self.cols, self.double_quant = int(rows), int(cols), bool(double_quant)
+        self.code_type = int(code_type)
         sizes = qlora_nf4_storage_bytes(self.rows * self.cols, self.double_quant)
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
         u8 = torch.uint8
@@ -188,7 +204,7 @@ class NF4Weight:
         d.rows, d.cols = self.rows, self.cols
         d.blocksize, d.blocksize2 = BLOCKSIZE, BLOCKSIZE2
         d.double_quant = int(self.double_quant)
-        d.reserved = 0
+        d.code_type = self.code_type
         d.codes = self.codes.data_ptr()
         d.absmax_q = self.absmax_q.data_ptr() if self.absmax_q is not None else None
         d.absmax = self.absmax.data_ptr() if self.absmax is not None else None
@@ -211,10 +227,12 @@ class NF4Weight:
 
 # ---------------------------------------------------------- device entry points
 
-def qlora_nf4_quantize(w, double_quant=True, out=None, workspace=None, stream=None):
+def qlora_nf4_quantize(w, double_quant=True, out=None, workspace=None, stream=None, code_type=QLORA_CODE_NF4):
     """Quantise fp32 or bf16 tensor `w` ([rows, cols] or 1-D) into an
-    NF4Weight (new or `out`).  `workspace`: optional uint8 device tensor of at
-    least qlora_nf4_quantize_workspace bytes."""
+    NF4Weight (new or `out`; `out` keeps its own code_type).  `code_type`
+    (a QLORA_CODE_* value) picks the 4-bit codebook of a new weight.
+    `workspace`: optional uint8 device tensor of at least
+    qlora_nf4_quantize_workspace bytes."""
     _need_cuda(w)
     if not w.is_contiguous():
         raise ValueError("w must be contiguous")
@@ -222,7 +240,7 @@ def qlora_nf4_quantize(w, double_quant=True, out=None, workspace=None, stream=No
     if dtype is None:
         raise ValueError("w must be float32 or bfloat16")
     rows, cols = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, w.numel())
-    q = out if out is not None else NF4Weight(rows, cols, double_quant, w.device)
+    q = out if out is not None else NF4Weight(rows, cols, double_quant, w.device, code_type)
     nws = qlora_nf4_quantize_workspace(q.numel, q.double_quant)
     ws = workspace if workspace is not None else torch.empty(max(nws, 16), dtype=torch.uint8, device=w.device)
     if ws.numel() < nws:

@@ -67,6 +67,8 @@ int check_desc(const qlora_nf4_t* q, const char* fn) {
     return fail(QLORA_ERR_INVALID_ARG, "%s: blocksize must be 64 and blocksize2 256", fn);
   if (q->double_quant != 0 && q->double_quant != 1)
     return fail(QLORA_ERR_INVALID_ARG, "%s: double_quant must be 0 or 1", fn);
+  if (q->code_type < 0 || q->code_type >= CODE_TYPES)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: code_type must be one of the qlora_code_type values", fn);
   if (q->rows * q->cols == 0) return QLORA_OK;
   if (!q->codes) return fail(QLORA_ERR_INVALID_ARG, "%s: codes is NULL", fn);
   if (!aligned16(q->codes)) return fail(QLORA_ERR_MISALIGNED, "%s: codes not 16-byte aligned", fn);
@@ -89,6 +91,7 @@ DQParams dq_params(const qlora_nf4_t* q) {
   p.scale2 = q->scale2;
   p.offset = q->offset;
   p.double_quant = q->double_quant;
+  p.code_type = q->code_type;
   return p;
 }
 
@@ -200,6 +203,14 @@ int qlora_nf4_codebook(float* out) {
   return QLORA_OK;
 }
 
+int qlora_codebook(int32_t code_type, float* out) {
+  if (!out) return fail(QLORA_ERR_INVALID_ARG, "qlora_codebook: out is NULL");
+  if (code_type < 0 || code_type >= CODE_TYPES)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_codebook: code_type must be one of the qlora_code_type values");
+  memcpy(out, code_values(code_type).v, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
 int qlora_nf4_storage_bytes(int64_t numel, int32_t double_quant, int64_t* bytes) {
   if (!bytes) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_storage_bytes: bytes is NULL");
   if (numel < 0 || numel >= kMaxNumel) return fail(QLORA_ERR_INVALID_ARG, "qlora_nf4_storage_bytes: bad numel");
@@ -250,7 +261,7 @@ int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q, voi
   hipError_t e;
   {
     ProfScope ps(QLORA_KERNEL_QUANTIZE, s);
-    e = launch_quantize(w, w_dtype == QLORA_DTYPE_BF16, numel, q->codes, c2, parts, s);
+    e = launch_quantize(w, w_dtype == QLORA_DTYPE_BF16, numel, q->code_type, q->codes, c2, parts, s);
   }
   if (e != hipSuccess) return hip_fail(e, fn);
   if (q->double_quant) {
@@ -272,7 +283,7 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, voi
   hipError_t e;
   {
     ProfScope ps(QLORA_KERNEL_DEQUANTIZE, (hipStream_t)stream);
-    e = launch_dequantize(q->codes, numel, q->double_quant != 0, q->absmax_q, q->absmax, q->scale2, q->offset, out,
+    e = launch_dequantize(q->codes, numel, q->code_type, q->double_quant != 0, q->absmax_q, q->absmax, q->scale2, q->offset, out,
                           out_dtype == QLORA_DTYPE_BF16, (hipStream_t)stream);
   }
   if (e != hipSuccess) return hip_fail(e, fn);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "codebooks.h"
+
 namespace qlora {
 
 // Quantisation lookup: x in [-1, 1] goes to bucket b = round(16 x + 16)
@@ -22,9 +24,28 @@ struct NF4Values {
   float v[16];
 };
 
-// Library copies of the NF4 values and the derived quantisation table.
-const NF4Values& nf4_values();
+// The codebooks other than NF4 are quantised through a finer table built by
+// each quantisation workgroup: kFineBuckets buckets of width 1/kFineScale,
+// b = round(kFineScale x + kFineScale), each holding at most one decision
+// point; an entry gives the threshold and the codes below and above it.
+// CodeSpec carries what the kernel needs to build it: the exact midpoints
+// between consecutive distinct values (fp64), the same rounded toward -inf to
+// fp32, and the code of each distinct value in increasing order.
+constexpr int kFineScale = 512;
+constexpr int kFineBuckets = 2 * kFineScale + 1;
+struct CodeSpec {
+  double mid[15];
+  float thr[15];
+  uint32_t rank_code[16];
+  int nmid;
+};
+
+// Library copies of the codebook values, the NF4 quantisation table and the
+// spec of the finer table of another codebook.
+const NF4Values& code_values(int code_type);
+inline const NF4Values& nf4_values() { return code_values(CODE_NF4); }
 const QuantTable& quant_table();
+const CodeSpec& code_spec(int code_type);
 
 // Quantisation writes the codes and the fp32 block absmax c2; with
 // `partials` it also writes, per workgroup, the exact sum of its c2 as
@@ -35,11 +56,11 @@ const QuantTable& quant_table();
 int quantize_parts(int64_t numel);
 constexpr int kMeanDigits = 10;  // 32-bit digits of the exact fixed-point sum
 
-hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2,
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_type, uint8_t* codes, float* c2,
                            uint64_t* partials, hipStream_t stream);
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts,
                                uint8_t* absmax_q, float* scale2, float* offset, hipStream_t stream);
-hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, bool dq, const uint8_t* absmax_q,
+hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, int code_type, bool dq, const uint8_t* absmax_q,
                              const float* absmax, const float* scale2, const float* offset,
                              void* out, bool out_bf16, hipStream_t stream);
 
@@ -50,6 +71,7 @@ struct DQParams {
   const float* scale2;      // double_quant: per 256 blocks
   const float* offset;      // double_quant: mean mu
   int double_quant;
+  int code_type;            // CodeType of the codes
 };
 
 // Linear-layer building blocks (all bf16 matrices row-major).

@@ -47,12 +47,10 @@ constexpr int PK = 72;  // pitch (bf16) of a [rows][64] reduction-contiguous til
 // banks apart and cover all 64 banks once (with +16 they overlapped 2-way).
 constexpr int kRcPad = 32;
 
-// Appendix E of QLoRA as immediates for the lookup-table build.
-constexpr float kNF4c[16] = {
-    -1.0f, -0.6961928009986877f, -0.5250730514526367f, -0.39491748809814453f,
-    -0.28444138169288635f, -0.18477343022823334f, -0.09105003625154495f, 0.0f,
-    0.07958029955625534f, 0.16093020141124725f, 0.24611230194568634f, 0.33791524171829224f,
-    0.44070982933044434f, 0.5626170039176941f, 0.7229568362236023f, 1.0f};
+// The codebooks (NF4 = QLoRA Appendix E, then the other 4-bit types of the
+// section 3 comparison) in constant memory, read through a wave-uniform
+// pointer for the lookup-table builds.
+__constant__ float kCodeValues[CODE_TYPES][16] = QLORA_CODE_VALUES;
 
 // c2_hat of one block (Eq. 6 inner dequant): two separately rounded fp32
 // operations for double quantisation, or the stored absmax.
@@ -62,10 +60,10 @@ __device__ __forceinline__ float block_scale(const DQParams& dq, uint32_t qbyte,
   return f;
 }
 
-__device__ __forceinline__ BlockLUT lut_for(float c) {
+__device__ __forceinline__ BlockLUT lut_for(float c, const float* cv) {
   uint32_t p[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) p[j] = pack_bf2(kNF4c[2 * j] * c, kNF4c[2 * j + 1] * c);
+  for (int j = 0; j < 8; ++j) p[j] = pack_bf2(cv[2 * j] * c, cv[2 * j + 1] * c);
   return make_lut(p);
 }
 
@@ -128,6 +126,7 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
   const float mu = a.dq.double_quant ? *a.dq.offset : 0.0f;
+  const float* cv = kCodeValues[a.dq.code_type];
   const int64_t kblocks = a.Kw >> 6;
   const int64_t nk = a.L >> 6;
 
@@ -190,7 +189,7 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
       sts16(&sA[buf][row * PK + ch * 8], xr[i]);
     }
     const float c = t_ok ? block_scale(a.dq, qb, sf, mu) : 0.0f;
-    const BlockLUT lut = lut_for(c);
+    const BlockLUT lut = lut_for(c, cv);
     __bf16* dst = BWD ? &sB[buf][t_row * C::PRC + t_col] : &sB[buf][t_row * PK + t_col];
 #pragma unroll
     for (int w = 0; w < C::DQW; ++w) {
@@ -342,6 +341,7 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
   const int nk = ke;
   const int64_t kblocks = a.Kw >> 6;
   const float mu = DQ ? *a.dq.offset : 0.0f;
+  const float* cv = kCodeValues[a.dq.code_type];
 
   // dequantisation task: one whole NF4 block (64 weights) per thread
   const int t_row = BWD ? (tid >> 2) : tid;
@@ -416,9 +416,9 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
       if (it == 0) {
         const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
         sc = t_ok ? bs : 0.0f;
-        pw[0] = pack_bf2(kNF4c[0] * sc, kNF4c[1] * sc);
+        pw[0] = pack_bf2(cv[0] * sc, cv[1] * sc);
       } else if (it <= 7) {
-        pw[it] = pack_bf2(kNF4c[2 * it] * sc, kNF4c[2 * it + 1] * sc);
+        pw[it] = pack_bf2(cv[2 * it] * sc, cv[2 * it + 1] * sc);
       } else if (it == 8) {
         lut = make_lut(pw);
       } else if (it < 9 + 32) {
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
   for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
   {
     const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
-    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f);
+    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f, cv);
     const uint32_t words[8] = {cwB[0].x, cwB[0].y, cwB[0].z, cwB[0].w, cwB[1].x, cwB[1].y, cwB[1].z, cwB[1].w};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -582,6 +582,7 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   const int nk = ke;
   const int64_t kblocks = a.Kw >> 6;
   const float mu = DQ ? *a.dq.offset : 0.0f;
+  const float* cv = kCodeValues[a.dq.code_type];
 
   // dequantisation task: half (t_half) of one NF4 block per thread; the 16
   // lanes of a store group take 16 different rows (fwd) or 4 rows x 4 blocks
@@ -659,9 +660,9 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
       if (it == 0) {
         const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
         sc = t_ok ? bs : 0.0f;
-        pw[0] = pack_bf2(kNF4c[0] * sc, kNF4c[1] * sc);
+        pw[0] = pack_bf2(cv[0] * sc, cv[1] * sc);
       } else if (it <= 7) {
-        pw[it] = pack_bf2(kNF4c[2 * it] * sc, kNF4c[2 * it + 1] * sc);
+        pw[it] = pack_bf2(cv[2 * it] * sc, cv[2 * it + 1] * sc);
       } else if (it == 8) {
         lut = make_lut(pw);
       } else if (it < 9 + 16) {
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
   {
     const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
-    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f);
+    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f, cv);
     const uint32_t words[4] = {cwB.x, cwB.y, cwB.z, cwB.w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -1203,6 +1204,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   __shared__ u32x4 stage[2][G3_CHUNK16];  // code chunks; the partial tiles at the end
   __shared__ float2 cst[2][G3_ROWS * G3_CB / 2];  // block constants cst[buf][row][block]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* cv = kCodeValues[dq.code_type];
 
   const int64_t nbk = K >> 6, half_k = K >> 1;
   const int64_t n0 = (int64_t)blockIdx.x * G3_ROWS;
@@ -1232,13 +1234,13 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   const uint16_t* xrow = X + (int64_t)(t < M ? t : M - 1) * K + 16 * g;
 
   {
-    // table: entry e (a code byte) = the bf16 pair (NF4[e % 16], NF4[e / 16]),
+    // table: entry e (a code byte) = the bf16 pair (value[e % 16], value[e / 16]),
     // 64 copies side by side
     u32x4* tv = reinterpret_cast<u32x4*>(tab);
 #pragma unroll
     for (int k = 0; k < 256 * 64 / 4 / G3_T; ++k) {
       const int i = k * G3_T + tid, e = i >> 4;
-      const uint32_t v = pack_bf2(kNF4c[e & 15], kNF4c[e >> 4]);
+      const uint32_t v = pack_bf2(cv[e & 15], cv[e >> 4]);
       tv[i] = u32x4{v, v, v, v};
     }
   }

@@ -38,33 +38,16 @@ constexpr float kPrescale = 0x1p32f;
 
 // ----------------------------------------------------------------- tables
 
-// QLoRA Appendix E, code 0 .. 15 (each value exact in fp32).
-static const float kNF4[16] = {
-    -1.0f,
-    -0.6961928009986877f,
-    -0.5250730514526367f,
-    -0.39491748809814453f,
-    -0.28444138169288635f,
-    -0.18477343022823334f,
-    -0.09105003625154495f,
-    0.0f,
-    0.07958029955625534f,
-    0.16093020141124725f,
-    0.24611230194568634f,
-    0.33791524171829224f,
-    0.44070982933044434f,
-    0.5626170039176941f,
-    0.7229568362236023f,
-    1.0f,
-};
-
-const NF4Values& nf4_values() {
-  static const NF4Values v = [] {
-    NF4Values t;
-    memcpy(t.v, kNF4, sizeof(kNF4));
-    return t;
+// Library copies of the codebooks (QLoRA Appendix E for NF4; the other
+// types of the section 3 comparison as defined in codebooks.h).
+const NF4Values& code_values(int code_type) {
+  static NF4Values v[CODE_TYPES];
+  static const bool filled = [] {
+    for (int c = 0; c < CODE_TYPES; ++c) memcpy(v[c].v, kCodeValuesHost[c], sizeof(v[c].v));
+    return true;
   }();
-  return v;
+  (void)filled;
+  return v[code_type];
 }
 
 // Decision thresholds between codes i and i+1 are the exact midpoints
@@ -80,7 +63,7 @@ const QuantTable& quant_table() {
     double mid[15];
     float thr[15];
     for (int i = 0; i < 15; ++i) {
-      mid[i] = 0.5 * ((double)kNF4[i] + (double)kNF4[i + 1]);
+      mid[i] = 0.5 * ((double)kCodeValuesHost[CODE_NF4][i] + (double)kCodeValuesHost[CODE_NF4][i + 1]);
       float f = (float)mid[i];
       if ((double)f > mid[i]) f = nextafterf(f, -INFINITY);
       thr[i] = f;
@@ -101,6 +84,52 @@ const QuantTable& quant_table() {
     return q;
   }();
   return t;
+}
+
+// Spec of the finer quantisation table of a codebook (any type): its
+// distinct values in increasing order (the smallest code for a repeated
+// value, so +0 rather than -0), the exact midpoints between neighbours and
+// those rounded toward -inf to fp32.  Checks once that no fine bucket holds
+// two midpoints (true for all four codebooks: the closest midpoints, E3M0's
+// around zero, are 2^-6 apart against a bucket width of 2^-9).
+const CodeSpec& code_spec(int code_type) {
+  static CodeSpec specs[CODE_TYPES];
+  static const bool built = [] {
+    for (int c = 0; c < CODE_TYPES; ++c) {
+      const float* v = kCodeValuesHost[c];
+      float vals[16];
+      uint32_t codes[16];
+      int n = 0;
+      for (int i = 0; i < 16; ++i) {  // insertion into the sorted distinct list
+        int j = 0;
+        while (j < n && vals[j] < v[i]) ++j;
+        if (j < n && vals[j] == v[i]) continue;  // repeated value (-0): keep the smaller code
+        for (int k = n; k > j; --k) { vals[k] = vals[k - 1]; codes[k] = codes[k - 1]; }
+        vals[j] = v[i];
+        codes[j] = (uint32_t)i;
+        ++n;
+      }
+      CodeSpec& sp = specs[c];
+      memset(&sp, 0, sizeof(sp));
+      sp.nmid = n - 1;
+      for (int i = 0; i < n; ++i) sp.rank_code[i] = codes[i];
+      for (int i = 0; i + 1 < n; ++i) {
+        sp.mid[i] = 0.5 * ((double)vals[i] + (double)vals[i + 1]);
+        float f = (float)sp.mid[i];
+        if ((double)f > sp.mid[i]) f = nextafterf(f, -INFINITY);
+        sp.thr[i] = f;
+      }
+      for (int b = 0; b < kFineBuckets; ++b) {
+        const double lo = (b - 0.5) / kFineScale - 1.0, hi = (b + 0.5) / kFineScale - 1.0;
+        int inside = 0;
+        for (int i = 0; i < sp.nmid; ++i) inside += sp.mid[i] >= lo && sp.mid[i] < hi;
+        if (inside > 1) abort();
+      }
+    }
+    return true;
+  }();
+  (void)built;
+  return specs[code_type];
 }
 
 // --------------------------------------------------- exact mean of c2
@@ -211,41 +240,71 @@ __device__ __forceinline__ float weight_of(const qz_u32x4* r, int i) {
 // 1, so b is the low mantissa field; shifting the bit pattern left by 3 and
 // removing the shifted exponent bits (mod 2^32) gives the table entry's byte
 // offset 8 b.
-constexpr float kBucketMagic = 12582928.0f;  // 1.5 * 2^23 + 16
+// With MAPPED (a codebook other than NF4) the same holds for the finer table:
+// scale 512 instead of 16, and the entry's second word holds the codes below
+// and above the threshold (low and high 16 bits) instead of a base code.
 constexpr uint32_t kBucketBits = 0x4B400000u; // bit pattern of 1.5 * 2^23
 constexpr uint32_t kBucketBias = 0u - (kBucketBits << 3);
 
+template <bool MAPPED>
+struct QzBuckets {
+  static constexpr float S = MAPPED ? (float)kFineScale : 16.0f;      // buckets per unit of x
+  static constexpr float MAGIC = 12582912.0f + S;                    // 1.5 * 2^23 + S
+  static constexpr int N = MAPPED ? kFineBuckets : kBuckets;
+};
+
+template <bool MAPPED>
+__device__ __forceinline__ uint32_t code_of(float x, uint2 t) {
+  const bool above = x > __uint_as_float(t.x);
+  if (MAPPED) return above ? (t.y >> 16) : (t.y & 0xFFFFu);
+  return t.y + (above ? 1u : 0u);
+}
+
 // Codes of a lane's 8 weights (normalised by inv, |x| <= 1), packed
 // low nibble first.
-template <bool BF16>
+template <bool BF16, bool MAPPED>
 __device__ __forceinline__ uint32_t code8_fast(const qz_u32x4* r, float inv, const uint2* s_tab) {
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float x = weight_of<BF16>(r, i) * inv;
-    const float y = __builtin_fmaf(x, 16.0f, kBucketMagic);
+    const float y = __builtin_fmaf(x, QzBuckets<MAPPED>::S, QzBuckets<MAPPED>::MAGIC);
     const uint32_t off = (__float_as_uint(y) << 3) + kBucketBias;
     const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) + off);
-    packed |= (t.y + (x > __uint_as_float(t.x) ? 1u : 0u)) << (4 * i);
+    packed |= code_of<MAPPED>(x, t) << (4 * i);
   }
   return packed;
 }
 
 // As code8_fast with the weights first scaled by sc (exact) and the bucket
 // index clamped, so that any input (NaN included) reads inside the table.
-template <bool BF16>
+template <bool BF16, bool MAPPED>
 __device__ __forceinline__ uint32_t code8_generic(const qz_u32x4* r, float sc, float inv, const uint2* s_tab) {
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float x = (weight_of<BF16>(r, i) * sc) * inv;
-    const float y = __builtin_fmaf(x, 16.0f, kBucketMagic);
+    const float y = __builtin_fmaf(x, QzBuckets<MAPPED>::S, QzBuckets<MAPPED>::MAGIC);
     int b = (int)(__float_as_uint(y) - kBucketBits);
-    b = b < 0 ? 0 : (b > kBuckets - 1 ? kBuckets - 1 : b);
+    b = b < 0 ? 0 : (b > QzBuckets<MAPPED>::N - 1 ? QzBuckets<MAPPED>::N - 1 : b);
     const uint2 t = s_tab[b];
-    packed |= (t.y + (x > __uint_as_float(t.x) ? 1u : 0u)) << (4 * i);
+    packed |= code_of<MAPPED>(x, t) << (4 * i);
   }
   return packed;
+}
+
+// Entry b of the finer table of a codebook: bucket [(b - 1/2)/S - 1,
+// (b + 1/2)/S - 1] holds at most one midpoint; below it lie `base` of them.
+__device__ __forceinline__ uint2 fine_entry(const CodeSpec& sp, int b) {
+  const double lo = (b - 0.5) / kFineScale - 1.0, hi = (b + 0.5) / kFineScale - 1.0;
+  int base = 0, in = -1;
+  for (int i = 0; i < sp.nmid; ++i) {
+    base += sp.mid[i] < lo;
+    if (sp.mid[i] >= lo && sp.mid[i] < hi) in = i;
+  }
+  const uint32_t below = sp.rank_code[base];
+  const uint32_t above = in >= 0 ? sp.rank_code[base + 1] : below;
+  return make_uint2(in >= 0 ? __float_as_uint(sp.thr[in]) : 0x7F800000u, below | (above << 16));
 }
 
 __device__ __forceinline__ void add_c2(unsigned long long* acc, float c2) {
@@ -258,7 +317,7 @@ __device__ __forceinline__ void add_c2(unsigned long long* acc, float c2) {
 // One wave step of 512 weights with every check: the lane's 8 weights start
 // at e0 (zeros past numel); block constants of blocks past nb are not
 // stored, and the nibble of a missing element is 0.
-template <bool BF16>
+template <bool BF16, bool MAPPED>
 __device__ __forceinline__ void generic_step(const qz_u32x4* r, int64_t e0, int64_t numel, int64_t nb,
                                              uint8_t* __restrict__ codes, float* __restrict__ c2out,
                                              unsigned long long* acc, const uint2* s_tab, int lane) {
@@ -267,7 +326,7 @@ __device__ __forceinline__ void generic_step(const qz_u32x4* r, int64_t e0, int6
   const float sc = tiny ? kPrescale : 1.0f;
   const float cs = c2 * sc;
   const float inv = cs > 0.0f ? 1.0f / cs : 0.0f;  // correctly rounded division
-  uint32_t packed = code8_generic<BF16>(r, sc, inv, s_tab);
+  uint32_t packed = code8_generic<BF16, MAPPED>(r, sc, inv, s_tab);
   if (e0 + 7 < numel) {
     *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
   } else if (e0 < numel) {
@@ -309,19 +368,24 @@ __device__ __forceinline__ void load_partial(const void* __restrict__ w, int64_t
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool MAPPED>
 __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
                                                                   uint8_t* __restrict__ codes,
                                                                   float* __restrict__ c2out,
-                                                                  uint64_t* __restrict__ partials, QuantTable tab) {
+                                                                  uint64_t* __restrict__ partials, QuantTable tab,
+                                                                  CodeSpec spec) {
   using Geo = QzGeo<BF16>;
   constexpr int STEPS = Geo::STEPS, NV = Geo::NV;
   constexpr int64_t CH = Geo::CH;
   constexpr int ES = BF16 ? 2 : 4;  // bytes per input weight
-  __shared__ uint2 s_tab[kBuckets];  // {threshold bits, base code}
+  __shared__ uint2 s_tab[QzBuckets<MAPPED>::N];  // {threshold bits, base code | codes below/above}
   __shared__ unsigned long long s_acc[QZ_WAVES][kMeanDigits];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < kBuckets) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
+  if (MAPPED) {
+    for (int b = tid; b < QzBuckets<MAPPED>::N; b += QZ_THREADS) s_tab[b] = fine_entry(spec, b);
+  } else if (tid < kBuckets) {
+    s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
+  }
   if (tid < QZ_WAVES * kMeanDigits) (&s_acc[0][0])[tid] = 0;
   __syncthreads();
 
@@ -354,8 +418,8 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
     if (__builtin_amdgcn_ballot_w64(mine && !normal)) {  // rare, wave-uniform
 #pragma unroll
       for (int s = 0; s < STEPS; ++s)
-        generic_step<BF16>(r[s], c * CH + s * QZ_WAVES * 512 + lane_off, numel, nb, codes, c2out, acc, s_tab,
-                           lane);
+        generic_step<BF16, MAPPED>(r[s], c * CH + s * QZ_WAVES * 512 + lane_off, numel, nb, codes, c2out, acc,
+                                   s_tab, lane);
       return;
     }
     // B: one block per lane
@@ -372,7 +436,7 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
     for (int s = 0; s < STEPS; ++s) {
       const float inv_s = __int_as_float(__builtin_amdgcn_ds_bpermute(src + 4 * s, __float_as_int(inv)));
       *reinterpret_cast<uint32_t*>(cb + (((uint32_t)(s * QZ_WAVES * 512) + lane_off) >> 1)) =
-          code8_fast<BF16>(r[s], inv_s, s_tab);
+          code8_fast<BF16, MAPPED>(r[s], inv_s, s_tab);
     }
   };
 
@@ -399,7 +463,7 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
       const int64_t e0 = tail0 + t * 512 + lane * 8;
       qz_u32x4 r[NV];
       load_partial<BF16>(w, e0, numel, r);
-      generic_step<BF16>(r, e0, numel, nb, codes, c2out, acc, s_tab, lane);
+      generic_step<BF16, MAPPED>(r, e0, numel, nb, codes, c2out, acc, s_tab, lane);
     }
   }
   if (partials) {
@@ -413,15 +477,27 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
   }
 }
 
-hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, uint8_t* codes, float* c2, uint64_t* partials,
-                           hipStream_t stream) {
-  const int grid = quantize_parts(numel);
-  if (w_bf16)
-    hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, w,
-                       numel, codes, c2, partials, quant_table());
-  else
-    hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, w,
-                       numel, codes, c2, partials, quant_table());
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_type, uint8_t* codes, float* c2,
+                           uint64_t* partials, hipStream_t stream) {
+  if (code_type < 0 || code_type >= CODE_TYPES) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)quantize_parts(numel)), block(QZ_THREADS);
+  const QuantTable& tab = quant_table();
+  const CodeSpec& spec = code_spec(code_type);
+  if (code_type == CODE_NF4) {
+    if (w_bf16)
+      hipLaunchKernelGGL((nf4_quantize_kernel<true, false>), grid, block, 0, stream, w, numel, codes, c2, partials,
+                         tab, spec);
+    else
+      hipLaunchKernelGGL((nf4_quantize_kernel<false, false>), grid, block, 0, stream, w, numel, codes, c2, partials,
+                         tab, spec);
+  } else {
+    if (w_bf16)
+      hipLaunchKernelGGL((nf4_quantize_kernel<true, true>), grid, block, 0, stream, w, numel, codes, c2, partials,
+                         tab, spec);
+    else
+      hipLaunchKernelGGL((nf4_quantize_kernel<false, true>), grid, block, 0, stream, w, numel, codes, c2, partials,
+                         tab, spec);
+  }
   return hipGetLastError();
 }
 
@@ -725,11 +801,12 @@ __global__ __launch_bounds__(DQZ_THREADS) void nf4_dequant_kernel(const uint8_t*
   }
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, bool dq, const uint8_t* absmax_q,
+hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, int code_type, bool dq, const uint8_t* absmax_q,
                              const float* absmax, const float* scale2, const float* offset, void* out,
                              bool out_bf16, hipStream_t stream) {
+  if (code_type < 0 || code_type >= CODE_TYPES) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((numel + DQZ_PER_WG - 1) / DQZ_PER_WG)), block(DQZ_THREADS);
-  const NF4Values& t = nf4_values();
+  const NF4Values& t = code_values(code_type);
   if (dq) {
     if (out_bf16)
       hipLaunchKernelGGL((nf4_dequant_kernel<true, true>), grid, block, 0, stream, codes, numel, absmax_q, absmax,

@@ -66,6 +66,24 @@ typedef enum {
   QLORA_DTYPE_BF16 = 1
 } qlora_dtype;
 
+/* The 4-bit codebook a quantised weight's codes index (qlora_nf4_t's
+ * code_type).  NF4 is QLoRA Appendix E (code 0 = -1.0, 7 = 0.0, 15 = 1.0).
+ * The other three are the types QLoRA section 3 compares NF4 with (Table 2:
+ * Int4, Float4 (E2M1), Float4 (E3M0)); the page gives no values, so each is
+ * its bit-field definition with the largest magnitude normalised to 1:
+ *   FP4_E2M1  code = s e1 e0 m, magnitude (m/2 for e = 0, else
+ *             2^(e-1) (1 + m/2)) / 6 (the OCP microscaling 4-bit float);
+ *   FP4_E3M0  code = s e2 e1 e0, magnitude 0 for e = 0, else 2^(e-7);
+ *   INT4      code = two's-complement k, value k / 7 (Eq. 1 with 7 levels
+ *             per side; code 8 = -8/7 is never produced by quantisation).
+ * Values are fp32; qlora_codebook() returns them. */
+typedef enum {
+  QLORA_CODE_NF4 = 0,
+  QLORA_CODE_FP4_E2M1 = 1,
+  QLORA_CODE_FP4_E3M0 = 2,
+  QLORA_CODE_INT4 = 3
+} qlora_code_type;
+
 /* Block sizes fixed by QLoRA section 3 ("QLoRA": block size 64 for W,
  * 256 for the first-level constants). */
 #define QLORA_NF4_BLOCKSIZE 64
@@ -74,7 +92,7 @@ typedef enum {
 #define QLORA_MAX_RANK 256
 
 /*
- * Descriptor of one NF4-quantised weight (the quantisation state).  Plain
+ * Descriptor of one 4-bit-quantised weight (the quantisation state).  Plain
  * data: the caller fills it and owns every buffer it points to.
  *
  *   rows, cols     weight shape [N, K]; numel = rows*cols, 0 < numel < 2^37.
@@ -95,6 +113,9 @@ typedef enum {
  *                  group is constant.
  *   offset         f32[1]: mu, the mean of all c2_b, exact and rounded once
  *                  to fp32 (nearest-even).
+ *   code_type      qlora_code_type of the codes (0 = NF4, the default).
+ *                  The codes description above is NF4's; for the other types
+ *                  code i stands for value i of that type's codebook.
  */
 typedef struct qlora_nf4 {
   int64_t rows;
@@ -102,7 +123,7 @@ typedef struct qlora_nf4 {
   int32_t blocksize;
   int32_t blocksize2;
   int32_t double_quant;
-  int32_t reserved;  /* set to 0 */
+  int32_t code_type;  /* qlora_code_type; 0 = NF4 */
   uint8_t* codes;
   uint8_t* absmax_q;
   float* absmax;
@@ -134,6 +155,10 @@ int qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r,
  * (QLoRA Appendix E, code order) into the host array out[16]. */
 int qlora_nf4_codebook(float* out);
 
+/* Host only.  Copies the 16 values of codebook `code_type` (a
+ * qlora_code_type, code order) into the host array out[16]. */
+int qlora_codebook(int32_t code_type, float* out);
+
 /* Text for a status code; never NULL. */
 const char* qlora_status_string(int32_t status);
 
@@ -157,8 +182,9 @@ const char* qlora_last_error(void);
  *            (may be NULL when that is 0); contents on entry are ignored.
  *
  * Per block b of 64 flattened weights: c2_b = max |w| (exact); each weight
- * x = fp32(w * fp32(1/c2_b)) gets the index of the nearest Appendix E value,
- * ties to the lower index; an all-zero block gets code 7 throughout.  With
+ * x = fp32(w * fp32(1/c2_b)) gets the code of the nearest value of the
+ * q->code_type codebook, ties to the smaller value (for NF4, the lower
+ * index); an all-zero block gets the code of 0.0 throughout (NF4: 7).  With
  * double quantisation, mu = mean(c2) and each group of 256 constants is
  * stored as described for qlora_nf4_t.
  */
@@ -174,7 +200,8 @@ int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q,
  *   out      device, [rows, cols] row-major, dtype out_dtype (F32 or BF16).
  *
  * c2_hat_b = fp32(fp32(fp8(absmax_q_b) * scale2_g) + mu) (two roundings,
- * no fused multiply-add), or absmax_b; w_hat = fp32(NF4[code] * c2_hat_b);
+ * no fused multiply-add), or absmax_b; w_hat = fp32(value[code] * c2_hat_b)
+ * with the q->code_type codebook;
  * bf16 output is w_hat rounded to nearest-even.
  */
 int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, void* stream);

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -50,6 +50,17 @@ def test_storage_bytes_match_closed_form():
 def test_library_codebook_is_appendix_e():
     assert np.array_equal(np.array(B.qlora_nf4_codebook(), np.float32).view(np.uint32),
                           codebook.NF4.view(np.uint32))
+
+
+def test_library_codebooks_equal_oracle_bit_exact():
+    """Every codebook the library quantises against equals the oracle's
+    (built independently from the format definitions), sign of zero included."""
+    for name, ct in B.CODE_TYPES.items():
+        got = np.array(B.qlora_codebook(ct), np.float32)
+        assert np.array_equal(got.view(np.uint32), codebook.CODEBOOKS[ct].view(np.uint32)), name
+    out = (ctypes.c_float * 16)()
+    assert B.lib().qlora_codebook(4, out) == B.QLORA_ERR_INVALID_ARG
+    assert B.lib().qlora_codebook(-1, out) == B.QLORA_ERR_INVALID_ARG
 
 
 def test_status_strings():
@@ -77,6 +88,10 @@ def test_quantize_validation():
     assert _quant(_desc(bs=32)) == B.QLORA_ERR_INVALID_ARG
     assert _quant(_desc(bs2=128)) == B.QLORA_ERR_INVALID_ARG
     assert _quant(_desc(dq=2)) == B.QLORA_ERR_INVALID_ARG
+    d = _desc()
+    d.code_type = 4
+    assert _quant(d) == B.QLORA_ERR_INVALID_ARG
+    assert "code_type" in L.qlora_last_error().decode()
     assert _quant(_desc(rows=-1)) == B.QLORA_ERR_INVALID_ARG
     assert _quant(_desc(rows=1 << 20, cols=1 << 20)) == B.QLORA_ERR_INVALID_ARG
     assert _quant(_desc(codes=None)) == B.QLORA_ERR_INVALID_ARG

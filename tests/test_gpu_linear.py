@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import blockwise, linear
+from oracle import blockwise, codebook, linear
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,8 @@ class OracleWeight:
     """Oracle-side quantisation of an fp32 weight [N, K] (K % 64 == 0):
     constants for every block, codes only where asked."""
 
-    def __init__(self, w_np, dq=True):
+    def __init__(self, w_np, dq=True, code_type=codebook.CODE_NF4):
+        self.code_type = code_type
         self.w = w_np.reshape(w_np.shape[0], -1)
         self.N, self.K = self.w.shape
         blocks = self.w.reshape(-1, 64)
@@ -71,8 +72,12 @@ class OracleWeight:
         self.blocks = blocks
 
     def bf16_blocks(self, sel):
-        codes, _ = blockwise.quantize_nf4(self.blocks[sel].reshape(-1))
-        return blockwise.bf16_round(blockwise.dequantize(codes, self.c2hat[sel])).reshape(-1, 64)
+        cb = codebook.CODEBOOKS[self.code_type]
+        if self.code_type == codebook.CODE_NF4:
+            codes, _ = blockwise.quantize_nf4(self.blocks[sel].reshape(-1))
+        else:
+            codes, _ = blockwise.quantize_4bit(self.blocks[sel].reshape(-1), cb)
+        return blockwise.bf16_round(blockwise.dequantize(codes, self.c2hat[sel], codebook=cb)).reshape(-1, 64)
 
     def rows(self, ns):
         kb = self.K // 64
@@ -88,15 +93,15 @@ class OracleWeight:
         return self.rows(np.arange(self.N))
 
 
-def _run(B, X, W, A, Bm, dY, s, dq=True, need_dx=True):
-    qw = B.qlora_nf4_quantize(W, double_quant=dq)
+def _run(B, X, W, A, Bm, dY, s, dq=True, need_dx=True, code_type=0):
+    qw = B.qlora_nf4_quantize(W, double_quant=dq, code_type=code_type)
     Y, XA = B.qlora_linear_fwd(X, qw, A, Bm, s)
     dX, dA, dB = B.qlora_linear_bwd(dY, X, XA, qw, A, Bm, s, need_dx=need_dx)
     torch.cuda.synchronize()
     return qw, Y, XA, dX, dA, dB
 
 
-def _full_check(B, M, N, K, r, s, seed, dq=True, w_zero=False, b_zero=False, wscale=0.02):
+def _full_check(B, M, N, K, r, s, seed, dq=True, w_zero=False, b_zero=False, wscale=0.02, code_type=0):
     g = torch.Generator(device="cuda").manual_seed(seed)
     W = torch.randn(N, K, generator=g, device="cuda") * wscale
     if w_zero:
@@ -107,8 +112,8 @@ def _full_check(B, M, N, K, r, s, seed, dq=True, w_zero=False, b_zero=False, wsc
     if b_zero:
         Bm.zero_()
     dY = torch.randn(M, N, generator=g, device="cuda").to(torch.bfloat16)
-    qw, Y, XA, dX, dA, dB = _run(B, X, W, A, Bm, dY, s, dq)
-    Wb = OracleWeight(_np(W), dq).full()
+    qw, Y, XA, dX, dA, dB = _run(B, X, W, A, Bm, dY, s, dq, code_type=code_type)
+    Wb = OracleWeight(_np(W), dq, code_type).full()
     Yr, XAr = linear.forward(_np(X), Wb, _np(A), _np(Bm), s)
     dXr, dAr, dBr = linear.backward(_np(dY), _np(X), Wb, _np(A), _np(Bm), s)
     _assert_close("Y", _np(Y), Yr)
@@ -228,12 +233,12 @@ def test_zero_tokens(B):
 
 # ---------------------------------------------------- workload-size checks
 
-def _sampled_check(B, lin, t, Y, XA, dX, dA, dB, n_rows=48, n_kblocks=2, fwd_only=False):
+def _sampled_check(B, lin, t, Y, XA, dX, dA, dB, n_rows=48, n_kblocks=2, fwd_only=False, code_type=0):
     """Y on sampled tokens x sampled output rows, dX on sampled tokens x
     sampled 64-column blocks, dA and dB in full."""
     rng = np.random.default_rng(lin.workload * 100 + lin.layer)
     M, N, K, s = t["X"].shape[0], lin.N, lin.K, lin.s
-    ow = OracleWeight(_np(t["W"]))
+    ow = OracleWeight(_np(t["W"]), code_type=code_type)
     ms = np.unique(np.concatenate([rng.integers(0, M, min(M, 64)), [0, M - 1]]))
     ns = np.unique(np.concatenate([rng.integers(0, N, n_rows), [0, N - 1]]))
     Xs, A, Bm = _np(t["X"][torch.from_numpy(ms).cuda()]), _np(t["A"]), _np(t["B"])
@@ -281,3 +286,26 @@ def test_small_batch_forward(B):
         Y, XA = B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s)
         torch.cuda.synchronize()
         _sampled_check(B, lin, t, Y, XA, None, None, None, n_rows=256, fwd_only=True)
+
+
+# ------------------------------------- the other 4-bit storage types (G14)
+
+@pytest.mark.parametrize("code_type", [1, 2, 3])
+@pytest.mark.parametrize("M,N,K,r", [(200, 192, 320, 8), (4, 192, 64 * 40, 16)])
+def test_code_types_linear(B, code_type, M, N, K, r):
+    """FP4 E2M1 / FP4 E3M0 / Int4 weights through the tiled forward and
+    backward and through the small-token forward."""
+    _log(f"linear code_type={code_type} M={M} N={N} K={K} r={r}")
+    _full_check(B, M, N, K, r, 16.0 / r, seed=code_type * 97 + M + K, code_type=code_type)
+
+
+@pytest.mark.parametrize("code_type", [1, 3])
+def test_code_types_attention_shape(B, code_type):
+    """The 4096x4096 attention projection with 4096 tokens (the 256 x 256
+    kernels) with an FP4 E2M1 or Int4 weight, sampled."""
+    from bit_nf4_quantized_quantize_amd import synth
+    lin = synth.workload(2)[0]
+    _log(f"linear workload 2 code_type={code_type}")
+    t = lin.draw("cuda")
+    qw, Y, XA, dX, dA, dB = _run(B, t["X"], t["W"], t["A"], t["B"], t["dY"], lin.s, code_type=code_type)
+    _sampled_check(B, lin, t, Y, XA, dX, dA, dB, code_type=code_type)

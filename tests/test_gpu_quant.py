@@ -47,12 +47,12 @@ def _check_dequant(B, qw, st):
     assert np.array_equal(out16, blockwise.bf16_bits(ref)), "bf16 dequant differs"
 
 
-def _roundtrip(B, w_t, dq):
+def _roundtrip(B, w_t, dq, code_type=0):
     """Quantise w_t on the GPU and compare everything with the oracle."""
     w_np = w_t.float().cpu().numpy()
-    qw = B.qlora_nf4_quantize(w_t.cuda(), double_quant=dq)
+    qw = B.qlora_nf4_quantize(w_t.cuda(), double_quant=dq, code_type=code_type)
     torch.cuda.synchronize()
-    st = blockwise.quantize(w_np, double_quant=dq)
+    st = blockwise.quantize(w_np, double_quant=dq, code_type=code_type)
     _check_state(B, qw, st)
     _check_dequant(B, qw, st)
 
@@ -268,3 +268,41 @@ def test_empty_weight(B):
     qw = B.qlora_nf4_quantize(torch.zeros(0, 64).cuda(), double_quant=True)
     torch.cuda.synchronize()
     assert qw.numel == 0
+
+
+# ------------------------------------- the other 4-bit storage types (G14)
+
+@pytest.mark.parametrize("code_type", [1, 2, 3])
+@pytest.mark.parametrize("numel,bf16", [(64 * 300, False), (64 * 700 + 37, False), (64 * 1100 + 5, True)])
+def test_code_types_round_trip(B, code_type, numel, bf16):
+    """Codes, constants and dequantised values of FP4 E2M1 / FP4 E3M0 / Int4
+    weights, bit-exact against the oracle; sizes cover whole chunks of the
+    quantiser, its ragged tail and a short last block."""
+    _log(f"quant code_type={code_type} numel={numel} bf16={bf16}")
+    g = torch.Generator().manual_seed(numel + code_type)
+    w = torch.randn(numel, generator=g) * 0.02
+    w[64 * 3: 64 * 4] = 0.0                      # an all-zero block
+    w[64 * 5: 64 * 6] *= 1e-39                  # a subnormal block (prescaled path)
+    if bf16:
+        w = w.to(torch.bfloat16)
+    for dq in (True, False):
+        _roundtrip(B, w, dq, code_type)
+
+
+@pytest.mark.parametrize("code_type", [1, 2, 3])
+def test_code_types_decision_points(B, code_type):
+    """Blocks with absmax 1 (x = w exactly) holding every decision point of
+    the codebook and its fp32 neighbours: ties go to the smaller value."""
+    _log(f"quant code_type={code_type} decision points")
+    vals, _ = codebook.sorted_levels(codebook.CODEBOOKS[code_type])
+    xs = []
+    for a, b in zip(vals[:-1], vals[1:]):
+        m = F32((float(a) + float(b)) / 2)
+        xs += [m, np.nextafter(m, F32(-2)), np.nextafter(m, F32(2))]
+    xs = [x for x in xs if abs(float(x)) <= 1.0]
+    blocks = []
+    for i in range(0, len(xs), 63):
+        blk = np.array(xs[i:i + 63] + [1.0] * (64 - len(xs[i:i + 63])), dtype=F32)
+        blocks.append(blk)
+    w = torch.from_numpy(np.concatenate(blocks))
+    _roundtrip(B, w, False, code_type)
