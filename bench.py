@@ -52,7 +52,7 @@ DEQUANT_BYTES_PER_PARAM = STORED_BYTES_PER_PARAM + 2.0    # bf16 out
 # of known size; profiles/*_hbm_bytes.md give the commands and tables).  Valid
 # only for the kernel sources they were taken on: `traffic` is null when the
 # digest of those sources differs.
-KERNEL_SOURCES = ("csrc/linear.hip", "csrc/quantize.hip", "csrc/device.h")
+KERNEL_SOURCES = ("csrc/linear.hip", "csrc/quantize.hip", "csrc/device.h", "csrc/codebooks.h")
 TRAFFIC_DIGEST = "3e8dd6db16f078ea"
 TRAFFIC_BYTES = {
     (2, "bwd_dx"): 111.7e6 + 37.2e6,
@@ -92,6 +92,8 @@ def parse():
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0: enough for > 256 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true", help="workload 5: skip the 32-layer 7B quantise/dequantise sweep")
+    p.add_argument("--no-code-types", action="store_true",
+                   help="workload 2: skip the NF4 / FP4 E2M1 / FP4 E3M0 / Int4 comparison")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="first run a plain device copy of this many MiB three times (a known-size kernel that "
                         "calibrates hardware byte counters taken over the same run)")
@@ -258,6 +260,54 @@ def run_sweep(B, synth, dev, reps=3):
         "host_enqueue_ms": {"quantize": q_enq, "dequantize": d_enq},
         "bytes_per_param": {"quantize": QUANT_BYTES_PER_PARAM, "dequantize": DEQUANT_BYTES_PER_PARAM},
     }
+
+
+def run_code_types(B, L, dev, reps=10):
+    """Section 3's data-type comparison on the same kernels: the layer's
+    N(0, 0.02^2) fp32 weight stored as NF4, FP4 E2M1, FP4 E3M0 and Int4 (all
+    with double quantisation).  Per type: the reconstruction error of the
+    dequantised weight (||W_hat - W|| / ||W||, fp32 on the device), and the
+    median over `reps` calls of the quantise call, the bf16 dequantise call
+    and one forward + backward, each between two events."""
+    import torch
+
+    lin, t = L["lin"], L["t"]
+    W = L["W"][0]
+    bf = torch.bfloat16
+    res = {}
+
+    def med(fn):
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    for name, ct in B.CODE_TYPES.items():
+        qw = B.NF4Weight(lin.N, lin.K, True, dev, ct)
+        q_us = med(lambda: B.qlora_nf4_quantize(W, double_quant=True, out=qw, workspace=L["qws"]))
+        d_us = med(lambda: B.qlora_nf4_dequantize(qw, bf, out=L["Wd"]))
+        Wd32 = B.qlora_nf4_dequantize(qw, torch.float32)
+        err = float(torch.linalg.vector_norm((Wd32 - W).double()) / torch.linalg.vector_norm(W.double()))
+        del Wd32
+
+        def fb():
+            B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
+            B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], qw, t["A"], t["B"], lin.s,
+                               dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
+        fb_us = med(fb)
+        p = lin.N * lin.K
+        res[name] = {"rel_rms_error": err,
+                     "quantize_us": q_us, "quantize_GBps": QUANT_BYTES_PER_PARAM * p / q_us / 1e3,
+                     "dequantize_us": d_us, "dequantize_GBps": DEQUANT_BYTES_PER_PARAM * p / d_us / 1e3,
+                     "fwd_bwd_us": fb_us, "fwd_bwd_TFLOPs": linear_flops(lin) / fb_us / 1e6}
+        del qw
+    return res
 
 
 def _dominant(per, layers, small):
@@ -514,6 +564,8 @@ def main():
         fb_us = sum(b["fwd_us"] + b["bwd_us"] for b in breakdown)
         fb = sum(linear_flops(L["lin"]) for L in layers) / fb_us / 1e6
         out["fwd_bwd"] = {"TFLOP/s": fb, "frac_mfma": fb / BF16_PEAK_TFLOPS}
+        if args.workload == 2 and not args.no_code_types:
+            out["code_types"] = run_code_types(B, layers[0], dev)
     elif not args.no_sweep:
         del layers, qws
         torch.cuda.empty_cache()
