@@ -41,6 +41,10 @@ is in tests/test_oracle_pins.py):
                                normal weights)
   linear.forward / backward    pinned (brute force, finite differences,
                                special cases, torch.autograd in fp64)
+  linear.forward_dropout /
+  linear.backward_dropout      pinned (reduction to the plain layer, brute
+                               force, finite differences, torch.autograd in
+                               fp64 with the mask as a tensor)
 """
 
 from . import codebook, fp8_e4m3, blockwise, linear  # noqa: F401

@@ -53,6 +53,43 @@ def backward(dY, X, W_bf16, A, B, s):
     return dX, dA, dB
 
 
+# ------------------------------------------------------------ LoRA dropout
+# Appendix B.2 ("Hyperparameters") trains with LoRA dropout 0.1 (models up to
+# 13B) or 0.05 (33B, 65B) but does not say where it acts.  Reading G15: the
+# usual LoRA dropout on the adapter's input, with the inverted scaling that
+# keeps its expectation,
+#     Y  = X W^T + s (drop(X) A) B,   drop(X) = X * keep / (1 - p),
+# where keep [M, K] is a Bernoulli(1 - p) mask drawn by the caller (an input
+# here, so both sides see the same draws).  Its gradients:
+#     T  = dY B^T
+#     dX = dY W + s (T A^T) * keep / (1 - p)
+#     dA = s drop(X)^T T
+#     dB = s (drop(X) A)^T dY
+# and the saved XA is drop(X) A.
+
+def forward_dropout(X, W_bf16, A, B, s, keep, p):
+    """Eq. (5) with LoRA dropout on the adapter input (G15).  keep: bool or
+    0/1 array [M, K]; p: drop probability in [0, 1).  Returns (Y, XA)."""
+    X, W, A, B = _f64(X), _f64(W_bf16), _f64(A), _f64(B)
+    Xd = X * _f64(keep) / (1.0 - p)
+    XA = Xd @ A
+    Y = X @ W.T + s * (XA @ B)
+    return Y, XA
+
+
+def backward_dropout(dY, X, W_bf16, A, B, s, keep, p):
+    """Gradients of forward_dropout for the adapters and the input (G15).
+    Returns (dX, dA, dB) in fp64."""
+    dY, X, W, A, B = _f64(dY), _f64(X), _f64(W_bf16), _f64(A), _f64(B)
+    kp = _f64(keep) / (1.0 - p)
+    Xd = X * kp
+    T = dY @ B.T
+    dX = dY @ W + s * (T @ A.T) * kp
+    dA = s * (Xd.T @ T)
+    dB = s * ((Xd @ A).T @ dY)
+    return dX, dA, dB
+
+
 def flops(M, N, K, r):
     """Algorithmic flops of one forward plus one backward (no dW)."""
     return 4 * M * N * K + 6 * M * r * (K + N)

@@ -542,3 +542,86 @@ def test_pins_catch_planted_code_order_tie_rule():
     wrong = int(np.argmin(np.abs(float(x) - cb.astype(np.float64))))
     assert wrong != _nearest_bruteforce(x, cb)
     assert int(blockwise.nearest_level(np.array([x]), cb)[0]) == _nearest_bruteforce(x, cb)
+
+
+# --------------------------------------------------- LoRA dropout (G15)
+
+def _keep_mask(seed, shape, p):
+    return np.random.default_rng(seed).random(shape) >= p
+
+
+def test_dropout_reduces_to_plain_layer():
+    """An all-ones mask with p = 0 is the plain layer (forward and backward)."""
+    X, W, A, B, dY = _tiny_linear(30)
+    keep = np.ones(X.shape, dtype=bool)
+    for a, b in zip(linear.forward_dropout(X, W, A, B, 0.5, keep, 0.0), linear.forward(X, W, A, B, 0.5)):
+        assert np.array_equal(a, b)
+    for a, b in zip(linear.backward_dropout(dY, X, W, A, B, 0.5, keep, 0.0), linear.backward(dY, X, W, A, B, 0.5)):
+        assert np.allclose(a, b, rtol=1e-15, atol=0)
+
+
+def test_dropout_forward_brute_force_loops():
+    X, W, A, B, _ = _tiny_linear(31)
+    s, p = 0.75, 0.25
+    keep = _keep_mask(1, X.shape, p)
+    Y, XA = linear.forward_dropout(X, W, A, B, s, keep, p)
+    M, K = X.shape
+    N, r = W.shape[0], A.shape[1]
+    for m, n in itertools.product(range(M), range(N)):
+        base = sum(X[m, k] * W[n, k] for k in range(K))
+        xa = [sum(X[m, k] * (1.0 if keep[m, k] else 0.0) / (1 - p) * A[k, j] for k in range(K)) for j in range(r)]
+        assert math.isclose(Y[m, n], base + s * sum(xa[j] * B[j, n] for j in range(r)), rel_tol=1e-12, abs_tol=1e-12)
+        for j in range(r):
+            assert math.isclose(XA[m, j], xa[j], rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_dropout_backward_finite_differences():
+    """With the mask fixed the layer is linear in X, A and B: central
+    differences of L = sum(dY * Y) match the analytic gradients."""
+    X, W, A, B, dY = _tiny_linear(32)
+    s, p = 0.5, 0.1
+    keep = _keep_mask(2, X.shape, p)
+    dX, dA, dB = linear.backward_dropout(dY, X, W, A, B, s, keep, p)
+
+    def loss(X_, A_, B_):
+        return float(np.sum(dY * linear.forward_dropout(X_, W, A_, B_, s, keep, p)[0]))
+
+    h = 1e-6
+    for name, arr, grad in (("X", X, dX), ("A", A, dA), ("B", B, dB)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            pl, mi = arr.copy(), arr.copy()
+            pl[idx] += h
+            mi[idx] -= h
+            args = {"X": X, "A": A, "B": B}
+            args[name] = pl
+            lp = loss(args["X"], args["A"], args["B"])
+            args[name] = mi
+            lm = loss(args["X"], args["A"], args["B"])
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), name
+
+
+def test_dropout_backward_matches_torch_autograd_fp64():
+    X, W, A, B, dY = _tiny_linear(33, M=6, K=16, N=7, r=3)
+    s, p = 0.25, 0.05
+    keep = _keep_mask(3, X.shape, p)
+    tX, tA, tB = (torch.tensor(v, dtype=torch.float64, requires_grad=True) for v in (X, A, B))
+    tW, tk = torch.tensor(W, dtype=torch.float64), torch.tensor(keep, dtype=torch.float64)
+    Y = tX @ tW.T + s * ((tX * tk / (1 - p)) @ tA) @ tB
+    (Y * torch.tensor(dY)).sum().backward()
+    dX, dA, dB = linear.backward_dropout(dY, X, W, A, B, s, keep, p)
+    assert np.allclose(dX, tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dA, tA.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_pins_catch_planted_dropout_mistake(monkeypatch):
+    """A dX that forgets to mask the adapter term fails the finite-difference pin."""
+    X, W, A, B, dY = _tiny_linear(34)
+    s, p = 0.5, 0.2
+    keep = _keep_mask(4, X.shape, p)
+    good = linear.backward_dropout(dY, X, W, A, B, s, keep, p)
+    T = dY @ B.T
+    bad_dX = dY @ W + s * (T @ A.T) / (1 - p)
+    assert not np.allclose(bad_dX, good[0], rtol=1e-6, atol=1e-7)
