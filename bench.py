@@ -310,6 +310,39 @@ def run_code_types(B, L, dev, reps=10):
     return res
 
 
+def run_dropout(B, L, dev, p=0.1, reps=10):
+    """LoRA dropout on the adapter input (QLoRA Appendix B.2 uses p = 0.1 up
+    to 13B): forward + backward of the layer with a Bernoulli(1 - p) keep
+    mask drawn once on the device, against the same calls without dropout.
+    Median over `reps` pairs of calls between two events."""
+    import torch
+
+    lin, t = L["lin"], L["t"]
+    g = torch.Generator(device=dev).manual_seed(11)
+    keep = B.pack_keep_mask(torch.rand(lin.M, lin.K, generator=g, device=dev) >= p)
+    qw = L["qw"]
+
+    def fb(kw):
+        B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"], **kw)
+        B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], qw, t["A"], t["B"], lin.s,
+                           dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"], **kw)
+
+    out = {"p": p}
+    for name, kw in (("dropout", {"keep": keep, "p": p}), ("plain", {})):
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fb(kw)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = sorted(ts[1:])
+        us = ts[len(ts) // 2]
+        out[name] = {"fwd_bwd_us": us, "fwd_bwd_TFLOPs": linear_flops(lin) / us / 1e6}
+    return out
+
+
 def _dominant(per, layers, small):
     """(kernel, bound, algorithmic work, mean us, linear index) of the kernel
     with the largest share of the step, from a per-linear kernel breakdown.
@@ -566,6 +599,7 @@ def main():
         out["fwd_bwd"] = {"TFLOP/s": fb, "frac_mfma": fb / BF16_PEAK_TFLOPS}
         if args.workload == 2 and not args.no_code_types:
             out["code_types"] = run_code_types(B, layers[0], dev)
+            out["lora_dropout"] = run_dropout(B, layers[0], dev)
     elif not args.no_sweep:
         del layers, qws
         torch.cuda.empty_cache()

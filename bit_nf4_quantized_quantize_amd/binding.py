@@ -42,6 +42,7 @@ EXPORTED = (
     "qlora_nf4_storage_bytes", "qlora_nf4_quantize_workspace", "qlora_linear_workspace",
     "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string", "qlora_last_error",
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
     "qlora_profile_events",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
@@ -96,6 +97,10 @@ def lib():
         "qlora_nf4_dequantize": (_i32, [_pdesc, _vp, _i32, _vp]),
         "qlora_linear_fwd": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i64, _vp]),
         "qlora_linear_bwd": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
+        "qlora_linear_fwd_dropout": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp, _vp, _i64,
+                                            _vp]),
+        "qlora_linear_bwd_dropout": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp,
+                                            _vp, _vp, _i64, _vp]),
         "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
@@ -291,14 +296,37 @@ def _ws(nbytes, device, ws):
     return ws.get(nbytes, device)
 
 
-def qlora_linear_fwd(X, q, A, B, s, save_xa=True, Y=None, XA=None, workspace=None, stream=None):
-    """Y = X W_bf16^T + s (X A) B.  Returns (Y, XA or None)."""
+def pack_keep_mask(keep):
+    """Bit-pack a boolean keep mask [M, K] (K % 8 == 0) into the uint8 [M, K/8]
+    layout the dropout entry points take: bit j of byte (m, c) is keep[m, 8c + j]."""
+    if keep.dtype != torch.bool or keep.dim() != 2 or keep.shape[1] % 8:
+        raise ValueError("keep must be a bool [M, K] tensor with K % 8 == 0")
+    w = (1 << torch.arange(8, device=keep.device, dtype=torch.int32))
+    return (keep.view(keep.shape[0], -1, 8).to(torch.int32) * w).sum(-1).to(torch.uint8).contiguous()
+
+
+def _keep_arg(keep, X, p):
+    if keep is None:
+        return None
+    _need_cuda(keep)
+    if keep.dtype != torch.uint8 or tuple(keep.shape) != (X.shape[0], X.shape[1] // 8) or not keep.is_contiguous():
+        raise ValueError("keep must be a contiguous uint8 [M, K/8] bit mask (see pack_keep_mask)")
+    if not 0.0 <= float(p) < 1.0:
+        raise ValueError("dropout p must be in [0, 1)")
+    return keep
+
+
+def qlora_linear_fwd(X, q, A, B, s, save_xa=True, Y=None, XA=None, workspace=None, stream=None, keep=None, p=0.0):
+    """Y = X W_bf16^T + s (X A) B.  Returns (Y, XA or None).  With `keep`
+    (a pack_keep_mask bit mask of X) and drop probability p the adapter sees
+    X * keep / (1 - p) (LoRA dropout)."""
     _need_cuda(X, A, B)
     M, K = X.shape
     N, r = q.rows, A.shape[1]
     _bf16_2d(X, "X", (M, q.cols))
     _bf16_2d(A, "A", (K, r))
     _bf16_2d(B, "B", (r, N))
+    keep = _keep_arg(keep, X, p)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     if save_xa and XA is None:
@@ -306,17 +334,26 @@ def qlora_linear_fwd(X, q, A, B, s, save_xa=True, Y=None, XA=None, workspace=Non
     nws, _ = qlora_linear_workspace(M, N, K, r)
     ws = _ws(nws, X.device, workspace)
     d = q.desc()
-    _check(lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s), _ptr(Y),
-                                  _ptr(XA) if save_xa else None, _ptr(ws), ws.numel(), _stream(stream)),
-           "qlora_linear_fwd")
+    if keep is None:
+        _check(lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s), _ptr(Y),
+                                      _ptr(XA) if save_xa else None, _ptr(ws), ws.numel(), _stream(stream)),
+               "qlora_linear_fwd")
+    else:
+        _check(lib().qlora_linear_fwd_dropout(_ptr(X), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s),
+                                              _ptr(keep), float(p), _ptr(Y), _ptr(XA) if save_xa else None,
+                                              _ptr(ws), ws.numel(), _stream(stream)),
+               "qlora_linear_fwd_dropout")
     return Y, (XA if save_xa else None)
 
 
-def qlora_linear_bwd(dY, X, XA, q, A, B, s, need_dx=True, dX=None, dA=None, dB=None, workspace=None, stream=None):
-    """Returns (dX or None, dA, dB) for Y = X W_bf16^T + s (X A) B."""
+def qlora_linear_bwd(dY, X, XA, q, A, B, s, need_dx=True, dX=None, dA=None, dB=None, workspace=None, stream=None,
+                     keep=None, p=0.0):
+    """Returns (dX or None, dA, dB) for Y = X W_bf16^T + s (X A) B; with
+    `keep` and p, the gradients of the dropout forward (same mask)."""
     _need_cuda(dY, X, XA, A, B)
     M, K = X.shape
     N, r = q.rows, A.shape[1]
+    keep = _keep_arg(keep, X, p)
     _bf16_2d(dY, "dY", (M, N))
     _bf16_2d(X, "X", (M, q.cols))
     _bf16_2d(XA, "XA", (M, r))
@@ -332,8 +369,14 @@ def qlora_linear_bwd(dY, X, XA, q, A, B, s, need_dx=True, dX=None, dA=None, dB=N
     _, nws = qlora_linear_workspace(M, N, K, r)
     ws = _ws(nws, dev, workspace)
     d = q.desc()
-    _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(XA), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s),
-                                  _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
-                                  _stream(stream)),
-           "qlora_linear_bwd")
+    if keep is None:
+        _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(XA), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s),
+                                      _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                      _stream(stream)),
+               "qlora_linear_bwd")
+    else:
+        _check(lib().qlora_linear_bwd_dropout(_ptr(dY), _ptr(X), _ptr(XA), M, ctypes.byref(d), _ptr(A), _ptr(B), r,
+                                              float(s), _ptr(keep), float(p), _ptr(dX) if need_dx else None,
+                                              _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
+               "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB

@@ -290,12 +290,29 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, voi
   return QLORA_OK;
 }
 
-int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void* A, const void* B, int32_t r, float s,
-                     void* Y, void* XA, void* ws, int64_t ws_bytes, void* stream) {
-  static const char* fn = "qlora_linear_fwd";
+}  // extern "C"
+
+namespace {
+
+// 1 / (1 - p) in fp32: the inverted-dropout scale of the kept elements.
+float keep_scale_of(float p) { return (float)(1.0 / (1.0 - (double)p)); }
+
+int check_dropout(const void* keep, float p, const char* fn) {
+  if (!keep) return QLORA_OK;
+  if (!(p >= 0.0f && p < 1.0f)) return fail(QLORA_ERR_INVALID_ARG, "%s: dropout p must be in [0, 1)", fn);
+  return check_ptr(keep, "keep_mask", fn);
+}
+
+// The forward with optional LoRA dropout (keep = null: none).
+int linear_fwd_impl(const void* X, int64_t M, const qlora_nf4_t* W, const void* A, const void* B, int32_t r, float s,
+                    const void* keep, float p, void* Y, void* XA, void* ws, int64_t ws_bytes, void* stream,
+                    const char* fn) {
   int st = check_linear_shape(W, M, r, fn);
   if (st) return st;
+  if ((st = check_dropout(keep, p, fn))) return st;
   if (M == 0) return QLORA_OK;
+  const uint8_t* km = (const uint8_t*)keep;
+  const float d = km ? keep_scale_of(p) : 1.0f;
   if ((st = check_ptr(X, "X", fn)) || (st = check_ptr(A, "A", fn)) || (st = check_ptr(B, "B", fn)) ||
       (st = check_ptr(Y, "Y", fn)))
     return st;
@@ -313,7 +330,7 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
     // few tokens: partials of X A, the weight-streaming product, then one
     // kernel that adds both sets of partials and the adapter term
     if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, nullptr, nullptr,
-                           rp, s, hs)) != hipSuccess)
+                           rp, s, 1.0f, km, hs)) != hipSuccess)
       return hip_fail(e, fn);
     float* gv = (float*)(base + L.gv);
     {
@@ -321,14 +338,14 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
       e = launch_gemv((const uint16_t*)X, M, K, W->codes, dq_params(W), N, gv, L.gemv_splits, hs);
     }
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, part, L.splits, rp, s, (const uint16_t*)B, r, (uint16_t*)Y,
+    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, part, L.splits, rp, s * d, d, (const uint16_t*)B, r, (uint16_t*)Y,
                            (uint16_t*)XA, hs);
     if (e != hipSuccess) return hip_fail(e, fn);
     return QLORA_OK;
   }
   // XA = X A [M, r]: bf16 copy for the backward, bf16(s XA) padded to rp for the adapter steps
   if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, (uint16_t*)XA, xas, rp,
-                         s, hs)) != hipSuccess)
+                         s * d, d, km, hs)) != hipSuccess)
     return hip_fail(e, fn);
   {
     ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
@@ -339,12 +356,15 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void*
   return QLORA_OK;
 }
 
-int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W, const void* A,
-                     const void* B, int32_t r, float s, void* dX, void* dA, void* dB, void* ws, int64_t ws_bytes,
-                     void* stream) {
-  static const char* fn = "qlora_linear_bwd";
+// The backward with optional LoRA dropout (keep = null: none).
+int linear_bwd_impl(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W, const void* A,
+                    const void* B, int32_t r, float s, const void* keep, float p, void* dX, void* dA, void* dB,
+                    void* ws, int64_t ws_bytes, void* stream, const char* fn) {
   int st = check_linear_shape(W, M, r, fn);
   if (st) return st;
+  if ((st = check_dropout(keep, p, fn))) return st;
+  const uint8_t* km = (const uint8_t*)keep;
+  const float d = km ? keep_scale_of(p) : 1.0f;
   if ((st = check_ptr(dA, "dA", fn)) || (st = check_ptr(dB, "dB", fn))) return st;
   const int64_t N = W->rows, K = W->cols, rp = round_up(r, 64);
   hipStream_t hs = (hipStream_t)stream;
@@ -367,22 +387,54 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, c
   float* part = (float*)(base + L.part);
   // s*T = s * dY B^T  [M, rp]
   if ((e = launch_skinny((const uint16_t*)dY, (const uint16_t*)B, false, M, r, N, part_t, L.splits_t, nullptr, ts, rp,
-                         s, hs)) != hipSuccess)
+                         s, 1.0f, nullptr, hs)) != hipSuccess)
     return hip_fail(e, fn);
   if (dX) {
     {
       ProfScope ps(QLORA_KERNEL_BWD_DX, hs);
       e = launch_bwd_dx((const uint16_t*)dY, M, N, W->codes, dq_params(W), K, ts, (const uint16_t*)A, r, rp,
-                        (uint16_t*)dX, part, hs);
+                        (uint16_t*)dX, part, km, d, hs);
     }
     if (e != hipSuccess) return hip_fail(e, fn);
   }
   // dA = X^T (s T) [K, r] and dB^T = s dY^T XA [N, r] (written as dB [r, N])
-  if ((e = launch_tn_pair((const uint16_t*)X, K, K, ts, rp, r, part, L.splits_a, (uint16_t*)dA, 1.0f,
+  if ((e = launch_tn_pair((const uint16_t*)X, K, K, km, ts, rp, r, part, L.splits_a, (uint16_t*)dA, d,
                           (const uint16_t*)dY, N, N, (const uint16_t*)XA, r, r,
                           (float*)((char*)part + L.part_b), L.splits_b, (uint16_t*)dB, s, M, hs)) != hipSuccess)
     return hip_fail(e, fn);
   return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W, const void* A, const void* B, int32_t r, float s,
+                     void* Y, void* XA, void* ws, int64_t ws_bytes, void* stream) {
+  return linear_fwd_impl(X, M, W, A, B, r, s, nullptr, 0.0f, Y, XA, ws, ws_bytes, stream, "qlora_linear_fwd");
+}
+
+int qlora_linear_fwd_dropout(const void* X, int64_t M, const qlora_nf4_t* W, const void* A, const void* B, int32_t r,
+                             float s, const void* keep_mask, float p, void* Y, void* XA, void* ws, int64_t ws_bytes,
+                             void* stream) {
+  static const char* fn = "qlora_linear_fwd_dropout";
+  if (!keep_mask) return fail(QLORA_ERR_INVALID_ARG, "%s: keep_mask is NULL", fn);
+  return linear_fwd_impl(X, M, W, A, B, r, s, keep_mask, p, Y, XA, ws, ws_bytes, stream, fn);
+}
+
+int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W, const void* A,
+                     const void* B, int32_t r, float s, void* dX, void* dA, void* dB, void* ws, int64_t ws_bytes,
+                     void* stream) {
+  return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, nullptr, 0.0f, dX, dA, dB, ws, ws_bytes, stream,
+                         "qlora_linear_bwd");
+}
+
+int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W,
+                             const void* A, const void* B, int32_t r, float s, const void* keep_mask, float p,
+                             void* dX, void* dA, void* dB, void* ws, int64_t ws_bytes, void* stream) {
+  static const char* fn = "qlora_linear_bwd_dropout";
+  if (!keep_mask) return fail(QLORA_ERR_INVALID_ARG, "%s: keep_mask is NULL", fn);
+  return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, keep_mask, p, dX, dA, dB, ws, ws_bytes, stream, fn);
 }
 
 }  // extern "C"

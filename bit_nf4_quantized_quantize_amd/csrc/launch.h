@@ -78,13 +78,15 @@ struct DQParams {
 //
 // Skinny product C[M, Q] = U[M, L] * V, V either [L, Q] (v_is_lq) or
 // [Q, L]; the reduction is split into `splits` chunks of fp32 partials
-// part[splits][M][QP], then out1 [M, Q] = bf16(C) (optional) and
+// part[splits][M][QP], then out1 [M, Q] = bf16(scale1 * C) (optional) and
 // out2 [M, QP] = bf16(alpha * C), zero in columns [Q, QP).  With out1 and
-// out2 both null only the partials are written.
+// out2 both null only the partials are written.  With `keep` (a bit mask
+// [M, L/8], bit j of byte (m, c) for U[m, 8c + j]; L % 8 == 0) the elements
+// of U whose bit is clear count as zero (LoRA dropout).
 int skinny_splits(int64_t M, int64_t Q, int64_t L);
 hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
                          float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
-                         hipStream_t stream);
+                         float scale1, const uint8_t* keep, hipStream_t stream);
 // Workspace bytes of the fp32 partial tiles a main product [M, ncols] with
 // reduction length L uses (0 when no tile is split).
 int64_t main_split_bytes(int64_t M, int64_t ncols, int64_t L);
@@ -96,26 +98,31 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
 // fp32 partials part[splits][M][N] of X * W_bf16^T over reduction splits;
 // launch_gemv_reduce adds them, forms C = X A from the skinny partials
 // xpart[xsplits][M][rp] (rp <= 256), and writes Y = bf16(sum + bf16(alpha C) * B)
-// and, when XA is given, XA = bf16(C) [M, r].
+// and, when XA is given, XA = bf16(scale1 C) [M, r].
 constexpr int kGemvMaxM = 16;
 int gemv_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
                        float* part, int splits, hipStream_t stream);
 hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const float* xpart, int xsplits,
-                              int64_t rp, float alpha, const uint16_t* B, int64_t r, uint16_t* Y, uint16_t* XA,
-                              hipStream_t stream);
-// Fused input gradient: dX = dY * W_bf16 + Ts * A_pad^T (Ts [M, rp]; A [K, r]).
+                              int64_t rp, float alpha, float scale1, const uint16_t* B, int64_t r, uint16_t* Y,
+                              uint16_t* XA, hipStream_t stream);
+// Fused input gradient: dX = dY * W_bf16 + Ts * A_pad^T (Ts [M, rp]; A [K, r]);
+// with `keep` (bit mask [M, K/8] as for launch_skinny) the adapter term is
+// multiplied by keep_scale where the bit is set and dropped where it is clear.
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                          const DQParams& dq, int64_t K, const uint16_t* Ts, const uint16_t* A,
-                         int64_t r, int64_t rp, uint16_t* dX, float* split_ws, hipStream_t stream);
+                         int64_t r, int64_t rp, uint16_t* dX, float* split_ws, const uint8_t* keep,
+                         float keep_scale, hipStream_t stream);
 // Two token reductions, one launch for both products and one for both
 // epilogues: C_a [Pa, Qa] = U_a[M, Pa]^T * V_a[M, Qa] and C_b likewise
 // (leading dimensions ld*), fp32 partials part_x [splits_x][P][Q], then
 // out_a [Pa, Qa] = bf16(alpha_a * sum) and out_b = bf16(alpha_b * sum) written
-// transposed, [Qb, Pb].
+// transposed, [Qb, Pb].  keep_a (optional, bit mask [M, ldua/8]) zeroes
+// elements of U_a as for launch_skinny.
 int tn_splits(int64_t M, int64_t P, int64_t Q);
-hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint16_t* Va, int64_t ldva, int64_t Qa,
-                          float* part_a, int splits_a, uint16_t* out_a, float alpha_a, const uint16_t* Ub,
+hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint8_t* keep_a, const uint16_t* Va,
+                          int64_t ldva, int64_t Qa, float* part_a, int splits_a, uint16_t* out_a, float alpha_a,
+                          const uint16_t* Ub,
                           int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb, float* part_b,
                           int splits_b, uint16_t* out_b, float alpha_b, int64_t M, hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);

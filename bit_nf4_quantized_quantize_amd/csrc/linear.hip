@@ -100,7 +100,36 @@ struct MainArgs {
   // partial tiles go to part[unit][256][256]; a fixup pass adds them.
   int full_tiles, split;
   float* part;
+  // LoRA dropout (backward only): bit mask [M, ncols/8] of the adapter term,
+  // kept elements multiplied by keep_scale; null without dropout
+  const uint8_t* keep;
+  float keep_scale;
 };
+
+// Zeroes the bf16 elements of an 8-element chunk whose keep bit is clear
+// (bit j of `keep` for element j).
+__device__ __forceinline__ uint4 apply_keep8(uint4 v, uint32_t keep) {
+  auto m2 = [&](int j) -> uint32_t {  // elements 2j (low half) and 2j + 1 (high half)
+    return (((keep >> (2 * j)) & 1u) ? 0x0000FFFFu : 0u) | (((keep >> (2 * j + 1)) & 1u) ? 0xFFFF0000u : 0u);
+  };
+  return make_uint4(v.x & m2(0), v.y & m2(1), v.z & m2(2), v.w & m2(3));
+}
+
+// One 32 x 32 accumulator tile (MFMA layout) at rows r0.., columns c0..:
+// element (row, col) times `scale` where bit col % 8 of keep[row * pitch +
+// col / 8] is set, zero where it is clear (rows and columns clamped to the
+// matrix, whose values outside are not stored).
+__device__ __forceinline__ void mask_acc32(floatx16& acc, int lane, int64_t r0, int64_t c0, int64_t M, int64_t ncols,
+                                           const uint8_t* __restrict__ keep, float scale) {
+  const int64_t col = c0 + (lane & 31) < ncols ? c0 + (lane & 31) : ncols - 1;
+  const int64_t pitch = ncols >> 3;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t row = r0 + acc_row32(e, lane) < M ? r0 + acc_row32(e, lane) : M - 1;
+    const uint32_t b = keep[row * pitch + (col >> 3)];
+    acc[e] = ((b >> (col & 7)) & 1u) ? acc[e] * scale : 0.0f;
+  }
+}
 
 template <int BM, int BN, bool BWD>
 struct MainCfg {
@@ -216,19 +245,8 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
     }
   };
 
-  // ---- main reduction over the quantised weight, two LDS stages
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nk) load_step(kt + 1);
-    mma_step(cur, BWD, BWD ? C::PRC : PK);
-    if (kt + 1 < nk) store_step(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- adapter term: rp/64 extra reduction steps over bf16 operands
+  // ---- adapter term first: rp/64 reduction steps over bf16 operands (both
+  // LDS stages are free), masked for LoRA dropout before the weight term
   for (int64_t jt = 0; jt < a.rp; jt += 64) {
 #pragma unroll
     for (int i = 0; i < C::XCH; ++i) {
@@ -251,6 +269,27 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
     }
     __syncthreads();
     mma_step(0, !BWD, BWD ? PK : C::PRC);
+    __syncthreads();
+  }
+
+  if (BWD && a.keep) {
+#pragma unroll
+    for (int i = 0; i < C::TMW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TNW; ++j)
+        mask_acc32(acc[i][j], lane, m0 + wm * C::WM + 32 * i, c0 + wn * C::WN + 32 * j, a.M, a.ncols, a.keep,
+                   a.keep_scale);
+  }
+
+  // ---- main reduction over the quantised weight, two LDS stages
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt & 1);
+    if (kt + 1 < nk) load_step(kt + 1);
+    mma_step(cur, BWD, BWD ? C::PRC : PK);
+    if (kt + 1 < nk) store_step(cur ^ 1);
     __syncthreads();
   }
 
@@ -718,34 +757,8 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
     __syncthreads();
   };
 
-  // ---- prologue: stage 0 filled; X(ks+1) and codes(ks+1) in flight
-  load_codes(ks, cwB, qbB, sfB);
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks));
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
-  {
-    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
-    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f, cv);
-    const uint32_t words[4] = {cwB.x, cwB.y, cwB.z, cwB.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t o[4];
-      lut_lookup8(lut, words[w], o);
-      sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
-    }
-  }
-  load_codes(ks + 1 < nk ? ks + 1 : ks, cwA, qbA, sfA);
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks + 1 < nk ? ks + 1 : ks));
-  __syncthreads();
-
-  for (int kt = ks; kt < nk; kt += 2) {
-    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
-    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
-  }
-
-  // ---- adapter term over bf16 operands (stage 0 is free)
+  // ---- adapter term first, over bf16 operands (both stages are free), masked
+  // for LoRA dropout before the weight term is added
   for (int64_t jt = 0; last_range && jt < a.rp; jt += 64) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -776,6 +789,42 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[0][i], fb[0][j], acc[i][j]);
     }
     __syncthreads();
+  }
+
+  if (BWD && a.keep && last_range) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        mask_acc32(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 64 + 32 * j, a.M, a.ncols, a.keep,
+                   a.keep_scale);
+  }
+
+  // ---- prologue: stage 0 filled; X(ks+1) and codes(ks+1) in flight
+  load_codes(ks, cwB, qbB, sfB);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks));
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
+  {
+    const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
+    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f, cv);
+    const uint32_t words[4] = {cwB.x, cwB.y, cwB.z, cwB.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o[4];
+      lut_lookup8(lut, words[w], o);
+      sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
+  load_codes(ks + 1 < nk ? ks + 1 : ks, cwA, qbA, sfA);
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks + 1 < nk ? ks + 1 : ks));
+  __syncthreads();
+
+  for (int kt = ks; kt < nk; kt += 2) {
+    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
+    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
   }
 
   // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
@@ -830,7 +879,8 @@ constexpr int SK_PV = 64 + kRcPad; // [128][64] transposed-read pitch
 template <bool NN>
 __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__ U, int64_t M, int64_t L,
                                                     const uint16_t* __restrict__ V, int64_t Q, int64_t chunk,
-                                                    float* __restrict__ part, int64_t QP) {
+                                                    float* __restrict__ part, int64_t QP,
+                                                    const uint8_t* __restrict__ keep) {
   constexpr int SV = NN ? SK_BK * SK_PV : 64 * SK_PU;
   __shared__ __attribute__((aligned(16))) __bf16 sU[64 * SK_PU];
   __shared__ __attribute__((aligned(16))) __bf16 sV[SV];
@@ -843,6 +893,8 @@ __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
   uint4 ru[4], rv[4];
+  uint32_t kb[4] = {0xFFu, 0xFFu, 0xFFu, 0xFFu};  // keep bits of the U chunks (dropout)
+  const int64_t kpitch = L >> 3;
   // whole, aligned tiles (the usual case) load without per-element checks, so
   // that all loads of a tile are in flight together
   const bool inner = m0 + 64 <= M && q0 + 64 <= Q && (L & 7) == 0 && (Q & 7) == 0;
@@ -852,6 +904,7 @@ __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__
       for (int i = 0; i < 4; ++i) {
         const int id = tid + NT * i;
         ru[i] = ldg16(U + (m0 + (id >> 4)) * L + lt + (id & 15) * 8);
+        if (keep) kb[i] = keep[(m0 + (id >> 4)) * kpitch + ((lt >> 3) + (id & 15))];
         rv[i] = NN ? ldg16(V + (lt + (id >> 3)) * Q + q0 + (id & 7) * 8)
                    : ldg16(V + (q0 + (id >> 4)) * L + lt + (id & 15) * 8);
       }
@@ -864,6 +917,7 @@ __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__
         const int row = id >> 4, ch = id & 15;
         const int64_t m = m0 + row, l = lt + ch * 8;
         ru[i] = (m < M && l < lend) ? ldg16(U + m * L + l) : make_uint4(0, 0, 0, 0);
+        if (keep && m < M && l < lend) kb[i] = keep[m * kpitch + (l >> 3)];
       }
       if (NN) {  // V tile [128 l][64 q]
         const int row = id >> 3, ch = id & 7;
@@ -879,7 +933,7 @@ __global__ __launch_bounds__(NT) void skinny_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int id = tid + NT * i;
-      sts16(&sU[(id >> 4) * SK_PU + (id & 15) * 8], ru[i]);
+      sts16(&sU[(id >> 4) * SK_PU + (id & 15) * 8], keep ? apply_keep8(ru[i], kb[i]) : ru[i]);
       if (NN) sts16(&sV[(id >> 3) * SK_PV + (id & 7) * 8], rv[i]);
       else sts16(&sV[(id >> 4) * SK_PU + (id & 15) * 8], rv[i]);
     }
@@ -950,11 +1004,13 @@ __device__ __forceinline__ float4 split_sum4(const float* part, int S, int64_t n
 }
 
 // XA-style epilogue: out2 [M, QP] = bf16(alpha * C) (C zero in columns
-// >= Q), out1 [M, Q] = bf16(C) when given.  part is [S][M][QP], QP % 64 == 0.
+// >= Q), out1 [M, Q] = bf16(scale1 * C) when given.  part is [S][M][QP],
+// QP % 64 == 0.
 template <int T>
 __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ part, int S, int64_t M,
                                                               int64_t Q, int64_t QP, uint16_t* __restrict__ out1,
-                                                              uint16_t* __restrict__ out2, float alpha) {
+                                                              uint16_t* __restrict__ out2, float alpha,
+                                                              float scale1) {
   __shared__ float4 red[T > 1 ? 256 : 1];
   constexpr int CPW = 256 / T;
   const int t = threadIdx.x / CPW;
@@ -971,7 +1027,7 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
   if (out1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (q + e < Q) out1[m * Q + q + e] = f2bf(sv[e]);
+      if (q + e < Q) out1[m * Q + q + e] = f2bf(scale1 * sv[e]);
   }
 }
 
@@ -986,7 +1042,8 @@ struct TnProblem {
   const uint16_t* U;
   const uint16_t* V;
   int64_t ldu, ldv, P, Q, M, chunk;
-  float* part;  // [splits][P][Q]
+  float* part;          // [splits][P][Q]
+  const uint8_t* keep;  // dropout bit mask [M, ldu/8] of U, or null
 };
 
 template <int BP, int BQ>
@@ -999,6 +1056,7 @@ __global__ __launch_bounds__(NT) void tn_kernel(const TnProblem pa, const TnProb
   const uint16_t* __restrict__ V = pr.V;
   const int64_t ldu = pr.ldu, ldv = pr.ldv, P = pr.P, Q = pr.Q, M = pr.M, chunk = pr.chunk;
   float* __restrict__ part = pr.part;
+  const uint8_t* __restrict__ keep = pr.keep;
   if ((int64_t)blockIdx.x * BP >= P || (int64_t)blockIdx.y * BQ >= Q) return;  // outside this problem's grid
   constexpr int PU = BP + kRcPad, PV = BQ + kRcPad;
   constexpr int TMW = BP / 64, TNW = BQ / 64;
@@ -1018,6 +1076,10 @@ __global__ __launch_bounds__(NT) void tn_kernel(const TnProblem pa, const TnProb
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   uint4 ru[CU_], rv[CV_];
+  uint32_t kb[CU_];  // keep bits of the U chunks (dropout)
+#pragma unroll
+  for (int i = 0; i < CU_; ++i) kb[i] = 0xFFu;
+  const int64_t kpitch = ldu >> 3;
   // whole, aligned tiles (the usual case) load without per-element checks, so
   // that all loads of a tile are in flight together
   const bool inner = p0 + BP <= P && q0 + BQ <= Q && (ldu & 7) == 0 && (ldv & 7) == 0;
@@ -1027,6 +1089,7 @@ __global__ __launch_bounds__(NT) void tn_kernel(const TnProblem pa, const TnProb
       for (int i = 0; i < CU_; ++i) {
         const int id = tid + NT * i, row = id / (BP / 8), ch = id % (BP / 8);
         ru[i] = ldg16(U + (mt + row) * ldu + p0 + ch * 8);
+        if (keep) kb[i] = keep[(mt + row) * kpitch + ((p0 >> 3) + ch)];
       }
 #pragma unroll
       for (int i = 0; i < CV_; ++i) {
@@ -1039,6 +1102,7 @@ __global__ __launch_bounds__(NT) void tn_kernel(const TnProblem pa, const TnProb
     for (int i = 0; i < CU_; ++i) {
       const int id = tid + NT * i, row = id / (BP / 8), ch = id % (BP / 8);
       ru[i] = load8_masked(U, ldu, mt + row, mend, p0 + ch * 8, P);
+      if (keep && mt + row < mend && p0 + ch * 8 < P) kb[i] = keep[(mt + row) * kpitch + ((p0 >> 3) + ch)];
     }
 #pragma unroll
     for (int i = 0; i < CV_; ++i) {
@@ -1051,7 +1115,7 @@ __global__ __launch_bounds__(NT) void tn_kernel(const TnProblem pa, const TnProb
 #pragma unroll
     for (int i = 0; i < CU_; ++i) {
       const int id = tid + NT * i;
-      sts16(&sU[(id / (BP / 8)) * PU + (id % (BP / 8)) * 8], ru[i]);
+      sts16(&sU[(id / (BP / 8)) * PU + (id % (BP / 8)) * 8], keep ? apply_keep8(ru[i], kb[i]) : ru[i]);
     }
 #pragma unroll
     for (int i = 0; i < CV_; ++i) {
@@ -1370,13 +1434,14 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
 // Y[m, n] = bf16(sum_s part[s][m][n] + sum_j XAs[m, j] B[j, n]), with the
 // adapter input formed here from the fp32 partials of X A, xpart[SX][M][rp]:
 // C = sum of the slices, XAs = bf16(alpha C) (columns >= r are zero
-// partials), and XA = bf16(C) [M, r] written by the blocks with
+// partials), and XA = bf16(scale1 C) [M, r] written by the blocks with
 // blockIdx.x == 0 when XA is given.  One token row per blockIdx.y, 4 columns
 // per thread (N % 4 == 0), rp <= 256.
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int S, int M, int64_t N,
                                                           const float* __restrict__ xpart, int SX, int rp,
-                                                          float alpha, const uint16_t* __restrict__ B, int r,
-                                                          uint16_t* __restrict__ Y, uint16_t* __restrict__ XA) {
+                                                          float alpha, float scale1, const uint16_t* __restrict__ B,
+                                                          int r, uint16_t* __restrict__ Y,
+                                                          uint16_t* __restrict__ XA) {
   __shared__ float4 xsum[256];  // [group][rp / 4]
   __shared__ float xas[256];
   const int tid = threadIdx.x, m = blockIdx.y;
@@ -1398,7 +1463,7 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
     float c = 0.0f;
     for (int w = 0; w < G; ++w) c += xs[w * rp + j];
     xas[j] = bf2f(f2bf(alpha * c));
-    if (XA != nullptr && blockIdx.x == 0 && j < r) XA[(int64_t)m * r + j] = f2bf(c);
+    if (XA != nullptr && blockIdx.x == 0 && j < r) XA[(int64_t)m * r + j] = f2bf(scale1 * c);
   }
   __syncthreads();
   const int64_t nc = ((int64_t)blockIdx.x * 256 + tid) * 4;
@@ -1541,21 +1606,22 @@ int skinny_splits(int64_t M, int64_t Q, int64_t L) {
 
 hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
                          float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
-                         hipStream_t stream) {
+                         float scale1, const uint8_t* keep, hipStream_t stream) {
+  if (keep && (L & 7)) return hipErrorInvalidValue;
   int64_t chunk = (L + splits - 1) / splits;
   chunk = (chunk + SK_BK - 1) / SK_BK * SK_BK;
   const dim3 grid(cdiv(QP, 64), cdiv(M, 64), (unsigned)splits);
   if (v_is_lq)
-    hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP);
+    hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP, keep);
   else
-    hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP);
+    hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(NT), 0, stream, U, M, L, V, Q, chunk, part, QP, keep);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (out1 == nullptr && out2 == nullptr)) return e;  // partials only
   const int T = split_sum_threads(cdiv(M * QP, 4), splits);
 #define QLORA_EPI(TT)                                                                                        \
   case TT:                                                                                                   \
     hipLaunchKernelGGL(skinny_epilogue_kernel<TT>, dim3(cdiv(cdiv(M * QP, 4), 256 / TT)), dim3(256), 0, stream, \
-                       part, splits, M, Q, QP, out1, out2, alpha);                                           \
+                       part, splits, M, Q, QP, out1, out2, alpha, scale1);                                   \
     break;
   switch (T) { QLORA_EPI(1) QLORA_EPI(2) QLORA_EPI(4) QLORA_EPI(8) QLORA_EPI(16) QLORA_EPI(32) default: QLORA_EPI(64) }
 #undef QLORA_EPI
@@ -1573,16 +1639,18 @@ int tn_splits(int64_t M, int64_t P, int64_t Q) {
   return (int)s;
 }
 
-hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint16_t* Va, int64_t ldva, int64_t Qa,
-                          float* part_a, int splits_a, uint16_t* out_a, float alpha_a, const uint16_t* Ub,
-                          int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb, float* part_b,
-                          int splits_b, uint16_t* out_b, float alpha_b, int64_t M, hipStream_t stream) {
+hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint8_t* keep_a, const uint16_t* Va,
+                          int64_t ldva, int64_t Qa, float* part_a, int splits_a, uint16_t* out_a, float alpha_a,
+                          const uint16_t* Ub, int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb,
+                          float* part_b, int splits_b, uint16_t* out_b, float alpha_b, int64_t M,
+                          hipStream_t stream) {
+  if (keep_a && (ldua & 7)) return hipErrorInvalidValue;
   auto chunk_of = [&](int splits) {
     const int64_t c = (M + splits - 1) / splits;
     return (c + TN_BK - 1) / TN_BK * TN_BK;
   };
-  const TnProblem pa{Ua, Va, ldua, ldva, Pa, Qa, M, chunk_of(splits_a), part_a};
-  const TnProblem pb{Ub, Vb, ldub, ldvb, Pb, Qb, M, chunk_of(splits_b), part_b};
+  const TnProblem pa{Ua, Va, ldua, ldva, Pa, Qa, M, chunk_of(splits_a), part_a, keep_a};
+  const TnProblem pb{Ub, Vb, ldub, ldvb, Pb, Qb, M, chunk_of(splits_b), part_b, nullptr};
   const dim3 grid(cdiv(Pa > Pb ? Pa : Pb, 128), cdiv(Qa > Qb ? Qa : Qb, 64), (unsigned)(splits_a + splits_b));
   hipLaunchKernelGGL((tn_kernel<128, 64>), grid, dim3(NT), 0, stream, pa, pb, splits_a);
   hipError_t e = hipGetLastError();
@@ -1622,6 +1690,7 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
   a.ext_act = XAs; a.ext_w = B; a.r = r; a.rp = rp;
   a.out = Y; a.ncols = N;
   a.full_tiles = 0; a.split = 1; a.part = nullptr;
+  a.keep = nullptr; a.keep_scale = 1.0f;
   return launch_main_any<false>(a, split_ws, stream);
 }
 
@@ -1650,23 +1719,25 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* c
 }
 
 hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const float* xpart, int xsplits,
-                              int64_t rp, float alpha, const uint16_t* B, int64_t r, uint16_t* Y, uint16_t* XA,
-                              hipStream_t stream) {
+                              int64_t rp, float alpha, float scale1, const uint16_t* B, int64_t r, uint16_t* Y,
+                              uint16_t* XA, hipStream_t stream) {
   if (N % 4 || rp % 64 || rp > 256 || r > rp || xsplits < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3(cdiv(N, 1024), (unsigned)M), dim3(256), 0, stream, part, splits, (int)M,
-                     N, xpart, xsplits, (int)rp, alpha, B, (int)r, Y, XA);
+                     N, xpart, xsplits, (int)rp, alpha, scale1, B, (int)r, Y, XA);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes, const DQParams& dq,
                          int64_t K, const uint16_t* Ts, const uint16_t* A, int64_t r, int64_t rp, uint16_t* dX,
-                         float* split_ws, hipStream_t stream) {
+                         float* split_ws, const uint8_t* keep, float keep_scale, hipStream_t stream) {
+  if (keep && (K & 7)) return hipErrorInvalidValue;
   MainArgs a;
   a.act = dY; a.M = M; a.L = N;
   a.codes = codes; a.dq = dq; a.Nw = N; a.Kw = K;
   a.ext_act = Ts; a.ext_w = A; a.r = r; a.rp = rp;
   a.out = dX; a.ncols = K;
   a.full_tiles = 0; a.split = 1; a.part = nullptr;
+  a.keep = keep; a.keep_scale = keep_scale;
   return launch_main_any<true>(a, split_ws, stream);
 }
 

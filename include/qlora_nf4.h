@@ -262,6 +262,37 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M,
                      int32_t r, float s, void* dX, void* dA, void* dB,
                      void* ws, int64_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- LoRA dropout variants */
+
+/*
+ * qlora_linear_fwd_dropout / qlora_linear_bwd_dropout - the layer with LoRA
+ * dropout on the adapter input (QLoRA Appendix B.2 trains with LoRA dropout
+ * 0.1 up to 13B and 0.05 for 33B and 65B; it is read as the usual dropout
+ * of the adapter's input with inverted scaling):
+ *     Y  = X * W_bf16^T + s * (drop(X) * A) * B,
+ *     drop(X) = X * keep / (1 - p)
+ *     dX = dY * W_bf16 + s * (T * A^T) * keep / (1 - p),  T = dY * B^T
+ *     dA = s * drop(X)^T * T,   dB = s * XA^T * dY,   XA = drop(X) * A
+ * The caller draws the mask (the library holds no random state):
+ *   keep_mask  device u8 [M, K/8]: bit j of byte (m, c) is 1 when X[m, 8c + j]
+ *              is kept; the backward must get the forward's mask.
+ *   p          drop probability, 0 <= p < 1; kept elements are scaled by
+ *              fp32(1 / (1 - p)).
+ * Every other argument, the workspace size and the error behaviour are those
+ * of qlora_linear_fwd / qlora_linear_bwd; XA returned by the forward is
+ * drop(X) * A.  A null keep_mask is QLORA_ERR_INVALID_ARG.
+ */
+int qlora_linear_fwd_dropout(const void* X, int64_t M, const qlora_nf4_t* W,
+                             const void* A, const void* B, int32_t r, float s,
+                             const void* keep_mask, float p,
+                             void* Y, void* XA, void* ws, int64_t ws_bytes, void* stream);
+
+int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int64_t M,
+                             const qlora_nf4_t* W, const void* A, const void* B,
+                             int32_t r, float s, const void* keep_mask, float p,
+                             void* dX, void* dA, void* dB,
+                             void* ws, int64_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

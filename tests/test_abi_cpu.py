@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -164,6 +164,31 @@ def test_linear_validation():
     assert _bwd(_desc(), dX=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert _bwd(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
     assert _bwd(_desc(), r=300) == B.QLORA_ERR_INVALID_ARG
+
+
+def _fwd_do(d, keep=FAKE, p=0.1, M=16, r=8, nws=1 << 30):
+    return B.lib().qlora_linear_fwd_dropout(FAKE, M, ctypes.byref(d), FAKE, FAKE, r, 2.0, keep, p, FAKE, FAKE, FAKE,
+                                            nws, None)
+
+
+def _bwd_do(d, keep=FAKE, p=0.1, M=16, r=8, nws=1 << 30):
+    return B.lib().qlora_linear_bwd_dropout(FAKE, FAKE, FAKE, M, ctypes.byref(d), FAKE, FAKE, r, 2.0, keep, p, FAKE,
+                                            FAKE, FAKE, FAKE, nws, None)
+
+
+def test_dropout_validation():
+    """The dropout entry points reject a missing or misaligned mask and p
+    outside [0, 1) on the host; shape errors as for the plain ones."""
+    for call in (_fwd_do, _bwd_do):
+        assert call(_desc(), keep=None) == B.QLORA_ERR_INVALID_ARG
+        assert "keep_mask" in B.lib().qlora_last_error().decode()
+        assert call(_desc(), keep=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+        assert call(_desc(), p=1.0) == B.QLORA_ERR_INVALID_ARG
+        assert call(_desc(), p=-0.1) == B.QLORA_ERR_INVALID_ARG
+        assert call(_desc(), p=float("nan")) == B.QLORA_ERR_INVALID_ARG
+        assert call(_desc(cols=200)) == B.QLORA_ERR_INVALID_ARG
+        assert call(_desc(), r=0) == B.QLORA_ERR_INVALID_ARG
+        assert call(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_profile_hook_validation():

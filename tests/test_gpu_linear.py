@@ -309,3 +309,91 @@ def test_code_types_attention_shape(B, code_type):
     t = lin.draw("cuda")
     qw, Y, XA, dX, dA, dB = _run(B, t["X"], t["W"], t["A"], t["B"], t["dY"], lin.s, code_type=code_type)
     _sampled_check(B, lin, t, Y, XA, dX, dA, dB, code_type=code_type)
+
+
+# --------------------------------------------------- LoRA dropout (G15)
+
+def _dropout_inputs(B, M, N, K, r, p, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    W = torch.randn(N, K, generator=g, device="cuda") * 0.02
+    X = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+    A = (torch.randn(K, r, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+    Bm = (torch.randn(r, N, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+    dY = torch.randn(M, N, generator=g, device="cuda").to(torch.bfloat16)
+    keep = torch.rand(M, K, generator=g, device="cuda") >= p
+    return W, X, A, Bm, dY, keep
+
+
+@pytest.mark.parametrize("M,N,K,r,p", [(200, 192, 320, 8, 0.1), (130, 384, 128, 64, 0.05), (4, 192, 64 * 40, 16, 0.1),
+                                       (16, 256, 64 * 9, 100, 0.05), (300, 256, 192, 256, 0.1)])
+def test_dropout_parity(B, M, N, K, r, p):
+    """Forward and backward with LoRA dropout against the fp64 oracle with the
+    same mask: tiled and small-token forward, tiled backward."""
+    _log(f"linear dropout M={M} N={N} K={K} r={r} p={p}")
+    s = 16.0 / r
+    W, X, A, Bm, dY, keep = _dropout_inputs(B, M, N, K, r, p, seed=M * 13 + K + r)
+    km = B.pack_keep_mask(keep)
+    qw = B.qlora_nf4_quantize(W)
+    Y, XA = B.qlora_linear_fwd(X, qw, A, Bm, s, keep=km, p=p)
+    dX, dA, dB = B.qlora_linear_bwd(dY, X, XA, qw, A, Bm, s, keep=km, p=p)
+    torch.cuda.synchronize()
+    Wb = OracleWeight(_np(W)).full()
+    kp = keep.cpu().numpy()
+    Yr, XAr = linear.forward_dropout(_np(X), Wb, _np(A), _np(Bm), s, kp, p)
+    dXr, dAr, dBr = linear.backward_dropout(_np(dY), _np(X), Wb, _np(A), _np(Bm), s, kp, p)
+    for name, o, ref in (("Y", Y, Yr), ("XA", XA, XAr), ("dX", dX, dXr), ("dA", dA, dAr), ("dB", dB, dBr)):
+        _assert_close(name, _np(o), ref)
+
+
+def test_dropout_p0_all_kept_is_the_plain_layer(B):
+    """p = 0 with every bit set gives exactly the plain layer's outputs."""
+    _log("linear dropout p=0 identity")
+    M, N, K, r = 256, 512, 512, 64
+    W, X, A, Bm, dY, _ = _dropout_inputs(B, M, N, K, r, 0.0, seed=77)
+    km = B.pack_keep_mask(torch.ones(M, K, dtype=torch.bool, device="cuda"))
+    qw = B.qlora_nf4_quantize(W)
+    plain = list(B.qlora_linear_fwd(X, qw, A, Bm, 0.25))
+    plain += list(B.qlora_linear_bwd(dY, X, plain[1], qw, A, Bm, 0.25))
+    drop = list(B.qlora_linear_fwd(X, qw, A, Bm, 0.25, keep=km, p=0.0))
+    drop += list(B.qlora_linear_bwd(dY, X, drop[1], qw, A, Bm, 0.25, keep=km, p=0.0))
+    torch.cuda.synchronize()
+    for a, b in zip(plain, drop):
+        assert torch.equal(a, b)
+
+
+def test_dropout_attention_shape(B):
+    """The 4096x4096 attention projection, 4096 tokens, p = 0.1 (the 256 x
+    256 kernels), sampled: Y and dX on sampled rows and columns, dA and dB in
+    full."""
+    from bit_nf4_quantized_quantize_amd import synth
+    lin = synth.workload(2)[0]
+    p = 0.1
+    _log("linear dropout workload 2")
+    t = lin.draw("cuda")
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    keep = torch.rand(lin.M, lin.K, generator=g, device="cuda") >= p
+    km = B.pack_keep_mask(keep)
+    s = lin.s
+    qw = B.qlora_nf4_quantize(t["W"])
+    Y, XA = B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], s, keep=km, p=p)
+    dX, dA, dB = B.qlora_linear_bwd(t["dY"], t["X"], XA, qw, t["A"], t["B"], s, keep=km, p=p)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    M, N, K = lin.M, lin.N, lin.K
+    ow = OracleWeight(_np(t["W"]))
+    kp = keep.cpu().numpy().astype(np.float64) / (1.0 - p)
+    X, A, Bm, dYn = _np(t["X"]).astype(np.float64), _np(t["A"]).astype(np.float64), _np(t["B"]).astype(np.float64), \
+        _np(t["dY"]).astype(np.float64)
+    Xd = X * kp
+    ms = np.unique(np.concatenate([rng.integers(0, M, 64), [0, M - 1]]))
+    ns = np.unique(np.concatenate([rng.integers(0, N, 48), [0, N - 1]]))
+    Yr = X[ms] @ ow.rows(ns).astype(np.float64).T + s * (Xd[ms] @ A) @ Bm[:, ns]
+    _assert_close("Y[sample]", _np(Y)[np.ix_(ms, ns)], Yr)
+    _assert_close("XA[sample]", _np(XA)[ms], Xd[ms] @ A)
+    kbs = np.unique(np.concatenate([rng.integers(0, K // 64, 2), [K // 64 - 1]]))
+    kcols = (kbs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+    T = dYn @ Bm.T
+    dXr = dYn[ms] @ ow.cols(kbs).astype(np.float64) + s * (T[ms] @ A[kcols].T) * kp[np.ix_(ms, kcols)]
+    _assert_close("dX[sample]", _np(dX)[np.ix_(ms, kcols)], dXr)
+    _assert_close("dA", _np(dA), s * (Xd.T @ T))
+    _assert_close("dB", _np(dB), s * ((Xd @ A).T @ dYn))
