@@ -41,10 +41,13 @@ is in tests/test_oracle_pins.py):
                                normal weights)
   linear.forward / backward    pinned (brute force, finite differences,
                                special cases, torch.autograd in fp64)
+  optim.clip_scale /
+  optim.adamw_step             pinned (torch.optim.AdamW and clip_grad_norm_
+                               in fp64 over five steps, closed forms)
   linear.forward_dropout /
   linear.backward_dropout      pinned (reduction to the plain layer, brute
                                force, finite differences, torch.autograd in
                                fp64 with the mask as a tensor)
 """
 
-from . import codebook, fp8_e4m3, blockwise, linear  # noqa: F401
+from . import codebook, fp8_e4m3, blockwise, linear, optim  # noqa: F401

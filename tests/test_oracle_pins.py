@@ -625,3 +625,47 @@ def test_pins_catch_planted_dropout_mistake(monkeypatch):
     T = dY @ B.T
     bad_dX = dY @ W + s * (T @ A.T) / (1 - p)
     assert not np.allclose(bad_dX, good[0], rtol=1e-6, atol=1e-7)
+
+
+# --------------------------------------------- LoRA optimizer step (G16)
+
+from oracle import optim  # noqa: E402
+
+
+def test_adamw_matches_torch_adamw_fp64():
+    """Five steps of the oracle equal torch.optim.AdamW in fp64, with global
+    gradient-norm clipping as torch.nn.utils.clip_grad_norm_ does it."""
+    rng = np.random.default_rng(40)
+    shapes = [(16, 4), (4, 24)]
+    params = [rng.standard_normal(s) * 0.01 for s in shapes]
+    tp = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in params]
+    opt = torch.optim.AdamW(tp, lr=2e-4, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    ps = [a.copy() for a in params]
+    ms = [np.zeros(s) for s in shapes]
+    vs = [np.zeros(s) for s in shapes]
+    for t in range(1, 6):
+        grads = [rng.standard_normal(s) * (3.0 if t % 2 else 0.01) for s in shapes]
+        for x, gr in zip(tp, grads):
+            x.grad = torch.tensor(gr, dtype=torch.float64)
+        torch.nn.utils.clip_grad_norm_(tp, 0.3)
+        opt.step()
+        sc = optim.clip_scale(grads, 0.3)
+        for i in range(len(shapes)):
+            ps[i], ms[i], vs[i] = optim.adamw_step(ps[i], grads[i], ms[i], vs[i], t, 2e-4, 0.9, 0.999, 1e-8, 0.01, sc)
+        for a, x in zip(ps, tp):
+            assert np.allclose(a, x.detach().numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_adamw_first_step_closed_form():
+    """At step 1 the bias-corrected moments are g and g^2, so without weight
+    decay the update is lr * g / (|g| + eps): about lr * sign(g)."""
+    g = np.array([1e-3, -2.0, 0.5, -1e-7])
+    p, m, v = optim.adamw_step(np.zeros(4), g, np.zeros(4), np.zeros(4), 1, 0.1, 0.9, 0.999, 1e-8, 0.0)
+    assert np.allclose(p, -0.1 * g / (np.abs(g) + 1e-8), rtol=1e-12)
+    assert np.allclose(m, 0.1 * g) and np.allclose(v, 0.001 * g * g)
+
+
+def test_clip_scale_closed_forms():
+    assert optim.clip_scale([np.array([3.0, 4.0])], 0.3) == 0.3 / (5.0 + 1e-6)
+    assert optim.clip_scale([np.array([0.1]), np.array([0.1])], 0.3) == 1.0
+    assert optim.clip_scale([np.zeros(3)], 0.3) == 1.0
