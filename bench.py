@@ -343,6 +343,45 @@ def run_dropout(B, L, dev, p=0.1, reps=10):
     return out
 
 
+OPT_BYTES_PER_PARAM = 30.0  # clip: bf16 grad read; step: grad, fp32 p/m/v read+write, bf16 p written
+
+
+def run_optimizer(B, L, dev, reps=20):
+    """The LoRA-only optimizer step (QLoRA Appendix B.2: beta2 0.999, max
+    grad norm 0.3) over the layer's adapters A and B in one flat buffer:
+    clip scale + AdamW, with the fp32 states on the device and in pinned host
+    memory (the paged optimizer's evicted state).  Median of `reps` steps
+    between two events each."""
+    import torch
+
+    lin = L["lin"]
+    n = lin.r * (lin.K + lin.N)
+    g = torch.Generator(device=dev).manual_seed(21)
+    grad = (torch.randn(n, generator=g, device=dev) * 1e-3).to(torch.bfloat16)
+    out = {"params": n, "bytes_per_param": OPT_BYTES_PER_PARAM}
+    for where in ("device", "pinned_host"):
+        p = torch.randn(n, generator=g, device=dev) * 0.01
+        pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        if where == "device":
+            m, v = torch.zeros(n, device=dev), torch.zeros(n, device=dev)
+        else:
+            m, v = torch.zeros(n).pin_memory(), torch.zeros(n).pin_memory()
+        sc = torch.empty(4, dtype=torch.float32, device=dev)
+        ts = []
+        for t in range(1, reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.qlora_clip_scale(grad, 0.3, scale=sc)
+            B.qlora_adamw_step(p, grad, m, v, t, 2e-4, (0.9, 0.999), 1e-8, 0.0, grad_scale=sc, param_bf16=pb)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = sorted(ts[1:])
+        us = ts[len(ts) // 2]
+        out[where] = {"step_us": us, "GB/s": OPT_BYTES_PER_PARAM * n / us / 1e3}
+    return out
+
+
 def _dominant(per, layers, small):
     """(kernel, bound, algorithmic work, mean us, linear index) of the kernel
     with the largest share of the step, from a per-linear kernel breakdown.
@@ -600,6 +639,7 @@ def main():
         if args.workload == 2 and not args.no_code_types:
             out["code_types"] = run_code_types(B, layers[0], dev)
             out["lora_dropout"] = run_dropout(B, layers[0], dev)
+            out["optimizer"] = run_optimizer(B, layers[0], dev)
     elif not args.no_sweep:
         del layers, qws
         torch.cuda.empty_cache()

@@ -43,6 +43,7 @@ EXPORTED = (
     "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string", "qlora_last_error",
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
+    "qlora_clip_scale_workspace", "qlora_clip_scale", "qlora_adamw_step",
     "qlora_profile_events",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
@@ -99,6 +100,9 @@ def lib():
         "qlora_linear_bwd": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
         "qlora_linear_fwd_dropout": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp, _vp, _i64,
                                             _vp]),
+        "qlora_clip_scale_workspace": (_i32, [_i64, ctypes.POINTER(_i64)]),
+        "qlora_clip_scale": (_i32, [_vp, _i64, _f32, _vp, _vp, _i64, _vp]),
+        "qlora_adamw_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _f32, _f32, _f32, _f32, _f32, _i32, _vp]),
         "qlora_linear_bwd_dropout": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp,
                                             _vp, _vp, _i64, _vp]),
         "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
@@ -380,3 +384,47 @@ def qlora_linear_bwd(dY, X, XA, q, A, B, s, need_dx=True, dX=None, dA=None, dB=N
                                               _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
                "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB
+
+
+# ------------------------------------------------------ LoRA optimizer step
+
+def qlora_clip_scale(grad, max_norm=0.3, scale=None, workspace=None, stream=None):
+    """Device fp32 scalar min(1, max_norm / (||grad|| + 1e-6)) for a flat bf16
+    gradient tensor (all LoRA gradients)."""
+    _need_cuda(grad)
+    if grad.dtype != torch.bfloat16 or not grad.is_contiguous():
+        raise ValueError("grad must be a contiguous bf16 tensor")
+    n = grad.numel()
+    if scale is None:
+        scale = torch.empty(4, dtype=torch.float32, device=grad.device)
+    nws = _i64(0)
+    _check(lib().qlora_clip_scale_workspace(n, ctypes.byref(nws)), "qlora_clip_scale_workspace")
+    ws = _ws(nws.value, grad.device, workspace)
+    _check(lib().qlora_clip_scale(_ptr(grad), n, float(max_norm), _ptr(scale), _ptr(ws), ws.numel(), _stream(stream)),
+           "qlora_clip_scale")
+    return scale
+
+
+def qlora_adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
+                     grad_scale=None, param_bf16=None, stream=None):
+    """One AdamW step in place on flat fp32 `param`, `exp_avg`, `exp_avg_sq`
+    (device or pinned host tensors for the states) with flat bf16 `grad`;
+    `grad_scale` a device fp32 scalar (qlora_clip_scale) or None; writes the
+    bf16 copy of the updated parameters into `param_bf16` when given."""
+    _need_cuda(param, grad)
+    n = param.numel()
+    for t, name, dt in ((param, "param", torch.float32), (grad, "grad", torch.bfloat16),
+                        (exp_avg, "exp_avg", torch.float32), (exp_avg_sq, "exp_avg_sq", torch.float32)):
+        if t.dtype != dt or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of {n} elements")
+    for t, name in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n):
+        raise ValueError("param_bf16 must be a bf16 tensor of the parameters' size")
+    _check(lib().qlora_adamw_step(_ptr(param), _ptr(param_bf16) if param_bf16 is not None else None, _ptr(grad),
+                                  _ptr(exp_avg), _ptr(exp_avg_sq), n,
+                                  _ptr(grad_scale) if grad_scale is not None else None, float(lr), float(betas[0]),
+                                  float(betas[1]), float(eps), float(weight_decay), int(step), _stream(stream)),
+           "qlora_adamw_step")
+    return param

@@ -16,8 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlora_nf4.so")
 
-SOURCES = ["quantize.hip", "linear.hip", "abi.cpp"]
-HEADERS = ["device.h", "launch.h"]
+SOURCES = ["quantize.hip", "linear.hip", "optim.hip", "abi.cpp"]
+HEADERS = ["device.h", "launch.h", "codebooks.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

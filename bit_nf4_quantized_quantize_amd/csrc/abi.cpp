@@ -437,4 +437,51 @@ int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int6
   return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, keep_mask, p, dX, dA, dB, ws, ws_bytes, stream, fn);
 }
 
+int qlora_clip_scale_workspace(int64_t n, int64_t* ws_bytes) {
+  if (!ws_bytes) return fail(QLORA_ERR_INVALID_ARG, "qlora_clip_scale_workspace: ws_bytes is NULL");
+  if (n < 0) return fail(QLORA_ERR_INVALID_ARG, "qlora_clip_scale_workspace: n < 0");
+  *ws_bytes = round_up((int64_t)clip_parts(n) * 8, kAlign);
+  return QLORA_OK;
+}
+
+int qlora_clip_scale(const void* grad, int64_t n, float max_norm, float* scale, void* ws, int64_t ws_bytes,
+                     void* stream) {
+  static const char* fn = "qlora_clip_scale";
+  int st;
+  if (n < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (!(max_norm > 0.0f)) return fail(QLORA_ERR_INVALID_ARG, "%s: max_norm must be > 0", fn);
+  if ((st = check_ptr(scale, "scale", fn))) return st;
+  if (n > 0 && (st = check_ptr(grad, "grad", fn))) return st;
+  const int64_t need = round_up((int64_t)clip_parts(n) * 8, kAlign);
+  if (ws_bytes < need) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)need);
+  if ((st = check_ptr(ws, "ws", fn))) return st;
+  const hipError_t e = launch_clip_scale((const uint16_t*)grad, n, max_norm, scale, (double*)ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+
+int qlora_adamw_step(float* param, void* param_bf16, const void* grad, float* exp_avg, float* exp_avg_sq, int64_t n,
+                     const float* grad_scale, float lr, float beta1, float beta2, float eps, float weight_decay,
+                     int32_t step, void* stream) {
+  static const char* fn = "qlora_adamw_step";
+  int st;
+  if (n < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (step < 1) return fail(QLORA_ERR_INVALID_ARG, "%s: step counts from 1", fn);
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: betas must be in [0, 1)", fn);
+  if (!(eps > 0.0f) || !(lr >= 0.0f) || !(weight_decay >= 0.0f))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: need eps > 0, lr >= 0, weight_decay >= 0", fn);
+  if (n == 0) return QLORA_OK;
+  if ((st = check_ptr(param, "param", fn)) || (st = check_ptr(grad, "grad", fn)) ||
+      (st = check_ptr(exp_avg, "exp_avg", fn)) || (st = check_ptr(exp_avg_sq, "exp_avg_sq", fn)))
+    return st;
+  if (param_bf16 && !aligned16(param_bf16)) return fail(QLORA_ERR_MISALIGNED, "%s: param_bf16 not 16-byte aligned", fn);
+  if (grad_scale && !aligned16(grad_scale))
+    return fail(QLORA_ERR_MISALIGNED, "%s: grad_scale not 16-byte aligned", fn);
+  const hipError_t e = launch_adamw(param, (uint16_t*)param_bf16, (const uint16_t*)grad, exp_avg, exp_avg_sq, n,
+                                    grad_scale, lr, beta1, beta2, eps, weight_decay, step, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+
 }  // extern "C"

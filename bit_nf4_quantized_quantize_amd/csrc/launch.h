@@ -127,4 +127,16 @@ hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const ui
                           int splits_b, uint16_t* out_b, float alpha_b, int64_t M, hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);
 
+// LoRA optimizer step.  launch_clip_scale writes scale = min(1, max_norm /
+// (||g||_2 + 1e-6)) for the bf16 gradient g [n], using clip_parts(n) fp64
+// partial sums; launch_adamw applies one AdamW step (bias corrections for
+// `step` >= 1, gradient times *gscale when given) to fp32 parameters p and
+// states m, v, and writes a bf16 copy of p when p_bf16 is given.
+int clip_parts(int64_t n);
+hipError_t launch_clip_scale(const uint16_t* g, int64_t n, float max_norm, float* scale, double* partials,
+                             hipStream_t stream);
+hipError_t launch_adamw(float* p, uint16_t* p_bf16, const uint16_t* g, float* m, float* v, int64_t n,
+                        const float* gscale, float lr, float beta1, float beta2, float eps, float weight_decay,
+                        int step, hipStream_t stream);
+
 }  // namespace qlora

@@ -1,0 +1,144 @@
+// The LoRA-only optimizer step for gfx950: global gradient-norm clipping and
+// AdamW over one flat buffer of LoRA parameters.
+//
+// QLoRA (Dettmers et al., arXiv 2305.14314): section 3 "Paged Optimizers"
+// (optimizer states that live in memory the CPU can hold and that are paged
+// to the GPU for the update step) and Appendix B.2 "Hyperparameters" (Adam
+// beta2 0.999, maximum gradient norm 0.3, constant learning rate); only the
+// adapters are trained (section 3 "QLoRA", after Eq. 6).  Read as AdamW with
+// decoupled weight decay and clip scale min(1, max_norm / (||g|| + 1e-6)).
+//
+// Both kernels are streams over the parameters (HBM-bound; 28 bytes per
+// parameter for the step with a bf16 copy of the updated weights).  The
+// states may live in pinned host memory, which the step kernel reads and
+// writes in place over the host link.
+#include "device.h"
+#include "launch.h"
+
+namespace qlora {
+
+constexpr int OPT_T = 256;
+constexpr int OPT_MAX_WG = 256;  // partial sums of the gradient norm
+
+// Sum of squares of grad[0, n) (bf16), one fp64 partial per workgroup,
+// accumulated in a fixed order: thread t takes elements 4(t + k T) .. +3 of
+// its workgroup's grid-stride sweep, then the wave and workgroup sums are
+// formed by a fixed butterfly and a fixed sum over waves.
+__global__ __launch_bounds__(OPT_T) void grad_sqnorm_kernel(const uint16_t* __restrict__ g, int64_t n,
+                                                            double* __restrict__ partials) {
+  __shared__ double s_w[OPT_T / 64];
+  const int64_t stride = (int64_t)gridDim.x * OPT_T * 4;
+  double acc = 0.0;
+  for (int64_t i = ((int64_t)blockIdx.x * OPT_T + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 3 < n) {
+      const uint2 v = *reinterpret_cast<const uint2*>(g + i);
+      const float a = __uint_as_float(v.x << 16), b = __uint_as_float(v.x & 0xFFFF0000u);
+      const float c = __uint_as_float(v.y << 16), d = __uint_as_float(v.y & 0xFFFF0000u);
+      acc += (double)a * a + (double)b * b + (double)c * c + (double)d * d;
+    } else {
+      for (int64_t j = i; j < n; ++j) {
+        const float a = bf2f(g[j]);
+        acc += (double)a * a;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < OPT_T / 64; ++w) t += s_w[w];
+    partials[blockIdx.x] = t;
+  }
+}
+
+// scale = min(1, max_norm / (sqrt(sum of partials) + 1e-6)), the partials
+// added in index order by one thread.
+__global__ __launch_bounds__(64) void clip_finish_kernel(const double* __restrict__ partials, int parts,
+                                                         float max_norm, float* __restrict__ scale) {
+  if (threadIdx.x != 0) return;
+  double t = 0.0;
+  for (int i = 0; i < parts; ++i) t += partials[i];
+  const double c = (double)max_norm / (sqrt(t) + 1e-6);
+  *scale = (float)(c < 1.0 ? c : 1.0);
+}
+
+int clip_parts(int64_t n) {
+  const int64_t wgs = (n + OPT_T * 4 - 1) / (OPT_T * 4);
+  return (int)(wgs < 1 ? 1 : (wgs > OPT_MAX_WG ? OPT_MAX_WG : wgs));
+}
+
+hipError_t launch_clip_scale(const uint16_t* g, int64_t n, float max_norm, float* scale, double* partials,
+                             hipStream_t stream) {
+  const int parts = clip_parts(n);
+  hipLaunchKernelGGL(grad_sqnorm_kernel, dim3((unsigned)parts), dim3(OPT_T), 0, stream, g, n, partials);
+  hipLaunchKernelGGL(clip_finish_kernel, dim3(1), dim3(64), 0, stream, partials, parts, max_norm, scale);
+  return hipGetLastError();
+}
+
+struct AdamWArgs {
+  float lr, beta1, beta2, eps, decay;  // decay = 1 - lr * weight_decay
+  float inv_bc1, inv_sqrt_bc2;         // 1 / (1 - beta1^t), 1 / sqrt(1 - beta2^t)
+};
+
+__device__ __forceinline__ float adamw_one(float p, float g, float& m, float& v, const AdamWArgs& a) {
+  m = a.beta1 * m + (1.0f - a.beta1) * g;
+  v = a.beta2 * v + (1.0f - a.beta2) * (g * g);
+  const float denom = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
+  return p * a.decay - (a.lr * a.inv_bc1) * (m / denom);
+}
+
+// One AdamW step over n parameters, 4 per thread and iteration.
+__global__ __launch_bounds__(OPT_T) void adamw_kernel(float* __restrict__ p, uint16_t* __restrict__ p_bf16,
+                                                      const uint16_t* __restrict__ g, float* __restrict__ m,
+                                                      float* __restrict__ v, int64_t n,
+                                                      const float* __restrict__ gscale, AdamWArgs a) {
+  const float sc = gscale ? *gscale : 1.0f;
+  const int64_t stride = (int64_t)gridDim.x * OPT_T * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * OPT_T + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 3 < n) {
+      float4 pv = *reinterpret_cast<const float4*>(p + i);
+      float4 mv = *reinterpret_cast<const float4*>(m + i);
+      float4 vv = *reinterpret_cast<const float4*>(v + i);
+      const uint2 gv = *reinterpret_cast<const uint2*>(g + i);
+      pv.x = adamw_one(pv.x, __uint_as_float(gv.x << 16) * sc, mv.x, vv.x, a);
+      pv.y = adamw_one(pv.y, __uint_as_float(gv.x & 0xFFFF0000u) * sc, mv.y, vv.y, a);
+      pv.z = adamw_one(pv.z, __uint_as_float(gv.y << 16) * sc, mv.z, vv.z, a);
+      pv.w = adamw_one(pv.w, __uint_as_float(gv.y & 0xFFFF0000u) * sc, mv.w, vv.w, a);
+      *reinterpret_cast<float4*>(p + i) = pv;
+      *reinterpret_cast<float4*>(m + i) = mv;
+      *reinterpret_cast<float4*>(v + i) = vv;
+      if (p_bf16) *reinterpret_cast<uint2*>(p_bf16 + i) = make_uint2(pack_bf2(pv.x, pv.y), pack_bf2(pv.z, pv.w));
+    } else {
+      for (int64_t j = i; j < n; ++j) {
+        float mj = m[j], vj = v[j];
+        const float pj = adamw_one(p[j], bf2f(g[j]) * sc, mj, vj, a);
+        p[j] = pj;
+        m[j] = mj;
+        v[j] = vj;
+        if (p_bf16) p_bf16[j] = f2bf(pj);
+      }
+    }
+  }
+}
+
+hipError_t launch_adamw(float* p, uint16_t* p_bf16, const uint16_t* g, float* m, float* v, int64_t n,
+                        const float* gscale, float lr, float beta1, float beta2, float eps, float weight_decay,
+                        int step, hipStream_t stream) {
+  AdamWArgs a;
+  a.lr = lr;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.decay = (float)(1.0 - (double)lr * weight_decay);
+  a.inv_bc1 = (float)(1.0 / (1.0 - pow((double)beta1, step)));
+  a.inv_sqrt_bc2 = (float)(1.0 / sqrt(1.0 - pow((double)beta2, step)));
+  const int64_t wgs = (n + OPT_T * 4 - 1) / (OPT_T * 4);
+  const unsigned grid = (unsigned)(wgs < 1 ? 1 : (wgs > 2048 ? 2048 : wgs));
+  hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(OPT_T), 0, stream, p, p_bf16, g, m, v, n, gscale, a);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

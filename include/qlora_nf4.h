@@ -293,6 +293,44 @@ int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int6
                              void* dX, void* dA, void* dB,
                              void* ws, int64_t ws_bytes, void* stream);
 
+/* --------------------------------------------- LoRA-only optimizer step */
+
+/*
+ * The update of the adapters (QLoRA section 3 "Paged Optimizers" and
+ * Appendix B.2: Adam beta2 = 0.999, maximum gradient norm 0.3, constant
+ * learning rate; only the LoRA parameters are trained).  Read as AdamW with
+ * decoupled weight decay and global gradient-norm clipping, over one flat
+ * buffer holding all LoRA parameters (their gradients can be the dA / dB
+ * outputs of qlora_linear_bwd written into slices of one flat buffer).
+ *
+ * qlora_clip_scale_workspace - host only: workspace bytes of
+ *   qlora_clip_scale for n gradient elements.
+ *
+ * qlora_clip_scale - device scalar *scale = min(1, max_norm / (||g||_2 +
+ *   1e-6)) for the bf16 gradient grad [n] (device).  The sum of squares is
+ *   taken in fp64 in a fixed order (bit-reproducible).  max_norm > 0.
+ *
+ * qlora_adamw_step - one step t = step (>= 1) of
+ *     g' = g * (*grad_scale, or 1 when grad_scale is NULL)
+ *     m = beta1 m + (1 - beta1) g';  v = beta2 v + (1 - beta2) g'^2
+ *     p = p (1 - lr weight_decay) - (lr / (1 - beta1^t)) m /
+ *         (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *   in fp32 over n elements: param, exp_avg (m), exp_avg_sq (v) fp32 [n],
+ *   updated in place; grad bf16 [n]; param_bf16 (bf16 [n] or NULL) receives
+ *   the updated parameters rounded to bf16 (the operands of the next
+ *   forward).  exp_avg and exp_avg_sq may be pinned host memory (the paged
+ *   optimizer's evicted state): the kernel reads and writes them in place
+ *   over the host link.  Requires 0 <= beta1, beta2 < 1, eps > 0, lr >= 0,
+ *   weight_decay >= 0.
+ */
+int qlora_clip_scale_workspace(int64_t n, int64_t* ws_bytes);
+int qlora_clip_scale(const void* grad, int64_t n, float max_norm, float* scale,
+                     void* ws, int64_t ws_bytes, void* stream);
+int qlora_adamw_step(float* param, void* param_bf16, const void* grad,
+                     float* exp_avg, float* exp_avg_sq, int64_t n,
+                     const float* grad_scale, float lr, float beta1, float beta2,
+                     float eps, float weight_decay, int32_t step, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -202,3 +202,32 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         B.qlora_nf4_quantize(torch.zeros(64))
+
+
+def test_optimizer_validation():
+    """The clip and AdamW entry points reject bad arguments on the host."""
+    L = B.lib()
+    ws = ctypes.c_int64(0)
+    assert L.qlora_clip_scale_workspace(1000, ctypes.byref(ws)) == B.QLORA_OK and ws.value >= 8
+    assert L.qlora_clip_scale_workspace(-1, ctypes.byref(ws)) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_clip_scale(FAKE, -1, 0.3, FAKE, FAKE, 1 << 20, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_clip_scale(FAKE, 100, 0.0, FAKE, FAKE, 1 << 20, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_clip_scale(FAKE, 100, 0.3, None, FAKE, 1 << 20, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_clip_scale(None, 100, 0.3, FAKE, FAKE, 1 << 20, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_clip_scale(FAKE, 100, 0.3, FAKE, FAKE, 1, None) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+
+    def step(**kw):
+        a = dict(param=FAKE, pbf=None, grad=FAKE, m=FAKE, v=FAKE, n=100, gs=None, lr=1e-4, b1=0.9, b2=0.999,
+                 eps=1e-8, wd=0.0, t=1)
+        a.update(kw)
+        return L.qlora_adamw_step(a["param"], a["pbf"], a["grad"], a["m"], a["v"], a["n"], a["gs"], a["lr"],
+                                  a["b1"], a["b2"], a["eps"], a["wd"], a["t"], None)
+    assert step(t=0) == B.QLORA_ERR_INVALID_ARG
+    assert step(b2=1.0) == B.QLORA_ERR_INVALID_ARG
+    assert step(eps=0.0) == B.QLORA_ERR_INVALID_ARG
+    assert step(lr=-1.0) == B.QLORA_ERR_INVALID_ARG
+    assert step(n=-5) == B.QLORA_ERR_INVALID_ARG
+    assert step(m=None) == B.QLORA_ERR_INVALID_ARG
+    assert step(param=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert step(pbf=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert step(n=0, param=None, grad=None, m=None, v=None) == B.QLORA_OK
