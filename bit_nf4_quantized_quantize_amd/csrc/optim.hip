@@ -54,15 +54,27 @@ __global__ __launch_bounds__(OPT_T) void grad_sqnorm_kernel(const uint16_t* __re
   }
 }
 
-// scale = min(1, max_norm / (sqrt(sum of partials) + 1e-6)), the partials
-// added in index order by one thread.
+// scale = min(1, max_norm / (sqrt(sum of partials) + 1e-6)).  One wave: lane
+// l adds partials l, l + 64, ... in order (all loads in flight together),
+// then a fixed butterfly adds the lanes.
 __global__ __launch_bounds__(64) void clip_finish_kernel(const double* __restrict__ partials, int parts,
                                                          float max_norm, float* __restrict__ scale) {
-  if (threadIdx.x != 0) return;
+  static_assert(OPT_MAX_WG % 64 == 0, "partials per lane");
+  double v[OPT_MAX_WG / 64];
+#pragma unroll
+  for (int k = 0; k < OPT_MAX_WG / 64; ++k) {
+    const int i = (int)threadIdx.x + 64 * k;
+    v[k] = i < parts ? partials[i] : 0.0;
+  }
   double t = 0.0;
-  for (int i = 0; i < parts; ++i) t += partials[i];
-  const double c = (double)max_norm / (sqrt(t) + 1e-6);
-  *scale = (float)(c < 1.0 ? c : 1.0);
+#pragma unroll
+  for (int k = 0; k < OPT_MAX_WG / 64; ++k) t += v[k];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+  if (threadIdx.x == 0) {
+    const double c = (double)max_norm / (sqrt(t) + 1e-6);
+    *scale = (float)(c < 1.0 ? c : 1.0);
+  }
 }
 
 int clip_parts(int64_t n) {
