@@ -1465,24 +1465,37 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
     xas[j] = bf2f(f2bf(alpha * c));
     if (XA != nullptr && blockIdx.x == 0 && j < r) XA[(int64_t)m * r + j] = f2bf(scale1 * c);
   }
-  __syncthreads();
-  const int64_t nc = ((int64_t)blockIdx.x * 256 + tid) * 4;
-  if (nc >= N) return;
+  // four groups of 64 threads share the workgroup's 256 columns: group q adds
+  // the partial slices q, q + 4, ... and the adapter rows q, q + 4, ...; the
+  // four group sums are then added in a fixed order
+  const int q = tid >> 6, cq = tid & 63;
+  const int64_t nc = ((int64_t)blockIdx.x * 64 + cq) * 4;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  __syncthreads();
+  if (nc < N) {
+#pragma unroll 2
+    for (int k = q; k < S; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)k * M + m) * N + nc);
+      a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
+    }
 #pragma unroll 4
-  for (int k = 0; k < S; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)k * M + m) * N + nc);
-    a0 += v.x; a1 += v.y; a2 += v.z; a3 += v.w;
+    for (int j = q; j < r; j += 4) {
+      const float x = xas[j];
+      const uint2 bv = *reinterpret_cast<const uint2*>(B + (int64_t)j * N + nc);
+      a0 = __builtin_fmaf(x, __uint_as_float(bv.x << 16), a0);
+      a1 = __builtin_fmaf(x, __uint_as_float(bv.x & 0xFFFF0000u), a1);
+      a2 = __builtin_fmaf(x, __uint_as_float(bv.y << 16), a2);
+      a3 = __builtin_fmaf(x, __uint_as_float(bv.y & 0xFFFF0000u), a3);
+    }
   }
-#pragma unroll 8
-  for (int j = 0; j < r; ++j) {
-    const float x = xas[j];
-    const uint2 bv = *reinterpret_cast<const uint2*>(B + (int64_t)j * N + nc);
-    a0 = __builtin_fmaf(x, __uint_as_float(bv.x << 16), a0);
-    a1 = __builtin_fmaf(x, __uint_as_float(bv.x & 0xFFFF0000u), a1);
-    a2 = __builtin_fmaf(x, __uint_as_float(bv.y << 16), a2);
-    a3 = __builtin_fmaf(x, __uint_as_float(bv.y & 0xFFFF0000u), a3);
-  }
+  xsum[tid] = make_float4(a0, a1, a2, a3);
+  __syncthreads();
+  if (q != 0 || nc >= N) return;
+  const float4 s1 = xsum[64 + cq], s2 = xsum[128 + cq], s3 = xsum[192 + cq];
+  a0 = ((a0 + s1.x) + s2.x) + s3.x;
+  a1 = ((a1 + s1.y) + s2.y) + s3.y;
+  a2 = ((a2 + s1.z) + s2.z) + s3.z;
+  a3 = ((a3 + s1.w) + s2.w) + s3.w;
   *reinterpret_cast<uint2*>(Y + (int64_t)m * N + nc) = make_uint2(pack_bf2(a0, a1), pack_bf2(a2, a3));
 }
 
@@ -1722,7 +1735,7 @@ hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t 
                               int64_t rp, float alpha, float scale1, const uint16_t* B, int64_t r, uint16_t* Y,
                               uint16_t* XA, hipStream_t stream) {
   if (N % 4 || rp % 64 || rp > 256 || r > rp || xsplits < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemv_reduce_kernel, dim3(cdiv(N, 1024), (unsigned)M), dim3(256), 0, stream, part, splits, (int)M,
+  hipLaunchKernelGGL(gemv_reduce_kernel, dim3(cdiv(N, 256), (unsigned)M), dim3(256), 0, stream, part, splits, (int)M,
                      N, xpart, xsplits, (int)rp, alpha, scale1, B, (int)r, Y, XA);
   return hipGetLastError();
 }
