@@ -33,12 +33,13 @@ is in tests/test_oracle_pins.py):
                                the round-trip special cases
   blockwise.dequantize         pinned (round trips)
   codebook.FP4_E2M1 / FP4_E3M0 pinned (format tables), INT4 pinned (two's
-                               complement over 7)
+                               complement over 7), INT8 pinned (each value the
+                               exact-rational nearest fp32 to k / 127)
   blockwise.nearest_level,
   blockwise.quantize_4bit      pinned (brute force at every decision point,
-                               Eq. 1 rounding for Int4, round trips, equality
-                               with the NF4 quantiser, NF4 lowest error on
-                               normal weights)
+                               Eq. 1 rounding for Int4 and Int8, round trips,
+                               equality with the NF4 quantiser, NF4 lowest
+                               error on normal weights)
   linear.forward / backward    pinned (brute force, finite differences,
                                special cases, torch.autograd in fp64)
   optim.clip_scale /

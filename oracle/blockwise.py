@@ -42,7 +42,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from .codebook import NF4, ZERO_CODE, CODEBOOKS, CODE_NF4, sorted_levels, zero_code
+from .codebook import NF4, ZERO_CODE, CODEBOOKS, CODE_NF4, CODE_INT8, INT8, codebook_of, sorted_levels, zero_code
 from . import fp8_e4m3
 
 BLOCKSIZE = 64      # first-level block (elements of W per constant)
@@ -80,7 +80,7 @@ def nearest_code(x, codebook=NF4):
     x = np.asarray(x, dtype=_F32).reshape(-1).astype(np.float64)
     q = np.asarray(codebook, dtype=np.float64)
     out = np.empty(x.size, dtype=np.int64)
-    step = 1 << 18
+    step = max(1024, (1 << 22) // q.size)  # rows per slice of the distance matrix
     for s in range(0, x.size, step):
         d = np.abs(x[s:s + step, None] - q[None, :])
         out[s:s + step] = np.argmin(d, axis=1)  # first occurrence = lower index
@@ -88,8 +88,8 @@ def nearest_code(x, codebook=NF4):
 
 
 def nearest_level(x, codebook):
-    """Code of the nearest value of a 16-entry codebook for each fp32 x, ties
-    to the smaller value (G6, G14).  Brute force over the codebook's sorted
+    """Code of the nearest value of a codebook (16 or 256 entries) for each
+    fp32 x, ties to the smaller value (G6, G14).  Brute force over the codebook's sorted
     distinct values in fp64, as nearest_code; for NF4, whose codes are in
     increasing order, the two agree."""
     vals, codes = sorted_levels(codebook)
@@ -118,9 +118,10 @@ def bf16_bits(x):
 
 def quantize_4bit(w, codebook, blocksize=BLOCKSIZE):
     """quantize_nf4 against any of the 4-bit codebooks of section 3's data
-    type comparison (G14): the same absmax scaling and reciprocal, then the
-    nearest codebook value, ties to the smaller value; an all-zero block gets
-    the code of 0.0.  For NF4 the result equals quantize_nf4's."""
+    type comparison (G14), or the 256-entry Int8 table (Eq. 1 read
+    blockwise): the same absmax scaling and reciprocal, then the nearest
+    codebook value, ties to the smaller value; an all-zero block gets the
+    code of 0.0.  For NF4 the result equals quantize_nf4's."""
     flat = np.asarray(w, dtype=_F32).reshape(-1)
     n = flat.size
     c2 = block_absmax(flat, blocksize)
@@ -295,7 +296,7 @@ class QuantState:
 
     def __init__(self, shape, codes, c2, double_quant, absmax_q=None, scale2=None, mu=None, code_type=CODE_NF4):
         self.shape = tuple(shape)
-        self.code_type = code_type  # which 4-bit codebook the codes index
+        self.code_type = code_type  # which codebook the codes index (4-bit types, Int8)
         self.codes = codes          # uint8 per element
         self.c2 = c2                # fp32 per block (exact first-level constant)
         self.double_quant = double_quant
@@ -305,6 +306,10 @@ class QuantState:
 
     @property
     def packed(self):
+        """The stored code bytes: two 4-bit codes per byte (G8); Int8 codes
+        one per byte."""
+        if self.code_type == CODE_INT8:
+            return np.asarray(self.codes, dtype=np.uint8).copy()
         return pack_nibbles(self.codes)
 
     def c2_hat(self):
@@ -313,28 +318,29 @@ class QuantState:
         return self.c2
 
     def dequantize(self):
-        return dequantize(self.codes, self.c2_hat(), codebook=CODEBOOKS[self.code_type]).reshape(self.shape)
+        return dequantize(self.codes, self.c2_hat(), codebook=codebook_of(self.code_type)).reshape(self.shape)
 
 
 def quantize(w, double_quant=True, code_type=CODE_NF4):
-    """NF4 (or another 4-bit type of section 3's comparison, G14) + optional
-    double quantisation of a tensor, as QLoRA section 3 defines its storage
-    type."""
+    """NF4 (or another 4-bit type of section 3's comparison, G14, or
+    blockwise Int8, Eq. 1) + optional double quantisation of a tensor, as
+    QLoRA section 3 defines its storage type."""
     w = np.asarray(w, dtype=_F32)
     if code_type == CODE_NF4:
         codes, c2 = quantize_nf4(w)
     else:
-        codes, c2 = quantize_4bit(w, CODEBOOKS[code_type])
+        codes, c2 = quantize_4bit(w, codebook_of(code_type))
     if not double_quant:
         return QuantState(w.shape, codes, c2, False, code_type=code_type)
     q, s2, mu = double_quantize(c2)
     return QuantState(w.shape, codes, c2, True, q, s2, mu, code_type=code_type)
 
 
-def storage_bytes(numel, double_quant=True):
-    """Bytes of each stored buffer for a tensor of `numel` elements."""
+def storage_bytes(numel, double_quant=True, code_type=CODE_NF4):
+    """Bytes of each stored buffer for a tensor of `numel` elements (Int8
+    codes take a byte each, the 4-bit types half a byte)."""
     nb = _num_blocks(numel, BLOCKSIZE)
-    out = {"codes": (numel + 1) // 2}
+    out = {"codes": numel if code_type == CODE_INT8 else (numel + 1) // 2}
     if double_quant:
         out["absmax_q"] = nb
         out["scale2"] = 4 * _num_blocks(nb, BLOCKSIZE2)

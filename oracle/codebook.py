@@ -113,17 +113,42 @@ INT4 = _int4()
 CODEBOOKS = {CODE_NF4: NF4, CODE_FP4_E2M1: FP4_E2M1, CODE_FP4_E3M0: FP4_E3M0, CODE_INT4: INT4}
 
 
+# ---------------------------------------------------- the 8-bit storage type
+# Section 2, Eq. 1 quantises to Int8 by absmax scaling into [-127, 127], and
+# Tables 3 and 4 of section 5 compare QLoRA with Int8 against NF4.  Read
+# blockwise (same 64-blocks and double quantisation as NF4) and exactly like
+# Int4 above with 2^7 - 1 = 127 levels per side: code = the two's-complement
+# byte of k, value k / 127 rounded to fp32; the byte 0x80 (k = -128) is never
+# produced by quantisation.  Not in CODEBOOKS, which holds the 4-bit types.
+CODE_INT8 = 4
+
+
+def _int8():
+    return np.array([(c - 256 if c >= 128 else c) / 127.0 for c in range(256)], dtype=np.float32)
+
+
+INT8 = _int8()
+
+
+def codebook_of(code_type):
+    """Value table of a code type: 16 entries for the 4-bit types, 256 for Int8."""
+    return INT8 if code_type == CODE_INT8 else CODEBOOKS[code_type]
+
+
 def sorted_levels(codebook):
-    """The distinct values of a 16-entry codebook in increasing order, each
-    with the code that stands for it (the smallest such code, so +0 rather
-    than -0 for the float types).  Nearest-value search runs over this list,
-    ties to the smaller value (G6 read per value: for NF4 the smaller value
-    is the lower index)."""
+    """The distinct values of a codebook (16 or 256 entries) in increasing
+    order, each with the code that stands for it (the smallest such code, so
+    +0 rather than -0 for the float types).  Nearest-value search runs over
+    this list, ties to the smaller value (G6 read per value: for NF4 the
+    smaller value is the lower index)."""
     cb = np.asarray(codebook, dtype=np.float32)
+    first = {}
+    for i, x in enumerate(cb):
+        first.setdefault(float(x), i)
     vals, codes = [], []
-    for v in sorted(set(float(x) for x in cb)):
+    for v in sorted(first):
         vals.append(v)
-        codes.append(min(i for i in range(16) if float(cb[i]) == v))
+        codes.append(first[v])
     return np.array(vals, dtype=np.float32), np.array(codes, dtype=np.uint8)
 
 

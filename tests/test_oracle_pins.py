@@ -464,14 +464,14 @@ def _nearest_bruteforce(x, cb):
     """Smallest-value code among those at minimal |x - v| (exact in fp64)."""
     d = [abs(float(x) - float(v)) for v in cb]
     best = min(d)
-    cands = [c for c in range(16) if d[c] == best]
+    cands = [c for c in range(len(cb)) if d[c] == best]
     vmin = min(float(cb[c]) for c in cands)
     return min(c for c in cands if float(cb[c]) == vmin)
 
 
 def test_nearest_level_bruteforce_all_types():
     rng = np.random.default_rng(21)
-    for ct, cb in codebook.CODEBOOKS.items():
+    for ct, cb in list(codebook.CODEBOOKS.items()) + [(codebook.CODE_INT8, codebook.INT8)]:
         vals, _ = codebook.sorted_levels(cb)
         mids = [(float(a) + float(b)) / 2 for a, b in zip(vals[:-1], vals[1:])]
         xs = list(rng.uniform(-1, 1, 300).astype(F32))
@@ -502,6 +502,102 @@ def test_int4_is_eq1_rounding_to_seven_levels():
     codes = blockwise.nearest_level(x, codebook.INT4)
     got_k = np.array([int(c) - 16 if c & 8 else int(c) for c in codes])
     assert np.array_equal(got_k[clear], k[clear].astype(int))
+
+
+# ------------------------------------------- blockwise Int8 (section 2, Eq. 1)
+
+def _nearest_f32(q):
+    """The fp32 value nearest to the rational q (ties to the even pattern),
+    by exact comparison of the candidates."""
+    c = F32(float(q))
+    cands = [np.nextafter(c, F32(-np.inf)), c, np.nextafter(c, F32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - q), int(np.asarray(v, F32).view(np.uint32)) & 1))
+
+
+def _int8_k(codes):
+    c = np.asarray(codes, dtype=np.int64)
+    return np.where(c >= 128, c - 256, c)
+
+
+def test_int8_table_is_k_over_127():
+    """Byte c stands for k / 127 rounded to fp32, k its two's-complement value."""
+    assert codebook.INT8.shape == (256,) and codebook.INT8.dtype == np.float32
+    for c in range(256):
+        k = c - 256 if c & 0x80 else c
+        assert float(codebook.INT8[c]) == float(_nearest_f32(Fraction(k, 127))), c
+    assert codebook.INT8[0] == 0.0 and codebook.INT8[127] == 1.0 and codebook.INT8[0x81] == -1.0
+    assert codebook.zero_code(codebook.INT8) == 0
+
+
+def test_int8_is_eq1_rounding_per_block():
+    """Blockwise Int8 is Eq. 1 on every 64-block: k = round(127 w / absmax),
+    ties to the smaller value, stored as its two's-complement byte (one per
+    weight); an all-zero block is all zeros and each block's absmax element
+    maps to +-127."""
+    rng = np.random.default_rng(41)
+    w = (rng.standard_normal(64 * 300) * 0.02).astype(F32)
+    w[64 * 7:64 * 8] = 0.0
+    q = blockwise.quantize(w, double_quant=False, code_type=codebook.CODE_INT8)
+    got = _int8_k(q.codes)
+    blk = np.arange(w.size) // 64
+    c2 = np.abs(w).reshape(-1, 64).max(axis=1)
+    assert np.array_equal(q.c2, c2)
+    t = 127.0 * w.astype(np.float64) / np.where(c2 > 0, c2, 1.0)[blk]
+    k = np.ceil(t - 0.5)
+    # x = w * fp32(1/absmax) is rounded to fp32 first, which moves t by under
+    # 2e-5: compare away from the decision points (the brute-force pin covers them)
+    clear = np.abs(np.abs(t - np.floor(t)) - 0.5) > 5e-5
+    assert clear.sum() > w.size - 10
+    assert np.array_equal(got[clear], k[clear].astype(np.int64))
+    assert np.all(got[64 * 7:64 * 8] == 0)
+    for b in range(300):
+        if b != 7:
+            assert abs(got[b * 64 + int(np.argmax(np.abs(w[b * 64:(b + 1) * 64])))]) == 127
+    assert q.packed.dtype == np.uint8 and np.array_equal(q.packed, q.codes.astype(np.uint8))
+    assert blockwise.storage_bytes(w.size, False, codebook.CODE_INT8)["codes"] == w.size
+
+
+def test_int8_round_trip_and_error_bound():
+    """Every level k / 127 survives quantise -> dequantise exactly when the
+    block's absmax is 1, and on normal weights the error is at most half a
+    step (absmax / 254) plus the fp32 roundings."""
+    vals = codebook.INT8[[c for c in range(256) if c != 0x80]]
+    blocks = []
+    for i in range(0, vals.size, 63):
+        b = np.zeros(64, dtype=F32)
+        part = vals[i:i + 63]
+        b[:part.size] = part
+        b[63] = F32(1.0)
+        blocks.append(b)
+    w = np.concatenate(blocks)
+    q = blockwise.quantize(w, double_quant=False, code_type=codebook.CODE_INT8)
+    assert np.array_equal(q.dequantize(), w)
+    w = (np.random.default_rng(42).standard_normal(64 * 500) * 0.02).astype(F32)
+    q = blockwise.quantize(w, double_quant=False, code_type=codebook.CODE_INT8)
+    c2 = q.c2[np.arange(w.size) // 64].astype(np.float64)
+    err = np.abs(q.dequantize().astype(np.float64) - w)
+    assert np.all(err <= c2 * (0.5 / 127 + 4e-7))
+    # Int8 reconstructs normal weights far better than any 4-bit type
+    e8 = np.sqrt(np.mean(err ** 2))
+    e4 = np.sqrt(np.mean((blockwise.quantize(w, False, codebook.CODE_NF4).dequantize() - w).astype(np.float64) ** 2))
+    assert e8 < e4 / 8
+
+
+def test_pins_catch_planted_int8_ties_to_even():
+    """Rounding 127 x half-to-even (np.rint) instead of to the smaller value
+    disagrees with the brute-force pin at an exact decision point."""
+    vals, codes = codebook.sorted_levels(codebook.INT8)
+    hits = 0
+    for i in range(1, vals.size - 1):
+        m = (float(vals[i]) + float(vals[i + 1])) / 2
+        if float(F32(m)) != m:
+            continue
+        x = F32(m)
+        right = _nearest_bruteforce(x, codebook.INT8)
+        assert int(blockwise.nearest_level(np.array([x]), codebook.INT8)[0]) == right
+        planted = int(np.rint(127.0 * float(x))) & 0xFF
+        hits += planted != right
+    assert hits > 0
 
 
 def test_other_types_round_trip_and_zero_block():
