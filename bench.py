@@ -264,11 +264,12 @@ def run_sweep(B, synth, dev, reps=3):
 
 def run_code_types(B, L, dev, reps=10):
     """Section 3's data-type comparison on the same kernels: the layer's
-    N(0, 0.02^2) fp32 weight stored as NF4, FP4 E2M1, FP4 E3M0 and Int4 (all
-    with double quantisation).  Per type: the reconstruction error of the
-    dequantised weight (||W_hat - W|| / ||W||, fp32 on the device), and the
-    median over `reps` calls of the quantise call, the bf16 dequantise call
-    and one forward + backward, each between two events."""
+    N(0, 0.02^2) fp32 weight stored as NF4, FP4 E2M1, FP4 E3M0 and Int4, and
+    as blockwise Int8 (Eq. 1; all with double quantisation).  Per type: the
+    reconstruction error of the dequantised weight (||W_hat - W|| / ||W||,
+    fp32 on the device), and the median over `reps` calls of the quantise
+    call, the bf16 dequantise call and (4-bit types; the linear kernels take
+    no Int8 weight) one forward + backward, each between two events."""
     import torch
 
     lin, t = L["lin"], L["t"]
@@ -288,7 +289,7 @@ def run_code_types(B, L, dev, reps=10):
         ts = sorted(ts[1:])
         return ts[len(ts) // 2]
 
-    for name, ct in B.CODE_TYPES.items():
+    for name, ct in list(B.CODE_TYPES.items()) + [("int8", B.QLORA_CODE_INT8)]:
         qw = B.NF4Weight(lin.N, lin.K, True, dev, ct)
         q_us = med(lambda: B.qlora_nf4_quantize(W, double_quant=True, out=qw, workspace=L["qws"]))
         d_us = med(lambda: B.qlora_nf4_dequantize(qw, bf, out=L["Wd"]))
@@ -300,12 +301,16 @@ def run_code_types(B, L, dev, reps=10):
             B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
             B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], qw, t["A"], t["B"], lin.s,
                                dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
-        fb_us = med(fb)
+        fb_us = med(fb) if ct != B.QLORA_CODE_INT8 else None
         p = lin.N * lin.K
+        code_bytes = 1.0 if ct == B.QLORA_CODE_INT8 else 0.5  # Int8 stores a byte per weight, not a nibble
         res[name] = {"rel_rms_error": err,
-                     "quantize_us": q_us, "quantize_GBps": QUANT_BYTES_PER_PARAM * p / q_us / 1e3,
-                     "dequantize_us": d_us, "dequantize_GBps": DEQUANT_BYTES_PER_PARAM * p / d_us / 1e3,
-                     "fwd_bwd_us": fb_us, "fwd_bwd_TFLOPs": linear_flops(lin) / fb_us / 1e6}
+                     "quantize_us": q_us,
+                     "quantize_GBps": (QUANT_BYTES_PER_PARAM + code_bytes - 0.5) * p / q_us / 1e3,
+                     "dequantize_us": d_us,
+                     "dequantize_GBps": (DEQUANT_BYTES_PER_PARAM + code_bytes - 0.5) * p / d_us / 1e3,
+                     "fwd_bwd_us": fb_us,
+                     "fwd_bwd_TFLOPs": linear_flops(lin) / fb_us / 1e6 if fb_us else None}
         del qw
     return res
 

@@ -26,11 +26,14 @@ QLORA_ERR_HIP = -5
 QLORA_DTYPE_F32 = 0
 QLORA_DTYPE_BF16 = 1
 
-# qlora_code_type: the 4-bit codebook of a quantised weight
+# qlora_code_type: the codebook of a quantised weight.  CODE_TYPES are the
+# 4-bit types, which every entry point takes; INT8 (one byte per weight) is
+# taken by quantisation and dequantisation only.
 QLORA_CODE_NF4 = 0
 QLORA_CODE_FP4_E2M1 = 1
 QLORA_CODE_FP4_E3M0 = 2
 QLORA_CODE_INT4 = 3
+QLORA_CODE_INT8 = 4
 CODE_TYPES = {"nf4": QLORA_CODE_NF4, "fp4_e2m1": QLORA_CODE_FP4_E2M1, "fp4_e3m0": QLORA_CODE_FP4_E3M0,
               "int4": QLORA_CODE_INT4}
 BLOCKSIZE = 64
@@ -39,7 +42,7 @@ MAX_RANK = 256
 
 # Every function declared in include/qlora_nf4.h.
 EXPORTED = (
-    "qlora_nf4_storage_bytes", "qlora_nf4_quantize_workspace", "qlora_linear_workspace",
+    "qlora_nf4_storage_bytes", "qlora_storage_bytes", "qlora_nf4_quantize_workspace", "qlora_linear_workspace",
     "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string", "qlora_last_error",
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
@@ -88,6 +91,7 @@ def lib():
         raise QLoraLibraryError(f"cannot load {LIB_PATH}: {e}") from e
     sig = {
         "qlora_nf4_storage_bytes": (_i32, [_i64, _i32, ctypes.POINTER(_i64)]),
+        "qlora_storage_bytes": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_i64)]),
         "qlora_nf4_quantize_workspace": (_i32, [_i64, _i32, ctypes.POINTER(_i64)]),
         "qlora_linear_workspace": (_i32, [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
         "qlora_nf4_codebook": (_i32, [ctypes.POINTER(_f32)]),
@@ -150,6 +154,12 @@ def qlora_nf4_storage_bytes(numel, double_quant=True):
     return dict(zip(("codes", "absmax_q", "absmax", "scale2", "offset"), list(out)))
 
 
+def qlora_storage_bytes(numel, double_quant=True, code_type=QLORA_CODE_NF4):
+    out = (_i64 * 5)()
+    _check(lib().qlora_storage_bytes(numel, int(double_quant), int(code_type), out), "qlora_storage_bytes")
+    return dict(zip(("codes", "absmax_q", "absmax", "scale2", "offset"), list(out)))
+
+
 def qlora_nf4_quantize_workspace(numel, double_quant=True):
     ws = _i64(0)
     _check(lib().qlora_nf4_quantize_workspace(numel, int(double_quant), ctypes.byref(ws)),
@@ -164,7 +174,7 @@ def qlora_linear_workspace(M, N, K, r):
 
 
 def qlora_codebook(code_type):
-    out = (_f32 * 16)()
+    out = (_f32 * (256 if int(code_type) == QLORA_CODE_INT8 else 16))()
     _check(lib().qlora_codebook(int(code_type), out), "qlora_codebook")
     return list(out)
 
@@ -186,13 +196,14 @@ def qlora_profile_events(kernel, start=None, stop=None):
 # ----------------------------------------------------------- quantised weight
 
 class NF4Weight:
-    """Device buffers of one NF4-quantised weight [rows, cols] plus the C
-    descriptor that points at them."""
+    """Device buffers of one NF4-quantised weight [rows, cols] (or one of
+    another storage type, `code_type`) plus the C descriptor that points at
+    them."""
 
     def __init__(self, rows, cols, double_quant=True, device=None, code_type=QLORA_CODE_NF4):
         self.rows, self.cols, self.double_quant = int(rows), int(cols), bool(double_quant)
         self.code_type = int(code_type)
-        sizes = qlora_nf4_storage_bytes(self.rows * self.cols, self.double_quant)
+        sizes = qlora_storage_bytes(self.rows * self.cols, self.double_quant, self.code_type)
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
         u8 = torch.uint8
         # Pad every buffer to a 16-byte multiple so vector accesses never leave it.
@@ -239,7 +250,7 @@ class NF4Weight:
 def qlora_nf4_quantize(w, double_quant=True, out=None, workspace=None, stream=None, code_type=QLORA_CODE_NF4):
     """Quantise fp32 or bf16 tensor `w` ([rows, cols] or 1-D) into an
     NF4Weight (new or `out`; `out` keeps its own code_type).  `code_type`
-    (a QLORA_CODE_* value) picks the 4-bit codebook of a new weight.
+    (a QLORA_CODE_* value) picks the codebook of a new weight.
     `workspace`: optional uint8 device tensor of at least
     qlora_nf4_quantize_workspace bytes."""
     _need_cuda(w)

@@ -67,7 +67,7 @@ int check_desc(const qlora_nf4_t* q, const char* fn) {
     return fail(QLORA_ERR_INVALID_ARG, "%s: blocksize must be 64 and blocksize2 256", fn);
   if (q->double_quant != 0 && q->double_quant != 1)
     return fail(QLORA_ERR_INVALID_ARG, "%s: double_quant must be 0 or 1", fn);
-  if (q->code_type < 0 || q->code_type >= CODE_TYPES)
+  if (q->code_type < 0 || q->code_type > CODE_INT8)
     return fail(QLORA_ERR_INVALID_ARG, "%s: code_type must be one of the qlora_code_type values", fn);
   if (q->rows * q->cols == 0) return QLORA_OK;
   if (!q->codes) return fail(QLORA_ERR_INVALID_ARG, "%s: codes is NULL", fn);
@@ -153,6 +153,9 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
 int check_linear_shape(const qlora_nf4_t* W, int64_t M, int32_t r, const char* fn) {
   int st = check_desc(W, fn);
   if (st) return st;
+  if (W->code_type == CODE_INT8)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: the linear kernels take 4-bit codes; Int8 weights are not supported",
+                fn);
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M < 0", fn);
   if (W->rows <= 0 || W->cols <= 0 || W->rows % 64 || W->cols % 64)
     return fail(QLORA_ERR_INVALID_ARG, "%s: weight [N, K] needs N, K > 0 and multiples of 64 (got %lld x %lld)",
@@ -205,9 +208,22 @@ int qlora_nf4_codebook(float* out) {
 
 int qlora_codebook(int32_t code_type, float* out) {
   if (!out) return fail(QLORA_ERR_INVALID_ARG, "qlora_codebook: out is NULL");
-  if (code_type < 0 || code_type >= CODE_TYPES)
+  if (code_type < 0 || code_type > CODE_INT8)
     return fail(QLORA_ERR_INVALID_ARG, "qlora_codebook: code_type must be one of the qlora_code_type values");
-  memcpy(out, code_values(code_type).v, sizeof(float) * 16);
+  if (code_type == CODE_INT8) memcpy(out, int8_tables().value, sizeof(float) * 256);
+  else memcpy(out, code_values(code_type).v, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_storage_bytes(int64_t numel, int32_t double_quant, int32_t code_type, int64_t* bytes) {
+  if (code_type < 0 || code_type > CODE_INT8)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_storage_bytes: code_type must be one of the qlora_code_type values");
+  if (!bytes) return fail(QLORA_ERR_INVALID_ARG, "qlora_storage_bytes: bytes is NULL");
+  if (numel < 0 || numel >= kMaxNumel) return fail(QLORA_ERR_INVALID_ARG, "qlora_storage_bytes: bad numel");
+  if (double_quant != 0 && double_quant != 1)
+    return fail(QLORA_ERR_INVALID_ARG, "qlora_storage_bytes: double_quant must be 0 or 1");
+  qlora_nf4_storage_bytes(numel, double_quant, bytes);
+  if (code_type == CODE_INT8) bytes[0] = numel;
   return QLORA_OK;
 }
 

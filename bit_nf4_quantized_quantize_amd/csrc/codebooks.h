@@ -17,6 +17,12 @@ namespace qlora {
 
 enum CodeType { CODE_NF4 = 0, CODE_FP4_E2M1 = 1, CODE_FP4_E3M0 = 2, CODE_INT4 = 3, CODE_TYPES = 4 };
 
+// The 8-bit storage type (QLoRA section 2, Eq. 1, read blockwise like the
+// 4-bit types): one byte per weight, the two's complement of k, value k / 127
+// rounded to fp32 (256 entries; k = -128 is never produced).  The 4-bit
+// tables above and the GEMM kernels do not cover it.
+constexpr int CODE_INT8 = CODE_TYPES;
+
 #define QLORA_CODE_VALUES                                                                                      \
   {                                                                                                            \
     {-1.0f, -0.6961928009986877f, -0.5250730514526367f, -0.39491748809814453f, -0.28444138169288635f,         \

@@ -40,6 +40,16 @@ struct CodeSpec {
   int nmid;
 };
 
+// Int8 tables: value[c] of code byte c, and the 254 decision thresholds
+// between the levels k and k + 1 (k = -127 .. 126) at thr[k + 127]: the
+// exact midpoint of the two fp32 values rounded toward -inf, so that
+// "x > thr" equals "x > midpoint" for every fp32 x.
+struct Int8Tables {
+  float value[256];
+  float thr[254];
+};
+const Int8Tables& int8_tables();
+
 // Library copies of the codebook values, the NF4 quantisation table and the
 // spec of the finer table of another codebook.
 const NF4Values& code_values(int code_type);

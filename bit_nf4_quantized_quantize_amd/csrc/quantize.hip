@@ -132,6 +132,24 @@ const CodeSpec& code_spec(int code_type) {
   return specs[code_type];
 }
 
+// Int8 values k / 127: the fp64 quotient is correctly rounded and, since
+// the binary expansion of k / 127 repeats every 7 bits, never lies on an fp32
+// rounding boundary, so converting it to fp32 rounds k / 127 once.
+const Int8Tables& int8_tables() {
+  static const Int8Tables t = [] {
+    Int8Tables q;
+    for (int c = 0; c < 256; ++c) q.value[c] = (float)((double)(c >= 128 ? c - 256 : c) / 127.0);
+    for (int k = -127; k < 127; ++k) {
+      const double mid = 0.5 * ((double)q.value[k & 0xFF] + (double)q.value[(k + 1) & 0xFF]);
+      float f = (float)mid;
+      if ((double)f > mid) f = nextafterf(f, -INFINITY);
+      q.thr[k + 127] = f;
+    }
+    return q;
+  }();
+  return t;
+}
+
 // --------------------------------------------------- exact mean of c2
 // The mean mu is the exact sum of all c2 divided by their count, rounded
 // once to fp32.  Every non-negative fp32 value is an integer multiple of
@@ -477,10 +495,158 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
   }
 }
 
+// ------------------------------------------------- Int8 quantise kernel
+// Blockwise Eq. 1 with 127 levels per side.  A lane codes 8 consecutive
+// weights (one 8-byte store), an octet of lanes one 64-block, a wave 512
+// weights per step.  Waves stride over the steps of the tensor, U steps per
+// iteration so that U loads are in flight (the last, partial step with
+// bounds checks); every lane takes its octet's
+// absmax (DPP) and the correctly rounded reciprocal itself.  The level of x:
+// p0 = rint(127 x) is within one of it, the side of 127 x from p0 names the
+// pair (p, p + 1) it lies between, and one threshold of that pair decides
+// (ties keep p, the smaller value).  NaN and out-of-range x clamp into
+// [-127, 127].  Away from the decision points p0 itself is the level, so the
+// threshold lookup runs only for lanes holding a weight near one.  Exact-sum counters and the c2 layout are those of the 4-bit
+// kernel, so double quantisation is shared.
+
+// 16 waves per workgroup (the grid is capped at QZ_MAX_WG workgroups, one
+// exact-sum partial each, so occupancy comes from the workgroup size).
+constexpr int Q8_THREADS = 1024;
+constexpr int Q8_WAVES = Q8_THREADS / 64;
+
+template <bool BF16>
+struct Q8Geo {
+  static constexpr int U = BF16 ? 4 : 1;   // steps in flight per wave
+  static constexpr int NV = BF16 ? 1 : 2;  // 16-byte loads per lane and step
+};
+
+__device__ __forceinline__ uint32_t int8_code_exact(float x, const float* s_thr) {
+  const float t = x * 127.0f;
+  const float p0 = __builtin_rintf(t);
+  float p = t >= p0 ? p0 : p0 - 1.0f;
+  p = fminf(fmaxf(p, -127.0f), 126.0f);  // NaN becomes -127
+  const int pi = (int)p;
+  return (uint32_t)(pi + (x > s_thr[pi + 127] ? 1 : 0)) & 0xFFu;
+}
+
+// Fast path: rint(127 x) is the level unless 127 x lies within 5e-4 of a
+// half-integer (the fp32 roundings of 127 x and of the levels k / 127 move
+// the comparison by under 1e-5).  Such an x, or NaN, sets `near`, and the
+// caller codes the lane again through the thresholds.
+__device__ __forceinline__ uint32_t int8_code_fast(float x, bool& near) {
+  const float t = x * 127.0f;
+  const float p0 = __builtin_rintf(t);
+  near = near || !(fabsf(t - p0) <= 0.4995f);
+  return (uint32_t)(int)p0 & 0xFFu;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* __restrict__ w, int64_t numel,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   float* __restrict__ c2out,
+                                                                   uint64_t* __restrict__ partials, Int8Tables tab) {
+  constexpr int U = Q8Geo<BF16>::U, NV = Q8Geo<BF16>::NV;
+  constexpr int ES = BF16 ? 2 : 4;
+  __shared__ float s_thr[254];
+  __shared__ unsigned long long s_acc[Q8_WAVES][kMeanDigits];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < 254) s_thr[tid] = tab.thr[tid];
+  if (tid < Q8_WAVES * kMeanDigits) (&s_acc[0][0])[tid] = 0;
+  __syncthreads();
+  unsigned long long* acc = partials ? s_acc[wave] : nullptr;
+  const int64_t nb = (numel + 63) >> 6;
+  const int64_t nsteps = (numel + 511) >> 9, GW = (int64_t)gridDim.x * Q8_WAVES;
+
+  // One step of a lane: 8 codes and, from lane 8j of each octet, the
+  // block's constant.  `full`: all 512 weights of the step exist.
+  auto code_step = [&](const qz_u32x4* r, int64_t e0, bool full) {
+    const float c2 = __uint_as_float(octet_max(absmax_bits<BF16>(r)));
+    const bool tiny = c2 > 0.0f && c2 < kTiny;
+    const float sc = tiny ? kPrescale : 1.0f;
+    const float cs = c2 * sc;
+    const float inv = cs > 0.0f ? 1.0f / cs : 0.0f;  // correctly rounded division
+    float x[8];
+    if (__builtin_amdgcn_ballot_w64(tiny)) {  // rare, wave-uniform
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (weight_of<BF16>(r, i) * sc) * inv;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = weight_of<BF16>(r, i) * inv;
+    }
+    bool near = false;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = int8_code_fast(x[i], near);
+      if (i < 4) lo |= b << (8 * i);
+      else hi |= b << (8 * (i - 4));
+    }
+    if (near) {
+      lo = hi = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = int8_code_exact(x[i], s_thr);
+        if (i < 4) lo |= b << (8 * i);
+        else hi |= b << (8 * (i - 4));
+      }
+    }
+    if (full || e0 + 7 < numel) {
+      *reinterpret_cast<uint2*>(codes + e0) = make_uint2(lo, hi);
+    } else if (e0 < numel) {
+      for (int i = 0; i < 8 && e0 + i < numel; ++i) codes[e0 + i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
+    }
+    const int64_t blk = e0 >> 6;
+    if ((lane & 7) == 0 && (full || blk < nb)) {
+      c2out[blk] = c2;
+      if (acc && c2 > 0.0f) add_c2(acc, c2);
+    }
+  };
+
+  const int64_t nfull = numel >> 9;  // steps with all 512 weights present
+  for (int64_t t = (int64_t)blockIdx.x * Q8_WAVES + wave; t < nsteps; t += U * GW) {  // wave-uniform
+    qz_u32x4 r[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tu = t + u * GW, e0 = (tu << 9) + lane * 8;
+      if (tu < nfull) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) r[u][v] = *reinterpret_cast<const qz_u32x4*>((const char*)w + e0 * ES + 16 * v);
+      } else if (tu < nsteps) {
+        load_partial<BF16>(w, e0, numel, r[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tu = t + u * GW;
+      if (tu < nfull) code_step(r[u], (tu << 9) + lane * 8, true);
+      else if (tu < nsteps) code_step(r[u], (tu << 9) + lane * 8, false);
+    }
+  }
+  if (partials) {
+    __syncthreads();
+    if (tid < kMeanDigits) {
+      unsigned long long s = 0;
+#pragma unroll
+      for (int v = 0; v < Q8_WAVES; ++v) s += s_acc[v][tid];
+      partials[(int64_t)tid * gridDim.x + blockIdx.x] = s;  // digit-major
+    }
+  }
+}
+
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_type, uint8_t* codes, float* c2,
                            uint64_t* partials, hipStream_t stream) {
-  if (code_type < 0 || code_type >= CODE_TYPES) return hipErrorInvalidValue;
+  if (code_type < 0 || code_type > CODE_INT8) return hipErrorInvalidValue;
   const dim3 grid((unsigned)quantize_parts(numel)), block(QZ_THREADS);
+  if (code_type == CODE_INT8) {
+    const Int8Tables& t8 = int8_tables();
+    if (w_bf16)
+      hipLaunchKernelGGL((int8_quantize_kernel<true>), grid, dim3(Q8_THREADS), 0, stream, w, numel, codes, c2,
+                         partials, t8);
+    else
+      hipLaunchKernelGGL((int8_quantize_kernel<false>), grid, dim3(Q8_THREADS), 0, stream, w, numel, codes, c2,
+                         partials, t8);
+    return hipGetLastError();
+  }
   const QuantTable& tab = quant_table();
   const CodeSpec& spec = code_spec(code_type);
   if (code_type == CODE_NF4) {
@@ -696,35 +862,89 @@ hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* part
 }
 
 // --------------------------------------------------------- dequantise
-// Each thread expands 8 codes (one 32-bit word) of one block; a workgroup of
-// 256 threads covers 4 x 2048 weights.  c2_hat is computed as two separately
-// rounded fp32 operations (this file is built without contraction).
+// Each thread expands 8 codes (one 32-bit word of 4-bit codes, or 8 Int8
+// bytes) of one block; a workgroup of 256 threads covers 4 x 2048 weights.
+// c2_hat is computed as two separately rounded fp32 operations (this file is
+// built without contraction).
 
 constexpr int DQZ_THREADS = 256;
 constexpr int DQZ_STEPS = 4;
 constexpr int DQZ_PER_WG = DQZ_THREADS * 8 * DQZ_STEPS;
 
-template <bool DQ, bool BF16_OUT>
+// Value of every code: 16 entries used for the 4-bit types, 256 for Int8.
+struct DequantTable {
+  float v[256];
+};
+
+// Codes e0 .. e0 + 7 as 8 table indices packed in 4 bits (uint2.x) or 8 bits
+// (uint2.y:x) each.
+template <bool INT8>
+__device__ __forceinline__ uint2 load_codes8(const uint8_t* __restrict__ codes, int64_t e0) {
+  if (INT8) return *reinterpret_cast<const uint2*>(codes + e0);
+  return make_uint2(*reinterpret_cast<const uint32_t*>(codes + (e0 >> 1)), 0u);
+}
+
+template <bool INT8>
+__device__ __forceinline__ uint2 load_codes8_partial(const uint8_t* __restrict__ codes, int64_t e0, int64_t numel) {
+  uint32_t lo = 0, hi = 0;
+  if (INT8) {
+    for (int i = 0; i < 8 && e0 + i < numel; ++i) {
+      const uint32_t b = codes[e0 + i];
+      if (i < 4) lo |= b << (8 * i);
+      else hi |= b << (8 * (i - 4));
+    }
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (e0 + 2 * i < numel) lo |= (uint32_t)codes[(e0 >> 1) + i] << (8 * i);
+  }
+  return make_uint2(lo, hi);
+}
+
+template <bool INT8>
+__device__ __forceinline__ uint32_t code_at(uint2 c, int i) {
+  if (INT8) return ((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu;
+  return (c.x >> (4 * i)) & 0xFu;
+}
+
+template <bool BF16_OUT>
+__device__ __forceinline__ void store8(void* __restrict__ out, int64_t e0, const float v[8]) {
+  if (BF16_OUT) {
+    uint4 o;
+    o.x = pack_bf2(v[0], v[1]);
+    o.y = pack_bf2(v[2], v[3]);
+    o.z = pack_bf2(v[4], v[5]);
+    o.w = pack_bf2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = o;
+  } else {
+    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <bool DQ, bool BF16_OUT, bool INT8>
 __global__ __launch_bounds__(DQZ_THREADS) void nf4_dequant_kernel(const uint8_t* __restrict__ codes, int64_t numel,
                                                                   const uint8_t* __restrict__ absmax_q,
                                                                   const float* __restrict__ absmax,
                                                                   const float* __restrict__ scale2,
                                                                   const float* __restrict__ offset,
-                                                                  void* __restrict__ out, NF4Values nf4) {
-  __shared__ float s_nf4[16];
-  if (threadIdx.x < 16) s_nf4[threadIdx.x] = nf4.v[threadIdx.x];
+                                                                  void* __restrict__ out, DequantTable tab) {
+  constexpr int NT = INT8 ? 256 : 16;
+  __shared__ float s_val[NT];
+  if (threadIdx.x < NT) s_val[threadIdx.x] = tab.v[threadIdx.x];
   __syncthreads();
   const float mu = DQ ? *offset : 0.0f;
   const int64_t wg0 = (int64_t)blockIdx.x * DQZ_PER_WG;
   if (wg0 + DQZ_PER_WG <= numel) {
     // a whole chunk: every load goes out before the first is used
-    uint32_t word[DQZ_STEPS], qb[DQZ_STEPS];
+    uint2 word[DQZ_STEPS];
+    uint32_t qb[DQZ_STEPS];
     float f[DQZ_STEPS];
 #pragma unroll
     for (int s = 0; s < DQZ_STEPS; ++s) {
       const int64_t e0 = wg0 + ((int64_t)s * DQZ_THREADS + threadIdx.x) * 8;
       const int64_t blk = e0 >> 6;
-      word[s] = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
+      word[s] = load_codes8<INT8>(codes, e0);
       if (DQ) {
         qb[s] = absmax_q[blk];
         f[s] = scale2[blk >> 8];
@@ -739,19 +959,8 @@ __global__ __launch_bounds__(DQZ_THREADS) void nf4_dequant_kernel(const uint8_t*
       const float c = DQ ? e4m3_decode(qb[s]) * f[s] + mu : f[s];
       float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = s_nf4[(word[s] >> (4 * i)) & 0xF] * c;
-      if (BF16_OUT) {
-        uint4 o;
-        o.x = pack_bf2(v[0], v[1]);
-        o.y = pack_bf2(v[2], v[3]);
-        o.z = pack_bf2(v[4], v[5]);
-        o.w = pack_bf2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = o;
-      } else {
-        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
-        o[0] = make_float4(v[0], v[1], v[2], v[3]);
-        o[1] = make_float4(v[4], v[5], v[6], v[7]);
-      }
+      for (int i = 0; i < 8; ++i) v[i] = s_val[code_at<INT8>(word[s], i)] * c;
+      store8<BF16_OUT>(out, e0, v);
     }
     return;
   }
@@ -767,30 +976,12 @@ __global__ __launch_bounds__(DQZ_THREADS) void nf4_dequant_kernel(const uint8_t*
     } else {
       c = absmax[blk];
     }
-    uint32_t word;
-    if (e0 + 7 < numel) {
-      word = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
-    } else {
-      word = 0;
-      for (int i = 0; i < 4; ++i)
-        if (e0 + 2 * i < numel) word |= (uint32_t)codes[(e0 >> 1) + i] << (8 * i);
-    }
+    const uint2 word = e0 + 7 < numel ? load_codes8<INT8>(codes, e0) : load_codes8_partial<INT8>(codes, e0, numel);
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = s_nf4[(word >> (4 * i)) & 0xF] * c;
+    for (int i = 0; i < 8; ++i) v[i] = s_val[code_at<INT8>(word, i)] * c;
     if (e0 + 7 < numel) {
-      if (BF16_OUT) {
-        uint4 o;
-        o.x = pack_bf2(v[0], v[1]);
-        o.y = pack_bf2(v[2], v[3]);
-        o.z = pack_bf2(v[4], v[5]);
-        o.w = pack_bf2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = o;
-      } else {
-        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
-        o[0] = make_float4(v[0], v[1], v[2], v[3]);
-        o[1] = make_float4(v[4], v[5], v[6], v[7]);
-      }
+      store8<BF16_OUT>(out, e0, v);
     } else {
       for (int i = 0; i < 8; ++i) {
         if (e0 + i >= numel) break;
@@ -801,28 +992,41 @@ __global__ __launch_bounds__(DQZ_THREADS) void nf4_dequant_kernel(const uint8_t*
   }
 }
 
+template <bool INT8>
+hipError_t launch_dequant_t(const uint8_t* codes, int64_t numel, bool dq, const uint8_t* absmax_q,
+                            const float* absmax, const float* scale2, const float* offset, void* out, bool out_bf16,
+                            const DequantTable& t, hipStream_t stream) {
+  const dim3 grid((unsigned)((numel + DQZ_PER_WG - 1) / DQZ_PER_WG)), block(DQZ_THREADS);
+  if (dq) {
+    if (out_bf16)
+      hipLaunchKernelGGL((nf4_dequant_kernel<true, true, INT8>), grid, block, 0, stream, codes, numel, absmax_q,
+                         absmax, scale2, offset, out, t);
+    else
+      hipLaunchKernelGGL((nf4_dequant_kernel<true, false, INT8>), grid, block, 0, stream, codes, numel, absmax_q,
+                         absmax, scale2, offset, out, t);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((nf4_dequant_kernel<false, true, INT8>), grid, block, 0, stream, codes, numel, absmax_q,
+                         absmax, scale2, offset, out, t);
+    else
+      hipLaunchKernelGGL((nf4_dequant_kernel<false, false, INT8>), grid, block, 0, stream, codes, numel, absmax_q,
+                         absmax, scale2, offset, out, t);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, int code_type, bool dq, const uint8_t* absmax_q,
                              const float* absmax, const float* scale2, const float* offset, void* out,
                              bool out_bf16, hipStream_t stream) {
-  if (code_type < 0 || code_type >= CODE_TYPES) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((numel + DQZ_PER_WG - 1) / DQZ_PER_WG)), block(DQZ_THREADS);
-  const NF4Values& t = code_values(code_type);
-  if (dq) {
-    if (out_bf16)
-      hipLaunchKernelGGL((nf4_dequant_kernel<true, true>), grid, block, 0, stream, codes, numel, absmax_q, absmax,
-                         scale2, offset, out, t);
-    else
-      hipLaunchKernelGGL((nf4_dequant_kernel<true, false>), grid, block, 0, stream, codes, numel, absmax_q, absmax,
-                         scale2, offset, out, t);
-  } else {
-    if (out_bf16)
-      hipLaunchKernelGGL((nf4_dequant_kernel<false, true>), grid, block, 0, stream, codes, numel, absmax_q, absmax,
-                         scale2, offset, out, t);
-    else
-      hipLaunchKernelGGL((nf4_dequant_kernel<false, false>), grid, block, 0, stream, codes, numel, absmax_q, absmax,
-                         scale2, offset, out, t);
+  if (code_type < 0 || code_type > CODE_INT8) return hipErrorInvalidValue;
+  DequantTable t;
+  memset(&t, 0, sizeof(t));
+  if (code_type == CODE_INT8) {
+    memcpy(t.v, int8_tables().value, sizeof(t.v));
+    return launch_dequant_t<true>(codes, numel, dq, absmax_q, absmax, scale2, offset, out, out_bf16, t, stream);
   }
-  return hipGetLastError();
+  memcpy(t.v, code_values(code_type).v, 16 * sizeof(float));
+  return launch_dequant_t<false>(codes, numel, dq, absmax_q, absmax, scale2, offset, out, out_bf16, t, stream);
 }
 
 }  // namespace qlora

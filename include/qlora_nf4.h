@@ -76,12 +76,21 @@ typedef enum {
  *   FP4_E3M0  code = s e2 e1 e0, magnitude 0 for e = 0, else 2^(e-7);
  *   INT4      code = two's-complement k, value k / 7 (Eq. 1 with 7 levels
  *             per side; code 8 = -8/7 is never produced by quantisation).
- * Values are fp32; qlora_codebook() returns them. */
+ * INT8 is the 8-bit type of QLoRA section 2, Eq. 1 (absmax scaling into
+ * [-127, 127]) that section 5's Tables 3 and 4 compare with NF4, read
+ * blockwise with the same 64-blocks and double quantisation: one byte per
+ * weight, the two's complement of k, value k / 127 (256 entries; byte 0x80,
+ * -128/127, is never produced by quantisation).  INT8 weights are accepted
+ * by quantisation, dequantisation and the queries; the linear entry points
+ * take the 4-bit types only and return QLORA_ERR_UNSUPPORTED_DTYPE for them.
+ * Values are fp32 (the ratios rounded to nearest); qlora_codebook() returns
+ * them. */
 typedef enum {
   QLORA_CODE_NF4 = 0,
   QLORA_CODE_FP4_E2M1 = 1,
   QLORA_CODE_FP4_E3M0 = 2,
-  QLORA_CODE_INT4 = 3
+  QLORA_CODE_INT4 = 3,
+  QLORA_CODE_INT8 = 4
 } qlora_code_type;
 
 /* Block sizes fixed by QLoRA section 3 ("QLoRA": block size 64 for W,
@@ -114,8 +123,10 @@ typedef enum {
  *   offset         f32[1]: mu, the mean of all c2_b, exact and rounded once
  *                  to fp32 (nearest-even).
  *   code_type      qlora_code_type of the codes (0 = NF4, the default).
- *                  The codes description above is NF4's; for the other types
- *                  code i stands for value i of that type's codebook.
+ *                  The codes description above is NF4's; for the other 4-bit
+ *                  types code i stands for value i of that type's codebook.
+ *                  INT8: codes is u8[numel], one byte per element in order,
+ *                  byte c standing for value c of the INT8 codebook.
  */
 typedef struct qlora_nf4 {
   int64_t rows;
@@ -141,6 +152,12 @@ typedef struct qlora_nf4 {
  * 4 + 8/64 + 32/(64*256) (+32/numel for mu) with it. */
 int qlora_nf4_storage_bytes(int64_t numel, int32_t double_quant, int64_t* bytes);
 
+/* Host only.  As qlora_nf4_storage_bytes for a weight of type `code_type`:
+ * the same constants, and codes of ceil(numel / 2) bytes for the 4-bit types
+ * or numel bytes for QLORA_CODE_INT8 (8 + 8/64 + 32/(64*256) bits per weight
+ * with double quantisation). */
+int qlora_storage_bytes(int64_t numel, int32_t double_quant, int32_t code_type, int64_t* bytes);
+
 /* Host only.  Workspace bytes qlora_nf4_quantize needs (0 without double
  * quantisation).  Written to the host pointer *ws_bytes. */
 int qlora_nf4_quantize_workspace(int64_t numel, int32_t double_quant, int64_t* ws_bytes);
@@ -155,8 +172,9 @@ int qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r,
  * (QLoRA Appendix E, code order) into the host array out[16]. */
 int qlora_nf4_codebook(float* out);
 
-/* Host only.  Copies the 16 values of codebook `code_type` (a
- * qlora_code_type, code order) into the host array out[16]. */
+/* Host only.  Copies the values of codebook `code_type` (a qlora_code_type,
+ * code order) into the host array out: 16 values, or 256 for
+ * QLORA_CODE_INT8 (out[256]). */
 int qlora_codebook(int32_t code_type, float* out);
 
 /* Text for a status code; never NULL. */
@@ -184,9 +202,10 @@ const char* qlora_last_error(void);
  * Per block b of 64 flattened weights: c2_b = max |w| (exact); each weight
  * x = fp32(w * fp32(1/c2_b)) gets the code of the nearest value of the
  * q->code_type codebook, ties to the smaller value (for NF4, the lower
- * index); an all-zero block gets the code of 0.0 throughout (NF4: 7).  With
- * double quantisation, mu = mean(c2) and each group of 256 constants is
- * stored as described for qlora_nf4_t.
+ * index); an all-zero block gets the code of 0.0 throughout (NF4: 7).  For
+ * QLORA_CODE_INT8 this is Eq. 1 per block: the byte of k = round(127 x),
+ * ties to the smaller k.  With double quantisation, mu = mean(c2) and each
+ * group of 256 constants is stored as described for qlora_nf4_t.
  */
 int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q,
                        void* ws, int64_t ws_bytes, void* stream);

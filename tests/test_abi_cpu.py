@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -45,6 +45,18 @@ def test_storage_bytes_match_closed_form():
     numel = 4096 * 4096
     bits = 8 * sum(B.qlora_nf4_storage_bytes(numel, True).values()) / numel
     assert bits == 4 + 8 / 64 + 32 / (64 * 256) + 32 / numel
+    for ct in (*B.CODE_TYPES.values(), B.QLORA_CODE_INT8):
+        for numel in (1, 63, 65, 4096 * 4096):
+            for dq in (True, False):
+                got = B.qlora_storage_bytes(numel, dq, ct)
+                assert {k: v for k, v in got.items() if v} == blockwise.storage_bytes(numel, dq, ct)
+    bits8 = 8 * sum(B.qlora_storage_bytes(numel, True, B.QLORA_CODE_INT8).values()) / numel
+    assert bits8 == 8 + 8 / 64 + 32 / (64 * 256) + 32 / numel
+    out = (ctypes.c_int64 * 5)()
+    assert B.lib().qlora_storage_bytes(64, 1, 5, out) == B.QLORA_ERR_INVALID_ARG
+    assert B.lib().qlora_storage_bytes(64, 2, 4, out) == B.QLORA_ERR_INVALID_ARG
+    assert B.lib().qlora_storage_bytes(-1, 1, 4, out) == B.QLORA_ERR_INVALID_ARG
+    assert B.lib().qlora_storage_bytes(64, 1, 4, None) == B.QLORA_ERR_INVALID_ARG
 
 
 def test_library_codebook_is_appendix_e():
@@ -58,8 +70,10 @@ def test_library_codebooks_equal_oracle_bit_exact():
     for name, ct in B.CODE_TYPES.items():
         got = np.array(B.qlora_codebook(ct), np.float32)
         assert np.array_equal(got.view(np.uint32), codebook.CODEBOOKS[ct].view(np.uint32)), name
-    out = (ctypes.c_float * 16)()
-    assert B.lib().qlora_codebook(4, out) == B.QLORA_ERR_INVALID_ARG
+    got = np.array(B.qlora_codebook(B.QLORA_CODE_INT8), np.float32)
+    assert np.array_equal(got.view(np.uint32), codebook.INT8.view(np.uint32))
+    out = (ctypes.c_float * 256)()
+    assert B.lib().qlora_codebook(5, out) == B.QLORA_ERR_INVALID_ARG
     assert B.lib().qlora_codebook(-1, out) == B.QLORA_ERR_INVALID_ARG
 
 
@@ -89,7 +103,7 @@ def test_quantize_validation():
     assert _quant(_desc(bs2=128)) == B.QLORA_ERR_INVALID_ARG
     assert _quant(_desc(dq=2)) == B.QLORA_ERR_INVALID_ARG
     d = _desc()
-    d.code_type = 4
+    d.code_type = 5
     assert _quant(d) == B.QLORA_ERR_INVALID_ARG
     assert "code_type" in L.qlora_last_error().decode()
     assert _quant(_desc(rows=-1)) == B.QLORA_ERR_INVALID_ARG
@@ -164,6 +178,14 @@ def test_linear_validation():
     assert _bwd(_desc(), dX=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert _bwd(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
     assert _bwd(_desc(), r=300) == B.QLORA_ERR_INVALID_ARG
+    # Int8 weights: quantisation and dequantisation only
+    d8 = _desc()
+    d8.code_type = B.QLORA_CODE_INT8
+    assert _fwd(d8) == B.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert "Int8" in B.lib().qlora_last_error().decode()
+    assert _bwd(d8) == B.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert _fwd_do(d8) == B.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert _bwd_do(d8) == B.QLORA_ERR_UNSUPPORTED_DTYPE
 
 
 def _fwd_do(d, keep=FAKE, p=0.1, M=16, r=8, nws=1 << 30):

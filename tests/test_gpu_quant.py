@@ -306,3 +306,58 @@ def test_code_types_decision_points(B, code_type):
         blocks.append(blk)
     w = torch.from_numpy(np.concatenate(blocks))
     _roundtrip(B, w, False, code_type)
+
+
+# --------------------------------------- blockwise Int8 (section 2, Eq. 1)
+
+@pytest.mark.parametrize("numel,bf16", [(1, False), (3, False), (63, False), (65, True), (1000, False),
+                                        (64 * 257 + 5, False), (64 * 1100 + 5, True), (64 * 256 * 3, False),
+                                        (64 * 70000 + 37, False)])
+def test_int8_round_trip(B, numel, bf16):
+    """Int8 codes (one byte per weight), constants and dequantised values,
+    bit-exact against the oracle; the sizes cover ragged tails, a short last
+    block and tensors large enough for several strides of the whole grid."""
+    _log(f"quant int8 numel={numel} bf16={bf16}")
+    g = torch.Generator().manual_seed(numel + 8)
+    w = torch.randn(numel, generator=g) * 0.02
+    if numel >= 64 * 7:
+        w[64 * 3: 64 * 4] = 0.0                  # an all-zero block
+        w[64 * 5: 64 * 6] *= 1e-39              # a subnormal block (prescaled)
+        w[64 * 6: 64 * 7] *= 1e30               # a huge block
+    if bf16:
+        w = w.to(torch.bfloat16)
+    for dq in (True, False):
+        _roundtrip(B, w, dq, B.QLORA_CODE_INT8)
+
+
+def test_int8_decision_points(B):
+    """Blocks with absmax 1 (x = w exactly) holding every decision point
+    between adjacent Int8 levels and its fp32 neighbours: ties keep the
+    smaller level."""
+    _log("quant int8 decision points")
+    vals, _ = codebook.sorted_levels(codebook.INT8)
+    xs = []
+    for a, b in zip(vals[:-1], vals[1:]):
+        m = F32((float(a) + float(b)) / 2)
+        xs += [m, np.nextafter(m, F32(-2)), np.nextafter(m, F32(2))]
+    xs = [x for x in xs if abs(float(x)) <= 1.0] + [F32(0.0), F32(-0.0), F32(-1.0)]
+    blocks = []
+    for i in range(0, len(xs), 63):
+        part = xs[i:i + 63]
+        blocks.append(np.array(part + [1.0] * (64 - len(part)), dtype=F32))
+    w = np.concatenate(blocks)
+    _roundtrip(B, torch.from_numpy(w), False, B.QLORA_CODE_INT8)
+    _roundtrip(B, torch.from_numpy(-w), True, B.QLORA_CODE_INT8)
+
+
+def test_int8_rejected_by_linear(B):
+    """The linear kernels take 4-bit codes: an Int8 weight is refused with
+    QLORA_ERR_UNSUPPORTED_DTYPE before anything is enqueued."""
+    w = torch.randn(64, 64, device="cuda") * 0.02
+    qw = B.qlora_nf4_quantize(w, code_type=B.QLORA_CODE_INT8)
+    X = torch.randn(4, 64, device="cuda").to(torch.bfloat16)
+    A = torch.zeros(64, 8, device="cuda", dtype=torch.bfloat16)
+    Bm = torch.zeros(8, 64, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(B.QLoraError) as e:
+        B.qlora_linear_fwd(X, qw, A, Bm, 2.0)
+    assert e.value.status == B.QLORA_ERR_UNSUPPORTED_DTYPE
