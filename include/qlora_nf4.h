@@ -77,7 +77,7 @@ typedef enum {
  *   INT4      code = two's-complement k, value k / 7 (Eq. 1 with 7 levels
  *             per side; code 8 = -8/7 is never produced by quantisation).
  * INT8 is the 8-bit type of QLoRA section 2, Eq. 1 (absmax scaling into
- * [-127, 127]) that section 5's Tables 3 and 4 compare with NF4, read
+ * [-127, 127]) that section 3's Table 3 compares with NF4, read
  * blockwise with the same 64-blocks and double quantisation: one byte per
  * weight, the two's complement of k, value k / 127 (256 entries; byte 0x80,
  * -128/127, is never produced by quantisation).  INT8 weights are accepted

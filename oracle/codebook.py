@@ -115,7 +115,7 @@ CODEBOOKS = {CODE_NF4: NF4, CODE_FP4_E2M1: FP4_E2M1, CODE_FP4_E3M0: FP4_E3M0, CO
 
 # ---------------------------------------------------- the 8-bit storage type
 # Section 2, Eq. 1 quantises to Int8 by absmax scaling into [-127, 127], and
-# Tables 3 and 4 of section 5 compare QLoRA with Int8 against NF4.  Read
+# section 3's Table 3 compares QLoRA with Int8 against NF4.  Read
 # blockwise (same 64-blocks and double quantisation as NF4) and exactly like
 # Int4 above with 2^7 - 1 = 127 levels per side: code = the two's-complement
 # byte of k, value k / 127 rounded to fp32; the byte 0x80 (k = -128) is never
