@@ -45,6 +45,12 @@ is in tests/test_oracle_pins.py):
   optim.clip_scale /
   optim.adamw_step             pinned (torch.optim.AdamW and clip_grad_norm_
                                in fp64 over five steps, closed forms)
+  block.forward /
+  block.forward_backward       pinned (attention against torch's causal
+                               scaled-dot-product attention and causality,
+                               rmsnorm scale invariance, identity with W = B
+                               = 0, Eq. 5 linears, finite differences of dx,
+                               dA, dB)
   linear.forward_dropout /
   linear.backward_dropout      pinned (reduction to the plain layer, brute
                                force, finite differences, torch.autograd in

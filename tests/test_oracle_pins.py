@@ -765,3 +765,106 @@ def test_clip_scale_closed_forms():
     assert optim.clip_scale([np.array([3.0, 4.0])], 0.3) == 0.3 / (5.0 + 1e-6)
     assert optim.clip_scale([np.array([0.1]), np.array([0.1])], 0.3) == 1.0
     assert optim.clip_scale([np.zeros(3)], 0.3) == 1.0
+
+
+# ------------------------------------ QLoRA decoder block (reading G18)
+
+from oracle import block  # noqa: E402
+
+
+def _tiny_block(seed, hidden=16, mlp=24, r=3, b=2, t=5):
+    rng = np.random.default_rng(seed)
+    W = {n: rng.standard_normal(sh) * 0.2 for n, sh in block.shapes(hidden, mlp).items()}
+    A = {n: rng.standard_normal((W[n].shape[1], r)) * 0.3 for n in block.LINEARS}
+    B = {n: rng.standard_normal((r, W[n].shape[0])) * 0.3 for n in block.LINEARS}
+    x = rng.standard_normal((b, t, hidden))
+    g1, g2 = 1 + 0.1 * rng.standard_normal(hidden), 1 + 0.1 * rng.standard_normal(hidden)
+    dy = rng.standard_normal((b, t, hidden))
+    return x, W, A, B, g1, g2, dy
+
+
+def _tt(a):
+    return torch.tensor(np.asarray(a, dtype=np.float64))
+
+
+def test_block_attention_is_sdpa_and_causal():
+    """The attention core equals torch's causal scaled-dot-product attention
+    (fp64), and position t ignores every later position."""
+    rng = np.random.default_rng(50)
+    q, k, v = (_tt(rng.standard_normal((2, 6, 8))) for _ in range(3))
+    got = block.causal_attention(q, k, v, heads=2)
+    split = lambda z: z.reshape(2, 6, 2, 4).permute(0, 2, 1, 3)  # noqa: E731
+    ref = torch.nn.functional.scaled_dot_product_attention(split(q), split(k), split(v), is_causal=True)
+    assert torch.allclose(got, ref.permute(0, 2, 1, 3).reshape(2, 6, 8), rtol=1e-12, atol=1e-12)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 4:] += 5.0
+    v2[:, 4:] -= 3.0
+    got2 = block.causal_attention(q, k2, v2, heads=2)
+    assert torch.equal(got[:, :4], got2[:, :4]) and not torch.allclose(got[:, 4:], got2[:, 4:])
+
+
+def test_block_rms_norm_and_identity():
+    """rmsnorm is invariant to scaling its input (up to eps); with every W and
+    every B zero the block is the identity (both residual branches vanish)."""
+    rng = np.random.default_rng(51)
+    z, g = _tt(rng.standard_normal((3, 16))), _tt(rng.standard_normal(16))
+    assert torch.allclose(block.rms_norm(z * 1e3, g), block.rms_norm(z, g), rtol=1e-6, atol=0)  # eps = 1e-6
+    one = torch.ones(16, dtype=torch.float64)
+    assert torch.allclose(torch.mean(block.rms_norm(z, one) ** 2, dim=-1), torch.ones(3, dtype=torch.float64), rtol=1e-5)
+    x, W, A, B, g1, g2, dy = _tiny_block(52)
+    W0 = {n: np.zeros_like(W[n]) for n in W}
+    B0 = {n: np.zeros_like(B[n]) for n in B}
+    y, dx, dA, dB = block.forward_backward(x, W0, A, B0, g1, g2, 0.5, 2, dy)
+    assert np.array_equal(y, x) and np.array_equal(dx, dy)
+    assert all(np.all(dA[n] == 0) for n in block.LINEARS)
+
+
+def test_block_linear_is_eq5():
+    """Each block linear is the oracle's Eq. 5 layer."""
+    x, W, A, B, *_ = _tiny_block(53)
+    X = x.reshape(-1, 16)
+    Y, _ = linear.forward(X, W["q"], A["q"], B["q"], 0.75)
+    got = block.qlora_linear(_tt(X), _tt(W["q"]), _tt(A["q"]), _tt(B["q"]), 0.75).numpy()
+    assert np.allclose(got, Y, rtol=1e-13, atol=1e-13)
+
+
+def test_block_gradients_finite_differences():
+    """Central differences of L = sum(dy * y) against the block's dx, dA, dB
+    on a sample of entries of every linear."""
+    x, W, A, B, g1, g2, dy = _tiny_block(54)
+    s, heads = 0.5, 2
+    y, dx, dA, dB = block.forward_backward(x, W, A, B, g1, g2, s, heads, dy)
+
+    def loss(x_, A_, B_):
+        with torch.no_grad():
+            out = block.forward(_tt(x_), {n: _tt(W[n]) for n in W}, {n: _tt(A_[n]) for n in A},
+                                {n: _tt(B_[n]) for n in B}, _tt(g1), _tt(g2), s, heads)
+        return float((out * _tt(dy)).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(55)
+    checks = [("x", None, dx)] + [("A", n, dA[n]) for n in block.LINEARS] + [("B", n, dB[n]) for n in block.LINEARS]
+    for kind, name, grad in checks:
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, d)) for d in grad.shape)
+            args = {"x": x.copy(), "A": {n: A[n].copy() for n in A}, "B": {n: B[n].copy() for n in B}}
+            tgt = args["x"] if kind == "x" else args[kind][name]
+            tgt[idx] += h
+            lp = loss(args["x"], args["A"], args["B"])
+            tgt[idx] -= 2 * h
+            lm = loss(args["x"], args["A"], args["B"])
+            num = (lp - lm) / (2 * h)
+            assert math.isclose(num, grad[idx], rel_tol=1e-5, abs_tol=1e-7), (kind, name, idx, num, grad[idx])
+
+
+def test_pins_catch_planted_non_causal_attention(monkeypatch):
+    """Attention without the causal mask fails the SDPA/causality pin."""
+    def no_mask(q, k, v, heads):
+        b, t, hd = q.shape
+        d = hd // heads
+        split = lambda z: z.reshape(b, t, heads, d).permute(0, 2, 1, 3)  # noqa: E731
+        p = torch.softmax(split(q) @ split(k).transpose(-1, -2) / math.sqrt(d), dim=-1)
+        return (p @ split(v)).permute(0, 2, 1, 3).reshape(b, t, hd)
+    monkeypatch.setattr(block, "causal_attention", no_mask)
+    with pytest.raises(AssertionError):
+        test_block_attention_is_sdpa_and_causal()
