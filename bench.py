@@ -93,7 +93,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true", help="workload 5: skip the 32-layer 7B quantise/dequantise sweep")
     p.add_argument("--no-code-types", action="store_true",
-                   help="workload 2: skip the NF4 / FP4 E2M1 / FP4 E3M0 / Int4 comparison")
+                   help="workload 2: skip the extra measurements (storage types, LoRA dropout, optimizer "
+                        "step, decoder block)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="first run a plain device copy of this many MiB three times (a known-size kernel that "
                         "calibrates hardware byte counters taken over the same run)")
@@ -312,6 +313,86 @@ def run_code_types(B, L, dev, reps=10):
                      "fwd_bwd_us": fb_us,
                      "fwd_bwd_TFLOPs": linear_flops(lin) / fb_us / 1e6 if fb_us else None}
         del qw
+    return res
+
+
+def run_block(dev, reps=5):
+    """The whole-layer workload behind the memory discussion (QLoRA section
+    2, "Memory Requirement of Parameter-Efficient Finetuning", and Appendix
+    G, Figure 6: batch 1, sequence 512, gradient checkpointing): a
+    LLaMA-7B-shaped decoder block (hidden 4096, MLP 11008, 32 heads) with
+    r = 64, alpha = 16 adapters on all seven linears, fwd + bwd with and
+    without checkpointing.  Per batch size: the activation bytes the forward
+    leaves for the backward, the peak bytes above the resident state during
+    fwd + bwd (adapter gradients included), and the median fwd + bwd time.
+    Resident state: the NF4+DQ weights, the bf16 adapters, and (computed,
+    not allocated here) their bf16 gradients and the optimizer's fp32
+    master weights and Adam moments."""
+    import torch
+    from bit_nf4_quantized_quantize_amd import block as BLK
+    from bit_nf4_quantized_quantize_amd import synth
+
+    hidden, mlp, heads, r, alpha, seq = 4096, 11008, 32, 64, 16, 512
+    W, A, Bm = {}, {}, {}
+    for i, (n, sh) in enumerate(BLK.linear_shapes(hidden, mlp).items()):
+        W[n] = synth.weight(sh, "normal", synth.seed_of(6, i, "W"), dev)
+        A[n] = synth.normal((sh[1], r), 0.01, synth.seed_of(6, i, "A"), dev)
+        Bm[n] = synth.normal((r, sh[0]), 0.01, synth.seed_of(6, i, "B"), dev)
+    ones = torch.ones(hidden, device=dev)
+    blk = BLK.QLoraBlock(W, A, Bm, ones, ones, alpha / r, heads)
+    del W, A, Bm
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    nparam = sum(p.numel() for p in blk.parameters())
+    res = {"config": {"hidden": hidden, "mlp": mlp, "heads": heads, "r": r, "alpha": alpha, "seq": seq,
+                      "linears": list(BLK.LINEARS)},
+           "weight_bytes": blk.weight_bytes(), "adapter_bytes": blk.adapter_bytes(),
+           "adapter_grad_bytes": 2 * nparam, "optimizer_state_bytes": 12 * nparam, "runs": []}
+
+    def fwd_bwd(xg, dy, ck):
+        for p in blk.parameters():
+            p.grad = None
+        y = blk(xg, checkpoint=ck)
+        y.backward(dy)
+        return y
+
+    for batch in (1, 4):
+        x = synth.normal((batch, seq, hidden), 1.0, synth.seed_of(6, 8, "X"), dev)
+        dy = synth.normal((batch, seq, hidden), 1.0, synth.seed_of(6, 8, "dY"), dev)
+        for ck in (False, True):
+            xg = x.clone().requires_grad_(True)
+            fwd_bwd(xg, dy, ck)  # warm-up: workspaces, allocator pools
+            for p in blk.parameters():
+                p.grad = None
+            xg.grad = None
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            y = blk(xg, checkpoint=ck)
+            torch.cuda.synchronize()
+            held = torch.cuda.memory_allocated() - base - y.numel() * y.element_size()
+            y.backward(dy)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated() - base
+            del y
+            ts = []
+            for _ in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                xg.grad = None
+                e0.record()
+                fwd_bwd(xg, dy, ck)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ts = sorted(ts[1:])
+            # saved_activation_bytes: held between forward and backward beyond
+            # the block input itself (which the caller keeps either way)
+            res["runs"].append({"batch": batch, "checkpoint": ck, "saved_activation_bytes": held,
+                                "saved_per_sequence_bytes": held / batch,
+                                "block_input_bytes": x.numel() * x.element_size(),
+                                "peak_fwd_bwd_bytes": peak, "fwd_bwd_ms": ts[len(ts) // 2]})
+    del blk
+    torch.cuda.empty_cache()
     return res
 
 
@@ -645,6 +726,7 @@ def main():
             out["code_types"] = run_code_types(B, layers[0], dev)
             out["lora_dropout"] = run_dropout(B, layers[0], dev)
             out["optimizer"] = run_optimizer(B, layers[0], dev)
+            out["qlora_block"] = run_block(dev)
     elif not args.no_sweep:
         del layers, qws
         torch.cuda.empty_cache()
