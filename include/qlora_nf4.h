@@ -234,7 +234,8 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, voi
  *
  *   X        device bf16 [M, K]; M >= 0 (M = 0 enqueues nothing).
  *   W        host pointer to the descriptor of the frozen weight [N, K];
- *            K % 64 == 0 and N % 64 == 0.
+ *            K % 64 == 0 and N % 64 == 0; a 4-bit code type (an INT8
+ *            weight returns QLORA_ERR_UNSUPPORTED_DTYPE).
  *   A        device bf16 [K, r]  (QLoRA L1).
  *   B        device bf16 [r, N]  (QLoRA L2).
  *   r        LoRA rank, 1 <= r <= QLORA_MAX_RANK.
