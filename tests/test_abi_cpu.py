@@ -253,3 +253,13 @@ def test_optimizer_validation():
     assert step(param=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert step(pbf=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert step(n=0, param=None, grad=None, m=None, v=None) == B.QLORA_OK
+
+
+def test_block_module_matches_oracle_layout():
+    """The decoder block's seven linears and their [out, in] shapes are the
+    oracle block's (host logic only; the block itself runs on the GPU)."""
+    from bit_nf4_quantized_quantize_amd import block
+    from oracle import block as oblock
+    assert block.LINEARS == oblock.LINEARS
+    assert block.linear_shapes(4096, 11008) == oblock.shapes(4096, 11008)
+    assert block.EPS == oblock.EPS
