@@ -272,8 +272,8 @@ def run_code_types(B, L, dev, reps=10):
     as blockwise Int8 (Eq. 1; all with double quantisation).  Per type: the
     reconstruction error of the dequantised weight (||W_hat - W|| / ||W||,
     fp32 on the device), and the median over `reps` calls of the quantise
-    call, the bf16 dequantise call and (4-bit types; the linear kernels take
-    no Int8 weight) one forward + backward, each between two events."""
+    call, the bf16 dequantise call and one forward + backward (Int8 on the
+    generic GEMM tiles), each between two events."""
     import torch
 
     lin, t = L["lin"], L["t"]
@@ -305,7 +305,7 @@ def run_code_types(B, L, dev, reps=10):
             B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"])
             B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], qw, t["A"], t["B"], lin.s,
                                dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
-        fb_us = med(fb) if ct != B.QLORA_CODE_INT8 else None
+        fb_us = med(fb)
         p = lin.N * lin.K
         code_bytes = 1.0 if ct == B.QLORA_CODE_INT8 else 0.5  # Int8 stores a byte per weight, not a nibble
         res[name] = {"rel_rms_error": err,
@@ -313,8 +313,7 @@ def run_code_types(B, L, dev, reps=10):
                      "quantize_GBps": (QUANT_BYTES_PER_PARAM + code_bytes - 0.5) * p / q_us / 1e3,
                      "dequantize_us": d_us,
                      "dequantize_GBps": (DEQUANT_BYTES_PER_PARAM + code_bytes - 0.5) * p / d_us / 1e3,
-                     "fwd_bwd_us": fb_us,
-                     "fwd_bwd_TFLOPs": linear_flops(lin) / fb_us / 1e6 if fb_us else None}
+                     "fwd_bwd_us": fb_us, "fwd_bwd_TFLOPs": linear_flops(lin) / fb_us / 1e6}
         del qw
     return res
 

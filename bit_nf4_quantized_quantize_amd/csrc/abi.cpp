@@ -153,9 +153,6 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
 int check_linear_shape(const qlora_nf4_t* W, int64_t M, int32_t r, const char* fn) {
   int st = check_desc(W, fn);
   if (st) return st;
-  if (W->code_type == CODE_INT8)
-    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: the linear kernels take 4-bit codes; Int8 weights are not supported",
-                fn);
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M < 0", fn);
   if (W->rows <= 0 || W->cols <= 0 || W->rows % 64 || W->cols % 64)
     return fail(QLORA_ERR_INVALID_ARG, "%s: weight [N, K] needs N, K > 0 and multiples of 64 (got %lld x %lld)",
@@ -342,7 +339,7 @@ int linear_fwd_impl(const void* X, int64_t M, const qlora_nf4_t* W, const void* 
   float* part = (float*)(base + L.part);
   uint16_t* xas = (uint16_t*)(base + L.xas);
   hipError_t e;
-  if (L.gemv_splits > 0) {
+  if (L.gemv_splits > 0 && W->code_type != CODE_INT8) {  // the weight-streaming kernel takes 4-bit codes
     // few tokens: partials of X A, the weight-streaming product, then one
     // kernel that adds both sets of partials and the adapter term
     if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, nullptr, nullptr,

@@ -20,7 +20,8 @@ enum CodeType { CODE_NF4 = 0, CODE_FP4_E2M1 = 1, CODE_FP4_E3M0 = 2, CODE_INT4 = 
 // The 8-bit storage type (QLoRA section 2, Eq. 1, read blockwise like the
 // 4-bit types): one byte per weight, the two's complement of k, value k / 127
 // rounded to fp32 (256 entries; k = -128 is never produced).  The 4-bit
-// tables above and the GEMM kernels do not cover it.
+// tables above do not cover it; the generic GEMM kernel has an 8-bit
+// variant, the 256 x 256 and weight-streaming kernels take 4-bit codes.
 constexpr int CODE_INT8 = CODE_TYPES;
 
 #define QLORA_CODE_VALUES                                                                                      \

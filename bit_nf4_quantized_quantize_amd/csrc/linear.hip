@@ -145,17 +145,26 @@ struct MainCfg {
   static_assert(DQE == 32 || DQE == 64, "tile");
 };
 
-template <int BM, int BN, bool BWD>
+// I8: the weight holds one Int8 code byte per element (value k / 127,
+// blockwise Eq. 1) instead of two 4-bit codes; each byte expands to
+// bf16(fp32(k / 127) * c2_hat), the value the dequantiser writes, through a
+// 256-entry LDS table of k / 127 (correctly rounded fp32 division).
+template <int BM, int BN, bool BWD, bool I8 = false>
 __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
   using C = MainCfg<BM, BN, BWD>;
   __shared__ __attribute__((aligned(16))) __bf16 sA[2][C::SA];
   __shared__ __attribute__((aligned(16))) __bf16 sB[2][C::SB];
+  __shared__ float s_i8[I8 ? 256 : 1];
+  if (I8) {
+    s_i8[threadIdx.x & 255] = (float)(int)(int8_t)(threadIdx.x & 255) / 127.0f;  // NT == 256
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.y * BM, c0 = (int64_t)blockIdx.x * BN;
   const float mu = a.dq.double_quant ? *a.dq.offset : 0.0f;
-  const float* cv = kCodeValues[a.dq.code_type];
+  const float* cv = kCodeValues[I8 ? 0 : a.dq.code_type];
   const int64_t kblocks = a.Kw >> 6;
   const int64_t nk = a.L >> 6;
 
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   uint4 xr[C::XCH];
-  uint32_t cw[C::DQW];
+  uint32_t cw[I8 ? 2 * C::DQW : C::DQW];  // 4-bit: 8 codes per word; Int8: 4
   uint32_t qb = 0;
   float sf = 0.0f;  // scale2 of the group (double quantisation) or the block absmax
 
@@ -194,10 +203,11 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
     }
     const int64_t n = BWD ? kt * 64 + t_row : c0 + t_row;
     const int64_t k = BWD ? c0 + t_col : kt * 64 + t_col;
+    constexpr int NW = I8 ? 2 * C::DQW : C::DQW;
     if (t_ok) {
-      const uint8_t* src = a.codes + ((n * a.Kw + k) >> 1);
+      const uint8_t* src = a.codes + (I8 ? n * a.Kw + k : ((n * a.Kw + k) >> 1));
 #pragma unroll
-      for (int w = 0; w < C::DQW; w += 4) {
+      for (int w = 0; w < NW; w += 4) {
         const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * w);
         cw[w] = v.x; cw[w + 1] = v.y; cw[w + 2] = v.z; cw[w + 3] = v.w;
       }
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
       sf = a.dq.double_quant ? a.dq.scale2[blk >> 8] : a.dq.absmax[blk];
     } else {
 #pragma unroll
-      for (int w = 0; w < C::DQW; ++w) cw[w] = 0x77777777u;  // code 7 = 0.0
+      for (int w = 0; w < NW; ++w) cw[w] = I8 ? 0u : 0x77777777u;  // the code of 0.0
       qb = 0; sf = 0.0f;
     }
   };
@@ -218,13 +228,27 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
       sts16(&sA[buf][row * PK + ch * 8], xr[i]);
     }
     const float c = t_ok ? block_scale(a.dq, qb, sf, mu) : 0.0f;
-    const BlockLUT lut = lut_for(c, cv);
     __bf16* dst = BWD ? &sB[buf][t_row * C::PRC + t_col] : &sB[buf][t_row * PK + t_col];
+    if (I8) {
 #pragma unroll
-    for (int w = 0; w < C::DQW; ++w) {
-      uint32_t o[4];
-      lut_lookup8(lut, cw[w], o);
-      sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
+      for (int w = 0; w < C::DQW; ++w) {  // 8 weights: code words 2w, 2w + 1
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t cwd = cw[2 * w + h];
+          o[2 * h] = pack_bf2(s_i8[cwd & 0xFFu] * c, s_i8[(cwd >> 8) & 0xFFu] * c);
+          o[2 * h + 1] = pack_bf2(s_i8[(cwd >> 16) & 0xFFu] * c, s_i8[cwd >> 24] * c);
+        }
+        sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    } else {
+      const BlockLUT lut = lut_for(c, cv);
+#pragma unroll
+      for (int w = 0; w < C::DQW; ++w) {
+        uint32_t o[4];
+        lut_lookup8(lut, cw[w], o);
+        sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
+      }
     }
   };
 
@@ -1559,15 +1583,18 @@ MainTile pick_tile(int64_t M, int64_t ncols, int64_t L) {
   return best;
 }
 
-template <int BM, int BN, bool BWD>
+template <int BM, int BN, bool BWD, bool I8 = false>
 hipError_t launch_main(const MainArgs& a, hipStream_t stream) {
   const dim3 grid(cdiv(a.ncols, BN), cdiv(a.M, BM));
-  hipLaunchKernelGGL((main_gemm_kernel<BM, BN, BWD>), grid, dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((main_gemm_kernel<BM, BN, BWD, I8>), grid, dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool BWD>
 hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
+  // Int8 weights: the generic kernel with 8-bit code loads (the 256 x 256
+  // kernels and their split plans take 4-bit codes only)
+  if (a.dq.code_type == CODE_INT8) return launch_main<256, 128, BWD, true>(a, stream);
   switch (pick_tile(a.M, a.ncols, a.L)) {
     case T256x256: {
       const SplitPlan p = plan_256(a.M, a.ncols, a.L);

@@ -80,9 +80,8 @@ typedef enum {
  * [-127, 127]) that section 3's Table 3 compares with NF4, read
  * blockwise with the same 64-blocks and double quantisation: one byte per
  * weight, the two's complement of k, value k / 127 (256 entries; byte 0x80,
- * -128/127, is never produced by quantisation).  INT8 weights are accepted
- * by quantisation, dequantisation and the queries; the linear entry points
- * take the 4-bit types only and return QLORA_ERR_UNSUPPORTED_DTYPE for them.
+ * -128/127, is never produced by quantisation).  Every entry point accepts
+ * INT8 weights; the linear layer runs them on its generic GEMM tiles.
  * Values are fp32 (the ratios rounded to nearest); qlora_codebook() returns
  * them. */
 typedef enum {
@@ -234,8 +233,8 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, voi
  *
  *   X        device bf16 [M, K]; M >= 0 (M = 0 enqueues nothing).
  *   W        host pointer to the descriptor of the frozen weight [N, K];
- *            K % 64 == 0 and N % 64 == 0; a 4-bit code type (an INT8
- *            weight returns QLORA_ERR_UNSUPPORTED_DTYPE).
+ *            K % 64 == 0 and N % 64 == 0; any code type (INT8 weights
+ *            run on the generic GEMM tiles, slower than the 4-bit ones).
  *   A        device bf16 [K, r]  (QLoRA L1).
  *   B        device bf16 [r, N]  (QLoRA L2).
  *   r        LoRA rank, 1 <= r <= QLORA_MAX_RANK.

@@ -72,7 +72,7 @@ class OracleWeight:
         self.blocks = blocks
 
     def bf16_blocks(self, sel):
-        cb = codebook.CODEBOOKS[self.code_type]
+        cb = codebook.codebook_of(self.code_type)
         if self.code_type == codebook.CODE_NF4:
             codes, _ = blockwise.quantize_nf4(self.blocks[sel].reshape(-1))
         else:
@@ -309,6 +309,44 @@ def test_code_types_attention_shape(B, code_type):
     t = lin.draw("cuda")
     qw, Y, XA, dX, dA, dB = _run(B, t["X"], t["W"], t["A"], t["B"], t["dY"], lin.s, code_type=code_type)
     _sampled_check(B, lin, t, Y, XA, dX, dA, dB, code_type=code_type)
+
+
+# ------------------------------------- blockwise Int8 weights (G17)
+
+@pytest.mark.parametrize("M,N,K,r", [(200, 192, 320, 8), (4, 192, 64 * 40, 16), (300, 256, 576, 64),
+                                     (1, 128, 256, 100)])
+def test_int8_linear(B, M, N, K, r):
+    """Int8 weights through the generic tiled forward and backward (also for
+    1-16 tokens, which the weight-streaming kernel leaves to it)."""
+    _log(f"linear int8 M={M} N={N} K={K} r={r}")
+    _full_check(B, M, N, K, r, 16.0 / r, seed=811 + M + K, code_type=codebook.CODE_INT8)
+
+
+def test_int8_linear_attention_shape(B):
+    """The 4096x4096 attention projection with 4096 tokens and an Int8
+    weight, sampled."""
+    from bit_nf4_quantized_quantize_amd import synth
+    lin = synth.workload(2)[0]
+    _log("linear workload 2 int8")
+    t = lin.draw("cuda")
+    qw, Y, XA, dX, dA, dB = _run(B, t["X"], t["W"], t["A"], t["B"], t["dY"], lin.s, code_type=codebook.CODE_INT8)
+    _sampled_check(B, lin, t, Y, XA, dX, dA, dB, code_type=codebook.CODE_INT8)
+
+
+def test_int8_identity_input_reproduces_dequantised_weight(B):
+    """X = I, B = 0: Y is the bf16 weight the dequantiser writes, exactly,
+    so the GEMM's 8-bit expansion matches qlora_nf4_dequantize bit for bit."""
+    _log("linear int8 identity")
+    g = torch.Generator().manual_seed(5)
+    N, K, r = 192, 256, 8
+    W = (torch.randn(N, K, generator=g) * 0.02).cuda()
+    qw = B.qlora_nf4_quantize(W, code_type=codebook.CODE_INT8)
+    X = torch.eye(K, device="cuda", dtype=torch.bfloat16)
+    A = torch.zeros(K, r, device="cuda", dtype=torch.bfloat16)
+    Bm = torch.zeros(r, N, device="cuda", dtype=torch.bfloat16)
+    Y, _ = B.qlora_linear_fwd(X, qw, A, Bm, 2.0)
+    Wd = B.qlora_nf4_dequantize(qw, torch.bfloat16)
+    assert torch.equal(Y.t().contiguous().view(torch.int16), Wd.view(torch.int16))
 
 
 # --------------------------------------------------- LoRA dropout (G15)

@@ -348,16 +348,3 @@ def test_int8_decision_points(B):
     w = np.concatenate(blocks)
     _roundtrip(B, torch.from_numpy(w), False, B.QLORA_CODE_INT8)
     _roundtrip(B, torch.from_numpy(-w), True, B.QLORA_CODE_INT8)
-
-
-def test_int8_rejected_by_linear(B):
-    """The linear kernels take 4-bit codes: an Int8 weight is refused with
-    QLORA_ERR_UNSUPPORTED_DTYPE before anything is enqueued."""
-    w = torch.randn(64, 64, device="cuda") * 0.02
-    qw = B.qlora_nf4_quantize(w, code_type=B.QLORA_CODE_INT8)
-    X = torch.randn(4, 64, device="cuda").to(torch.bfloat16)
-    A = torch.zeros(64, 8, device="cuda", dtype=torch.bfloat16)
-    Bm = torch.zeros(8, 64, device="cuda", dtype=torch.bfloat16)
-    with pytest.raises(B.QLoraError) as e:
-        B.qlora_linear_fwd(X, qw, A, Bm, 2.0)
-    assert e.value.status == B.QLORA_ERR_UNSUPPORTED_DTYPE
