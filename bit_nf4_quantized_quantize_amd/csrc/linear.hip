@@ -1594,7 +1594,7 @@ template <bool BWD>
 hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
   // Int8 weights: the generic kernel with 8-bit code loads (the 256 x 256
   // kernels and their split plans take 4-bit codes only)
-  if (a.dq.code_type == CODE_INT8) return launch_main<256, 128, BWD, true>(a, stream);
+  if (a.dq.code_type == CODE_INT8) return launch_main<256, 256, BWD, true>(a, stream);
   switch (pick_tile(a.M, a.ncols, a.L)) {
     case T256x256: {
       const SplitPlan p = plan_256(a.M, a.ncols, a.L);
