@@ -147,18 +147,24 @@ struct MainCfg {
 
 // I8: the weight holds one Int8 code byte per element (value k / 127,
 // blockwise Eq. 1) instead of two 4-bit codes; each byte expands to
-// bf16(fp32(k / 127) * c2_hat), the value the dequantiser writes, through a
-// 256-entry LDS table of k / 127 (correctly rounded fp32 division).
+// bf16(fp32(k / 127) * c2_hat), the value the dequantiser writes.
+// fp32(k / 127) for the Int8 code byte b (k its two's complement), without
+// a division: q0 = k * fp32(1/127), then one correction step with the exact
+// residual k - 127 q0.  Correctly rounded for all 256 codes (checked
+// exhaustively in exact rational arithmetic).
+__device__ __forceinline__ float i8_value(uint32_t b) {
+  const float k = (float)(int)(int8_t)b;
+  const float R = 0x1.020408p-7f;  // fp32(1 / 127)
+  const float q0 = k * R;
+  const float r = __builtin_fmaf(-q0, 127.0f, k);
+  return __builtin_fmaf(r, R, q0);
+}
+
 template <int BM, int BN, bool BWD, bool I8 = false>
 __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
   using C = MainCfg<BM, BN, BWD>;
   __shared__ __attribute__((aligned(16))) __bf16 sA[2][C::SA];
   __shared__ __attribute__((aligned(16))) __bf16 sB[2][C::SB];
-  __shared__ float s_i8[I8 ? 256 : 1];
-  if (I8) {
-    s_i8[threadIdx.x & 255] = (float)(int)(int8_t)(threadIdx.x & 255) / 127.0f;  // NT == 256
-    __syncthreads();
-  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -236,8 +242,8 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const uint32_t cwd = cw[2 * w + h];
-          o[2 * h] = pack_bf2(s_i8[cwd & 0xFFu] * c, s_i8[(cwd >> 8) & 0xFFu] * c);
-          o[2 * h + 1] = pack_bf2(s_i8[(cwd >> 16) & 0xFFu] * c, s_i8[cwd >> 24] * c);
+          o[2 * h] = pack_bf2(i8_value(cwd & 0xFFu) * c, i8_value((cwd >> 8) & 0xFFu) * c);
+          o[2 * h + 1] = pack_bf2(i8_value((cwd >> 16) & 0xFFu) * c, i8_value(cwd >> 24) * c);
         }
         sts16(dst + 8 * w, make_uint4(o[0], o[1], o[2], o[3]));
       }
