@@ -3,31 +3,35 @@
 
 One step = one pass of the whole path over one batch, for every linear of the
 workload: NF4 quantisation with double quantisation of the fp32 weight,
-dequantisation to bf16, the fused forward, and the backward (dX, dA, dB).
-Inputs are drawn once and stay resident in HBM; the weight is rotated over
-several copies (> 256 MB in total) so the quantiser does not read it from the
-Infinity Cache.  Workload 5 (small batch) times only the forward at 1, 4 and
-16 tokens against one NF4 weight (rotated copies) and reports GB/s; it then
-times the 32-layer 7B-shaped sweep (quantise+DQ of all 224 fp32 weights, then
-dequantisation of all of them to bf16) and reports it under "sweep".
+dequantisation to bf16, the fused forward, and the backward (dX, dA, dB),
+taken phase by phase over the linears.  The default workload is the largest
+that fits one GPU, the 65B-shaped MLP layer (gate and up 22016x8192, down
+8192x22016, 8192 tokens, Student-t weights); its line also carries the 7B
+attention projection (4096x4096, 4096 tokens) under "attn_4096" and the
+small-batch forward (1, 4 and 16 tokens against the 8192x22016 weight, GB/s,
+with the 32-layer 7B quantise/dequantise sweep) under "small_batch".
+Inputs are drawn once and stay resident in HBM; the fp32 weights are rotated
+over more than 1 GB of copies and the quantise and dequantise phases are
+timed one call at a time after a 1 GiB cache scrub, so no input comes from
+the 256 MB Infinity Cache.
 
 Measurement:
   1. W untimed warm-up steps;
   2. a breakdown pass: a few steps with HIP events around every library
      kernel of interest (each event costs the stream a few us, so this pass
-     is not used for `value`), then each phase timed as a run of back-to-back
-     calls between two events;
+     is not used for `value`), then each phase timed per call;
   3. the timed region: K steps bracketed by synchronisation, with events
      only around the dominant kernel (found in pass 2), recorded by the
      library on the kernel's own launch stream; its mean duration over the
      K launches gives `roofline.achieved`.
+"achievable" is what the device streams in a plain copy and a plain read.
 
 Prints one JSON line.  `value` is the step's algorithmic fwd+bwd flops
 (4MNK + 6Mr(K+N) per linear) over the measured step time, in TFLOP/s (GB/s
 of algorithmic bytes for workload 5).  `cpu_baseline` times the CPU oracle
-on a bounded sample of the same workload (rank 0, N = 1).
+on a bounded sample of the same workload (rank 0, N = 1), scaled to it.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload 2]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 4]
 """
 
 import argparse
@@ -86,11 +90,14 @@ WORKLOAD_NAMES = {
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    p.add_argument("--workload", type=int, default=4, choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0: enough for > 256 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="measure only the chosen workload (no achievable-bandwidth probe; for workload 4 no "
+                        "7B-attention and small-batch keys)")
     p.add_argument("--no-sweep", action="store_true", help="workload 5: skip the 32-layer 7B quantise/dequantise sweep")
     p.add_argument("--no-code-types", action="store_true",
                    help="workload 2: skip the extra measurements (storage types, LoRA dropout, optimizer "
@@ -173,6 +180,49 @@ def cpu_baseline(lin, tensors, min_s=10.0, max_steps=20):
         "sample": (f"{n} full steps of the {lin.name} linear ({lin.N}x{lin.K} weight, {lin.M} tokens, r={lin.r}): "
                    f"oracle quantise+DQ, dequantise, fwd and bwd in fp64 numpy; {dt:.2f} s per step; "
                    f"BLAS threads {threads}, os.cpu_count() {os.cpu_count()}"),
+    }
+
+
+def cpu_baseline_scaled(lins, tensors, rows=5504, tokens=1024):
+    """The CPU oracle on a bounded sample of the 65B-shaped step, scaled to
+    the whole step (the whole step is 18 TFLOP of fp64 products plus the
+    quantisation of 541M weights, minutes of CPU time): quantise+DQ and
+    dequantise a `rows`-row slice of the first linear's fp32 weight, scaled
+    by parameter count to all three weights; forward and backward of the first
+    linear over `tokens` tokens (fp64 products against that slice's bf16
+    weight, completed to the full weight by flop count), scaled by flops to
+    every linear at its full token count."""
+    from oracle import blockwise, linear
+
+    lin0 = lins[0]
+    W = tensors["W"][:rows].cpu().numpy()
+    X = tensors["X"][:tokens].float().cpu().numpy()
+    A, Bm = tensors["A"].float().cpu().numpy(), tensors["B"].float().cpu().numpy()[:, :rows]
+    dY = tensors["dY"][:tokens, :rows].float().cpu().numpy()
+    t0 = time.perf_counter()
+    st = blockwise.quantize(W, double_quant=True)
+    Wb = blockwise.bf16_round(st.dequantize())
+    t_q = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Y, XA = linear.forward(X, Wb, A, Bm, lin0.s)
+    dX, dA, dB = linear.backward(dY, X, Wb, A, Bm, lin0.s)
+    t_g = time.perf_counter() - t0
+    del st, Wb, Y, XA, dX, dA, dB
+    sample_params = rows * lin0.K
+    sample_flops = 4 * tokens * rows * lin0.K + 6 * tokens * lin0.r * (lin0.K + rows)
+    params = sum(l.N * l.K for l in lins)
+    flops = sum(linear_flops(l) for l in lins)
+    t_step = t_q * params / sample_params + t_g * flops / sample_flops
+    threads = _blas_threads()
+    return {
+        "value": flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"oracle quantise+DQ and dequantise of a {rows}x{lin0.K} slice of the {lin0.name} weight "
+                   f"({t_q:.2f} s, scaled by parameters to the 3 weights), fwd+bwd in fp64 numpy over {tokens} "
+                   f"tokens against that slice ({t_g:.2f} s, scaled by flops to the 3 linears at {lin0.M} tokens); "
+                   f"{t_step:.1f} s per step estimated; BLAS threads {threads}, os.cpu_count() {os.cpu_count()}"),
     }
 
 
@@ -491,42 +541,68 @@ def _dominant(per, layers, small):
     return best
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
-        sys.exit(2)
+def achievable_bandwidth(dev, mib=1024, reps=5):
+    """What this device streams, as the roofline's "achievable" companion to
+    the datasheet figure: a plain device copy (torch copy_, read + write
+    bytes) and a plain read (torch.sum over the same buffer) of `mib` MiB,
+    median of `reps` after a warm-up."""
+    import torch
 
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def med(fn):
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    copy_ms = med(lambda: dst.copy_(src))
+    read_ms = med(lambda: src.sum())
+    del src, dst
+    torch.cuda.empty_cache()
+    nbytes = 4 * n
+    return {"copy_GBps": 2 * nbytes / copy_ms / 1e6, "read_GBps": nbytes / read_ms / 1e6, "buffer_MiB": mib,
+            "how": "torch copy_ (read + write bytes) and torch.sum (read bytes) of one fp32 buffer, median of "
+                   f"{reps}"}
+
+
+class Scrub:
+    """A 1 GiB device buffer rewritten between timed calls, so that a timed
+    call finds none of its inputs in the 256 MB Infinity Cache."""
+
+    def __init__(self, dev, mib=1024):
+        import torch
+        self.buf = torch.empty(mib << 18, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(0.5)
+
+
+def measure(args, workload, steps, warmup, with_cpu, dev):
+    """The measurement of one workload (see the module docstring); returns
+    the JSON object of its line."""
     import torch
 
     from bit_nf4_quantized_quantize_amd import binding as B
     from bit_nf4_quantized_quantize_amd import synth
 
-    B.lib()  # raises if the HIP library is missing: there is no fallback
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     bf = torch.bfloat16
-    small = args.workload == 5
-    if args.copy_probe_mib > 0:
-        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    lins = synth.workload(args.workload)
+    small = workload == 5
+    lins = synth.workload(workload)
     if small:
         # the three token counts share one weight (rows drawn for the largest)
         base = lins[-1]
         t0 = base.draw(dev, with_grad=False)
         wbytes = base.N * base.K * 0.516
-        rotate = args.rotate or max(1, -(-(300 << 20) // int(wbytes)))
+        rotate = args.rotate or max(1, -(-(1200 << 20) // int(wbytes)))
         qws = [B.qlora_nf4_quantize(t0["W"] * (1.0 + 1e-3 * i)) for i in range(rotate)]
         del t0["W"]
         layers = []
@@ -537,8 +613,10 @@ def main():
         kernels = ("fwd_main",)
         phases = ("fwd",)
     else:
+        # fp32 weights rotated over more than 1 GB (the 65B-shaped layer's
+        # three weights are 2.2 GB already)
         wbytes = sum(l.N * l.K * 4 for l in lins)
-        rotate = args.rotate or max(1, -(-(300 << 20) // wbytes))
+        rotate = args.rotate or max(1, -(-(1200 << 20) // wbytes))
         layers = []
         for lin in lins:
             t = lin.draw(dev)
@@ -561,6 +639,7 @@ def main():
 
     hev = HipEvents()
     tev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    scrub = Scrub(dev)
 
     def run_phase(li, p, i):
         """One call of phase p for linear li (rotation index i)."""
@@ -582,60 +661,76 @@ def main():
                                dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"])
 
     def run_step(i, kev=None):
-        """One step; kev[li][kernel] = (start, stop) hipEvents the library
+        """One step, phase by phase over all linears (so a linear's codes are
+        dequantised after the other linears' weights have streamed through
+        the cache); kev[li][kernel] = (start, stop) hipEvents the library
         records around its kernels."""
-        for li in range(len(layers)):
-            if kev is not None:
-                for k, (e0, e1) in kev[li].items():
-                    B.lib().qlora_profile_events(B.QLORA_KERNEL[k], e0, e1)
-            for p in phases:
+        for p in phases:
+            for li in range(len(layers)):
+                if kev is not None:
+                    for k, (e0, e1) in kev[li].items():
+                        B.lib().qlora_profile_events(B.QLORA_KERNEL[k], e0, e1)
                 run_phase(li, p, i)
         if kev is not None:
             for k in kernels:
                 B.lib().qlora_profile_events(B.QLORA_KERNEL[k], None, None)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
 
     # 1) breakdown (untimed for `value`): kernel durations from events around
-    # each library kernel; phase durations from nprof back-to-back calls of
-    # each phase between two events (no events inside the calls)
-    nprof = max(3, min(args.steps, 10))
+    # each library kernel; call durations of each phase: HBM-bound phases
+    # (quantise, dequantise, the small-token forward) one call at a time after
+    # a 1 GiB cache scrub (median), the GEMM phases as nprof back-to-back calls
+    nprof = max(3, min(steps, 10))
     kev_all = [[{k: (hev.create(), hev.create()) for k in kernels} for _ in layers] for _ in range(nprof)]
     for i in range(nprof):
-        run_step(args.warmup + i, kev_all[i])
+        run_step(warmup + i, kev_all[i])
     torch.cuda.synchronize()
     per = []
     for li in range(len(layers)):
         kt = {k: sum(hev.elapsed_ms(*kev_all[i][li][k]) for i in range(nprof)) * 1e3 / nprof for k in kernels}
         pt = {}
         for p in phases:
-            e0, e1 = tev(), tev()
-            e0.record()
-            for i in range(nprof):
-                run_phase(li, p, args.warmup + i)
-            e1.record()
-            torch.cuda.synchronize()
-            pt[p] = e0.elapsed_time(e1) * 1e3 / nprof
+            if small or p in ("quantize", "dequantize"):
+                ts = []
+                for i in range(nprof):
+                    scrub()
+                    e0, e1 = tev(), tev()
+                    e0.record()
+                    run_phase(li, p, warmup + i)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+                pt[p] = sorted(ts)[len(ts) // 2]
+            else:
+                e0, e1 = tev(), tev()
+                e0.record()
+                for i in range(nprof):
+                    run_phase(li, p, warmup + i)
+                e1.record()
+                torch.cuda.synchronize()
+                pt[p] = e0.elapsed_time(e1) * 1e3 / nprof
         per.append((kt, pt))
     name, bound, work, _, dli = _dominant(per, layers, small)
 
     # 2) timed region: K steps, events only around the dominant kernel
     kev_t = [[{name: (hev.create(), hev.create())} if li == dli else {} for li in range(len(layers))]
-             for _ in range(args.steps)]
+             for _ in range(steps)]
     start, stop = tev(), tev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    for i in range(args.steps):
-        run_step(args.warmup + nprof + i, kev_t[i])
+    for i in range(steps):
+        run_step(warmup + nprof + i, kev_t[i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(stop) / args.steps
-    us = sum(hev.elapsed_ms(*kev_t[i][dli][name]) for i in range(args.steps)) * 1e3 / args.steps
+    ms_per_step = start.elapsed_time(stop) / steps
+    us = sum(hev.elapsed_ms(*kev_t[i][dli][name]) for i in range(steps)) * 1e3 / steps
     hev.close()
+    del scrub
 
     if bound == "mfma":
         achieved = work / us / 1e6
@@ -647,8 +742,8 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
     roof.update({"kernel": name, "linear": layers[dli]["lin"].name, "algorithmic_per_launch": work,
                  "avg_launch_us": us})
-    if kernel_digest() == TRAFFIC_DIGEST and (args.workload, name) in TRAFFIC_BYTES:
-        roof["traffic"] = TRAFFIC_BYTES[(args.workload, name)]
+    if kernel_digest() == TRAFFIC_DIGEST and (workload, name) in TRAFFIC_BYTES:
+        roof["traffic"] = TRAFFIC_BYTES[(workload, name)]
         roof["traffic_unit"] = "bytes per launch (HBM read + write)"
 
     breakdown = []
@@ -665,8 +760,8 @@ def main():
             row.update({
                 "quantize_call_us": pt["quantize"], "quantize_kernel_us": kt["quantize"],
                 "quantize_GBps": QUANT_BYTES_PER_PARAM * p / pt["quantize"] / 1e3,
-                "dequantize_us": kt["dequantize"],
-                "dequantize_GBps": DEQUANT_BYTES_PER_PARAM * p / kt["dequantize"] / 1e3,
+                "dequantize_call_us": pt["dequantize"], "dequantize_kernel_us": kt["dequantize"],
+                "dequantize_GBps": DEQUANT_BYTES_PER_PARAM * p / pt["dequantize"] / 1e3,
                 "fwd_us": pt["fwd"], "fwd_main_kernel_us": kt["fwd_main"],
                 "fwd_TFLOPs": (2 * lin.M * lin.N * lin.K + 2 * lin.M * lin.r * (lin.K + lin.N)) / pt["fwd"] / 1e6,
                 "bwd_us": pt["bwd"], "bwd_dx_kernel_us": kt["bwd_dx"],
@@ -676,8 +771,13 @@ def main():
         breakdown.append(row)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline_small(layers[-1]) if small else cpu_baseline(layers[0]["lin"], layers[0]["t"])
+    if with_cpu:
+        if small:
+            cpu = cpu_baseline_small(layers[-1])
+        elif workload == 4:
+            cpu = cpu_baseline_scaled([L["lin"] for L in layers], layers[0]["t"])
+        else:
+            cpu = cpu_baseline(layers[0]["lin"], layers[0]["t"])
 
     lin0 = layers[0]["lin"]
     if small:
@@ -690,14 +790,15 @@ def main():
     else:
         metric, unit = METRIC, "TFLOP/s"
         value = sum(linear_flops(L["lin"]) for L in layers) / (ms_per_step / 1e3) / 1e12
-        step_desc = "quantize+DQ, dequantize->bf16, fwd, bwd (dX, dA, dB) per linear"
+        step_desc = ("quantize+DQ, dequantize->bf16, fwd, bwd (dX, dA, dB) of every linear, phase by phase over "
+                     "the linears")
     out = {
         "metric": metric,
         "value": value,
         "unit": unit,
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -705,7 +806,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.workload],
+            "workload": WORKLOAD_NAMES[workload],
             "linears": [{"name": L["lin"].name, "M": L["lin"].M, "N": L["lin"].N, "K": L["lin"].K,
                          "r": L["lin"].r, "alpha": L["lin"].alpha} for L in layers],
             "global_batch": lin0.M, "weight_copies_rotated": rotate, "step": step_desc,
@@ -719,21 +820,79 @@ def main():
     if not small:
         q_us = sum(b["quantize_call_us"] for b in breakdown)
         q_bytes = sum(QUANT_BYTES_PER_PARAM * L["lin"].N * L["lin"].K for L in layers)
+        d_us = sum(b["dequantize_call_us"] for b in breakdown)
+        d_bytes = sum(DEQUANT_BYTES_PER_PARAM * L["lin"].N * L["lin"].K for L in layers)
         out["quantize"] = {"GB/s": q_bytes / q_us / 1e3, "frac_hbm": q_bytes / q_us / 1e3 / HBM_PEAK_GBS,
-                           "bytes_per_param": QUANT_BYTES_PER_PARAM}
+                           "bytes_per_param": QUANT_BYTES_PER_PARAM, "cold_cache": True}
+        out["dequantize"] = {"GB/s": d_bytes / d_us / 1e3, "frac_hbm": d_bytes / d_us / 1e3 / HBM_PEAK_GBS,
+                             "bytes_per_param": DEQUANT_BYTES_PER_PARAM, "cold_cache": True}
         fb_us = sum(b["fwd_us"] + b["bwd_us"] for b in breakdown)
         fb = sum(linear_flops(L["lin"]) for L in layers) / fb_us / 1e6
         out["fwd_bwd"] = {"TFLOP/s": fb, "frac_mfma": fb / BF16_PEAK_TFLOPS}
-        if args.workload == 2 and not args.no_code_types:
+        if workload == 2 and not args.no_code_types:
             out["code_types"] = run_code_types(B, layers[0], dev)
             out["lora_dropout"] = run_dropout(B, layers[0], dev)
             out["optimizer"] = run_optimizer(B, layers[0], dev)
             if not args.no_block:
                 out["qlora_block"] = run_block(dev)
-    elif not args.no_sweep:
+        del layers
+        torch.cuda.empty_cache()
+    else:
         del layers, qws
         torch.cuda.empty_cache()
-        out["sweep"] = run_sweep(B, synth, dev)
+        if not args.no_sweep:
+            out["sweep"] = run_sweep(B, synth, dev)
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_nf4_quantized_quantize_amd import binding as B
+
+    B.lib()  # raises if the HIP library is missing: there is no fallback
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ach = achievable_bandwidth(dev) if not args.no_extras else None
+    out = measure(args, args.workload, args.steps, args.warmup, not args.no_cpu_baseline, dev)
+    if ach is not None:
+        out["achievable"] = ach
+        if out["roofline"]["unit"] == "GB/s":
+            out["roofline"]["achievable"] = ach["read_GBps"]
+            out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / ach["read_GBps"]
+        for key in ("quantize", "dequantize"):
+            if key in out:
+                out[key]["frac_of_achievable_copy"] = out[key]["GB/s"] / ach["copy_GBps"]
+    if args.workload == 4 and not args.no_extras:
+        # the other two headline shapes, as extra keys of the same line
+        print("bench: 65B-shaped layer done; 7B attention projection next", file=sys.stderr, flush=True)
+        sub = argparse.Namespace(**vars(args))
+        sub.rotate = 0
+        out["attn_4096"] = measure(sub, 2, 20, 3, False, dev)
+        print("bench: 7B attention done; small batch next", file=sys.stderr, flush=True)
+        out["small_batch"] = measure(sub, 5, 20, 3, False, dev)
+        if ach is not None:
+            sb = out["small_batch"]["roofline"]
+            sb["achievable"] = ach["read_GBps"]
+            sb["frac_of_achievable"] = sb["achieved"] / ach["read_GBps"]
     print(json.dumps(out), flush=True)
 
 

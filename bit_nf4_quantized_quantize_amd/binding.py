@@ -23,12 +23,15 @@ QLORA_ERR_UNSUPPORTED_DTYPE = -2
 QLORA_ERR_WORKSPACE_TOO_SMALL = -3
 QLORA_ERR_MISALIGNED = -4
 QLORA_ERR_HIP = -5
+QLORA_ERR_INTERNAL = -6
 QLORA_DTYPE_F32 = 0
 QLORA_DTYPE_BF16 = 1
 
 # qlora_code_type: the codebook of a quantised weight.  CODE_TYPES are the
-# 4-bit types, which every entry point takes; INT8 (one byte per weight) is
-# taken by quantisation and dequantisation only.
+# 4-bit types; INT8 (one byte per weight) is QLORA_CODE_INT8.  Every entry
+# point takes every type; the linear layer runs Int8 weights on its generic
+# 256 x 256 GEMM tiles, for 1-16 tokens as well (the weight-streaming kernel
+# for few tokens takes 4-bit codes only).
 QLORA_CODE_NF4 = 0
 QLORA_CODE_FP4_E2M1 = 1
 QLORA_CODE_FP4_E3M0 = 2
@@ -101,14 +104,15 @@ def lib():
         "qlora_nf4_quantize": (_i32, [_vp, _i32, _pdesc, _vp, _i64, _vp]),
         "qlora_nf4_dequantize": (_i32, [_pdesc, _vp, _i32, _vp]),
         "qlora_linear_fwd": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i64, _vp]),
-        "qlora_linear_bwd": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _i64, _vp]),
+        "qlora_linear_bwd": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i32, _vp, _i64,
+                                    _vp]),
         "qlora_linear_fwd_dropout": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp, _vp, _i64,
                                             _vp]),
         "qlora_clip_scale_workspace": (_i32, [_i64, ctypes.POINTER(_i64)]),
         "qlora_clip_scale": (_i32, [_vp, _i64, _f32, _vp, _vp, _i64, _vp]),
         "qlora_adamw_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _f32, _f32, _f32, _f32, _f32, _i32, _vp]),
         "qlora_linear_bwd_dropout": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp,
-                                            _vp, _vp, _i64, _vp]),
+                                            _vp, _i32, _vp, _i64, _vp]),
         "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
@@ -362,37 +366,46 @@ def qlora_linear_fwd(X, q, A, B, s, save_xa=True, Y=None, XA=None, workspace=Non
 
 
 def qlora_linear_bwd(dY, X, XA, q, A, B, s, need_dx=True, dX=None, dA=None, dB=None, workspace=None, stream=None,
-                     keep=None, p=0.0):
+                     keep=None, p=0.0, accumulate=False):
     """Returns (dX or None, dA, dB) for Y = X W_bf16^T + s (X A) B; with
-    `keep` and p, the gradients of the dropout forward (same mask)."""
+    `keep` and p, the gradients of the dropout forward (same mask).  XA may
+    be None: the library then recomputes it (bit-identical to the forward's).
+    With `accumulate` the gradients are added to the given dA and dB."""
     _need_cuda(dY, X, XA, A, B)
     M, K = X.shape
     N, r = q.rows, A.shape[1]
     keep = _keep_arg(keep, X, p)
     _bf16_2d(dY, "dY", (M, N))
     _bf16_2d(X, "X", (M, q.cols))
-    _bf16_2d(XA, "XA", (M, r))
+    if XA is not None:
+        _bf16_2d(XA, "XA", (M, r))
     _bf16_2d(A, "A", (K, r))
     _bf16_2d(B, "B", (r, N))
     dev = X.device
+    if accumulate and (dA is None or dB is None):
+        raise ValueError("accumulate needs the dA and dB to add to")
     if need_dx and dX is None:
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     if dA is None:
         dA = torch.empty((K, r), dtype=torch.bfloat16, device=dev)
     if dB is None:
         dB = torch.empty((r, N), dtype=torch.bfloat16, device=dev)
+    _bf16_2d(dA, "dA", (K, r))
+    _bf16_2d(dB, "dB", (r, N))
+    _need_cuda(dA, dB)
     _, nws = qlora_linear_workspace(M, N, K, r)
     ws = _ws(nws, dev, workspace)
     d = q.desc()
+    acc = 1 if accumulate else 0
     if keep is None:
         _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(XA), M, ctypes.byref(d), _ptr(A), _ptr(B), r, float(s),
-                                      _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                      _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), acc, _ptr(ws), ws.numel(),
                                       _stream(stream)),
                "qlora_linear_bwd")
     else:
         _check(lib().qlora_linear_bwd_dropout(_ptr(dY), _ptr(X), _ptr(XA), M, ctypes.byref(d), _ptr(A), _ptr(B), r,
                                               float(s), _ptr(keep), float(p), _ptr(dX) if need_dx else None,
-                                              _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
+                                              _ptr(dA), _ptr(dB), acc, _ptr(ws), ws.numel(), _stream(stream)),
                "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB
 

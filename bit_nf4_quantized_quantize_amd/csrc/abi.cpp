@@ -124,16 +124,25 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   return w;
 }
 
+// The forward takes the small-token path (weight-streaming kernel) for these
+// shapes; the backward's recomputation of XA follows the same path.
+bool small_token_path(int64_t M, int64_t N, int64_t r, int32_t code_type) {
+  return M >= 1 && M <= kGemvMaxM && N % 4 == 0 && r <= 256 && code_type != CODE_INT8;
+}
+
 struct BwdWs {
-  // fp32 partials of dY B^T, bf16 s*T [M, rp], fp32 partials of the token
-  // reductions and of the main product's split tiles (one region, used in turn)
-  int64_t part_t, ts, part, part_b, total;
-  int splits_t, splits_a, splits_b;
+  // fp32 partials of dY B^T (and before them, when XA is recomputed, those of
+  // X A), bf16 s*T [M, rp], the recomputed bf16 XA [M, r], fp32 partials of
+  // the token reductions and of the main product's split tiles (one region,
+  // used in turn)
+  int64_t part_t, ts, xa, part, part_b, total;
+  int splits_t, splits_x, splits_a, splits_b;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = round_up(r, 64);
   BwdWs w;
   w.splits_t = skinny_splits(M, r, N);
+  w.splits_x = skinny_splits(M, r, K);  // as the forward's X A
   w.splits_a = tn_splits(M, K, r);
   w.splits_b = tn_splits(M, N, r);  // dB is formed as dB^T [N, r]
   // the two token reductions run together (dA partials at part, dB^T
@@ -143,9 +152,11 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   int64_t pbytes = w.part_b + (int64_t)w.splits_b * N * r * 4;
   const int64_t pm = main_split_bytes(M, K, N);
   if (pm > pbytes) pbytes = pm;
+  const int64_t st = w.splits_t > w.splits_x ? w.splits_t : w.splits_x;
   w.part_t = 0;
-  w.ts = w.part_t + round_up((int64_t)w.splits_t * M * rp * 4, kAlign);
-  w.part = w.ts + round_up(M * rp * 2, kAlign);
+  w.ts = w.part_t + round_up(st * M * rp * 4, kAlign);
+  w.xa = w.ts + round_up(M * rp * 2, kAlign);
+  w.part = w.xa + round_up(M * r * 2, kAlign);
   w.total = w.part + round_up(pbytes, kAlign);
   return w;
 }
@@ -181,6 +192,7 @@ const char* qlora_status_string(int32_t status) {
     case QLORA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case QLORA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case QLORA_ERR_HIP: return "HIP launch error";
+    case QLORA_ERR_INTERNAL: return "internal consistency check failed";
     default: return "unknown status";
   }
 }
@@ -267,6 +279,8 @@ int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q, voi
   const int64_t need = quant_ws(numel, q->double_quant);
   if (ws_bytes < need) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)need);
   if (need > 0 && (st = check_ptr(ws, "ws", fn))) return st;
+  if (!quant_tables_ok(q->code_type))
+    return fail(QLORA_ERR_INTERNAL, "%s: the quantisation table of code type %d is inconsistent", fn, q->code_type);
   hipStream_t s = (hipStream_t)stream;
   const int64_t nb = nblocks(numel);
   float* c2 = q->double_quant ? (float*)ws : q->absmax;
@@ -339,7 +353,7 @@ int linear_fwd_impl(const void* X, int64_t M, const qlora_nf4_t* W, const void* 
   float* part = (float*)(base + L.part);
   uint16_t* xas = (uint16_t*)(base + L.xas);
   hipError_t e;
-  if (L.gemv_splits > 0 && W->code_type != CODE_INT8) {  // the weight-streaming kernel takes 4-bit codes
+  if (small_token_path(M, N, r, W->code_type)) {  // the weight-streaming kernel takes 4-bit codes
     // few tokens: partials of X A, the weight-streaming product, then one
     // kernel that adds both sets of partials and the adapter term
     if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, nullptr, nullptr,
@@ -372,24 +386,27 @@ int linear_fwd_impl(const void* X, int64_t M, const qlora_nf4_t* W, const void* 
 // The backward with optional LoRA dropout (keep = null: none).
 int linear_bwd_impl(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W, const void* A,
                     const void* B, int32_t r, float s, const void* keep, float p, void* dX, void* dA, void* dB,
-                    void* ws, int64_t ws_bytes, void* stream, const char* fn) {
+                    int32_t accumulate, void* ws, int64_t ws_bytes, void* stream, const char* fn) {
   int st = check_linear_shape(W, M, r, fn);
   if (st) return st;
   if ((st = check_dropout(keep, p, fn))) return st;
+  if (accumulate != 0 && accumulate != 1) return fail(QLORA_ERR_INVALID_ARG, "%s: accumulate must be 0 or 1", fn);
   const uint8_t* km = (const uint8_t*)keep;
   const float d = km ? keep_scale_of(p) : 1.0f;
   if ((st = check_ptr(dA, "dA", fn)) || (st = check_ptr(dB, "dB", fn))) return st;
   const int64_t N = W->rows, K = W->cols, rp = round_up(r, 64);
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e;
-  if (M == 0) {
+  if (M == 0) {  // no tokens: the gradients are zero (nothing to add when accumulating)
+    if (accumulate) return QLORA_OK;
     if ((e = launch_fill_zero_u16((uint16_t*)dA, K * r, hs)) != hipSuccess) return hip_fail(e, fn);
     if ((e = launch_fill_zero_u16((uint16_t*)dB, (int64_t)r * N, hs)) != hipSuccess) return hip_fail(e, fn);
     return QLORA_OK;
   }
-  if ((st = check_ptr(dY, "dY", fn)) || (st = check_ptr(X, "X", fn)) || (st = check_ptr(XA, "XA", fn)) ||
-      (st = check_ptr(A, "A", fn)) || (st = check_ptr(B, "B", fn)))
+  if ((st = check_ptr(dY, "dY", fn)) || (st = check_ptr(X, "X", fn)) || (st = check_ptr(A, "A", fn)) ||
+      (st = check_ptr(B, "B", fn)))
     return st;
+  if (XA && !aligned16(XA)) return fail(QLORA_ERR_MISALIGNED, "%s: XA not 16-byte aligned", fn);
   if (dX && !aligned16(dX)) return fail(QLORA_ERR_MISALIGNED, "%s: dX not 16-byte aligned", fn);
   const BwdWs L = bwd_ws(M, N, K, r);
   if (ws_bytes < L.total) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)L.total);
@@ -398,6 +415,21 @@ int linear_bwd_impl(const void* dY, const void* X, const void* XA, int64_t M, co
   float* part_t = (float*)(base + L.part_t);
   uint16_t* ts = (uint16_t*)(base + L.ts);
   float* part = (float*)(base + L.part);
+  if (!XA) {
+    // recompute XA = (drop(X)) A exactly as the forward writes it: the same
+    // split partials, then the forward's own reduction for its path
+    uint16_t* xa = (uint16_t*)(base + L.xa);
+    if (small_token_path(M, N, r, W->code_type)) {
+      if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part_t, L.splits_x, nullptr,
+                             nullptr, rp, s, 1.0f, km, hs)) != hipSuccess)
+        return hip_fail(e, fn);
+      if ((e = launch_xa_reduce(part_t, L.splits_x, M, rp, d, r, xa, hs)) != hipSuccess) return hip_fail(e, fn);
+    } else if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part_t, L.splits_x, xa,
+                                  nullptr, rp, s * d, d, km, hs)) != hipSuccess) {
+      return hip_fail(e, fn);
+    }
+    XA = xa;
+  }
   // s*T = s * dY B^T  [M, rp]
   if ((e = launch_skinny((const uint16_t*)dY, (const uint16_t*)B, false, M, r, N, part_t, L.splits_t, nullptr, ts, rp,
                          s, 1.0f, nullptr, hs)) != hipSuccess)
@@ -413,7 +445,8 @@ int linear_bwd_impl(const void* dY, const void* X, const void* XA, int64_t M, co
   // dA = X^T (s T) [K, r] and dB^T = s dY^T XA [N, r] (written as dB [r, N])
   if ((e = launch_tn_pair((const uint16_t*)X, K, K, km, ts, rp, r, part, L.splits_a, (uint16_t*)dA, d,
                           (const uint16_t*)dY, N, N, (const uint16_t*)XA, r, r,
-                          (float*)((char*)part + L.part_b), L.splits_b, (uint16_t*)dB, s, M, hs)) != hipSuccess)
+                          (float*)((char*)part + L.part_b), L.splits_b, (uint16_t*)dB, s, M, accumulate != 0,
+                          hs)) != hipSuccess)
     return hip_fail(e, fn);
   return QLORA_OK;
 }
@@ -436,18 +469,20 @@ int qlora_linear_fwd_dropout(const void* X, int64_t M, const qlora_nf4_t* W, con
 }
 
 int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W, const void* A,
-                     const void* B, int32_t r, float s, void* dX, void* dA, void* dB, void* ws, int64_t ws_bytes,
-                     void* stream) {
-  return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, nullptr, 0.0f, dX, dA, dB, ws, ws_bytes, stream,
+                     const void* B, int32_t r, float s, void* dX, void* dA, void* dB, int32_t accumulate, void* ws,
+                     int64_t ws_bytes, void* stream) {
+  return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, nullptr, 0.0f, dX, dA, dB, accumulate, ws, ws_bytes, stream,
                          "qlora_linear_bwd");
 }
 
 int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int64_t M, const qlora_nf4_t* W,
                              const void* A, const void* B, int32_t r, float s, const void* keep_mask, float p,
-                             void* dX, void* dA, void* dB, void* ws, int64_t ws_bytes, void* stream) {
+                             void* dX, void* dA, void* dB, int32_t accumulate, void* ws, int64_t ws_bytes,
+                             void* stream) {
   static const char* fn = "qlora_linear_bwd_dropout";
   if (!keep_mask) return fail(QLORA_ERR_INVALID_ARG, "%s: keep_mask is NULL", fn);
-  return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, keep_mask, p, dX, dA, dB, ws, ws_bytes, stream, fn);
+  return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, keep_mask, p, dX, dA, dB, accumulate, ws, ws_bytes, stream,
+                         fn);
 }
 
 int qlora_clip_scale_workspace(int64_t n, int64_t* ws_bytes) {

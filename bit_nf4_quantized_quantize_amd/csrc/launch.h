@@ -56,6 +56,10 @@ const NF4Values& code_values(int code_type);
 inline const NF4Values& nf4_values() { return code_values(CODE_NF4); }
 const QuantTable& quant_table();
 const CodeSpec& code_spec(int code_type);
+// False when the quantisation table of `code_type` could not be built (a
+// bucket would hold two decision points; never the case for the built-in
+// codebooks).
+bool quant_tables_ok(int code_type);
 
 // Quantisation writes the codes and the fp32 block absmax c2; with
 // `partials` it also writes, per workgroup, the exact sum of its c2 as
@@ -65,6 +69,32 @@ const CodeSpec& code_spec(int code_type);
 // and encodes the constants.
 int quantize_parts(int64_t numel);
 constexpr int kMeanDigits = 10;  // 32-bit digits of the exact fixed-point sum
+constexpr int kQuantMaxParts = 256;          // quantisation workgroups (and exact-sum partials) at most
+constexpr int64_t kQuantGridUnit = 16384;    // weights per workgroup when sizing that grid
+
+// Tiling constants the kernels and the host planning share.
+constexpr int kCUs = 256;        // MI355X compute units
+constexpr int SK_BK = 128;       // reduction indices per iteration of the skinny products
+constexpr int TN_BK = 128;       // tokens per iteration of the token reductions
+constexpr int G3_ROWS = 256;     // weight rows per workgroup of the small-token forward
+constexpr int G3_CB = 4;         // 64-blocks per chunk of the small-token forward
+constexpr int kOptThreads = 256; // threads per workgroup of the optimizer kernels
+constexpr int kOptMaxParts = 256;// partial sums of the gradient norm at most
+
+// Main-GEMM tile choice.  The 256 x 256 kernels run one workgroup per CU;
+// their tiles go in rounds of kCUs, and when the last round would leave CUs
+// idle its R tiles are cut along the reduction into `split` ranges
+// (split * R <= kCUs) whose fp32 partial tiles a fixup pass adds.  The
+// 128-wide generic tiles remain for shapes where even that leaves most of
+// the chip idle.
+struct SplitPlan {
+  int tiles, full, split;  // split == 1: no split units
+  int64_t units() const { return full + (int64_t)(tiles - full) * split; }
+  int64_t part_floats() const { return split > 1 ? (int64_t)(tiles - full) * split * 65536 : 0; }
+};
+SplitPlan plan_256(int64_t M, int64_t ncols, int64_t L);
+enum MainTile { T256x256 = 0, T256x128 = 1, T128x128 = 2 };
+MainTile pick_tile(int64_t M, int64_t ncols, int64_t L);
 
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_type, uint8_t* codes, float* c2,
                            uint64_t* partials, hipStream_t stream);
@@ -88,9 +118,9 @@ struct DQParams {
 //
 // Skinny product C[M, Q] = U[M, L] * V, V either [L, Q] (v_is_lq) or
 // [Q, L]; the reduction is split into `splits` chunks of fp32 partials
-// part[splits][M][QP], then out1 [M, Q] = bf16(scale1 * C) (optional) and
-// out2 [M, QP] = bf16(alpha * C), zero in columns [Q, QP).  With out1 and
-// out2 both null only the partials are written.  With `keep` (a bit mask
+// part[splits][M][QP], then out1 [M, Q] = bf16(scale1 * C) and out2 [M, QP]
+// = bf16(alpha * C), zero in columns [Q, QP), each when given.  With out1
+// and out2 both null only the partials are written.  With `keep` (a bit mask
 // [M, L/8], bit j of byte (m, c) for U[m, 8c + j]; L % 8 == 0) the elements
 // of U whose bit is clear count as zero (LoRA dropout).
 int skinny_splits(int64_t M, int64_t Q, int64_t L);
@@ -113,6 +143,11 @@ constexpr int kGemvMaxM = 16;
 int gemv_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
                        float* part, int splits, hipStream_t stream);
+// XA [M, r] = bf16(scale1 C) from the skinny partials of C = X A exactly as
+// launch_gemv_reduce forms it (the backward recomputes the small-token
+// forward's XA with it, bit for bit).
+hipError_t launch_xa_reduce(const float* xpart, int xsplits, int64_t M, int64_t rp, float scale1, int64_t r,
+                            uint16_t* XA, hipStream_t stream);
 hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const float* xpart, int xsplits,
                               int64_t rp, float alpha, float scale1, const uint16_t* B, int64_t r, uint16_t* Y,
                               uint16_t* XA, hipStream_t stream);
@@ -127,14 +162,16 @@ hipError_t launch_bwd_dx(const uint16_t* dY, int64_t M, int64_t N, const uint8_t
 // epilogues: C_a [Pa, Qa] = U_a[M, Pa]^T * V_a[M, Qa] and C_b likewise
 // (leading dimensions ld*), fp32 partials part_x [splits_x][P][Q], then
 // out_a [Pa, Qa] = bf16(alpha_a * sum) and out_b = bf16(alpha_b * sum) written
-// transposed, [Qb, Pb].  keep_a (optional, bit mask [M, ldua/8]) zeroes
-// elements of U_a as for launch_skinny.
+// transposed, [Qb, Pb]; with `accumulate` the bf16 outputs are added to:
+// out = bf16(out + alpha * sum).  keep_a (optional, bit mask [M, ldua/8])
+// zeroes elements of U_a as for launch_skinny.
 int tn_splits(int64_t M, int64_t P, int64_t Q);
 hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint8_t* keep_a, const uint16_t* Va,
                           int64_t ldva, int64_t Qa, float* part_a, int splits_a, uint16_t* out_a, float alpha_a,
                           const uint16_t* Ub,
                           int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb, float* part_b,
-                          int splits_b, uint16_t* out_b, float alpha_b, int64_t M, hipStream_t stream);
+                          int splits_b, uint16_t* out_b, float alpha_b, int64_t M, bool accumulate,
+                          hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);
 
 // LoRA optimizer step.  launch_clip_scale writes scale = min(1, max_norm /

@@ -902,7 +902,6 @@ __global__ __launch_bounds__(256) void main_fixup_kernel(const float* __restrict
 // reduction indices per iteration with the next iteration's loads in flight.
 //   NN: V(l, q) = V[l * Q + q]   (A [K, r] for XA)   -> tile [128 l][64 q], transposed reads
 //   NT: V(l, q) = V[q * L + l]   (B [r, N] for dY B^T) -> tile [64 q][128 l]
-constexpr int SK_BK = 128;
 constexpr int SK_PU = SK_BK + 8;   // [64][128] reduction-contiguous pitch
 constexpr int SK_PV = 64 + kRcPad; // [128][64] transposed-read pitch
 
@@ -1034,8 +1033,8 @@ __device__ __forceinline__ float4 split_sum4(const float* part, int S, int64_t n
 }
 
 // XA-style epilogue: out2 [M, QP] = bf16(alpha * C) (C zero in columns
-// >= Q), out1 [M, Q] = bf16(scale1 * C) when given.  part is [S][M][QP],
-// QP % 64 == 0.
+// >= Q) and out1 [M, Q] = bf16(scale1 * C), each when given.  part is
+// [S][M][QP], QP % 64 == 0.
 template <int T>
 __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ part, int S, int64_t M,
                                                               int64_t Q, int64_t QP, uint16_t* __restrict__ out1,
@@ -1050,10 +1049,12 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
   if (!ok || t != 0) return;
   const int64_t m = idx / QP, q = idx - m * QP;
   const float sv[4] = {s.x, s.y, s.z, s.w};
-  uint2 o;
-  o.x = pack_bf2(alpha * sv[0], alpha * sv[1]);
-  o.y = pack_bf2(alpha * sv[2], alpha * sv[3]);
-  *reinterpret_cast<uint2*>(out2 + idx) = o;
+  if (out2) {
+    uint2 o;
+    o.x = pack_bf2(alpha * sv[0], alpha * sv[1]);
+    o.y = pack_bf2(alpha * sv[2], alpha * sv[3]);
+    *reinterpret_cast<uint2*>(out2 + idx) = o;
+  }
   if (out1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -1066,7 +1067,6 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
 // (U [M, P] and V [M, Q] row-major, leading dimensions ldu, ldv).  Tile
 // BP x BQ, waves 2 x 2; 128 tokens per iteration, next iteration's loads in
 // flight; both tiles are staged as [128 m][cols] and read transposed.
-constexpr int TN_BK = 128;
 
 struct TnProblem {
   const uint16_t* U;
@@ -1195,6 +1195,7 @@ struct TnOut {
   uint16_t* out;
   float alpha;
   int trans;
+  int accumulate;  // out = bf16(out + alpha * sum) instead of bf16(alpha * sum)
 };
 
 template <int T>
@@ -1211,18 +1212,23 @@ __global__ __launch_bounds__(256) void tn_reduce_kernel(const TnOut oa, const Tn
   const float4 s = split_sum4<T>(o.part, o.S, PQ, idx, ok, t, red);
   if (!ok || t != 0) return;
   const float sv[4] = {s.x, s.y, s.z, s.w};
+  // the bf16 value of element e: alpha * sum, plus the old value when accumulating
+  auto val = [&](int e, int64_t at) -> uint16_t {
+    const float v = o.alpha * sv[e];
+    return f2bf(o.accumulate ? bf2f(o.out[at]) + v : v);
+  };
   if (o.trans) {
     for (int e = 0; e < 4 && idx + e < PQ; ++e) {
       const int64_t p = (idx + e) / o.Q, q = (idx + e) - p * o.Q;
-      o.out[q * o.P + p] = f2bf(o.alpha * sv[e]);
+      o.out[q * o.P + p] = val(e, q * o.P + p);
     }
   } else if (idx + 4 <= PQ && (PQ & 3) == 0) {
     uint2 w;
-    w.x = pack_bf2(o.alpha * sv[0], o.alpha * sv[1]);
-    w.y = pack_bf2(o.alpha * sv[2], o.alpha * sv[3]);
+    w.x = (uint32_t)val(0, idx) | ((uint32_t)val(1, idx + 1) << 16);
+    w.y = (uint32_t)val(2, idx + 2) | ((uint32_t)val(3, idx + 3) << 16);
     *reinterpret_cast<uint2*>(o.out + idx) = w;
   } else {
-    for (int e = 0; e < 4 && idx + e < PQ; ++e) o.out[idx + e] = f2bf(o.alpha * sv[e]);
+    for (int e = 0; e < 4 && idx + e < PQ; ++e) o.out[idx + e] = val(e, idx + e);
   }
 }
 
@@ -1269,8 +1275,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
 // part[S][M][N].
 constexpr int G3_WAVES = 8;
 constexpr int G3_T = G3_WAVES * 64;
-constexpr int G3_ROWS = 256;                     // weight rows per workgroup
-constexpr int G3_CB = 4;                         // blocks per chunk
 constexpr int G3_RT = G3_ROWS * G3_CB / (16 * G3_WAVES);  // 16-row tiles per wave (8)
 constexpr int G3_CHUNK16 = G3_ROWS * 2 * G3_CB;  // 16-byte pieces per chunk (2048)
 constexpr int G3_LPT = G3_CHUNK16 / G3_T;        // piece loads per thread per chunk (4)
@@ -1467,16 +1471,16 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
 // partials), and XA = bf16(scale1 C) [M, r] written by the blocks with
 // blockIdx.x == 0 when XA is given.  One token row per blockIdx.y, 4 columns
 // per thread (N % 4 == 0), rp <= 256.
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int S, int M, int64_t N,
-                                                          const float* __restrict__ xpart, int SX, int rp,
-                                                          float alpha, float scale1, const uint16_t* __restrict__ B,
-                                                          int r, uint16_t* __restrict__ Y,
-                                                          uint16_t* __restrict__ XA) {
-  __shared__ float4 xsum[256];  // [group][rp / 4]
-  __shared__ float xas[256];
-  const int tid = threadIdx.x, m = blockIdx.y;
-  // thread (group u, column quad c4): the slices u, u + G, ... of 4 columns;
-  // the G group sums are then added in a fixed order
+// Row m of C = X A from the split partials xpart[SX][M][rp] (256 threads,
+// rp <= 256): xas[j] = bf16(alpha C[m, j]) as fp32 for j < rp, and, when XA
+// is given, XA[m, j] = bf16(scale1 C[m, j]) for j < r.  Thread (group u,
+// column quad c4) adds the slices u, u + G, ... of 4 columns; the G group
+// sums are then added in a fixed order.  The forward's small-token path and
+// the backward's recomputation of XA both take XA from here, so the two are
+// bit-identical.
+__device__ __forceinline__ void xa_row(const float* __restrict__ xpart, int SX, int M, int m, int rp, float alpha,
+                                       float scale1, int r, uint16_t* __restrict__ XA, float4* xsum, float* xas) {
+  const int tid = threadIdx.x;
   const int nq = rp >> 2, G = 256 / nq, c4 = tid % nq, u = tid / nq;
   {
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -1493,8 +1497,28 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
     float c = 0.0f;
     for (int w = 0; w < G; ++w) c += xs[w * rp + j];
     xas[j] = bf2f(f2bf(alpha * c));
-    if (XA != nullptr && blockIdx.x == 0 && j < r) XA[(int64_t)m * r + j] = f2bf(scale1 * c);
+    if (XA != nullptr && j < r) XA[(int64_t)m * r + j] = f2bf(scale1 * c);
   }
+}
+
+// XA [M, r] = bf16(scale1 * X A) from the split partials (one token row per
+// workgroup).
+__global__ __launch_bounds__(256) void xa_reduce_kernel(const float* __restrict__ xpart, int SX, int M, int rp,
+                                                        float scale1, int r, uint16_t* __restrict__ XA) {
+  __shared__ float4 xsum[256];
+  __shared__ float xas[256];
+  xa_row(xpart, SX, M, blockIdx.x, rp, 1.0f, scale1, r, XA, xsum, xas);
+}
+
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int S, int M, int64_t N,
+                                                          const float* __restrict__ xpart, int SX, int rp,
+                                                          float alpha, float scale1, const uint16_t* __restrict__ B,
+                                                          int r, uint16_t* __restrict__ Y,
+                                                          uint16_t* __restrict__ XA) {
+  __shared__ float4 xsum[256];  // [group][rp / 4]
+  __shared__ float xas[256];
+  const int tid = threadIdx.x, m = blockIdx.y;
+  xa_row(xpart, SX, M, m, rp, alpha, scale1, r, blockIdx.x == 0 ? XA : nullptr, xsum, xas);
   // four groups of 64 threads share the workgroup's 256 columns: group q adds
   // the partial slices q, q + 4, ... and the adapter rows q, q + 4, ...; the
   // four group sums are then added in a fixed order
@@ -1537,56 +1561,6 @@ int split_sum_threads(int64_t chunks, int S) {
   int T = 1;
   while (T < 64 && chunks * T < 65536 && 4 * T < S) T *= 2;
   return T;
-}
-
-// ------------------------------------------------ main-GEMM tile choice
-// The 256 x 256 kernel runs one workgroup per CU.  Its tiles go in rounds of
-// kCUs; when the last round would leave CUs idle, its R tiles are cut along
-// the reduction into `split` ranges (split * R <= kCUs), whose fp32 partial
-// tiles a fixup pass adds.  The older 128-wide kernels remain for shapes
-// where even that leaves most of the chip idle.
-constexpr int kCUs = 256;  // MI355X compute units
-
-struct SplitPlan {
-  int tiles, full, split;  // split == 1: no split units
-  int64_t units() const { return full + (int64_t)(tiles - full) * split; }
-  int64_t part_floats() const { return split > 1 ? (int64_t)(tiles - full) * split * 65536 : 0; }
-};
-
-SplitPlan plan_256(int64_t M, int64_t ncols, int64_t L) {
-  SplitPlan p;
-  p.tiles = (int)(cdiv(M, 256) * cdiv(ncols, 256));
-  const int nkt = (int)(L >> 6);
-  const int R = p.tiles % kCUs;
-  int split = R > 0 ? kCUs / R : 1;
-  if (split > nkt / 2) split = nkt / 2;  // at least two k-steps per range
-  if (split < 2) {
-    p.full = p.tiles;
-    p.split = 1;
-  } else {
-    p.full = p.tiles - R;
-    p.split = split;
-  }
-  return p;
-}
-
-enum MainTile { T256x256 = 0, T256x128 = 1, T128x128 = 2 };
-
-// Rough time in units of one 256 x 256 tile on a CU.
-MainTile pick_tile(int64_t M, int64_t ncols, int64_t L) {
-  const SplitPlan p = plan_256(M, ncols, L);
-  double best_t = (double)(p.full / kCUs) + (p.full % kCUs ? 1.0 : 0.0) +
-                  (p.split > 1 ? 1.0 / p.split + 0.05 : 0.0);
-  MainTile best = T256x256;
-  struct Cand { MainTile t; int bm, bn; double cost; };
-  const Cand cands[2] = {{T256x128, 256, 128, 0.56}, {T128x128, 128, 128, 0.30}};
-  for (const Cand& c : cands) {
-    const int64_t tiles = (int64_t)cdiv(M, c.bm) * cdiv(ncols, c.bn);
-    const double waves = (double)((tiles + 2 * kCUs - 1) / (2 * kCUs));
-    const double t = waves * c.cost * 2;
-    if (t < best_t - 1e-9) { best_t = t; best = c.t; }
-  }
-  return best;
 }
 
 template <int BM, int BN, bool BWD, bool I8 = false>
@@ -1640,15 +1614,6 @@ hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
 
 // ------------------------------------------------------------ launchers
 
-int skinny_splits(int64_t M, int64_t Q, int64_t L) {
-  int64_t tiles = (int64_t)cdiv(M, 64) * cdiv(Q, 64);
-  if (tiles < 1) tiles = 1;
-  int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t max_s = L / SK_BK > 0 ? L / SK_BK : 1;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return (int)s;
-}
 
 hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int64_t M, int64_t Q, int64_t L,
                          float* part, int splits, uint16_t* out1, uint16_t* out2, int64_t QP, float alpha,
@@ -1674,21 +1639,11 @@ hipError_t launch_skinny(const uint16_t* U, const uint16_t* V, bool v_is_lq, int
   return hipGetLastError();
 }
 
-int tn_splits(int64_t M, int64_t P, int64_t Q) {
-  int64_t tiles = (int64_t)cdiv(P, 128) * cdiv(Q, 64);
-  if (tiles < 1) tiles = 1;
-  int64_t s = (256 + tiles - 1) / tiles;  // about one workgroup per CU
-  const int64_t max_s = M / TN_BK > 0 ? M / TN_BK : 1;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return (int)s;
-}
 
 hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const uint8_t* keep_a, const uint16_t* Va,
                           int64_t ldva, int64_t Qa, float* part_a, int splits_a, uint16_t* out_a, float alpha_a,
                           const uint16_t* Ub, int64_t ldub, int64_t Pb, const uint16_t* Vb, int64_t ldvb, int64_t Qb,
-                          float* part_b, int splits_b, uint16_t* out_b, float alpha_b, int64_t M,
+                          float* part_b, int splits_b, uint16_t* out_b, float alpha_b, int64_t M, bool accumulate,
                           hipStream_t stream) {
   if (keep_a && (ldua & 7)) return hipErrorInvalidValue;
   auto chunk_of = [&](int splits) {
@@ -1703,8 +1658,8 @@ hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const ui
   if (e != hipSuccess) return e;
   const int64_t ca = cdiv(Pa * Qa, 4), cb = cdiv(Pb * Qb, 4);
   const int T = split_sum_threads(ca < cb ? ca : cb, splits_a > splits_b ? splits_a : splits_b);
-  const TnOut oa{part_a, splits_a, Pa, Qa, out_a, alpha_a, 0};
-  const TnOut ob{part_b, splits_b, Pb, Qb, out_b, alpha_b, 1};
+  const TnOut oa{part_a, splits_a, Pa, Qa, out_a, alpha_a, 0, accumulate ? 1 : 0};
+  const TnOut ob{part_b, splits_b, Pb, Qb, out_b, alpha_b, 1, accumulate ? 1 : 0};
 #define QLORA_RED(TT)                                                                                       \
   case TT: {                                                                                                \
     const int na = (int)cdiv(ca, 256 / TT), nb = (int)cdiv(cb, 256 / TT);                                  \
@@ -1722,10 +1677,6 @@ hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int64_t main_split_bytes(int64_t M, int64_t ncols, int64_t L) {
-  if (pick_tile(M, ncols, L) != T256x256) return 0;
-  return plan_256(M, ncols, L).part_floats() * 4;
-}
 
 hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq,
                            int64_t N, const uint16_t* XAs, const uint16_t* B, int64_t r, int64_t rp, uint16_t* Y,
@@ -1740,17 +1691,6 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
   return launch_main_any<false>(a, split_ws, stream);
 }
 
-int gemv_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = (int64_t)cdiv(N, G3_ROWS), nchunks = ((K >> 6) + G3_CB - 1) / G3_CB;
-  // one workgroup per CU over the whole grid
-  int64_t s = (kCUs + tiles - 1) / tiles;
-  // keep the fp32 partials (S * M * N * 4 bytes, written and read once)
-  // below about 1/4 of the packed weight (N * K / 2 bytes)
-  const int64_t by_bytes = K / (32 * (M > 0 ? M : 1));
-  if (s > by_bytes) s = by_bytes;
-  if (s > nchunks) s = nchunks;  // every split holds at least one chunk
-  return (int)(s < 1 ? 1 : s);
-}
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
                        float* part, int splits, hipStream_t stream) {
@@ -1770,6 +1710,14 @@ hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t 
   if (N % 4 || rp % 64 || rp > 256 || r > rp || xsplits < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3(cdiv(N, 256), (unsigned)M), dim3(256), 0, stream, part, splits, (int)M,
                      N, xpart, xsplits, (int)rp, alpha, scale1, B, (int)r, Y, XA);
+  return hipGetLastError();
+}
+
+hipError_t launch_xa_reduce(const float* xpart, int xsplits, int64_t M, int64_t rp, float scale1, int64_t r,
+                            uint16_t* XA, hipStream_t stream) {
+  if (rp % 64 || rp > 256 || r > rp || xsplits < 1 || M < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xa_reduce_kernel, dim3((unsigned)M), dim3(256), 0, stream, xpart, xsplits, (int)M, (int)rp,
+                     scale1, (int)r, XA);
   return hipGetLastError();
 }
 

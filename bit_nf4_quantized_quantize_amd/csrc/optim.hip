@@ -17,8 +17,7 @@
 
 namespace qlora {
 
-constexpr int OPT_T = 256;
-constexpr int OPT_MAX_WG = 256;  // partial sums of the gradient norm
+constexpr int OPT_T = kOptThreads;
 
 // Sum of squares of grad[0, n) (bf16), one fp64 partial per workgroup,
 // accumulated in a fixed order: thread t takes elements 4(t + k T) .. +3 of
@@ -59,16 +58,16 @@ __global__ __launch_bounds__(OPT_T) void grad_sqnorm_kernel(const uint16_t* __re
 // then a fixed butterfly adds the lanes.
 __global__ __launch_bounds__(64) void clip_finish_kernel(const double* __restrict__ partials, int parts,
                                                          float max_norm, float* __restrict__ scale) {
-  static_assert(OPT_MAX_WG % 64 == 0, "partials per lane");
-  double v[OPT_MAX_WG / 64];
+  static_assert(kOptMaxParts % 64 == 0, "partials per lane");
+  double v[kOptMaxParts / 64];
 #pragma unroll
-  for (int k = 0; k < OPT_MAX_WG / 64; ++k) {
+  for (int k = 0; k < kOptMaxParts / 64; ++k) {
     const int i = (int)threadIdx.x + 64 * k;
     v[k] = i < parts ? partials[i] : 0.0;
   }
   double t = 0.0;
 #pragma unroll
-  for (int k = 0; k < OPT_MAX_WG / 64; ++k) t += v[k];
+  for (int k = 0; k < kOptMaxParts / 64; ++k) t += v[k];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
   if (threadIdx.x == 0) {
@@ -77,10 +76,6 @@ __global__ __launch_bounds__(64) void clip_finish_kernel(const double* __restric
   }
 }
 
-int clip_parts(int64_t n) {
-  const int64_t wgs = (n + OPT_T * 4 - 1) / (OPT_T * 4);
-  return (int)(wgs < 1 ? 1 : (wgs > OPT_MAX_WG ? OPT_MAX_WG : wgs));
-}
 
 hipError_t launch_clip_scale(const uint16_t* g, int64_t n, float max_norm, float* scale, double* partials,
                              hipStream_t stream) {

@@ -36,120 +36,6 @@ constexpr float kTiny = 0x1p-126f;
 constexpr float kTinyDQ = 0x1p-118f;
 constexpr float kPrescale = 0x1p32f;
 
-// ----------------------------------------------------------------- tables
-
-// Library copies of the codebooks (QLoRA Appendix E for NF4; the other
-// types of the section 3 comparison as defined in codebooks.h).
-const NF4Values& code_values(int code_type) {
-  static NF4Values v[CODE_TYPES];
-  static const bool filled = [] {
-    for (int c = 0; c < CODE_TYPES; ++c) memcpy(v[c].v, kCodeValuesHost[c], sizeof(v[c].v));
-    return true;
-  }();
-  (void)filled;
-  return v[code_type];
-}
-
-// Decision thresholds between codes i and i+1 are the exact midpoints
-// (NF4[i] + NF4[i+1]) / 2 (exact in double), rounded toward -inf to fp32 so
-// that "x > thr" equals "x > midpoint" for every fp32 x; a tie (x equal to a
-// midpoint) keeps the lower code.  Each bucket (width 1/16) holds at most one
-// midpoint, since adjacent midpoints are more than 1/16 apart.  The bucket
-// index is computed exactly from x; an x on the edge between two buckets
-// gets the same code from either of them.
-const QuantTable& quant_table() {
-  static const QuantTable t = [] {
-    QuantTable q;
-    double mid[15];
-    float thr[15];
-    for (int i = 0; i < 15; ++i) {
-      mid[i] = 0.5 * ((double)kCodeValuesHost[CODE_NF4][i] + (double)kCodeValuesHost[CODE_NF4][i + 1]);
-      float f = (float)mid[i];
-      if ((double)f > mid[i]) f = nextafterf(f, -INFINITY);
-      thr[i] = f;
-    }
-    for (int b = 0; b < kBuckets; ++b) {
-      const double lo = (b - 0.5) / 16.0 - 1.0, hi = (b + 0.5) / 16.0 - 1.0;
-      uint32_t base = 0;
-      float t_in = INFINITY;
-      int inside = 0;
-      for (int i = 0; i < 15; ++i) {
-        if (mid[i] < lo) ++base;
-        else if (mid[i] < hi) { t_in = thr[i]; ++inside; }
-      }
-      if (inside > 1) abort();  // cannot happen for the Appendix E values
-      q.thr[b] = t_in;
-      q.base[b] = base;
-    }
-    return q;
-  }();
-  return t;
-}
-
-// Spec of the finer quantisation table of a codebook (any type): its
-// distinct values in increasing order (the smallest code for a repeated
-// value, so +0 rather than -0), the exact midpoints between neighbours and
-// those rounded toward -inf to fp32.  Checks once that no fine bucket holds
-// two midpoints (true for all four codebooks: the closest midpoints, E3M0's
-// around zero, are 2^-6 apart against a bucket width of 2^-9).
-const CodeSpec& code_spec(int code_type) {
-  static CodeSpec specs[CODE_TYPES];
-  static const bool built = [] {
-    for (int c = 0; c < CODE_TYPES; ++c) {
-      const float* v = kCodeValuesHost[c];
-      float vals[16];
-      uint32_t codes[16];
-      int n = 0;
-      for (int i = 0; i < 16; ++i) {  // insertion into the sorted distinct list
-        int j = 0;
-        while (j < n && vals[j] < v[i]) ++j;
-        if (j < n && vals[j] == v[i]) continue;  // repeated value (-0): keep the smaller code
-        for (int k = n; k > j; --k) { vals[k] = vals[k - 1]; codes[k] = codes[k - 1]; }
-        vals[j] = v[i];
-        codes[j] = (uint32_t)i;
-        ++n;
-      }
-      CodeSpec& sp = specs[c];
-      memset(&sp, 0, sizeof(sp));
-      sp.nmid = n - 1;
-      for (int i = 0; i < n; ++i) sp.rank_code[i] = codes[i];
-      for (int i = 0; i + 1 < n; ++i) {
-        sp.mid[i] = 0.5 * ((double)vals[i] + (double)vals[i + 1]);
-        float f = (float)sp.mid[i];
-        if ((double)f > sp.mid[i]) f = nextafterf(f, -INFINITY);
-        sp.thr[i] = f;
-      }
-      for (int b = 0; b < kFineBuckets; ++b) {
-        const double lo = (b - 0.5) / kFineScale - 1.0, hi = (b + 0.5) / kFineScale - 1.0;
-        int inside = 0;
-        for (int i = 0; i < sp.nmid; ++i) inside += sp.mid[i] >= lo && sp.mid[i] < hi;
-        if (inside > 1) abort();
-      }
-    }
-    return true;
-  }();
-  (void)built;
-  return specs[code_type];
-}
-
-// Int8 values k / 127: the fp64 quotient is correctly rounded and, since
-// the binary expansion of k / 127 repeats every 7 bits, never lies on an fp32
-// rounding boundary, so converting it to fp32 rounds k / 127 once.
-const Int8Tables& int8_tables() {
-  static const Int8Tables t = [] {
-    Int8Tables q;
-    for (int c = 0; c < 256; ++c) q.value[c] = (float)((double)(c >= 128 ? c - 256 : c) / 127.0);
-    for (int k = -127; k < 127; ++k) {
-      const double mid = 0.5 * ((double)q.value[k & 0xFF] + (double)q.value[(k + 1) & 0xFF]);
-      float f = (float)mid;
-      if ((double)f > mid) f = nextafterf(f, -INFINITY);
-      q.thr[k + 127] = f;
-    }
-    return q;
-  }();
-  return t;
-}
-
 // --------------------------------------------------- exact mean of c2
 // The mean mu is the exact sum of all c2 divided by their count, rounded
 // once to fp32.  Every non-negative fp32 value is an integer multiple of
@@ -195,8 +81,7 @@ __device__ __forceinline__ void c2_digits(float c, uint32_t& d, uint32_t& lo, ui
 
 constexpr int QZ_THREADS = 512;
 constexpr int QZ_WAVES = QZ_THREADS / 64;
-constexpr int QZ_MAX_WG = 256;       // also the number of exact-sum partials
-constexpr int64_t QZ_GRID_UNIT = 16384;  // weights per workgroup when sizing the grid
+constexpr int QZ_MAX_WG = kQuantMaxParts;  // also the number of exact-sum partials
 
 typedef uint32_t qz_u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short qz_u16x2 __attribute__((ext_vector_type(2)));
@@ -207,11 +92,6 @@ struct QzGeo {
   static constexpr int NV = BF16 ? 1 : 2;      // 16-byte loads per lane and step
   static constexpr int64_t CH = (int64_t)STEPS * QZ_WAVES * 512;
 };
-
-int quantize_parts(int64_t numel) {
-  const int64_t units = (numel + QZ_GRID_UNIT - 1) / QZ_GRID_UNIT;
-  return (int)(units < 1 ? 1 : (units > QZ_MAX_WG ? QZ_MAX_WG : units));
-}
 
 // Max over the 8 lanes of each octet (every lane gets its octet's max).
 __device__ __forceinline__ uint32_t octet_max(uint32_t v) {

@@ -58,7 +58,8 @@ typedef enum {
   QLORA_ERR_UNSUPPORTED_DTYPE = -2,  /* dtype code not accepted by this call     */
   QLORA_ERR_WORKSPACE_TOO_SMALL = -3,/* ws_bytes below what the call needs        */
   QLORA_ERR_MISALIGNED = -4,         /* a tensor pointer not 16-byte aligned      */
-  QLORA_ERR_HIP = -5                 /* a kernel launch failed                     */
+  QLORA_ERR_HIP = -5,                /* a kernel launch failed                     */
+  QLORA_ERR_INTERNAL = -6            /* a library-internal table failed its check  */
 } qlora_status;
 
 typedef enum {
@@ -266,20 +267,32 @@ int qlora_linear_fwd(const void* X, int64_t M, const qlora_nf4_t* W,
  *
  *   dY       device bf16 [M, N].
  *   X        device bf16 [M, K] (the forward input).
- *   XA       device bf16 [M, r], as written by qlora_linear_fwd.
+ *   XA       device bf16 [M, r] as written by qlora_linear_fwd, or NULL: the
+ *            call then recomputes X * A itself, bit-identical to what the
+ *            forward writes for the same X, A and M (it costs one more
+ *            read of X; the forward need not keep XA).
  *   W, A, B, r, s, M   as for qlora_linear_fwd.
- *   dX       device bf16 [M, K] or NULL (input gradient not wanted).
- *   dA       device bf16 [K, r], written.
- *   dB       device bf16 [r, N], written.
+ *   dX       device bf16 [M, K] or NULL (input gradient not wanted); always
+ *            written, never added to.
+ *   dA       device bf16 [K, r].
+ *   dB       device bf16 [r, N].
+ *   accumulate  0: dA and dB are written; 1: the gradients of this batch are
+ *            added to the values dA and dB hold on entry, dA = bf16(dA +
+ *            s X^T T) and likewise dB, so the gradients of several
+ *            micro-batches (QLoRA Appendix B.2, Table 9 trains with batch
+ *            sizes 16 to 64) sum in place with no caller-side temporary.
+ *            Any other value is QLORA_ERR_INVALID_ARG.
  *   ws       device workspace, ws_bytes >= the bwd figure of
- *            qlora_linear_workspace.
- * With M = 0, dA and dB are set to zero.  Products accumulate in fp32; T
- * enters the products as bf16(s * T).
+ *            qlora_linear_workspace (which includes the room for a
+ *            recomputed XA).
+ * With M = 0, dA and dB are set to zero (left as they are when
+ * accumulating).  Products accumulate in fp32; T enters the products as
+ * bf16(s * T).
  */
 int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M,
                      const qlora_nf4_t* W, const void* A, const void* B,
                      int32_t r, float s, void* dX, void* dA, void* dB,
-                     void* ws, int64_t ws_bytes, void* stream);
+                     int32_t accumulate, void* ws, int64_t ws_bytes, void* stream);
 
 /* ------------------------------------------------- LoRA dropout variants */
 
@@ -298,8 +311,9 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M,
  *   p          drop probability, 0 <= p < 1; kept elements are scaled by
  *              fp32(1 / (1 - p)).
  * Every other argument, the workspace size and the error behaviour are those
- * of qlora_linear_fwd / qlora_linear_bwd; XA returned by the forward is
- * drop(X) * A.  A null keep_mask is QLORA_ERR_INVALID_ARG.
+ * of qlora_linear_fwd / qlora_linear_bwd; XA returned by the forward (and
+ * recomputed by the backward when XA is NULL) is drop(X) * A.  A null
+ * keep_mask is QLORA_ERR_INVALID_ARG.
  */
 int qlora_linear_fwd_dropout(const void* X, int64_t M, const qlora_nf4_t* W,
                              const void* A, const void* B, int32_t r, float s,
@@ -309,7 +323,7 @@ int qlora_linear_fwd_dropout(const void* X, int64_t M, const qlora_nf4_t* W,
 int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int64_t M,
                              const qlora_nf4_t* W, const void* A, const void* B,
                              int32_t r, float s, const void* keep_mask, float p,
-                             void* dX, void* dA, void* dB,
+                             void* dX, void* dA, void* dB, int32_t accumulate,
                              void* ws, int64_t ws_bytes, void* stream);
 
 /* --------------------------------------------- LoRA-only optimizer step */

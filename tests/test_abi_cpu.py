@@ -79,8 +79,8 @@ def test_library_codebooks_equal_oracle_bit_exact():
 
 def test_status_strings():
     L = B.lib()
-    for s in range(-5, 1):
-        assert L.qlora_status_string(s).decode()
+    for s in range(-6, 1):
+        assert L.qlora_status_string(s).decode() != "unknown status"
     assert L.qlora_status_string(-99).decode() == "unknown status"
 
 
@@ -155,8 +155,9 @@ def _fwd(d, M=16, r=8, X=FAKE, A=FAKE, Bp=FAKE, Y=FAKE, XA=FAKE, ws=FAKE, nws=1 
     return B.lib().qlora_linear_fwd(X, M, ctypes.byref(d), A, Bp, r, 2.0, Y, XA, ws, nws, None)
 
 
-def _bwd(d, M=16, r=8, dY=FAKE, X=FAKE, XA=FAKE, A=FAKE, Bp=FAKE, dX=FAKE, dA=FAKE, dB=FAKE, ws=FAKE, nws=1 << 30):
-    return B.lib().qlora_linear_bwd(dY, X, XA, M, ctypes.byref(d), A, Bp, r, 2.0, dX, dA, dB, ws, nws, None)
+def _bwd(d, M=16, r=8, dY=FAKE, X=FAKE, XA=FAKE, A=FAKE, Bp=FAKE, dX=FAKE, dA=FAKE, dB=FAKE, acc=0, ws=FAKE,
+         nws=1 << 30):
+    return B.lib().qlora_linear_bwd(dY, X, XA, M, ctypes.byref(d), A, Bp, r, 2.0, dX, dA, dB, acc, ws, nws, None)
 
 
 def test_linear_validation():
@@ -174,7 +175,15 @@ def test_linear_validation():
     assert _fwd(_desc(), M=0, X=None, Y=None, ws=None, nws=0) == B.QLORA_OK
     assert _bwd(_desc(cols=100)) == B.QLORA_ERR_INVALID_ARG
     assert _bwd(_desc(), dA=None) == B.QLORA_ERR_INVALID_ARG
-    assert _bwd(_desc(), XA=None) == B.QLORA_ERR_INVALID_ARG
+    # XA may be NULL (recomputed); a bad one is still refused, before any launch
+    assert _bwd(_desc(), XA=None, nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert _bwd(_desc(), XA=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert _bwd(_desc(), X=None, XA=None) == B.QLORA_ERR_INVALID_ARG
+    assert _bwd(_desc(), acc=2) == B.QLORA_ERR_INVALID_ARG
+    assert "accumulate" in B.lib().qlora_last_error().decode()
+    assert _bwd(_desc(), acc=-1) == B.QLORA_ERR_INVALID_ARG
+    # no tokens and accumulate: nothing to add, nothing enqueued
+    assert _bwd(_desc(), M=0, acc=1, dY=None, X=None, XA=None, ws=None, nws=0) == B.QLORA_OK
     assert _bwd(_desc(), dX=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert _bwd(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
     assert _bwd(_desc(), r=300) == B.QLORA_ERR_INVALID_ARG
@@ -192,7 +201,7 @@ def _fwd_do(d, keep=FAKE, p=0.1, M=16, r=8, nws=1 << 30):
 
 def _bwd_do(d, keep=FAKE, p=0.1, M=16, r=8, nws=1 << 30):
     return B.lib().qlora_linear_bwd_dropout(FAKE, FAKE, FAKE, M, ctypes.byref(d), FAKE, FAKE, r, 2.0, keep, p, FAKE,
-                                            FAKE, FAKE, FAKE, nws, None)
+                                            FAKE, FAKE, 0, FAKE, nws, None)
 
 
 def test_dropout_validation():
