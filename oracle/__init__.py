@@ -55,6 +55,10 @@ is in tests/test_oracle_pins.py):
   linear.backward_dropout      pinned (reduction to the plain layer, brute
                                force, finite differences, torch.autograd in
                                fp64 with the mask as a tensor)
+  dropout_rng.*                pinned (numpy.random.Philox, the bit
+                               generator numpy ships for Philox4x64-10;
+                               per-element evaluation of the mask layout;
+                               exact threshold; binomial keep rate)
 """
 
-from . import codebook, fp8_e4m3, blockwise, linear, optim  # noqa: F401
+from . import codebook, fp8_e4m3, blockwise, linear, optim, dropout_rng  # noqa: F401
