@@ -611,6 +611,32 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     }
 }
 
+// The backward kernel's dequantised weight tile [64 n][256 k] (row pitch
+// 288 bf16) holds the 16-byte chunks of each 64-byte half-block permuted:
+// chunk c of block b (b = k / 64) in tile row n sits at position
+// c ^ ((b + 2 ((n >> 1) & 1)) & 3).  A dequantisation store instruction
+// writes 4 rows x 4 blocks (16 lanes); with the plain layout the row pitch
+// (16 banks mod 64) and the block stride (32 banks) put those 16 lanes on
+// 4 bank offsets only (4-way conflicts), with the permutation on 16.  A
+// transposed fragment read touches 8 bytes of one chunk per lane and 4 rows
+// per 16 lanes, each inside its row's own 16-bank window, so the
+// permutation leaves the reads conflict-free too.
+__device__ __forceinline__ int bwd_tile_col(int n, int col) {
+  const int s = (((col >> 6) & 3) + 2 * ((n >> 1) & 1)) & 3;
+  return (col & ~31) | ((((col >> 3) & 3) ^ s) << 3) | (col & 7);
+}
+
+// frag_rc over the permuted backward tile (same lanes, same values).
+__device__ __forceinline__ bf16x8 frag_rc_bwd(const __bf16* s, int pitch, int r0, int k0, int lane) {
+  const int g = lane >> 4, q = lane & 15;
+  const int col = r0 + 16 * (g & 1) + 4 * (q & 3);
+  const int red = k0 + 8 * (g >> 1) + (q >> 2);
+  const short4_t lo = ds_read_tr16(s + red * pitch + bwd_tile_col(red, col));
+  const short4_t hi = ds_read_tr16(s + (red + 4) * pitch + bwd_tile_col(red + 4, col));
+  const short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // ================================== main GEMM, 256 x 256, 8 waves, v6
 // Two waves per SIMD, each owning a 128 x 64 output tile (128 fp32
 // accumulators), so that one wave's LDS reads and dequantisation VALU overlap
@@ -697,9 +723,12 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
       f = a.dq.absmax[blk];
     }
   };
+  // backward: chunk w of the thread's half-block goes to its permuted place
+  // (see bwd_tile_col)
+  const int t_swz = ((t_col >> 6) + 2 * ((t_row >> 1) & 1)) & 3;
   auto wdst = [&](int buf, int w) -> __bf16* {
-    const int off = t_col + 32 * t_half + 8 * w;
-    return BWD ? &sB[buf][t_row * PRC + off] : &sB[buf][t_row * PK + off];
+    return BWD ? &sB[buf][t_row * PRC + t_col + 32 * t_half + 8 * (w ^ t_swz)]
+               : &sB[buf][t_row * PK + t_col + 32 * t_half + 8 * w];
   };
 
   bf16x8 fa[2][4], fb[2][2];
@@ -708,7 +737,8 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
     for (int i = 0; i < 4; ++i) fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      fb[slot][j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane)
+      fb[slot][j] = b_rc ? (BWD ? frag_rc_bwd(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane)
+                                : frag_rc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane))
                          : frag_kc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane);
   };
 
