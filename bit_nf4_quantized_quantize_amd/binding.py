@@ -50,7 +50,7 @@ EXPORTED = (
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
     "qlora_clip_scale_workspace", "qlora_clip_scale", "qlora_adamw_step",
-    "qlora_profile_events",
+    "qlora_profile_events", "qlora_linear_fwd_noalloc",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
 
@@ -114,6 +114,7 @@ def lib():
         "qlora_linear_bwd_dropout": (_i32, [_vp, _vp, _vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _f32, _vp, _vp,
                                             _vp, _i32, _vp, _i64, _vp]),
         "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
+        "qlora_linear_fwd_noalloc": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

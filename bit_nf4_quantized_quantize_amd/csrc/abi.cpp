@@ -199,6 +199,17 @@ const char* qlora_status_string(int32_t status) {
 
 const char* qlora_last_error(void) { return g_err; }
 
+}  // extern "C"
+
+// Records a failure message for the calling thread (for entry points defined
+// in other files of the library) and returns `status`.
+int qlora::record_failure(int status, const char* msg) {
+  snprintf(g_err, sizeof(g_err), "%s", msg);
+  return status;
+}
+
+extern "C" {
+
 int qlora_profile_events(int32_t kernel_id, void* start_event, void* stop_event) {
   if (kernel_id < 0 || kernel_id >= QLORA_KERNEL_COUNT)
     return fail(QLORA_ERR_INVALID_ARG, "qlora_profile_events: unknown kernel id %d", kernel_id);

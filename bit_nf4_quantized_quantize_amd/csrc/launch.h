@@ -174,6 +174,9 @@ hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const ui
                           hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);
 
+// Sets the calling thread's qlora_last_error() message and returns status.
+int record_failure(int status, const char* msg);
+
 // LoRA optimizer step.  launch_clip_scale writes scale = min(1, max_norm /
 // (||g||_2 + 1e-6)) for the bf16 gradient g [n], using clip_parts(n) fp64
 // partial sums; launch_adamw applies one AdamW step (bias corrections for

@@ -294,6 +294,24 @@ int qlora_linear_bwd(const void* dY, const void* X, const void* XA, int64_t M,
                      int32_t r, float s, void* dX, void* dA, void* dB,
                      int32_t accumulate, void* ws, int64_t ws_bytes, void* stream);
 
+/*
+ * qlora_linear_fwd_noalloc - qlora_linear_fwd for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * results, with no workspace argument.  The workspace comes from a fixed
+ * 96 MiB array of device memory the library holds on every GPU it runs on
+ * (from the first use on that GPU until the process ends); the call itself
+ * allocates and frees nothing.  Calls whose workspace (the fwd figure of
+ * qlora_linear_workspace) exceeds 96 MiB return
+ * QLORA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The array is
+ * shared by every call on one GPU: calls that overlap on the same GPU (on
+ * different streams, or from different threads) race on it; serialise them.
+ * The current HIP device must be the one `stream` belongs to.
+ */
+int qlora_linear_fwd_noalloc(const void* X, int64_t M, const qlora_nf4_t* W,
+                             const void* A, const void* B, int32_t r, float s,
+                             void* Y, void* XA, void* stream);
+
 /* ------------------------------------------------- LoRA dropout variants */
 
 /*

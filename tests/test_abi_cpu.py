@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
