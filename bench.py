@@ -450,22 +450,31 @@ def run_block(dev, reps=5):
 
 def run_dropout(B, L, dev, p=0.1, reps=10):
     """LoRA dropout on the adapter input (QLoRA Appendix B.2 uses p = 0.1 up
-    to 13B): forward + backward of the layer with a Bernoulli(1 - p) keep
-    mask drawn once on the device, against the same calls without dropout.
-    Median over `reps` pairs of calls between two events."""
+    to 13B): the keep mask drawn on the device (qlora_dropout_mask,
+    Philox4x64-10), then forward + backward of the layer with it, against the
+    same calls without dropout.  Median over `reps` calls between two
+    events."""
     import torch
 
     lin, t = L["lin"], L["t"]
-    g = torch.Generator(device=dev).manual_seed(11)
-    keep = B.pack_keep_mask(torch.rand(lin.M, lin.K, generator=g, device=dev) >= p)
+    keep = B.qlora_dropout_mask(11, 0, lin.M, lin.K, p, device=dev)
     qw = L["qw"]
+    ts = []
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.qlora_dropout_mask(11, i, lin.M, lin.K, p, out=keep)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    mask_us = sorted(ts[1:])[len(ts) // 2]
 
     def fb(kw):
         B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s, Y=L["Y"], XA=L["XA"], workspace=L["ws"], **kw)
         B.qlora_linear_bwd(t["dY"], t["X"], L["XA"], qw, t["A"], t["B"], lin.s,
                            dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["ws"], **kw)
 
-    out = {"p": p}
+    out = {"p": p, "mask_us": mask_us, "mask_bytes": lin.M * lin.K // 8}
     for name, kw in (("dropout", {"keep": keep, "p": p}), ("plain", {})):
         ts = []
         for _ in range(reps + 1):

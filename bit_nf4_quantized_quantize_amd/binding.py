@@ -50,7 +50,7 @@ EXPORTED = (
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
     "qlora_clip_scale_workspace", "qlora_clip_scale", "qlora_adamw_step",
-    "qlora_profile_events", "qlora_linear_fwd_noalloc",
+    "qlora_profile_events", "qlora_linear_fwd_noalloc", "qlora_dropout_mask",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
 
@@ -115,6 +115,7 @@ def lib():
                                             _vp, _i32, _vp, _i64, _vp]),
         "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
         "qlora_linear_fwd_noalloc": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp]),
+        "qlora_dropout_mask": (_i32, [ctypes.c_uint64, ctypes.c_uint64, _i64, _i64, _f32, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -323,6 +324,20 @@ def pack_keep_mask(keep):
         raise ValueError("keep must be a bool [M, K] tensor with K % 8 == 0")
     w = (1 << torch.arange(8, device=keep.device, dtype=torch.int32))
     return (keep.view(keep.shape[0], -1, 8).to(torch.int32) * w).sum(-1).to(torch.uint8).contiguous()
+
+
+def qlora_dropout_mask(seed, offset, M, K, p, out=None, device=None, stream=None):
+    """The packed keep mask u8 [M, K/8] of LoRA dropout with drop probability
+    p, drawn on the device from Philox4x64-10 keyed by (seed, offset)."""
+    if out is None:
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        out = torch.empty((M, K // 8), dtype=torch.uint8, device=dev)
+    _need_cuda(out)
+    if out.dtype != torch.uint8 or tuple(out.shape) != (M, K // 8) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 [M, K/8] tensor")
+    _check(lib().qlora_dropout_mask(int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1), M, K, float(p),
+                                    _ptr(out), _stream(stream)), "qlora_dropout_mask")
+    return out
 
 
 def _keep_arg(keep, X, p):

@@ -5,6 +5,7 @@
 #include "qlora_nf4_profile.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -494,6 +495,22 @@ int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int6
   if (!keep_mask) return fail(QLORA_ERR_INVALID_ARG, "%s: keep_mask is NULL", fn);
   return linear_bwd_impl(dY, X, XA, M, W, A, B, r, s, keep_mask, p, dX, dA, dB, accumulate, ws, ws_bytes, stream,
                          fn);
+}
+
+int qlora_dropout_mask(uint64_t seed, uint64_t offset, int64_t M, int64_t K, float p, void* keep_mask,
+                       void* stream) {
+  static const char* fn = "qlora_dropout_mask";
+  if (M < 0 || K <= 0 || K % 8) return fail(QLORA_ERR_INVALID_ARG, "%s: need M >= 0, K > 0 and K %% 8 == 0", fn);
+  if (M > kMaxNumel / K) return fail(QLORA_ERR_INVALID_ARG, "%s: M * K must be below 2^37", fn);
+  if (!(p >= 0.0f && p < 1.0f)) return fail(QLORA_ERR_INVALID_ARG, "%s: dropout p must be in [0, 1)", fn);
+  if (M == 0) return QLORA_OK;
+  int st;
+  if ((st = check_ptr(keep_mask, "keep_mask", fn))) return st;
+  // T = floor(p * 2^32), exact in double (p has 24 significant bits)
+  const uint32_t T = (uint32_t)floor((double)p * 4294967296.0);
+  const hipError_t e = launch_dropout_mask((uint8_t*)keep_mask, M * (K / 8), seed, offset, T, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
 }
 
 int qlora_clip_scale_workspace(int64_t n, int64_t* ws_bytes) {

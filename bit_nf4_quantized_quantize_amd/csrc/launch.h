@@ -174,6 +174,12 @@ hipError_t launch_tn_pair(const uint16_t* Ua, int64_t ldua, int64_t Pa, const ui
                           hipStream_t stream);
 hipError_t launch_fill_zero_u16(uint16_t* dst, int64_t n, hipStream_t stream);
 
+// LoRA dropout keep mask [nbytes] (packed, bit j of byte b for element
+// 8 b + j in row-major order) from Philox4x64-10: key (seed, 0), counter
+// (b, offset, 0, 0), bit j set iff 32-bit word j of the output >= T.
+hipError_t launch_dropout_mask(uint8_t* mask, int64_t nbytes, uint64_t seed, uint64_t offset, uint32_t T,
+                               hipStream_t stream);
+
 // Sets the calling thread's qlora_last_error() message and returns status.
 int record_failure(int status, const char* msg);
 

@@ -344,6 +344,28 @@ int qlora_linear_bwd_dropout(const void* dY, const void* X, const void* XA, int6
                              void* dX, void* dA, void* dB, int32_t accumulate,
                              void* ws, int64_t ws_bytes, void* stream);
 
+/*
+ * qlora_dropout_mask - draws the keep mask of the dropout entry points on the
+ * device (QLoRA Appendix B.2's LoRA dropout; each element kept with
+ * probability 1 - p).  The draw is Philox4x64-10 (Salmon, Moraes, Dror,
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) and fully
+ * determined by (seed, offset): byte b = m * (K/8) + c of the mask takes key
+ * (seed, 0) and counter (b, offset, 0, 0); the generator's four 64-bit
+ * outputs o_0..o_3 give eight 32-bit words u_j = o_{j/2} >> (32 (j % 2)),
+ * and bit j (element X[m, 8c + j]) is 1 (kept) iff u_j >= floor(p * 2^32).
+ * Use a new offset (or seed) for every layer and step; the backward must get
+ * the forward's mask.
+ *
+ *   seed, offset  the key and the second counter word.
+ *   M, K          the shape of the adapter input X [M, K]; K % 8 == 0.
+ *   p             drop probability, 0 <= p < 1.
+ *   keep_mask     device u8 [M, K/8], written (the layout the dropout entry
+ *                 points take).
+ * M = 0 enqueues nothing.  Bad sizes or p are QLORA_ERR_INVALID_ARG.
+ */
+int qlora_dropout_mask(uint64_t seed, uint64_t offset, int64_t M, int64_t K, float p,
+                       void* keep_mask, void* stream);
+
 /* --------------------------------------------- LoRA-only optimizer step */
 
 /*

@@ -137,6 +137,13 @@ int main() {
                             (float*)P(kBuf + 0x3000), n, nullptr, 1e-4f, 0.9f, 0.999f, 1e-8f, 0.0f, 1, nullptr) ==
            QLORA_OK);
   }
+  // the dropout mask generator
+  EXPECT(qlora_dropout_mask(1, 2, 4096, 4096, 0.1f, P(kBuf), nullptr) == QLORA_OK);
+  EXPECT(qlora_dropout_mask(~0ull, ~0ull, 3, 8, 0.999f, P(kBuf), nullptr) == QLORA_OK);
+  EXPECT(qlora_dropout_mask(1, 2, 0, 64, 0.1f, nullptr, nullptr) == QLORA_OK);
+  EXPECT(qlora_dropout_mask(1, 2, 4, 60, 0.1f, P(kBuf), nullptr) == QLORA_ERR_INVALID_ARG);
+  EXPECT(qlora_dropout_mask(1, 2, 4, 64, 1.0f, P(kBuf), nullptr) == QLORA_ERR_INVALID_ARG);
+  EXPECT(qlora_dropout_mask(1, 2, (int64_t)1 << 40, 64, 0.1f, P(kBuf), nullptr) == QLORA_ERR_INVALID_ARG);
   EXPECT(stub::calls > 0);
   EXPECT(stub::bad == 0);
   if (fails) {

@@ -124,6 +124,11 @@ hipError_t launch_clip_scale(const uint16_t*, int64_t n, float, float* scale, do
   region(partials, 8 * (int64_t)clip_parts(n), "norm partials");
   return hipSuccess;
 }
+hipError_t launch_dropout_mask(uint8_t* mask, int64_t nbytes, uint64_t, uint64_t, uint32_t, hipStream_t) {
+  ++stub::calls;
+  region(mask, nbytes, "dropout mask");
+  return hipSuccess;
+}
 hipError_t launch_adamw(float*, uint16_t*, const uint16_t*, float*, float*, int64_t, const float*, float, float, float,
                         float, float, int, hipStream_t) {
   ++stub::calls;

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -217,6 +217,20 @@ def test_dropout_validation():
         assert call(_desc(cols=200)) == B.QLORA_ERR_INVALID_ARG
         assert call(_desc(), r=0) == B.QLORA_ERR_INVALID_ARG
         assert call(_desc(), nws=1024) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_dropout_mask_validation():
+    """The mask generator rejects bad sizes, p outside [0, 1) and a missing or
+    misaligned buffer on the host; no tokens is a no-op."""
+    L = B.lib()
+    assert L.qlora_dropout_mask(1, 0, 16, 60, 0.1, FAKE, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_dropout_mask(1, 0, -1, 64, 0.1, FAKE, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_dropout_mask(1, 0, 16, 64, 1.0, FAKE, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_dropout_mask(1, 0, 16, 64, -0.5, FAKE, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_dropout_mask(1, 0, 16, 64, float("nan"), FAKE, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_dropout_mask(1, 0, 16, 64, 0.1, None, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_dropout_mask(1, 0, 16, 64, 0.1, FAKE_MIS, None) == B.QLORA_ERR_MISALIGNED
+    assert L.qlora_dropout_mask(1, 0, 0, 64, 0.1, None, None) == B.QLORA_OK
 
 
 def test_profile_hook_validation():
