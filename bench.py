@@ -266,8 +266,8 @@ def cpu_baseline_small(L, rows=1024, min_s=10.0, max_reps=50):
 def run_sweep(B, synth, dev, reps=3):
     """The 32-layer 7B-shaped sweep: every fp32 weight (224 matrices, 6.48e9
     parameters, each drawn with its own seed and resident in HBM) is quantised
-    with double quantisation, then every stored weight is dequantised to its
-    own bf16 output.  Each pass (224 back-to-back calls) is timed between two
+    with double quantisation (one batched call, and as 224 single calls), then
+    every stored weight is dequantised to its own bf16 output.  Each pass (224 back-to-back calls) is timed between two
     events, `reps` times after a warm-up pass; the median pass is reported,
     with the host time to enqueue a pass (the GPU time is only meaningful
     while that stays below it)."""
@@ -300,20 +300,40 @@ def run_sweep(B, synth, dev, reps=3):
                 enq = max(enq, (t1 - t0) * 1e3)
         return sorted(times)[len(times) // 2], enq
 
-    q_ms, q_enq = timed(lambda i: B.qlora_nf4_quantize(W[i], double_quant=True, out=Q[i], workspace=qws))
+    q1_ms, q1_enq = timed(lambda i: B.qlora_nf4_quantize(W[i], double_quant=True, out=Q[i], workspace=qws))
+    del qws
+    nbw = ctypes_workspace_bytes(B, Q)
+    bws = torch.empty(max(nbw, 16), dtype=torch.uint8, device=dev)
+
+    def batched(i):  # the whole sweep in one batched call (issued at i == 0)
+        if i == 0:
+            B.qlora_nf4_quantize_batched(W, Q, workspace=bws)
+    q_ms, q_enq = timed(batched)
     d_ms, d_enq = timed(lambda i: B.qlora_nf4_dequantize(Q[i], torch.bfloat16, out=D[i]))
     params = sum(n * k for n, k in shapes)
     qb, db = QUANT_BYTES_PER_PARAM * params, DEQUANT_BYTES_PER_PARAM * params
-    del W, Q, D, qws
+    del W, Q, D, bws
     torch.cuda.empty_cache()
     return {
         "matrices": len(shapes), "params": params, "passes": reps,
         "quantize_ms": q_ms, "quantize_GBps": qb / q_ms / 1e6, "quantize_frac_hbm": qb / q_ms / 1e6 / HBM_PEAK_GBS,
+        "quantize_how": "one qlora_nf4_quantize_batched call for all 224 matrices",
+        "quantize_single_calls_ms": q1_ms, "quantize_single_calls_GBps": qb / q1_ms / 1e6,
         "dequantize_ms": d_ms, "dequantize_GBps": db / d_ms / 1e6,
         "dequantize_frac_hbm": db / d_ms / 1e6 / HBM_PEAK_GBS,
-        "host_enqueue_ms": {"quantize": q_enq, "dequantize": d_enq},
+        "host_enqueue_ms": {"quantize": q_enq, "quantize_single_calls": q1_enq, "dequantize": d_enq},
         "bytes_per_param": {"quantize": QUANT_BYTES_PER_PARAM, "dequantize": DEQUANT_BYTES_PER_PARAM},
     }
+
+
+def ctypes_workspace_bytes(B, weights):
+    """Workspace bytes of one batched quantisation of `weights`."""
+    import ctypes
+    descs = (B.qlora_nf4_t * len(weights))(*[q.desc() for q in weights])
+    n = ctypes.c_int64(0)
+    B._check(B.lib().qlora_nf4_quantize_batched_workspace(descs, len(weights), ctypes.byref(n)),
+             "qlora_nf4_quantize_batched_workspace")
+    return n.value
 
 
 def run_code_types(B, L, dev, reps=10):

@@ -51,6 +51,7 @@ EXPORTED = (
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
     "qlora_clip_scale_workspace", "qlora_clip_scale", "qlora_adamw_step",
     "qlora_profile_events", "qlora_linear_fwd_noalloc", "qlora_dropout_mask",
+    "qlora_nf4_quantize_batched_workspace", "qlora_nf4_quantize_batched",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
 
@@ -116,6 +117,8 @@ def lib():
         "qlora_profile_events": (_i32, [_i32, _vp, _vp]),
         "qlora_linear_fwd_noalloc": (_i32, [_vp, _i64, _pdesc, _vp, _vp, _i32, _f32, _vp, _vp, _vp]),
         "qlora_dropout_mask": (_i32, [ctypes.c_uint64, ctypes.c_uint64, _i64, _i64, _f32, _vp, _vp]),
+        "qlora_nf4_quantize_batched_workspace": (_i32, [_pdesc, _i32, ctypes.POINTER(_i64)]),
+        "qlora_nf4_quantize_batched": (_i32, [ctypes.POINTER(_vp), _i32, _pdesc, _i32, _vp, _i64, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -277,6 +280,37 @@ def qlora_nf4_quantize(w, double_quant=True, out=None, workspace=None, stream=No
            "qlora_nf4_quantize")
     q._ws = ws  # keep the workspace alive until the stream has used it
     return q
+
+
+def qlora_nf4_quantize_batched(ws_list, outs, workspace=None, stream=None):
+    """Quantise the tensors in ws_list (all float32 or all bfloat16) into the
+    NF4Weight objects in outs (sharing code_type and double_quant) with one
+    batched call; returns outs."""
+    n = len(ws_list)
+    if n != len(outs):
+        raise ValueError("one output weight per input tensor")
+    if n == 0:
+        return outs
+    _need_cuda(*ws_list)
+    dtype = {torch.float32: QLORA_DTYPE_F32, torch.bfloat16: QLORA_DTYPE_BF16}.get(ws_list[0].dtype)
+    if dtype is None or any(w.dtype != ws_list[0].dtype or not w.is_contiguous() for w in ws_list):
+        raise ValueError("inputs must be contiguous and all float32 or all bfloat16")
+    for w, q in zip(ws_list, outs):
+        if w.numel() != q.numel:
+            raise ValueError("each input must have its weight's number of elements")
+    descs = (qlora_nf4_t * n)(*[q.desc() for q in outs])
+    ptrs = (_vp * n)(*[w.data_ptr() for w in ws_list])
+    nws = _i64(0)
+    _check(lib().qlora_nf4_quantize_batched_workspace(descs, n, ctypes.byref(nws)), "qlora_nf4_quantize_batched_workspace")
+    ws = workspace if workspace is not None else torch.empty(max(nws.value, 16), dtype=torch.uint8,
+                                                             device=ws_list[0].device)
+    if ws.numel() < nws.value:
+        raise ValueError(f"batched quantize workspace needs {nws.value} bytes")
+    _check(lib().qlora_nf4_quantize_batched(ptrs, dtype, descs, n, _ptr(ws), ws.numel(), _stream(stream)),
+           "qlora_nf4_quantize_batched")
+    for q in outs:
+        q._ws = ws
+    return outs
 
 
 def qlora_nf4_dequantize(q, dtype=torch.bfloat16, out=None, stream=None):

@@ -50,6 +50,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxNumel = (int64_t)1 << 37;
 constexpr int64_t kAlign = 256;  // alignment of workspace regions
+constexpr int kMaxBatch = 4096;  // tensors per batched quantisation call
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -307,6 +308,69 @@ int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q, voi
     e = launch_double_quant(c2, nb, parts, quantize_parts(numel), q->absmax_q, q->scale2, q->offset, s);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
+  return QLORA_OK;
+}
+
+int qlora_nf4_quantize_batched_workspace(const qlora_nf4_t* q, int32_t count, int64_t* ws_bytes) {
+  static const char* fn = "qlora_nf4_quantize_batched_workspace";
+  if (!ws_bytes) return fail(QLORA_ERR_INVALID_ARG, "%s: ws_bytes is NULL", fn);
+  if (count < 0 || count > kMaxBatch) return fail(QLORA_ERR_INVALID_ARG, "%s: count must be in [0, %d]", fn, kMaxBatch);
+  if (count > 0 && !q) return fail(QLORA_ERR_INVALID_ARG, "%s: q is NULL", fn);
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    int st = check_desc(&q[i], fn);
+    if (st) return st;
+    total += quant_ws(q[i].rows * q[i].cols, q[i].double_quant);
+  }
+  *ws_bytes = total;
+  return QLORA_OK;
+}
+
+int qlora_nf4_quantize_batched(const void* const* w, int32_t w_dtype, const qlora_nf4_t* q, int32_t count, void* ws,
+                               int64_t ws_bytes, void* stream) {
+  static const char* fn = "qlora_nf4_quantize_batched";
+  if (count < 0 || count > kMaxBatch) return fail(QLORA_ERR_INVALID_ARG, "%s: count must be in [0, %d]", fn, kMaxBatch);
+  if (count == 0) return QLORA_OK;
+  if (!w || !q) return fail(QLORA_ERR_INVALID_ARG, "%s: w and q must be host arrays of count entries", fn);
+  if (w_dtype != QLORA_DTYPE_F32 && w_dtype != QLORA_DTYPE_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: w_dtype must be F32 or BF16", fn);
+  int st;
+  int64_t need = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if ((st = check_desc(&q[i], fn))) return st;
+    if (q[i].code_type != q[0].code_type || q[i].double_quant != q[0].double_quant)
+      return fail(QLORA_ERR_INVALID_ARG, "%s: every descriptor must share code_type and double_quant", fn);
+    if (q[i].rows * q[i].cols > 0 && (st = check_ptr(w[i], "w[i]", fn))) return st;
+    need += quant_ws(q[i].rows * q[i].cols, q[i].double_quant);
+  }
+  if (ws_bytes < need) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)need);
+  if (need > 0 && (st = check_ptr(ws, "ws", fn))) return st;
+  if (!quant_tables_ok(q[0].code_type))
+    return fail(QLORA_ERR_INTERNAL, "%s: the quantisation table of code type %d is inconsistent", fn, q[0].code_type);
+  // each non-empty tensor's workspace regions, in order, laid out as qlora_nf4_quantize lays out its own
+  QuantJob jobs[kMaxBatch];
+  int n = 0;
+  char* base = (char*)ws;
+  for (int32_t i = 0; i < count; ++i) {
+    const int64_t numel = q[i].rows * q[i].cols;
+    const int64_t wsi = quant_ws(numel, q[i].double_quant);
+    if (numel > 0) {
+      QuantJob& jb = jobs[n++];
+      const int64_t nb = nblocks(numel);
+      jb.w = w[i];
+      jb.numel = numel;
+      jb.codes = q[i].codes;
+      jb.c2 = q[i].double_quant ? (float*)base : q[i].absmax;
+      jb.partials = q[i].double_quant ? (uint64_t*)(base + round_up(nb * 4, kAlign)) : nullptr;
+      jb.absmax_q = q[i].absmax_q;
+      jb.scale2 = q[i].scale2;
+      jb.offset = q[i].offset;
+    }
+    base += wsi;
+  }
+  const hipError_t e = launch_quantize_batched(jobs, n, w_dtype == QLORA_DTYPE_BF16, q[0].code_type,
+                                               q[0].double_quant != 0, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
 }
 

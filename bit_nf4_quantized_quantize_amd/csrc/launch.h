@@ -100,6 +100,24 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_t
                            uint64_t* partials, hipStream_t stream);
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts,
                                uint8_t* absmax_q, float* scale2, float* offset, hipStream_t stream);
+// Quantisation (and, with dq, double quantisation) of `count` tensors of
+// one input dtype and code type: one quantise and one encode launch per
+// kQuantBatch tensors, each tensor coded exactly as by its own launches.
+// c2 and partials are the tensor's workspace regions (as for
+// launch_quantize and launch_double_quant).
+constexpr int kQuantBatch = 32;
+struct QuantJob {
+  const void* w;
+  int64_t numel;
+  uint8_t* codes;
+  float* c2;
+  uint64_t* partials;
+  uint8_t* absmax_q;
+  float* scale2;
+  float* offset;
+};
+hipError_t launch_quantize_batched(const QuantJob* jobs, int count, bool w_bf16, int code_type, bool dq,
+                                   hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* codes, int64_t numel, int code_type, bool dq, const uint8_t* absmax_q,
                              const float* absmax, const float* scale2, const float* offset,
                              void* out, bool out_bf16, hipStream_t stream);

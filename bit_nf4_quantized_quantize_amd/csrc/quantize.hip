@@ -266,12 +266,12 @@ __device__ __forceinline__ void load_partial(const void* __restrict__ w, int64_t
   }
 }
 
+// The work of workgroup `bid` of `G` quantising one tensor (the grid of a
+// single-tensor launch, or this tensor's share of a batched launch).
 template <bool BF16, bool MAPPED>
-__global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
-                                                                  uint8_t* __restrict__ codes,
-                                                                  float* __restrict__ c2out,
-                                                                  uint64_t* __restrict__ partials, QuantTable tab,
-                                                                  CodeSpec spec) {
+__device__ __forceinline__ void nf4_quantize_wg(const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ codes,
+                                                float* __restrict__ c2out, uint64_t* __restrict__ partials,
+                                                const QuantTable& tab, const CodeSpec& spec, int64_t G, int64_t bid) {
   using Geo = QzGeo<BF16>;
   constexpr int STEPS = Geo::STEPS, NV = Geo::NV;
   constexpr int64_t CH = Geo::CH;
@@ -289,7 +289,6 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
 
   const int64_t nb = (numel + 63) >> 6;
   const int64_t nfull = numel / CH;
-  const int64_t G = gridDim.x;
   unsigned long long* acc = partials ? s_acc[wave] : nullptr;
   const uint32_t lane_off = (uint32_t)(wave * 512 + lane * 8);  // weights, within a step row
   const int k = lane & 7;
@@ -339,7 +338,7 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
   };
 
   qz_u32x4 ra[STEPS][NV], rb[STEPS][NV];
-  int64_t c = blockIdx.x;
+  int64_t c = bid;
   if (c < nfull) load_chunk(c, ra);
   while (c < nfull) {
     const int64_t c1 = c + G;
@@ -356,7 +355,7 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
   const int64_t tail0 = nfull * CH;
   if (tail0 < numel) {
     const int64_t T = (numel - tail0 + 511) >> 9;
-    const int64_t rot = (blockIdx.x + G - nfull % G) % G;  // workgroups with fewer full chunks first
+    const int64_t rot = (bid + G - nfull % G) % G;  // workgroups with fewer full chunks first
     for (int64_t t = rot * QZ_WAVES + wave; t < T; t += G * QZ_WAVES) {
       const int64_t e0 = tail0 + t * 512 + lane * 8;
       qz_u32x4 r[NV];
@@ -370,9 +369,18 @@ __global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __
       unsigned long long t = 0;
 #pragma unroll
       for (int v = 0; v < QZ_WAVES; ++v) t += s_acc[v][tid];
-      partials[(int64_t)tid * gridDim.x + blockIdx.x] = t;  // digit-major
+      partials[(int64_t)tid * G + bid] = t;  // digit-major
     }
   }
+}
+
+template <bool BF16, bool MAPPED>
+__global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_kernel(const void* __restrict__ w, int64_t numel,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  float* __restrict__ c2out,
+                                                                  uint64_t* __restrict__ partials, QuantTable tab,
+                                                                  CodeSpec spec) {
+  nf4_quantize_wg<BF16, MAPPED>(w, numel, codes, c2out, partials, tab, spec, gridDim.x, blockIdx.x);
 }
 
 // ------------------------------------------------- Int8 quantise kernel
@@ -421,10 +429,10 @@ __device__ __forceinline__ uint32_t int8_code_fast(float x, bool& near) {
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* __restrict__ w, int64_t numel,
-                                                                   uint8_t* __restrict__ codes,
-                                                                   float* __restrict__ c2out,
-                                                                   uint64_t* __restrict__ partials, Int8Tables tab) {
+__device__ __forceinline__ void int8_quantize_wg(const void* __restrict__ w, int64_t numel,
+                                                 uint8_t* __restrict__ codes, float* __restrict__ c2out,
+                                                 uint64_t* __restrict__ partials, const Int8Tables& tab, int64_t G,
+                                                 int64_t bid) {
   constexpr int U = Q8Geo<BF16>::U, NV = Q8Geo<BF16>::NV;
   constexpr int ES = BF16 ? 2 : 4;
   __shared__ float s_thr[254];
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* _
   __syncthreads();
   unsigned long long* acc = partials ? s_acc[wave] : nullptr;
   const int64_t nb = (numel + 63) >> 6;
-  const int64_t nsteps = (numel + 511) >> 9, GW = (int64_t)gridDim.x * Q8_WAVES;
+  const int64_t nsteps = (numel + 511) >> 9, GW = G * Q8_WAVES;
 
   // One step of a lane: 8 codes and, from lane 8j of each octet, the
   // block's constant.  `full`: all 512 weights of the step exist.
@@ -483,7 +491,7 @@ __global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* _
   };
 
   const int64_t nfull = numel >> 9;  // steps with all 512 weights present
-  for (int64_t t = (int64_t)blockIdx.x * Q8_WAVES + wave; t < nsteps; t += U * GW) {  // wave-uniform
+  for (int64_t t = bid * Q8_WAVES + wave; t < nsteps; t += U * GW) {  // wave-uniform
     qz_u32x4 r[U][NV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -508,9 +516,69 @@ __global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* _
       unsigned long long s = 0;
 #pragma unroll
       for (int v = 0; v < Q8_WAVES; ++v) s += s_acc[v][tid];
-      partials[(int64_t)tid * gridDim.x + blockIdx.x] = s;  // digit-major
+      partials[(int64_t)tid * G + bid] = s;  // digit-major
     }
   }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* __restrict__ w, int64_t numel,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   float* __restrict__ c2out,
+                                                                   uint64_t* __restrict__ partials, Int8Tables tab) {
+  int8_quantize_wg<BF16>(w, numel, codes, c2out, partials, tab, gridDim.x, blockIdx.x);
+}
+
+// ------------------------------------------------ batched quantisation
+// Up to kQuantBatch tensors per launch: tensor i takes workgroups
+// [begin[i], begin[i + 1]) of the grid, as many as its own launch would
+// have, so every tensor is coded exactly as by its own call.  The tensor of
+// a workgroup is found with an unrolled scan over constant indices (no
+// dynamic indexing of the kernel argument, which would go through scratch).
+struct QuantBatchArgs {
+  const void* w[kQuantBatch];
+  int64_t numel[kQuantBatch];
+  uint8_t* codes[kQuantBatch];
+  float* c2[kQuantBatch];
+  uint64_t* partials[kQuantBatch];
+  int parts[kQuantBatch];
+  int begin[kQuantBatch];
+  int count;
+};
+
+struct QuantBatchPick {
+  const void* w;
+  int64_t numel;
+  uint8_t* codes;
+  float* c2;
+  uint64_t* partials;
+  int parts, begin;
+};
+
+__device__ __forceinline__ QuantBatchPick pick_tensor(const QuantBatchArgs& b) {
+  QuantBatchPick t{b.w[0], b.numel[0], b.codes[0], b.c2[0], b.partials[0], b.parts[0], b.begin[0]};
+  const int bid = blockIdx.x;
+#pragma unroll
+  for (int j = 1; j < kQuantBatch; ++j) {
+    if (j < b.count && bid >= b.begin[j]) {
+      t = QuantBatchPick{b.w[j], b.numel[j], b.codes[j], b.c2[j], b.partials[j], b.parts[j], b.begin[j]};
+    }
+  }
+  return t;
+}
+
+template <bool BF16, bool MAPPED>
+__global__ __launch_bounds__(QZ_THREADS) void nf4_quantize_batched_kernel(const QuantBatchArgs b, QuantTable tab,
+                                                                          CodeSpec spec) {
+  const QuantBatchPick t = pick_tensor(b);
+  nf4_quantize_wg<BF16, MAPPED>(t.w, t.numel, t.codes, t.c2, t.partials, tab, spec, t.parts,
+                                (int64_t)blockIdx.x - t.begin);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(Q8_THREADS) void int8_quantize_batched_kernel(const QuantBatchArgs b, Int8Tables tab) {
+  const QuantBatchPick t = pick_tensor(b);
+  int8_quantize_wg<BF16>(t.w, t.numel, t.codes, t.c2, t.partials, tab, t.parts, (int64_t)blockIdx.x - t.begin);
 }
 
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_type, uint8_t* codes, float* c2,
@@ -546,6 +614,27 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t numel, int code_t
   }
   return hipGetLastError();
 }
+
+namespace {
+
+// Workgroups of the encode kernel for nb constants.
+int encode_wgs(int64_t nb);
+
+}  // namespace
+
+// Encode workgroups of tensor i: [begin[i], begin[i + 1]) of the grid.
+struct EncodeBatchArgs {
+  const float* c2[kQuantBatch];
+  int64_t nb[kQuantBatch];
+  const uint64_t* partials[kQuantBatch];
+  int parts[kQuantBatch];
+  uint8_t* absmax_q[kQuantBatch];
+  float* scale2[kQuantBatch];
+  float* offset[kQuantBatch];
+  int wgs[kQuantBatch];
+  int begin[kQuantBatch];
+  int count;
+};
 
 // Round the rational (sum / nb) in units of 2^-149 to the nearest fp32
 // (ties to even).  The fp32 bit pattern of a value v < 2^-125 is v / 2^-149
@@ -710,18 +799,18 @@ __device__ __forceinline__ void encode_group(const float cv[4], int64_t g, int64
 // capped, so mu is formed at most DQE_MAX_WG times.
 constexpr int DQE_MAX_WG = 512;
 
-__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ c2, int64_t nb,
-                                                        const uint64_t* __restrict__ partials, int parts,
-                                                        float* __restrict__ mu_out,
-                                                        uint8_t* __restrict__ absmax_q,
-                                                        float* __restrict__ scale2) {
+// The work of encode workgroup `bid` of `G` for one tensor.
+__device__ __forceinline__ void dq_encode_wg(const float* __restrict__ c2, int64_t nb,
+                                             const uint64_t* __restrict__ partials, int parts,
+                                             float* __restrict__ mu_out, uint8_t* __restrict__ absmax_q,
+                                             float* __restrict__ scale2, int64_t G, int64_t bid) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t ng = (nb + 255) >> 8, gstep = (int64_t)gridDim.x * 4;
-  int64_t g = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t ng = (nb + 255) >> 8, gstep = G * 4;
+  int64_t g = bid * 4 + wave;
   float cv[4];
   load_group(c2, g < ng ? g : 0, nb, lane, cv);  // independent of mu: these loads go out first
   const float mu = mean_from_partials<4>(partials, parts, nb);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+  if (bid == 0 && threadIdx.x == 0) *mu_out = mu;
   for (; g < ng; g += gstep) {  // wave-uniform
     float cn[4];
     if (g + gstep < ng) load_group(c2, g + gstep, nb, lane, cn);
@@ -731,14 +820,114 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
   }
 }
 
+__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ c2, int64_t nb,
+                                                        const uint64_t* __restrict__ partials, int parts,
+                                                        float* __restrict__ mu_out,
+                                                        uint8_t* __restrict__ absmax_q,
+                                                        float* __restrict__ scale2) {
+  dq_encode_wg(c2, nb, partials, parts, mu_out, absmax_q, scale2, gridDim.x, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void dq_encode_batched_kernel(const EncodeBatchArgs b) {
+  const float* c2 = b.c2[0];
+  int64_t nb = b.nb[0];
+  const uint64_t* partials = b.partials[0];
+  int parts = b.parts[0], wgs = b.wgs[0], begin = b.begin[0];
+  uint8_t* absmax_q = b.absmax_q[0];
+  float* scale2 = b.scale2[0];
+  float* offset = b.offset[0];
+  const int bid = blockIdx.x;
+#pragma unroll
+  for (int j = 1; j < kQuantBatch; ++j) {
+    if (j < b.count && bid >= b.begin[j]) {
+      c2 = b.c2[j]; nb = b.nb[j]; partials = b.partials[j]; parts = b.parts[j]; wgs = b.wgs[j];
+      begin = b.begin[j]; absmax_q = b.absmax_q[j]; scale2 = b.scale2[j]; offset = b.offset[j];
+    }
+  }
+  dq_encode_wg(c2, nb, partials, parts, offset, absmax_q, scale2, wgs, bid - begin);
+}
+
+namespace {
+int encode_wgs(int64_t nb) {
+  const int64_t ng = (nb + 255) / 256;
+  return (int)((ng + 3) / 4 < DQE_MAX_WG ? (ng + 3) / 4 : DQE_MAX_WG);
+}
+}  // namespace
+
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts, uint8_t* absmax_q,
                                float* scale2, float* offset, hipStream_t stream) {
   if (parts < 1 || parts > QZ_MAX_WG || QZ_MAX_WG > 256) return hipErrorInvalidValue;
-  const int64_t ng = (nb + 255) / 256;
-  const int64_t wgs = (ng + 3) / 4 < DQE_MAX_WG ? (ng + 3) / 4 : DQE_MAX_WG;
+  const int64_t wgs = encode_wgs(nb);
   hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, c2, nb, partials, parts, offset,
                      absmax_q, scale2);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_batched(const QuantJob* jobs, int count, bool w_bf16, int code_type, bool dq,
+                                   hipStream_t stream) {
+  if (code_type < 0 || code_type > CODE_INT8 || count < 0) return hipErrorInvalidValue;
+  for (int j0 = 0; j0 < count; j0 += kQuantBatch) {
+    const int n = count - j0 < kQuantBatch ? count - j0 : kQuantBatch;
+    QuantBatchArgs qa;
+    memset(&qa, 0, sizeof(qa));
+    int total = 0;
+    for (int i = 0; i < n; ++i) {
+      const QuantJob& jb = jobs[j0 + i];
+      qa.w[i] = jb.w; qa.numel[i] = jb.numel; qa.codes[i] = jb.codes; qa.c2[i] = jb.c2;
+      qa.partials[i] = dq ? jb.partials : nullptr;
+      qa.parts[i] = quantize_parts(jb.numel);
+      qa.begin[i] = total;
+      total += qa.parts[i];
+    }
+    qa.count = n;
+    const dim3 grid((unsigned)total);
+    if (code_type == CODE_INT8) {
+      const Int8Tables& t8 = int8_tables();
+      if (w_bf16)
+        hipLaunchKernelGGL((int8_quantize_batched_kernel<true>), grid, dim3(Q8_THREADS), 0, stream, qa, t8);
+      else
+        hipLaunchKernelGGL((int8_quantize_batched_kernel<false>), grid, dim3(Q8_THREADS), 0, stream, qa, t8);
+    } else {
+      const QuantTable& tab = quant_table();
+      const CodeSpec& spec = code_spec(code_type);
+      if (code_type == CODE_NF4) {
+        if (w_bf16)
+          hipLaunchKernelGGL((nf4_quantize_batched_kernel<true, false>), grid, dim3(QZ_THREADS), 0, stream, qa, tab,
+                             spec);
+        else
+          hipLaunchKernelGGL((nf4_quantize_batched_kernel<false, false>), grid, dim3(QZ_THREADS), 0, stream, qa,
+                             tab, spec);
+      } else {
+        if (w_bf16)
+          hipLaunchKernelGGL((nf4_quantize_batched_kernel<true, true>), grid, dim3(QZ_THREADS), 0, stream, qa, tab,
+                             spec);
+        else
+          hipLaunchKernelGGL((nf4_quantize_batched_kernel<false, true>), grid, dim3(QZ_THREADS), 0, stream, qa, tab,
+                             spec);
+      }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !dq) {
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    EncodeBatchArgs ea;
+    memset(&ea, 0, sizeof(ea));
+    total = 0;
+    for (int i = 0; i < n; ++i) {
+      const QuantJob& jb = jobs[j0 + i];
+      const int64_t nb = (jb.numel + 63) / 64;
+      ea.c2[i] = jb.c2; ea.nb[i] = nb; ea.partials[i] = jb.partials; ea.parts[i] = qa.parts[i];
+      ea.absmax_q[i] = jb.absmax_q; ea.scale2[i] = jb.scale2; ea.offset[i] = jb.offset;
+      ea.wgs[i] = encode_wgs(nb);
+      ea.begin[i] = total;
+      total += ea.wgs[i];
+    }
+    ea.count = n;
+    hipLaunchKernelGGL(dq_encode_batched_kernel, dim3((unsigned)total), dim3(256), 0, stream, ea);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // --------------------------------------------------------- dequantise

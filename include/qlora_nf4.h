@@ -211,6 +211,26 @@ int qlora_nf4_quantize(const void* w, int32_t w_dtype, const qlora_nf4_t* q,
                        void* ws, int64_t ws_bytes, void* stream);
 
 /*
+ * qlora_nf4_quantize_batched - qlora_nf4_quantize of `count` weights in one
+ * call (a model's weights at load time): the same codes and constants as
+ * `count` separate calls, bit for bit, with one quantisation launch and one
+ * double-quantisation launch per 32 weights instead of two launches per
+ * weight.
+ *
+ *   w        host array of `count` device pointers; w[i] is weight i
+ *            ([q[i].rows, q[i].cols], dtype w_dtype).
+ *   q        host array of `count` descriptors; all must share code_type and
+ *            double_quant (else QLORA_ERR_INVALID_ARG).
+ *   count    0 <= count <= 4096 (0 enqueues nothing).
+ *   ws       device workspace of ws_bytes >= qlora_nf4_quantize_batched_
+ *            workspace(q, count) (the sum of the weights' own workspaces).
+ * Every descriptor and pointer is validated before anything is enqueued.
+ */
+int qlora_nf4_quantize_batched_workspace(const qlora_nf4_t* q, int32_t count, int64_t* ws_bytes);
+int qlora_nf4_quantize_batched(const void* const* w, int32_t w_dtype, const qlora_nf4_t* q,
+                               int32_t count, void* ws, int64_t ws_bytes, void* stream);
+
+/*
  * qlora_nf4_dequantize - doubleDequant of QLoRA Eq. 6 (or the single
  * dequant of Eq. 2 without double quantisation).
  *

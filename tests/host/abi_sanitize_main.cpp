@@ -102,6 +102,27 @@ int main() {
                            {4096, 4096}, {11008, 4096}, {22016, 8192}, {7, 1 << 20}};
   for (const auto& q : qs)
     for (int ct = 0; ct <= 4; ++ct) quant_case(q[0], q[1], ct);
+  // batched quantisation of every quantisation size at once (and a
+  // mismatched batch)
+  for (int ct = 0; ct <= 4; ++ct) {
+    for (int dq = 0; dq <= 1; ++dq) {
+      const int n = (int)(sizeof(qs) / sizeof(qs[0]));
+      qlora_nf4_t ds[16];
+      const void* ws_ptrs[16];
+      for (int i = 0; i < n; ++i) {
+        ds[i] = desc(qs[i][0], qs[i][1], dq, ct);
+        ws_ptrs[i] = P(kBuf + 0xD0000 + 0x1000 * i);
+      }
+      int64_t need = -1;
+      EXPECT(qlora_nf4_quantize_batched_workspace(ds, n, &need) == QLORA_OK && need >= 0);
+      use_ws(need);
+      EXPECT(qlora_nf4_quantize_batched(ws_ptrs, 0, ds, n, need ? P(kWs) : nullptr, need, nullptr) == QLORA_OK);
+      if (need > 0) EXPECT(qlora_nf4_quantize_batched(ws_ptrs, 0, ds, n, P(kWs), need - 1, nullptr) ==
+                           QLORA_ERR_WORKSPACE_TOO_SMALL);
+      ds[1].code_type = (ct + 1) % 5;
+      EXPECT(qlora_nf4_quantize_batched(ws_ptrs, 0, ds, n, P(kWs), need, nullptr) == QLORA_ERR_INVALID_ARG);
+    }
+  }
   // storage and workspace queries at the size limits
   int64_t bytes[5], ws;
   EXPECT(qlora_nf4_storage_bytes(((int64_t)1 << 37) - 1, 1, bytes) == QLORA_OK);

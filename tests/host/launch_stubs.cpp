@@ -35,6 +35,16 @@ hipError_t launch_quantize(const void*, bool, int64_t numel, int code_type, uint
   region(partials, 8 * (int64_t)kMeanDigits * quantize_parts(numel), "mean partials");
   return hipSuccess;
 }
+hipError_t launch_quantize_batched(const QuantJob* jobs, int count, bool, int code_type, bool dq, hipStream_t) {
+  ++stub::calls;
+  for (int i = 0; i < count; ++i) {
+    const QuantJob& j = jobs[i];
+    region(j.codes, code_type == CODE_INT8 ? j.numel : (j.numel + 1) / 2, "batched codes");
+    region(j.c2, 4 * ((j.numel + 63) / 64), "batched c2");
+    if (dq) region(j.partials, 8 * (int64_t)kMeanDigits * quantize_parts(j.numel), "batched mean partials");
+  }
+  return hipSuccess;
+}
 hipError_t launch_double_quant(const float* c2, int64_t nb, const uint64_t* partials, int parts, uint8_t* absmax_q,
                                float* scale2, float* offset, hipStream_t) {
   ++stub::calls;

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -123,6 +123,35 @@ def test_quantize_validation():
     assert _quant(d) == B.QLORA_ERR_INVALID_ARG
     # an empty weight is a successful no-op
     assert _quant(_desc(rows=0), w=None, ws=None, nws=0) == B.QLORA_OK
+
+
+def test_batched_quantize_validation():
+    """The batched call validates every descriptor and pointer before any
+    launch: mixed code types or double_quant, a null weight pointer, a small
+    workspace, a bad count."""
+    L = B.lib()
+    n = 3
+    descs = (B.qlora_nf4_t * n)(*[_desc() for _ in range(n)])
+    ptrs = (ctypes.c_void_p * n)(FAKE, FAKE, FAKE)
+    need = ctypes.c_int64(0)
+    assert L.qlora_nf4_quantize_batched_workspace(descs, n, ctypes.byref(need)) == B.QLORA_OK
+    assert need.value == 3 * B.qlora_nf4_quantize_workspace(256 * 256, True)
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, n, FAKE, need.value - 1, None) == \
+        B.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, -1, FAKE, need.value, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, 5000, FAKE, need.value, None) == B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_nf4_quantize_batched(ptrs, 3, descs, n, FAKE, need.value, None) == B.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert L.qlora_nf4_quantize_batched(None, 0, None, 0, None, 0, None) == B.QLORA_OK
+    descs[1].code_type = 4
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, n, FAKE, need.value, None) == B.QLORA_ERR_INVALID_ARG
+    descs[1].code_type = 0
+    descs[2].double_quant = 0
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, n, FAKE, need.value, None) == B.QLORA_ERR_INVALID_ARG
+    descs[2].double_quant = 1
+    ptrs[1] = None
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, n, FAKE, need.value, None) == B.QLORA_ERR_INVALID_ARG
+    ptrs[1] = FAKE_MIS
+    assert L.qlora_nf4_quantize_batched(ptrs, 0, descs, n, FAKE, need.value, None) == B.QLORA_ERR_MISALIGNED
 
 
 def test_dequantize_validation():
