@@ -51,7 +51,7 @@ EXPORTED = (
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
     "qlora_clip_scale_workspace", "qlora_clip_scale", "qlora_adamw_step",
     "qlora_profile_events", "qlora_linear_fwd_noalloc", "qlora_dropout_mask",
-    "qlora_nf4_quantize_batched_workspace", "qlora_nf4_quantize_batched",
+    "qlora_nf4_quantize_batched_workspace", "qlora_nf4_quantize_batched", "qlora_adamw_step_paged",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
 
@@ -119,6 +119,8 @@ def lib():
         "qlora_dropout_mask": (_i32, [ctypes.c_uint64, ctypes.c_uint64, _i64, _i64, _f32, _vp, _vp]),
         "qlora_nf4_quantize_batched_workspace": (_i32, [_pdesc, _i32, ctypes.POINTER(_i64)]),
         "qlora_nf4_quantize_batched": (_i32, [ctypes.POINTER(_vp), _i32, _pdesc, _i32, _vp, _i64, _vp]),
+        "qlora_adamw_step_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _f32, _f32, _f32, _f32, _f32, _i32,
+                                          _vp, _i64, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -501,4 +503,31 @@ def qlora_adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr, betas=(0.9, 0.9
                                   _ptr(grad_scale) if grad_scale is not None else None, float(lr), float(betas[0]),
                                   float(betas[1]), float(eps), float(weight_decay), int(step), _stream(stream)),
            "qlora_adamw_step")
+    return param
+
+
+def qlora_adamw_step_paged(param, grad, exp_avg, exp_avg_sq, step, lr, staging, betas=(0.9, 0.999), eps=1e-8,
+                           weight_decay=0.0, grad_scale=None, param_bf16=None, stream=None, copy_stream=None):
+    """qlora_adamw_step with exp_avg and exp_avg_sq in pinned host memory,
+    paged through the uint8 device tensor `staging` chunk by chunk; copies
+    run on `copy_stream` (a torch.cuda.Stream) when given, overlapping the
+    updates."""
+    _need_cuda(param, grad, staging)
+    n = param.numel()
+    for t, name, dt in ((param, "param", torch.float32), (grad, "grad", torch.bfloat16),
+                        (exp_avg, "exp_avg", torch.float32), (exp_avg_sq, "exp_avg_sq", torch.float32)):
+        if t.dtype != dt or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of {n} elements")
+    for t, name in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if t.is_cuda or not t.is_pinned():
+            raise ValueError(f"{name} must be in pinned host memory")
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n):
+        raise ValueError("param_bf16 must be a bf16 tensor of the parameters' size")
+    cs = ctypes.c_void_p(copy_stream.cuda_stream) if copy_stream is not None else None
+    _check(lib().qlora_adamw_step_paged(_ptr(param), _ptr(param_bf16) if param_bf16 is not None else None, _ptr(grad),
+                                        _ptr(exp_avg), _ptr(exp_avg_sq), n,
+                                        _ptr(grad_scale) if grad_scale is not None else None, float(lr),
+                                        float(betas[0]), float(betas[1]), float(eps), float(weight_decay), int(step),
+                                        _ptr(staging), staging.numel(), _stream(stream), cs),
+           "qlora_adamw_step_paged")
     return param

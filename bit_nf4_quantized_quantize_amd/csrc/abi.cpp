@@ -105,19 +105,27 @@ int64_t quant_ws(int64_t numel, int dq) {
   return round_up(nb * 4, kAlign) + round_up((int64_t)quantize_parts(numel) * kMeanDigits * 8, kAlign);
 }
 
+// Shapes the small-token path can take (it also needs 4-bit codes); the
+// workspace layouts are sized for it whatever the code type.
+bool small_token_shape(int64_t M, int64_t N, int64_t r) {
+  return M >= 1 && M <= kGemvMaxM && N % 4 == 0 && r <= 256;
+}
+
 struct FwdWs {
-  // byte offsets: fp32 partials of X A, bf16 s*XA [M, rp], and for the
-  // small-token path fp32 partials of X W^T [gemv_splits][M][N]
-  // small-token path and the main product's split tiles share one region
+  // byte offsets: fp32 partials of X A (split partials, or on the
+  // small-token path one slice per 256-wide reduction chunk), bf16 s*XA
+  // [M, rp], then one region for the small-token path's fp32 partials of
+  // X W^T [gemv_splits][M][N] or the main product's split tiles
   int64_t part, xas, gv, total;
   int splits, gemv_splits;
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t rp = round_up(r, 64);
   FwdWs w;
-  const bool small = M >= 1 && M <= kGemvMaxM && N % 4 == 0 && r <= 256;
+  const bool small = small_token_shape(M, N, r);
   w.gemv_splits = small ? gemv_splits(M, N, K) : 0;
   w.splits = skinny_splits(M, r, K);
+  if (small && xa_chunks(K) > w.splits) w.splits = xa_chunks(K);
   w.part = 0;
   w.xas = w.part + round_up((int64_t)w.splits * M * rp * 4, kAlign);
   w.gv = w.xas + round_up(M * rp * 2, kAlign);
@@ -129,7 +137,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
 // The forward takes the small-token path (weight-streaming kernel) for these
 // shapes; the backward's recomputation of XA follows the same path.
 bool small_token_path(int64_t M, int64_t N, int64_t r, int32_t code_type) {
-  return M >= 1 && M <= kGemvMaxM && N % 4 == 0 && r <= 256 && code_type != CODE_INT8;
+  return small_token_shape(M, N, r) && code_type != CODE_INT8;
 }
 
 struct BwdWs {
@@ -145,6 +153,7 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   BwdWs w;
   w.splits_t = skinny_splits(M, r, N);
   w.splits_x = skinny_splits(M, r, K);  // as the forward's X A
+  if (small_token_shape(M, N, r) && xa_chunks(K) > w.splits_x) w.splits_x = xa_chunks(K);
   w.splits_a = tn_splits(M, K, r);
   w.splits_b = tn_splits(M, N, r);  // dB is formed as dB^T [N, r]
   // the two token reductions run together (dA partials at part, dB^T
@@ -430,19 +439,18 @@ int linear_fwd_impl(const void* X, int64_t M, const qlora_nf4_t* W, const void* 
   uint16_t* xas = (uint16_t*)(base + L.xas);
   hipError_t e;
   if (small_token_path(M, N, r, W->code_type)) {  // the weight-streaming kernel takes 4-bit codes
-    // few tokens: partials of X A, the weight-streaming product, then one
-    // kernel that adds both sets of partials and the adapter term
-    if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part, L.splits, nullptr, nullptr,
-                           rp, s, 1.0f, km, hs)) != hipSuccess)
-      return hip_fail(e, fn);
+    // few tokens: the weight-streaming product, which also writes the X A
+    // partials per reduction chunk, then one kernel that adds both sets of
+    // partials and the adapter term
     float* gv = (float*)(base + L.gv);
     {
       ProfScope ps(QLORA_KERNEL_FWD_MAIN, hs);
-      e = launch_gemv((const uint16_t*)X, M, K, W->codes, dq_params(W), N, gv, L.gemv_splits, hs);
+      e = launch_gemv((const uint16_t*)X, M, K, W->codes, dq_params(W), N, gv, L.gemv_splits, (const uint16_t*)A, r,
+                      rp, km, part, hs);
     }
     if (e != hipSuccess) return hip_fail(e, fn);
-    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, part, L.splits, rp, s * d, d, (const uint16_t*)B, r, (uint16_t*)Y,
-                           (uint16_t*)XA, hs);
+    e = launch_gemv_reduce(gv, L.gemv_splits, M, N, part, xa_chunks(K), rp, s * d, d, (const uint16_t*)B, r,
+                           (uint16_t*)Y, (uint16_t*)XA, hs);
     if (e != hipSuccess) return hip_fail(e, fn);
     return QLORA_OK;
   }
@@ -496,10 +504,9 @@ int linear_bwd_impl(const void* dY, const void* X, const void* XA, int64_t M, co
     // split partials, then the forward's own reduction for its path
     uint16_t* xa = (uint16_t*)(base + L.xa);
     if (small_token_path(M, N, r, W->code_type)) {
-      if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part_t, L.splits_x, nullptr,
-                             nullptr, rp, s, 1.0f, km, hs)) != hipSuccess)
+      if ((e = launch_xa_chunks((const uint16_t*)X, M, K, (const uint16_t*)A, r, rp, km, part_t, hs)) != hipSuccess)
         return hip_fail(e, fn);
-      if ((e = launch_xa_reduce(part_t, L.splits_x, M, rp, d, r, xa, hs)) != hipSuccess) return hip_fail(e, fn);
+      if ((e = launch_xa_reduce(part_t, xa_chunks(K), M, rp, d, r, xa, hs)) != hipSuccess) return hip_fail(e, fn);
     } else if ((e = launch_skinny((const uint16_t*)X, (const uint16_t*)A, true, M, r, K, part_t, L.splits_x, xa,
                                   nullptr, rp, s * d, d, km, hs)) != hipSuccess) {
       return hip_fail(e, fn);
@@ -596,6 +603,37 @@ int qlora_clip_scale(const void* grad, int64_t n, float max_norm, float* scale, 
   if (ws_bytes < need) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %lld bytes", fn, (long long)need);
   if ((st = check_ptr(ws, "ws", fn))) return st;
   const hipError_t e = launch_clip_scale((const uint16_t*)grad, n, max_norm, scale, (double*)ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+
+int qlora_adamw_step_paged(float* param, void* param_bf16, const void* grad, float* exp_avg, float* exp_avg_sq,
+                           int64_t n, const float* grad_scale, float lr, float beta1, float beta2, float eps,
+                           float weight_decay, int32_t step, void* staging, int64_t staging_bytes, void* stream,
+                           void* copy_stream) {
+  static const char* fn = "qlora_adamw_step_paged";
+  int st;
+  if (n < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: n < 0", fn);
+  if (step < 1) return fail(QLORA_ERR_INVALID_ARG, "%s: step counts from 1", fn);
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: betas must be in [0, 1)", fn);
+  if (!(eps > 0.0f) || !(lr >= 0.0f) || !(weight_decay >= 0.0f))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: need eps > 0, lr >= 0, weight_decay >= 0", fn);
+  // chunk: floats per state and slot, a multiple of 256 (staging = 2 slots x 2 states)
+  const int64_t chunk = staging_bytes / 16 / 256 * 256;
+  if (chunk < 256) return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: staging needs at least 4096 bytes", fn);
+  if (n == 0) return QLORA_OK;
+  if ((st = check_ptr(param, "param", fn)) || (st = check_ptr(grad, "grad", fn)) ||
+      (st = check_ptr(exp_avg, "exp_avg", fn)) || (st = check_ptr(exp_avg_sq, "exp_avg_sq", fn)) ||
+      (st = check_ptr(staging, "staging", fn)))
+    return st;
+  if (param_bf16 && !aligned16(param_bf16)) return fail(QLORA_ERR_MISALIGNED, "%s: param_bf16 not 16-byte aligned", fn);
+  if (grad_scale && !aligned16(grad_scale))
+    return fail(QLORA_ERR_MISALIGNED, "%s: grad_scale not 16-byte aligned", fn);
+  const hipError_t e =
+      launch_adamw_paged(param, (uint16_t*)param_bf16, (const uint16_t*)grad, exp_avg, exp_avg_sq, n, grad_scale, lr,
+                         beta1, beta2, eps, weight_decay, step, (float*)staging, chunk, (hipStream_t)stream,
+                         (hipStream_t)copy_stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
 }

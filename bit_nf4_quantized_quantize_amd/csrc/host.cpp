@@ -218,6 +218,7 @@ int gemv_splits(int64_t M, int64_t N, int64_t K) {
   if (s > nchunks) s = nchunks;  // every split holds at least one chunk
   return (int)(s < 1 ? 1 : s);
 }
+int xa_chunks(int64_t K) { return (int)((K + kXaChunk - 1) / kXaChunk); }
 int64_t main_split_bytes(int64_t M, int64_t ncols, int64_t L) {
   if (pick_tile(M, ncols, L) != T256x256) return 0;
   return plan_256(M, ncols, L).part_floats() * 4;

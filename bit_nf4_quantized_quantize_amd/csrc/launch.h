@@ -153,14 +153,21 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
                            const DQParams& dq, int64_t N, const uint16_t* XAs, const uint16_t* B,
                            int64_t r, int64_t rp, uint16_t* Y, float* split_ws, hipStream_t stream);
 // Small-token forward (1 <= M <= kGemvMaxM, N % 4 == 0): launch_gemv writes
-// fp32 partials part[splits][M][N] of X * W_bf16^T over reduction splits;
-// launch_gemv_reduce adds them, forms C = X A from the skinny partials
-// xpart[xsplits][M][rp] (rp <= 256), and writes Y = bf16(sum + bf16(alpha C) * B)
-// and, when XA is given, XA = bf16(scale1 C) [M, r].
+// fp32 partials part[splits][M][N] of X * W_bf16^T over reduction splits
+// and, per 256-wide reduction chunk, the partials xpart[xa_chunks(K)][M][rp]
+// of C = X A (X keep-masked when `keep` is given; rp <= 256);
+// launch_gemv_reduce adds both sets and writes Y = bf16(sum + bf16(alpha C)
+// * B) and, when XA is given, XA = bf16(scale1 C) [M, r].  launch_xa_chunks
+// writes the same X A partials alone (the backward's recomputation).
 constexpr int kGemvMaxM = 16;
+constexpr int kXaChunk = 256;  // reduction indices per X A partial slice
 int gemv_splits(int64_t M, int64_t N, int64_t K);
+int xa_chunks(int64_t K);      // ceil(K / kXaChunk)
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
-                       float* part, int splits, hipStream_t stream);
+                       float* part, int splits, const uint16_t* A, int64_t r, int64_t rp, const uint8_t* keep,
+                       float* xpart, hipStream_t stream);
+hipError_t launch_xa_chunks(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int64_t r, int64_t rp,
+                            const uint8_t* keep, float* xpart, hipStream_t stream);
 // XA [M, r] = bf16(scale1 C) from the skinny partials of C = X A exactly as
 // launch_gemv_reduce forms it (the backward recomputes the small-token
 // forward's XA with it, bit for bit).
@@ -212,5 +219,12 @@ hipError_t launch_clip_scale(const uint16_t* g, int64_t n, float max_norm, float
 hipError_t launch_adamw(float* p, uint16_t* p_bf16, const uint16_t* g, float* m, float* v, int64_t n,
                         const float* gscale, float lr, float beta1, float beta2, float eps, float weight_decay,
                         int step, hipStream_t stream);
+// The step with m, v in pinned host memory, paged through `staging`
+// ([2][2][chunk] floats, chunk % 256 == 0) in chunks: copied in, updated by
+// launch_adamw, copied back; copies on `copy` (if given and not `stream`),
+// ordered against the updates by events.
+hipError_t launch_adamw_paged(float* p, uint16_t* p_bf16, const uint16_t* g, float* m_host, float* v_host, int64_t n,
+                              const float* gscale, float lr, float beta1, float beta2, float eps, float weight_decay,
+                              int step, float* staging, int64_t chunk, hipStream_t stream, hipStream_t copy);
 
 }  // namespace qlora

@@ -1324,13 +1324,104 @@ struct G3Set {
   uint8_t q[2];
 };
 
+// The adapter input of the few-token forward, per reduction chunk: the
+// partial X A over the 256 reduction indices of chunk c (fewer in the last
+// chunk), xpart[c][m][j] for m < M, j < rp (columns past r are zero).  The
+// whole 512-thread workgroup calls it.  The chunk of X (keep-masked for LoRA
+// dropout when `keep` is given; rows 16..31 of the MFMA tile repeat row
+// M - 1 and are not stored) goes to `lx` as [32][XA_PX] together with the
+// first tile of A rows, which pass through `la` (64 KiB) in as few
+// [rows][rp + kRcPad] tiles as fit; wave w multiplies column tile w (32
+// columns) with 32x32x16 MFMAs in ascending reduction order.  The forward's
+// weight-streaming kernel and the backward's recomputation of XA both take
+// XA from these partials, so the two are bit-identical.
+constexpr int XA_CHUNK = kXaChunk;
+constexpr int XA_LDS_A = 65536;             // bytes of the A tiles
+constexpr int XA_PX = XA_CHUNK + 8;          // pitch (bf16) of the X tile
+constexpr int XA_LDS_X = 32 * XA_PX * 2;     // bytes of the X tile
+__device__ __forceinline__ void xa_chunk_partial(const uint16_t* __restrict__ X, int M, int64_t K,
+                                                 const uint16_t* __restrict__ A, int r, int rp,
+                                                 const uint8_t* __restrict__ keep, int64_t c,
+                                                 float* __restrict__ xpart, __bf16* la, __bf16* lx) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pa = rp + kRcPad, ppr = rp >> 3;  // A tile pitch, 16-byte pieces per A row
+  const int64_t kc = c * XA_CHUNK;
+  const int rows = (int)(K - kc < XA_CHUNK ? K - kc : XA_CHUNK);  // a multiple of 64 (K % 64 == 0)
+  const int rows_pass = 64 * (XA_LDS_A / (64 * pa * 2));           // 256 (rp = 64), 192, 128 or 64 (rp = 256)
+  // X: piece q = 512 i + tid is row q / 32 (clamped), columns 8 (q % 32) ..
+  uint4 xv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = 512 * i + tid, m = q >> 5, kk = 8 * (q & 31);
+    const int64_t row = m < M ? m : M - 1;
+    if (kk < rows) {
+      xv[i] = ldg16(X + row * K + kc + kk);
+      if (keep) xv[i] = apply_keep8(xv[i], keep[row * (K >> 3) + ((kc + kk) >> 3)]);
+    }
+  }
+  const bool active = 32 * wave < rp;
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int r0 = 0; r0 < rows; r0 += rows_pass) {
+    const int nr = rows - r0 < rows_pass ? rows - r0 : rows_pass;
+    // A: piece q = 512 i + tid of this tile is row q / ppr, columns 8 (q % ppr) ..
+    uint4 av[6];  // rows_pass * ppr <= 6 * 512
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int q = 512 * i + tid;
+      if (q < nr * ppr) av[i] = load8_masked(A, r, kc + r0 + q / ppr, K, 8 * (q % ppr), r);
+    }
+    if (r0) __syncthreads();  // the previous tile has been read
+    if (r0 == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = 512 * i + tid, kk = 8 * (q & 31);
+        if (kk < rows) sts16(&lx[(q >> 5) * XA_PX + kk], xv[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int q = 512 * i + tid;
+      if (q < nr * ppr) sts16(&la[(q / ppr) * pa + 8 * (q % ppr)], av[i]);
+    }
+    __syncthreads();
+    if (active) {
+      for (int kk = 0; kk < nr; kk += 16) {
+        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(&lx[(lane & 31) * XA_PX + r0 + kk + 8 * (lane >> 5)]);
+        acc = mfma32(xf, frag_rc(la, pa, 32 * wave, kk, lane), acc);
+      }
+    }
+  }
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = acc_row32(e, lane);
+      if (m < M) xpart[(c * M + m) * rp + 32 * wave + (lane & 31)] = acc[e];
+    }
+  }
+}
+
+// XA partials of every reduction chunk (one workgroup per chunk), for the
+// backward's recomputation of the few-token forward's XA.
+__global__ __launch_bounds__(512) void xa_chunks_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
+                                                        const uint16_t* __restrict__ A, int r, int rp,
+                                                        const uint8_t* __restrict__ keep, float* __restrict__ xpart) {
+  __shared__ __attribute__((aligned(16))) __bf16 la[XA_LDS_A / 2];
+  __shared__ __attribute__((aligned(16))) __bf16 lx[XA_LDS_X / 2];
+  xa_chunk_partial(X, M, K, A, r, rp, keep, blockIdx.x, xpart, la, lx);
+}
+
 template <bool DQ>
 __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
                                                        const uint8_t* __restrict__ codes, const DQParams dq,
-                                                       int64_t N, int S, float* __restrict__ part) {
+                                                       int64_t N, int S, float* __restrict__ part,
+                                                       const uint16_t* __restrict__ lora_a, int rank, int rank_pad,
+                                                       const uint8_t* __restrict__ keep, float* __restrict__ xpart) {
   __shared__ uint32_t tab[256 * 64];
   __shared__ u32x4 stage[2][G3_CHUNK16];  // code chunks; the partial tiles at the end
   __shared__ float2 cst[2][G3_ROWS * G3_CB / 2];  // block constants cst[buf][row][block]
+  static_assert(sizeof(stage) >= XA_LDS_A && sizeof(tab) >= XA_LDS_X, "the X A tiles fit in the stages and table");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* cv = kCodeValues[dq.code_type];
 
@@ -1360,18 +1451,6 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   // activations: lane (t, g) of wave w, block w % 4 of the chunk
   const int t = lane & 15, g = lane >> 4, q = wave & 3, hrow = 128 * (wave >> 2);
   const uint16_t* xrow = X + (int64_t)(t < M ? t : M - 1) * K + 16 * g;
-
-  {
-    // table: entry e (a code byte) = the bf16 pair (value[e % 16], value[e / 16]),
-    // 64 copies side by side
-    u32x4* tv = reinterpret_cast<u32x4*>(tab);
-#pragma unroll
-    for (int k = 0; k < 256 * 64 / 4 / G3_T; ++k) {
-      const int i = k * G3_T + tid, e = i >> 4;
-      const uint32_t v = pack_bf2(cv[e & 15], cv[e >> 4]);
-      tv[i] = u32x4{v, v, v, v};
-    }
-  }
 
   // chunk kc >= c_hi (the pipeline's run-out) reloads chunk c_hi - 1, which
   // is still in L2; blocks past the weight's end reload its last block
@@ -1470,6 +1549,32 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   issue_x(c_lo + 1, B);
   issue_codes(c_lo + 2, C);
   issue_x(c_lo + 2, C);
+
+  // while the first chunks are in flight, the first workgroups each take
+  // one reduction chunk of X A (more when the grid is smaller than the
+  // chunk count), in the space of the code stages and the table
+  {
+    const int64_t nxc = (K + XA_CHUNK - 1) / XA_CHUNK, wid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    if (wid < nxc) {
+      for (int64_t c = wid; c < nxc; c += (int64_t)gridDim.x * gridDim.y)
+        xa_chunk_partial(X, M, K, lora_a, rank, rank_pad, keep, c, xpart, reinterpret_cast<__bf16*>(stage),
+                         reinterpret_cast<__bf16*>(tab));
+      __syncthreads();  // the tiles have been read before the table and stages are filled
+    }
+  }
+
+  {
+    // table: entry e (a code byte) = the bf16 pair (value[e % 16], value[e / 16]),
+    // 64 copies side by side
+    u32x4* tv = reinterpret_cast<u32x4*>(tab);
+#pragma unroll
+    for (int k = 0; k < 256 * 64 / 4 / G3_T; ++k) {
+      const int i = k * G3_T + tid, e = i >> 4;
+      const uint32_t v = pack_bf2(cv[e & 15], cv[e >> 4]);
+      tv[i] = u32x4{v, v, v, v};
+    }
+  }
+
   int kc = c_lo;
   for (; kc + G3_D <= c_hi; kc += G3_D) {
     step(kc, A);
@@ -1723,14 +1828,27 @@ hipError_t launch_fwd_main(const uint16_t* X, int64_t M, int64_t K, const uint8_
 
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, const DQParams& dq, int64_t N,
-                       float* part, int splits, hipStream_t stream) {
+                       float* part, int splits, const uint16_t* A, int64_t r, int64_t rp, const uint8_t* keep,
+                       float* xpart, hipStream_t stream) {
   if (M < 1 || M > kGemvMaxM || splits < 1 || K < 64 || N < 1) return hipErrorInvalidValue;
   if (splits > ((K >> 6) + G3_CB - 1) / G3_CB) return hipErrorInvalidValue;  // an empty split
+  if (K % 64 || rp % 64 || rp > 256 || r > rp) return hipErrorInvalidValue;
+  static_assert(G3_T == 512, "the X A chunks are computed by 512-thread workgroups");
   const dim3 grid(cdiv(N, G3_ROWS), (unsigned)splits);
   if (dq.double_quant)
-    hipLaunchKernelGGL((gemv3_kernel<true>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part);
+    hipLaunchKernelGGL((gemv3_kernel<true>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part,
+                       A, (int)r, (int)rp, keep, xpart);
   else
-    hipLaunchKernelGGL((gemv3_kernel<false>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part);
+    hipLaunchKernelGGL((gemv3_kernel<false>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part,
+                       A, (int)r, (int)rp, keep, xpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_xa_chunks(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int64_t r, int64_t rp,
+                            const uint8_t* keep, float* xpart, hipStream_t stream) {
+  if (M < 1 || M > kGemvMaxM || rp % 64 || rp > 256 || r > rp || K < 64 || K % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xa_chunks_kernel, dim3((unsigned)xa_chunks(K)), dim3(512), 0, stream, X, (int)M, K, A, (int)r,
+                     (int)rp, keep, xpart);
   return hipGetLastError();
 }
 

@@ -148,4 +148,58 @@ hipError_t launch_adamw(float* p, uint16_t* p_bf16, const uint16_t* g, float* m,
   return hipGetLastError();
 }
 
+// The paged step: the states live in pinned host memory and are paged
+// through the device staging area [2 slots][m, v][chunk] floats, chunk by
+// chunk.  Slot c % 2 takes chunk c: its states are copied in (host to
+// device), updated by the same AdamW kernel as device-resident states, and
+// copied back; chunk c + 2 is copied into the slot after chunk c's copy
+// back.  With a separate copy stream the copies run on it, ordered against
+// the updates by events, so the copies of one chunk overlap the update of
+// the other; without one everything runs in order on `stream`.  Either way
+// `stream` reaches its end only after the last copy back.
+hipError_t launch_adamw_paged(float* p, uint16_t* p_bf16, const uint16_t* g, float* m_host, float* v_host, int64_t n,
+                              const float* gscale, float lr, float beta1, float beta2, float eps, float weight_decay,
+                              int step, float* staging, int64_t chunk, hipStream_t stream, hipStream_t copy) {
+  if (n <= 0) return hipSuccess;
+  if (chunk <= 0 || chunk % 256) return hipErrorInvalidValue;
+  const int64_t nch = (n + chunk - 1) / chunk;
+  const bool two = copy != nullptr && copy != stream;
+  hipStream_t cs = two ? copy : stream;
+  hipEvent_t ev[6] = {};  // start, end, loaded[2], updated[2]
+  hipError_t e = hipSuccess;
+  if (two) {
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  }
+  auto slot_m = [&](int64_t c) { return staging + ((c & 1) * 2 + 0) * chunk; };
+  auto slot_v = [&](int64_t c) { return staging + ((c & 1) * 2 + 1) * chunk; };
+  auto len_of = [&](int64_t c) { return (c + 1) * chunk <= n ? chunk : n - c * chunk; };
+  auto page_in = [&](int64_t c) {
+    const int64_t off = c * chunk, len = len_of(c);
+    if (e == hipSuccess) e = hipMemcpyAsync(slot_m(c), m_host + off, len * 4, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipMemcpyAsync(slot_v(c), v_host + off, len * 4, hipMemcpyHostToDevice, cs);
+    if (two && e == hipSuccess) e = hipEventRecord(ev[2 + (c & 1)], cs);
+  };
+  if (two && e == hipSuccess) e = hipEventRecord(ev[0], stream);  // after the work before this call
+  if (two && e == hipSuccess) e = hipStreamWaitEvent(cs, ev[0], 0);
+  page_in(0);
+  if (nch > 1) page_in(1);
+  for (int64_t c = 0; c < nch && e == hipSuccess; ++c) {
+    const int64_t off = c * chunk, len = len_of(c);
+    if (two) e = hipStreamWaitEvent(stream, ev[2 + (c & 1)], 0);
+    if (e == hipSuccess)
+      e = launch_adamw(p + off, p_bf16 ? p_bf16 + off : nullptr, g + off, slot_m(c), slot_v(c), len, gscale, lr,
+                       beta1, beta2, eps, weight_decay, step, stream);
+    if (two && e == hipSuccess) e = hipEventRecord(ev[4 + (c & 1)], stream);
+    if (two && e == hipSuccess) e = hipStreamWaitEvent(cs, ev[4 + (c & 1)], 0);
+    if (e == hipSuccess) e = hipMemcpyAsync(m_host + off, slot_m(c), len * 4, hipMemcpyDeviceToHost, cs);
+    if (e == hipSuccess) e = hipMemcpyAsync(v_host + off, slot_v(c), len * 4, hipMemcpyDeviceToHost, cs);
+    if (c + 2 < nch) page_in(c + 2);
+  }
+  if (two && e == hipSuccess) e = hipEventRecord(ev[1], cs);
+  if (two && e == hipSuccess) e = hipStreamWaitEvent(stream, ev[1], 0);
+  for (int i = 0; i < 6; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);  // released once the streams have passed them
+  return e;
+}
+
 }  // namespace qlora

@@ -424,6 +424,36 @@ int qlora_adamw_step(float* param, void* param_bf16, const void* grad,
                      const float* grad_scale, float lr, float beta1, float beta2,
                      float eps, float weight_decay, int32_t step, void* stream);
 
+/*
+ * qlora_adamw_step_paged - qlora_adamw_step with the optimizer states paged
+ * (QLoRA section 3 "Paged Optimizers": the states are evicted to CPU RAM
+ * and paged back to the GPU for the update).  exp_avg and exp_avg_sq live
+ * in pinned host memory (allocated pinned, e.g. hipHostMalloc; never
+ * registered after the fact); the call pages them through the device
+ * staging buffer in chunks: each chunk is copied in, updated by the same
+ * kernel as device-resident states (so the results are bit-identical to
+ * qlora_adamw_step on device states), and copied back.  param, param_bf16,
+ * grad and grad_scale are device pointers as for qlora_adamw_step.
+ *
+ *   staging        device workspace of staging_bytes >= 4096: two slots of
+ *                  (m, v) chunks; chunk = staging_bytes / 16 rounded down to
+ *                  a multiple of 256 elements.
+ *   copy_stream    a second stream (hipStream_t as void*) for the copies, or
+ *                  NULL: with it the copies of one chunk overlap the update
+ *                  of the other (ordered by events the call creates and
+ *                  releases); without it everything runs in order on
+ *                  `stream`.
+ * In both cases `stream` reaches the end of the call only after the last
+ * state is back in host memory.  Other arguments and errors as for
+ * qlora_adamw_step; a staging buffer below 4096 bytes is
+ * QLORA_ERR_WORKSPACE_TOO_SMALL.
+ */
+int qlora_adamw_step_paged(float* param, void* param_bf16, const void* grad,
+                           float* exp_avg, float* exp_avg_sq, int64_t n,
+                           const float* grad_scale, float lr, float beta1, float beta2,
+                           float eps, float weight_decay, int32_t step,
+                           void* staging, int64_t staging_bytes, void* stream, void* copy_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,6 +165,14 @@ int main() {
   EXPECT(qlora_dropout_mask(1, 2, 4, 60, 0.1f, P(kBuf), nullptr) == QLORA_ERR_INVALID_ARG);
   EXPECT(qlora_dropout_mask(1, 2, 4, 64, 1.0f, P(kBuf), nullptr) == QLORA_ERR_INVALID_ARG);
   EXPECT(qlora_dropout_mask(1, 2, (int64_t)1 << 40, 64, 0.1f, P(kBuf), nullptr) == QLORA_ERR_INVALID_ARG);
+  // the paged optimizer step: staging sizes around the minimum
+  for (int64_t sb : {(int64_t)4095, (int64_t)4096, (int64_t)16385, (int64_t)1 << 20, (int64_t)3 * 4096 + 7}) {
+    use_ws(sb);
+    const int want = sb >= 4096 ? QLORA_OK : QLORA_ERR_WORKSPACE_TOO_SMALL;
+    EXPECT(qlora_adamw_step_paged((float*)P(kBuf), nullptr, P(kBuf + 0x1000), (float*)P(kBuf + 0x2000),
+                                  (float*)P(kBuf + 0x3000), 100003, nullptr, 1e-4f, 0.9f, 0.999f, 1e-8f, 0.0f, 1,
+                                  P(kWs), sb, nullptr, nullptr) == want);
+  }
   EXPECT(stub::calls > 0);
   EXPECT(stub::bad == 0);
   if (fails) {

@@ -80,10 +80,17 @@ hipError_t launch_fwd_main(const uint16_t*, int64_t M, int64_t K, const uint8_t*
   region(split_ws, dq.code_type == CODE_INT8 ? 0 : main_split_bytes(M, N, K), "fwd split tiles");
   return hipSuccess;
 }
-hipError_t launch_gemv(const uint16_t*, int64_t M, int64_t, const uint8_t*, const DQParams&, int64_t N, float* part,
-                       int splits, hipStream_t) {
+hipError_t launch_gemv(const uint16_t*, int64_t M, int64_t K, const uint8_t*, const DQParams&, int64_t N, float* part,
+                       int splits, const uint16_t*, int64_t, int64_t rp, const uint8_t*, float* xpart, hipStream_t) {
   ++stub::calls;
   region(part, 4 * (int64_t)splits * M * N, "gemv partials");
+  region(xpart, 4 * (int64_t)xa_chunks(K) * M * rp, "xa chunk partials");
+  return hipSuccess;
+}
+hipError_t launch_xa_chunks(const uint16_t*, int64_t M, int64_t K, const uint16_t*, int64_t, int64_t rp,
+                            const uint8_t*, float* xpart, hipStream_t) {
+  ++stub::calls;
+  region(xpart, 4 * (int64_t)xa_chunks(K) * M * rp, "xa chunk partials (recompute)");
   return hipSuccess;
 }
 hipError_t launch_gemv_reduce(const float* part, int splits, int64_t M, int64_t N, const float* xpart, int xsplits,
@@ -143,5 +150,11 @@ hipError_t launch_adamw(float*, uint16_t*, const uint16_t*, float*, float*, int6
                         float, float, int, hipStream_t) {
   ++stub::calls;
   return hipSuccess;
+}
+hipError_t launch_adamw_paged(float*, uint16_t*, const uint16_t*, float*, float*, int64_t, const float*, float, float,
+                              float, float, float, int, float* staging, int64_t chunk, hipStream_t, hipStream_t) {
+  ++stub::calls;
+  region(staging, 16 * chunk, "paged optimizer staging");
+  return chunk > 0 && chunk % 256 == 0 ? hipSuccess : hipErrorInvalidValue;
 }
 }  // namespace qlora

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -302,6 +302,19 @@ def test_optimizer_validation():
     assert step(param=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert step(pbf=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
     assert step(n=0, param=None, grad=None, m=None, v=None) == B.QLORA_OK
+
+    def paged(**kw):
+        a = dict(param=FAKE, pbf=None, grad=FAKE, m=FAKE, v=FAKE, n=100, gs=None, lr=1e-4, b1=0.9, b2=0.999,
+                 eps=1e-8, wd=0.0, t=1, st=FAKE, sb=1 << 20)
+        a.update(kw)
+        return L.qlora_adamw_step_paged(a["param"], a["pbf"], a["grad"], a["m"], a["v"], a["n"], a["gs"], a["lr"],
+                                        a["b1"], a["b2"], a["eps"], a["wd"], a["t"], a["st"], a["sb"], None, None)
+    assert paged(sb=4095) == B.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert paged(st=None) == B.QLORA_ERR_INVALID_ARG
+    assert paged(st=FAKE_MIS) == B.QLORA_ERR_MISALIGNED
+    assert paged(t=0) == B.QLORA_ERR_INVALID_ARG
+    assert paged(m=None) == B.QLORA_ERR_INVALID_ARG
+    assert paged(n=0, param=None, grad=None, m=None, v=None, st=FAKE) == B.QLORA_OK
 
 
 def test_block_module_matches_oracle_layout():

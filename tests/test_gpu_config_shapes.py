@@ -108,17 +108,19 @@ def _first_diff(a, b):
     return f"{bad} (of {(a.view(torch.int16) != b.view(torch.int16)).sum().item()})"
 
 
-@pytest.mark.parametrize("wl,name", [(3, "gate"), (3, "down")])
-def test_identity_bit_exact_split_tail(B, wl, name):
+@pytest.mark.parametrize("wl,name,dq", [(3, "gate", True), (3, "down", True), (3, "gate", False),
+                                         (3, "down", False)])
+def test_identity_bit_exact_split_tail(B, wl, name, dq):
     """Partial identities of 2048 tokens on the 7B MLP weights (the forward
-    and backward products have 344 and 128 tiles of 256 x 256: split tails):
-    X = I rows gives Y = W_bf16[:, off:off+2048]^T and dY = I rows gives
-    dX = W_bf16[off:off+2048, :], both bit for bit; B = 0."""
+    and backward products have 344 and 128 tiles of 256 x 256: split tails),
+    with and without double quantisation: X = I rows gives
+    Y = W_bf16[:, off:off+2048]^T and dY = I rows gives dX =
+    W_bf16[off:off+2048, :], both bit for bit; B = 0."""
     lin = _lin(wl, name)
     N, K, Mi = lin.N, lin.K, 2048
-    _log(f"identity workload {wl} {name} N={N} K={K}")
+    _log(f"identity workload {wl} {name} N={N} K={K} dq={dq}")
     t = lin.draw("cuda", M=1, with_grad=False)
-    qw = B.qlora_nf4_quantize(t["W"])
+    qw = B.qlora_nf4_quantize(t["W"], double_quant=dq)
     Wd = B.qlora_nf4_dequantize(qw, torch.bfloat16)
     A = t["A"]
     Bz = torch.zeros(lin.r, N, dtype=torch.bfloat16, device="cuda")
@@ -258,3 +260,29 @@ def test_int8_all_levels_bit_exact_both_directions(B):
     yt = Y.t().contiguous()
     assert torch.equal(yt.view(torch.int16), Wd.view(torch.int16)), _first_diff(yt, Wd)
     assert torch.equal(dX.view(torch.int16), Wd.view(torch.int16)), _first_diff(dX, Wd)
+
+
+def test_no_double_quant_attention_shape(B):
+    """The 4096 x 4096 attention projection without double quantisation (the
+    256 x 256 kernels with fp32 block constants), sampled against the fp64
+    oracle."""
+    from bit_nf4_quantized_quantize_amd import synth
+    lin = synth.workload(2)[0]
+    _log("linear workload 2 without double quantisation")
+    t = lin.draw("cuda")
+    qw = B.qlora_nf4_quantize(t["W"], double_quant=False)
+    Y, XA = B.qlora_linear_fwd(t["X"], qw, t["A"], t["B"], lin.s)
+    dX, dA, dB = B.qlora_linear_bwd(t["dY"], t["X"], XA, qw, t["A"], t["B"], lin.s)
+    torch.cuda.synchronize()
+    ow = OracleWeight(_np(t["W"]), dq=False)
+    rng = np.random.default_rng(3)
+    M, N = lin.M, lin.N
+    ms = np.unique(np.concatenate([rng.integers(0, M, 64), [0, M - 1]]))
+    ns = np.unique(np.concatenate([rng.integers(0, N, 64), [0, N - 1]]))
+    X, A, Bm = (_np(t[k]).astype(np.float64) for k in ("X", "A", "B"))
+    _close("Y[sample]", _np(Y)[np.ix_(ms, ns)], X[ms] @ ow.rows(ns).astype(np.float64).T + lin.s * (X[ms] @ A) @ Bm[:, ns])
+    dYn = _np(t["dY"]).astype(np.float64)
+    kbs = np.array([0, 17, 63])
+    kcols = (kbs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+    dXr = dYn[ms] @ ow.cols(kbs).astype(np.float64) + lin.s * (dYn[ms] @ Bm.T) @ A[kcols].T
+    _close("dX[sample]", _np(dX)[np.ix_(ms, kcols)], dXr)
