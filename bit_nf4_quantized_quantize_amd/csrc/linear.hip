@@ -1280,8 +1280,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
 // pieces, so one load instruction covers 8 rows x 128 bytes.  The chunk goes
 // to LDS with the 16-byte pieces of row r XOR-permuted by (r / 2) % 8, so the
 // MFMA-layout reads below (16 rows x 8 bytes per half wave) hit 64 distinct
-// banks.  The chunk's block constants travel with it (one row and two
-// blocks per thread, decoded to fp32 as they are stored).  Three chunks are in
+// banks.  The chunk's block constants travel with it (one row's four
+// blocks per thread of the first four waves, decoded to fp32 as they are
+// stored).  Three chunks are in
 // flight in registers (a set's codes are reloaded as soon as they are in LDS,
 // its activations once they have been used), LDS is double buffered, and one
 // barrier per chunk orders the two.
@@ -1309,19 +1310,24 @@ constexpr int G3_RT = G3_ROWS * G3_CB / (16 * G3_WAVES);  // 16-row tiles per wa
 constexpr int G3_CHUNK16 = G3_ROWS * 2 * G3_CB;  // 16-byte pieces per chunk (2048)
 constexpr int G3_LPT = G3_CHUNK16 / G3_T;        // piece loads per thread per chunk (4)
 constexpr int G3_D = 3;                          // chunks in flight in registers
-static_assert(G3_T == 2 * G3_ROWS, "one thread per (row, block pair) for the constants");
+constexpr int G3_XA4 = 7;                        // an X A chunk's cost in code chunks, times 4
+static_assert(G3_T == 2 * G3_ROWS && G3_CB == 4, "threads 0 .. G3_ROWS - 1 take a row's 4 block constants");
 static_assert(G3_CB * kGemvMaxM * G3_ROWS * 4 <= 2 * G3_CHUNK16 * 16, "reduction buffer aliases the stages");
 
 // Native 4 x u32 vectors (not HIP's uint4 struct), so that copies between
 // global memory, registers and LDS stay plain vector loads and stores.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+template <bool DQ>
 struct G3Set {
   u32x4 c[G3_LPT];  // this thread's code pieces of one chunk
   u32x4 x[2];       // the activations of this wave's block of the chunk
-  float f[2];       // constants of this thread's row and block pair: fp32 absmax, or the
-                    // second-level scales of the E4M3 bytes in q (double quantisation)
-  uint8_t q[2];
+  // constants of this thread's row (threads < G3_ROWS): the fp32 absmax of
+  // the chunk's 4 blocks, or (double quantisation) their E4M3 bytes in q4
+  // and the second-level scales of the chunk's first and last block (4
+  // consecutive blocks lie in at most two groups of 256)
+  float f[DQ ? 2 : 4];
+  uint32_t q4;
 };
 
 // The adapter input of the few-token forward, per reduction chunk: the
@@ -1420,7 +1426,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
                                                        const uint8_t* __restrict__ keep, float* __restrict__ xpart) {
   __shared__ uint32_t tab[256 * 64];
   __shared__ u32x4 stage[2][G3_CHUNK16];  // code chunks; the partial tiles at the end
-  __shared__ float2 cst[2][G3_ROWS * G3_CB / 2];  // block constants cst[buf][row][block]
+  __shared__ float4 cst[2][G3_ROWS];  // block constants cst[buf][row][block]
   static_assert(sizeof(stage) >= XA_LDS_A && sizeof(tab) >= XA_LDS_X, "the X A tiles fit in the stages and table");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* cv = kCodeValues[dq.code_type];
@@ -1428,8 +1434,20 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   const int64_t nbk = K >> 6, half_k = K >> 1;
   const int64_t n0 = (int64_t)blockIdx.x * G3_ROWS;
   const int nchunks = (int)((nbk + G3_CB - 1) / G3_CB);
-  const int c_lo = (int)((int64_t)blockIdx.y * nchunks / S);
-  const int c_hi = (int)((int64_t)(blockIdx.y + 1) * nchunks / S);  // c_hi > c_lo (S <= nchunks)
+  // the reduction splits of this row tile: the splits whose workgroup also
+  // computes an X A chunk (the first nxc workgroups, one chunk each when the
+  // grid has that many) are G3_XA4 / 4 chunks shorter, the others longer,
+  // so that every workgroup of the tile streams for about as long
+  const int64_t nxc = (K + XA_CHUNK - 1) / XA_CHUNK, T = gridDim.x;
+  const int nx = (int64_t)blockIdx.x < nxc ? (int)min((int64_t)S, (nxc - blockIdx.x + T - 1) / T) : 0;
+  int x4 = T * S >= nxc ? G3_XA4 : 0;
+  if (4 * (int64_t)nchunks - 4 * (int64_t)S < (int64_t)x4 * (S - nx)) x4 = 0;  // every split keeps a chunk
+  auto split_lo = [&](int y) -> int {
+    return (int)((4 * (int64_t)y * nchunks + (int64_t)x4 * ((int64_t)y * nx - (int64_t)S * (y < nx ? y : nx))) /
+                 (4 * (int64_t)S));
+  };
+  const int c_lo = split_lo(blockIdx.y);
+  const int c_hi = split_lo(blockIdx.y + 1);  // c_hi > c_lo, split_lo(S) = nchunks
   const float mu = DQ ? *dq.offset : 0.0f;
 
   // code pieces: load u of thread tid fills LDS slot P = u * G3_T + tid, i.e.
@@ -1444,10 +1462,13 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
     gblk[u] = piece >> 1;
     gsrc[u] = codes + row * half_k + 16 * (piece & 1);
   }
-  // constants: thread -> row tid / 2, blocks 2 (tid % 2) + {0, 1} of the chunk
-  const bool crow_ok = n0 + (tid >> 1) < N;
-  const int64_t cbase = (crow_ok ? n0 + (tid >> 1) : N - 1) * nbk;
-  const int cpair = 2 * (tid & 1);
+  // constants: threads 0..255 (waves 0..3) take row tid, the chunk's 4
+  // blocks; with nbk % 4 == 0 those are one aligned 4-byte word (E4M3) or
+  // 16 bytes (fp32) under one second-level scale
+  const bool crow_ok = n0 + tid < N;
+  const int64_t cbase = (crow_ok ? n0 + tid : N - 1) * nbk;
+  const bool cwhole = (nbk & 3) == 0 && ((uintptr_t)(DQ ? (const void*)dq.absmax_q : (const void*)dq.absmax) &
+                                            (DQ ? 3 : 15)) == 0;  // uniform
   // activations: lane (t, g) of wave w, block w % 4 of the chunk
   const int t = lane & 15, g = lane >> 4, q = wave & 3, hrow = 128 * (wave >> 2);
   const uint16_t* xrow = X + (int64_t)(t < M ? t : M - 1) * K + 16 * g;
@@ -1462,23 +1483,31 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   // loads of chunk kc into register set d: the code pieces and constants,
   // then (separately, once the set's activations have been used) the
   // activations
-  auto issue_codes = [&](int kc, G3Set& d) {
+  auto issue_codes = [&](int kc, G3Set<DQ>& d) {
 #pragma unroll
     for (int u = 0; u < G3_LPT; ++u) d.c[u] = *reinterpret_cast<const u32x4*>(gsrc[u] + blk(kc, gblk[u]) * 32);
+    if (tid < G3_ROWS) {
+      if constexpr (DQ) {
+        if (cwhole) {
+          d.q4 = *reinterpret_cast<const uint32_t*>(dq.absmax_q + cbase + blk(kc, 0));
+        } else {
+          d.q4 = 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t fb = cbase + blk(kc, cpair + j);
-      if (DQ) {
-        d.q[j] = dq.absmax_q[fb];
-        d.f[j] = dq.scale2[fb >> 8];
+          for (int j = 0; j < 4; ++j) d.q4 |= (uint32_t)dq.absmax_q[cbase + blk(kc, j)] << (8 * j);
+        }
+        d.f[0] = dq.scale2[(cbase + blk(kc, 0)) >> 8];
+        d.f[1] = dq.scale2[(cbase + blk(kc, 3)) >> 8];
+      } else if (cwhole) {
+        const float4 a = *reinterpret_cast<const float4*>(dq.absmax + cbase + blk(kc, 0));
+        d.f[0] = a.x; d.f[1] = a.y; d.f[2] = a.z; d.f[3] = a.w;
       } else {
-        d.q[j] = 0;
-        d.f[j] = dq.absmax[fb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d.f[j] = dq.absmax[cbase + blk(kc, j)];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto issue_x = [&](int kc, G3Set& d) {
+  auto issue_x = [&](int kc, G3Set<DQ>& d) {
     const uint16_t* xp = xrow + blk(kc, q) * 64;
     d.x[0] = *reinterpret_cast<const u32x4*>(xp);
     d.x[1] = *reinterpret_cast<const u32x4*>(xp + 8);
@@ -1494,19 +1523,25 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   // buffer kc & 1, the set refilled with the codes of chunk kc + G3_D,
   // barrier, then this wave's block of the chunk for its 128 rows, and the
   // set's activations refilled last
-  auto step = [&](int kc, G3Set& d) {
+  auto step = [&](int kc, G3Set<DQ>& d) {
     const int sbuf = kc & 1;
 #pragma unroll
     for (int u = 0; u < G3_LPT; ++u) stage[sbuf][u * G3_T + tid] = d.c[u];
-    {
-      float c[2];
+    if (tid < G3_ROWS) {
+      float c[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool ok = crow_ok && (int64_t)G3_CB * kc + cpair + j < nbk;
-        const float v = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(d.q[j]), d.f[j]), mu) : d.f[j];
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = crow_ok && (int64_t)G3_CB * kc + j < nbk;
+        float v;
+        if constexpr (DQ) {
+          const bool first = ((cbase + blk(kc, j)) >> 8) == ((cbase + blk(kc, 0)) >> 8);
+          v = __fadd_rn(__fmul_rn(e4m3_decode((d.q4 >> (8 * j)) & 0xFFu), first ? d.f[0] : d.f[1]), mu);
+        } else {
+          v = d.f[j];
+        }
         c[j] = ok ? v : 0.0f;
       }
-      cst[sbuf][tid] = make_float2(c[0], c[1]);
+      cst[sbuf][tid] = make_float4(c[0], c[1], c[2], c[3]);
     }
     issue_codes(kc + G3_D, d);
     __syncthreads();
@@ -1542,7 +1577,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
     issue_x(kc + G3_D, d);
   };
 
-  G3Set A, B, C;  // G3_D register sets in rotation
+  G3Set<DQ> A, B, C;  // G3_D register sets in rotation
   issue_codes(c_lo, A);
   issue_x(c_lo, A);
   issue_codes(c_lo + 1, B);
@@ -1554,7 +1589,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   // one reduction chunk of X A (more when the grid is smaller than the
   // chunk count), in the space of the code stages and the table
   {
-    const int64_t nxc = (K + XA_CHUNK - 1) / XA_CHUNK, wid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t wid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     if (wid < nxc) {
       for (int64_t c = wid; c < nxc; c += (int64_t)gridDim.x * gridDim.y)
         xa_chunk_partial(X, M, K, lora_a, rank, rank_pad, keep, c, xpart, reinterpret_cast<__bf16*>(stage),
