@@ -147,6 +147,11 @@ int quantize_parts(int64_t numel) {
   const int64_t units = (numel + kQuantGridUnit - 1) / kQuantGridUnit;
   return (int)(units < 1 ? 1 : (units > kQuantMaxParts ? kQuantMaxParts : units));
 }
+int quantize_parts_batched(int64_t numel) {
+  const int64_t unit = kQuantGridUnit * kQuantBatchUnits;
+  const int64_t units = (numel + unit - 1) / unit;
+  return (int)(units < 1 ? 1 : (units > kQuantMaxParts ? kQuantMaxParts : units));
+}
 
 // ------------------------------------------------ main-GEMM tile choice
 // The 256 x 256 kernel runs one workgroup per CU.  Its tiles go in rounds of

@@ -68,9 +68,15 @@ bool quant_tables_ok(int code_type);
 // quantisation then divides the total by nb for the mean
 // and encodes the constants.
 int quantize_parts(int64_t numel);
+// A tensor's share of a batched launch: workgroups of at least
+// kQuantBatchUnits grid units each (the batch fills the chip by itself, so
+// every workgroup keeps a longer stream in flight); never more workgroups
+// than quantize_parts, so the workspace of a single call holds its partials.
+int quantize_parts_batched(int64_t numel);
 constexpr int kMeanDigits = 10;  // 32-bit digits of the exact fixed-point sum
 constexpr int kQuantMaxParts = 256;          // quantisation workgroups (and exact-sum partials) at most
 constexpr int64_t kQuantGridUnit = 16384;    // weights per workgroup when sizing that grid
+constexpr int64_t kQuantBatchUnits = 16;     // grid units per workgroup at least, in a batched launch
 
 // Tiling constants the kernels and the host planning share.
 constexpr int kCUs = 256;        // MI355X compute units

@@ -531,10 +531,13 @@ __global__ __launch_bounds__(Q8_THREADS) void int8_quantize_kernel(const void* _
 
 // ------------------------------------------------ batched quantisation
 // Up to kQuantBatch tensors per launch: tensor i takes workgroups
-// [begin[i], begin[i + 1]) of the grid, as many as its own launch would
-// have, so every tensor is coded exactly as by its own call.  The tensor of
-// a workgroup is found with an unrolled scan over constant indices (no
-// dynamic indexing of the kernel argument, which would go through scratch).
+// [begin[i], begin[i + 1]) of the grid, quantize_parts_batched of them
+// (fewer than its own launch for small tensors: the batch fills the chip,
+// so each workgroup streams longer).  Codes and c2 are per element and the
+// exact-sum partials add to the same total in any split, so every tensor is
+// coded exactly as by its own call.  The tensor of a workgroup is found
+// with an unrolled scan over constant indices (no dynamic indexing of the
+// kernel argument, which would go through scratch).
 struct QuantBatchArgs {
   const void* w[kQuantBatch];
   int64_t numel[kQuantBatch];
@@ -875,7 +878,7 @@ hipError_t launch_quantize_batched(const QuantJob* jobs, int count, bool w_bf16,
       const QuantJob& jb = jobs[j0 + i];
       qa.w[i] = jb.w; qa.numel[i] = jb.numel; qa.codes[i] = jb.codes; qa.c2[i] = jb.c2;
       qa.partials[i] = dq ? jb.partials : nullptr;
-      qa.parts[i] = quantize_parts(jb.numel);
+      qa.parts[i] = quantize_parts_batched(jb.numel);
       qa.begin[i] = total;
       total += qa.parts[i];
     }
