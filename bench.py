@@ -588,9 +588,12 @@ def _dominant(per, layers, small):
 def achievable_bandwidth(dev, mib=1024, reps=5):
     """What this device streams, as the roofline's "achievable" companion to
     the datasheet figure: a plain device copy (torch copy_, read + write
-    bytes) and a plain read (torch.sum over the same buffer) of `mib` MiB,
-    median of `reps` after a warm-up."""
+    bytes) and a plain read (the library's streaming-read probe, 16-byte
+    loads, four in flight per thread) of `mib` MiB, median of `reps` after a
+    warm-up."""
     import torch
+
+    from bit_nf4_quantized_quantize_amd import binding as B
 
     n = mib << 18
     src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -608,14 +611,15 @@ def achievable_bandwidth(dev, mib=1024, reps=5):
         ts = sorted(ts[1:])
         return ts[len(ts) // 2]
 
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
     copy_ms = med(lambda: dst.copy_(src))
-    read_ms = med(lambda: src.sum())
+    read_ms = med(lambda: B.qlora_probe_read(src, sink))
     del src, dst
     torch.cuda.empty_cache()
     nbytes = 4 * n
     return {"copy_GBps": 2 * nbytes / copy_ms / 1e6, "read_GBps": nbytes / read_ms / 1e6, "buffer_MiB": mib,
-            "how": "torch copy_ (read + write bytes) and torch.sum (read bytes) of one fp32 buffer, median of "
-                   f"{reps}"}
+            "how": "torch copy_ (read + write bytes) and the library's streaming-read probe qlora_probe_read "
+                   f"(read bytes) of one fp32 buffer, median of {reps}"}
 
 
 class Scrub:

@@ -52,6 +52,7 @@ EXPORTED = (
     "qlora_clip_scale_workspace", "qlora_clip_scale", "qlora_adamw_step",
     "qlora_profile_events", "qlora_linear_fwd_noalloc", "qlora_dropout_mask",
     "qlora_nf4_quantize_batched_workspace", "qlora_nf4_quantize_batched", "qlora_adamw_step_paged",
+    "qlora_probe_read",
 )
 QLORA_KERNEL = {"quantize": 0, "dequantize": 1, "fwd_main": 2, "bwd_dx": 3}
 
@@ -121,6 +122,7 @@ def lib():
         "qlora_nf4_quantize_batched": (_i32, [ctypes.POINTER(_vp), _i32, _pdesc, _i32, _vp, _i64, _vp]),
         "qlora_adamw_step_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _f32, _f32, _f32, _f32, _f32, _i32,
                                           _vp, _i64, _vp, _vp]),
+        "qlora_probe_read": (_i32, [_vp, _i64, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -202,6 +204,15 @@ def qlora_profile_events(kernel, start=None, stop=None):
     for the calling thread."""
     kid = QLORA_KERNEL[kernel]
     _check(lib().qlora_profile_events(kid, start, stop), "qlora_profile_events")
+
+
+def qlora_probe_read(buf, out, stream=None):
+    """Measurement probe: one streaming read of the device tensor `buf`
+    (contiguous, 16-byte aligned, a multiple of 16 bytes); `out` is a device
+    tensor of at least 4 bytes the kernel may write."""
+    _need_cuda(buf, out)
+    _check(lib().qlora_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), _stream(stream)),
+           "qlora_probe_read")
 
 
 # ----------------------------------------------------------- quantised weight

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlora_nf4.so")
 
-SOURCES = ["quantize.hip", "linear.hip", "optim.hip", "dropout.hip", "noalloc.hip", "host.cpp", "abi.cpp"]
+SOURCES = ["quantize.hip", "linear.hip", "optim.hip", "dropout.hip", "noalloc.hip", "probe.hip", "host.cpp", "abi.cpp"]
 HEADERS = ["device.h", "launch.h", "codebooks.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -32,6 +32,24 @@ typedef enum {
 
 int qlora_profile_events(int32_t kernel_id, void* start_event, void* stop_event);
 
+/*
+ * qlora_probe_read - measurement probe, not part of the computation: reads
+ * `bytes` bytes of the device buffer `src` once, with 16-byte loads, four in
+ * flight per thread, consecutive lanes on consecutive pieces (at most 4096
+ * workgroups of 512 threads, grid-stride), so that a benchmark can report
+ * what this device streams next to the datasheet HBM figure.
+ *
+ *   src      device pointer, 16-byte aligned; not modified.
+ *   bytes    a multiple of 16, >= 0 (0 enqueues nothing).
+ *   out      device pointer to 4 writable bytes; written only to keep the
+ *            loads alive (its contents afterwards are unspecified).
+ *   stream   hipStream_t as void* (NULL: the default stream).
+ * Returns QLORA_OK, QLORA_ERR_INVALID_ARG (misaligned src, bytes not a
+ * multiple of 16, NULL pointers) before anything is enqueued, or
+ * QLORA_ERR_HIP if the launch fails.
+ */
+int qlora_probe_read(const void* src, int64_t bytes, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -325,3 +325,14 @@ def test_block_module_matches_oracle_layout():
     assert block.LINEARS == oblock.LINEARS
     assert block.linear_shapes(4096, 11008) == oblock.shapes(4096, 11008)
     assert block.EPS == oblock.EPS
+
+
+def test_probe_read_validates_on_host():
+    L = B.lib()
+    bad = B.QLORA_ERR_INVALID_ARG
+    assert L.qlora_probe_read(FAKE, 15, FAKE, None) == bad          # not a multiple of 16 bytes
+    assert L.qlora_probe_read(FAKE_MIS, 16, FAKE, None) == bad      # misaligned source
+    assert L.qlora_probe_read(None, 16, FAKE, None) == bad
+    assert L.qlora_probe_read(FAKE, 16, None, None) == bad
+    assert L.qlora_probe_read(FAKE, -16, FAKE, None) == bad
+    assert L.qlora_probe_read(None, 0, None, None) == B.QLORA_OK     # nothing to read: nothing enqueued
