@@ -17,8 +17,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two of them packed (lo in bits 0..15): one v_cvt_pk_bf16_f32 on both
+// operands, where two scalar conversions would need a shift and an or more.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
@@ -217,25 +221,6 @@ __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
 // Row of accumulator register j of a 32x32 tile for a lane (column: lane % 32).
 __device__ __forceinline__ int acc_row32(int j, int lane) {
   return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-}
-
-// 4 x 4 transpose inside each quad of lanes.  On entry lane c = lane % 4
-// holds column c of rows 0..3 in v[0..3]; on exit it holds row c, columns
-// 0..3.  Two DPP exchange stages: the off-diagonal 2 x 2 blocks between lanes
-// c and c ^ 2, then the off-diagonal elements of each 2 x 2 block between
-// lanes c and c ^ 1.
-template <int CTRL>
-__device__ __forceinline__ float quad_xchg(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ void quad_transpose4(float (&v)[4], int lane) {
-  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
-  float x = quad_xchg<0x4E>(b1 ? v[0] : v[2]);  // quad_perm [2,3,0,1]
-  float y = quad_xchg<0x4E>(b1 ? v[1] : v[3]);
-  if (b1) { v[0] = x; v[1] = y; } else { v[2] = x; v[3] = y; }
-  x = quad_xchg<0xB1>(b0 ? v[0] : v[1]);        // quad_perm [1,0,3,2]
-  y = quad_xchg<0xB1>(b0 ? v[2] : v[3]);
-  if (b0) { v[0] = x; v[2] = y; } else { v[1] = x; v[3] = y; }
 }
 
 }  // namespace qlora

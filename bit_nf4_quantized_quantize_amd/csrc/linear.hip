@@ -131,6 +131,22 @@ __device__ __forceinline__ void mask_acc32(floatx16& acc, int lane, int64_t r0, 
   }
 }
 
+// The same for a block accumulated transposed (store_acc32t's layout: lane
+// l holds row r0 + (l & 31), element 4 g + i column c0 + 8 g + 4 (l >> 5) + i,
+// so each group's 4 columns share one mask byte).
+__device__ __forceinline__ void mask_acc32t(floatx16& acc, int lane, int64_t r0, int64_t c0, int64_t M, int64_t ncols,
+                                            const uint8_t* __restrict__ keep, float scale) {
+  const int64_t row = r0 + (lane & 31) < M ? r0 + (lane & 31) : M - 1;
+  const int64_t pitch = ncols >> 3;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t col = c0 + 8 * g + 4 * (lane >> 5);
+    const uint32_t b = keep[row * pitch + ((col < ncols ? col : 0) >> 3)] >> (col & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4 * g + i] = ((b >> i) & 1u) ? acc[4 * g + i] * scale : 0.0f;
+  }
+}
+
 template <int BM, int BN, bool BWD>
 struct MainCfg {
   static constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
@@ -338,28 +354,36 @@ __global__ __launch_bounds__(NT, 1) void main_gemm_kernel(const MainArgs a) {
     }
 }
 
-// Stores one 32 x 32 fp32 accumulator tile (MFMA 32x32 layout) at rows r0..,
-// columns c0.. of `out` (bf16, row pitch ncols; rows >= M dropped), or of an
-// fp32 partial tile `pt` (row pitch pitch_pt) when pt is given.  Groups of 4
-// accumulator rows are transposed inside each quad of lanes, so every lane
-// writes 4 consecutive columns of one row (8 or 16 bytes) instead of 4
-// single elements.  Needs ncols % 4 == 0 and c0 + 32 <= ncols.
-__device__ __forceinline__ void store_acc32(const floatx16& acc, int lane, int64_t r0, int64_t c0, int64_t M,
-                                            int64_t ncols, uint16_t* __restrict__ out, float* __restrict__ pt,
-                                            int pitch_pt) {
-  const int col = 4 * ((lane & 31) >> 2);
+// Stores a 32 x 32 output block accumulated transposed, i.e. with the weight
+// fragment as the MFMA's first operand and the activation fragment as its
+// second: lane l then holds output row r0 + (l & 31), columns
+// c0 + 8 g + 4 (l >> 5) + i of group g (i = 0..3), so each group is one
+// 8-byte bf16 store with no exchange between lanes (rows >= M dropped).  The
+// block's columns are inside the output (callers check the block's first
+// column; widths are multiples of 32).
+__device__ __forceinline__ void store_acc32t(const floatx16& acc, int lane, int64_t r0, int64_t c0, int64_t M,
+                                             int64_t ncols, uint16_t* __restrict__ out) {
+  const int64_t r = r0 + (lane & 31);
+  if (r < M) {
+    uint16_t* o = out + r * ncols + c0 + 4 * (lane >> 5);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-    quad_transpose4(v, lane);
-    const int rr = 8 * g + 4 * (lane >> 5) + (lane & 3);
-    if (pt) {
-      *reinterpret_cast<float4*>(pt + (int64_t)(r0 + rr) * pitch_pt + c0 + col) = make_float4(v[0], v[1], v[2], v[3]);
-    } else if (r0 + rr < M) {
-      *reinterpret_cast<uint2*>(out + (r0 + rr) * ncols + c0 + col) =
-          make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-    }
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint2*>(o + 8 * g) =
+          make_uint2(pack_bf2(acc[4 * g], acc[4 * g + 1]), pack_bf2(acc[4 * g + 2], acc[4 * g + 3]));
   }
+  // one block at a time: keeps the compiler from reading every accumulator
+  // out first (which spills)
+  __builtin_amdgcn_sched_barrier(0);
+}
+// The same block into an fp32 partial tile (row pitch `pitch`): one 16-byte
+// store per group.
+__device__ __forceinline__ void store_acc32t_f32(const floatx16& acc, int lane, int r0, int c0, float* __restrict__ pt,
+                                                 int pitch) {
+  float* o = pt + (int64_t)(r0 + (lane & 31)) * pitch + c0 + 4 * (lane >> 5);
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<float4*>(o + 8 * g) = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ================================== main GEMM, 256 x 256, 4 waves, v5
@@ -528,7 +552,7 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
 #pragma unroll
       for (int ij = 0; ij < 16; ++ij) {
         const int i = ij >> 2, j = ij & 3;
-        acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
+        acc[i][j] = mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
         if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
         item(kk * 16 + ij);
         __builtin_amdgcn_sched_barrier(0);
@@ -592,23 +616,27 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[0][i], fb[0][j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fb[0][j], fa[0][i], acc[i][j]);
     }
     __syncthreads();
   }
 
   // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
-  float* pt = unit >= 0 ? a.part + (int64_t)unit * (BM * BN) : nullptr;
+  __builtin_amdgcn_sched_barrier(0);
+  if (unit >= 0) {
+    float* pt = a.part + (int64_t)unit * (BM * BN);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (pt) {
-        store_acc32(acc[i][j], lane, wm * 128 + 32 * i, wn * 128 + 32 * j, BM, BN, nullptr, pt, BN);
-      } else if (c0 + wn * 128 + 32 * j < a.ncols) {
-        store_acc32(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 128 + 32 * j, a.M, a.ncols, a.out, nullptr, 0);
-      }
-    }
+      for (int j = 0; j < 4; ++j) store_acc32t_f32(acc[i][j], lane, wm * 128 + 32 * i, wn * 128 + 32 * j, pt, BN);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + wn * 128 + 32 * j < a.ncols)
+          store_acc32t(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 128 + 32 * j, a.M, a.ncols, a.out);
+  }
 }
 
 // The backward kernel's dequantised weight tile [64 n][256 k] (row pitch
@@ -802,7 +830,7 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
 #pragma unroll
       for (int ij = 0; ij < 8; ++ij) {
         const int i = ij >> 1, j = ij & 1;
-        acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
+        acc[i][j] = mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
         if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
         const int sl = kk * 8 + ij;
         if (sl == 0) {
@@ -846,7 +874,7 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[0][i], fb[0][j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fb[0][j], fa[0][i], acc[i][j]);
     }
     __syncthreads();
   }
@@ -856,8 +884,8 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        mask_acc32(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 64 + 32 * j, a.M, a.ncols, a.keep,
-                   a.keep_scale);
+        mask_acc32t(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 64 + 32 * j, a.M, a.ncols, a.keep,
+                    a.keep_scale);
   }
 
   // ---- prologue: stage 0 filled; X(ks+1) and codes(ks+1) in flight
@@ -888,17 +916,21 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   }
 
   // ---- epilogue: bf16 output, or the fp32 partial tile of a split unit
-  float* pt = unit >= 0 ? a.part + (int64_t)unit * (BM * BN) : nullptr;
+  __builtin_amdgcn_sched_barrier(0);
+  if (unit >= 0) {
+    float* pt = a.part + (int64_t)unit * (BM * BN);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (pt) {
-        store_acc32(acc[i][j], lane, wm * 128 + 32 * i, wn * 64 + 32 * j, BM, BN, nullptr, pt, BN);
-      } else if (c0 + wn * 64 + 32 * j < a.ncols) {
-        store_acc32(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 64 + 32 * j, a.M, a.ncols, a.out, nullptr, 0);
-      }
-    }
+      for (int j = 0; j < 2; ++j) store_acc32t_f32(acc[i][j], lane, wm * 128 + 32 * i, wn * 64 + 32 * j, pt, BN);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (c0 + wn * 64 + 32 * j < a.ncols)
+          store_acc32t(acc[i][j], lane, m0 + wm * 128 + 32 * i, c0 + wn * 64 + 32 * j, a.M, a.ncols, a.out);
+  }
 }
 
 // Adds the `split` fp32 partial tiles of each split tile (fixed order) and
