@@ -504,7 +504,11 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     WordState ws[8];
     load_codes(k2, cl, ql, fl);
     read_frags(cur, 0, 0, BWD, BWD ? PRC : PK);
-    // items interleaved with the 64 MFMAs, in order
+    // items interleaved with the 64 MFMAs, in order: 0-8 build the block's
+    // lookup table, 9-48 expand the 8 code words (5 stages each, the last one
+    // storing the word's 8 bf16 weights), 49-56 store the activation chunk of
+    // step kt + 1 and load that of step kt + 2.  The three slots that issue
+    // fragment reads take no item: a heavy item there delays the next MFMA.
     auto item = [&](int it) {
       if (it == 0) {
         const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
@@ -514,8 +518,8 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
         pw[it] = pack_bf2(cv[2 * it] * sc, cv[2 * it + 1] * sc);
       } else if (it == 8) {
         lut = make_lut(pw);
-      } else if (it < 9 + 32) {
-        const int w = (it - 9) >> 2, stg = (it - 9) & 3;
+      } else if (it < 9 + 40) {
+        const int w = (it - 9) / 5, stg = (it - 9) % 5;
         WordState& st = ws[w];
         const uint32_t wd = words[w];
         if (stg == 0) {
@@ -530,19 +534,22 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
         } else if (stg == 2) {
           st.loO = perm_b32(perm_b32(lut.lo[3], lut.lo[2], st.o7), perm_b32(lut.lo[1], lut.lo[0], st.o7), st.mo);
           st.hiO = perm_b32(perm_b32(lut.hi[3], lut.hi[2], st.o7), perm_b32(lut.hi[1], lut.hi[0], st.o7), st.mo);
-        } else {
+        } else if (stg == 3) {
           const uint32_t e01 = perm_b32(st.hiE, st.loE, 0x05010400u);
           const uint32_t o01 = perm_b32(st.hiO, st.loO, 0x05010400u);
           const uint32_t e23 = perm_b32(st.hiE, st.loE, 0x07030602u);
           const uint32_t o23 = perm_b32(st.hiO, st.loO, 0x07030602u);
-          sts16(wdst(nxt, w), make_uint4(perm_b32(o01, e01, 0x05040100u), perm_b32(o01, e01, 0x07060302u),
-                                         perm_b32(o23, e23, 0x05040100u), perm_b32(o23, e23, 0x07060302u)));
+          st.loE = e01;  // the interleaved pairs, in the fields they came from
+          st.hiE = o01;
+          st.loO = e23;
+          st.hiO = o23;
+        } else {
+          sts16(wdst(nxt, w), make_uint4(perm_b32(st.hiE, st.loE, 0x05040100u), perm_b32(st.hiE, st.loE, 0x07060302u),
+                                         perm_b32(st.hiO, st.loO, 0x05040100u), perm_b32(st.hiO, st.loO, 0x07060302u)));
         }
-      } else if (it < 41 + XCH) {
-        const int i = it - 41;
+      } else if (it < 49 + XCH) {
+        const int i = it - 49;
         sts16(x_dst(i, nxt), xr[i]);
-      } else if (it < 41 + 2 * XCH) {
-        const int i = it - 41 - XCH;
         xr[i] = ldg16(x_src(i, k2));
       }
     };
@@ -554,7 +561,10 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
         const int i = ij >> 2, j = ij & 3;
         acc[i][j] = mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
         if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
-        item(kk * 16 + ij);
+        {
+          const int sl = kk * 16 + ij;  // slots 0, 16, 32 issue the fragment reads and take no item
+          if (sl != 0 && sl != 16 && sl != 32) item(sl - 1 - (sl > 16) - (sl > 32));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
