@@ -484,13 +484,22 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
   };
 
   bf16x8 fa[2][4], fb[2][4];
+  // The reads are issued in the order the sub-step's MFMAs consume them
+  // (a0, b0..b3, a1..a3; scheduling barriers keep it), so the first MFMA of
+  // a k-step waits for two reads instead of most of them.
   auto read_frags = [&](int buf, int kk, int slot, bool b_rc, int pitch_b) {
+    fa[slot][0] = frag_kc(sA[buf], PK, wm * 128, kk, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
       fb[slot][j] = b_rc ? frag_rc(sB[buf], pitch_b, wn * 128 + 32 * j, kk, lane)
                          : frag_kc(sB[buf], pitch_b, wn * 128 + 32 * j, kk, lane);
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
+    }
   };
 
   // ---- one k-step: multiply stage `cur` while producing stage `nxt`
@@ -504,6 +513,7 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     WordState ws[8];
     load_codes(k2, cl, ql, fl);
     read_frags(cur, 0, 0, BWD, BWD ? PRC : PK);
+    __builtin_amdgcn_sched_barrier(0);
     // items interleaved with the 64 MFMAs, in order: 0-8 build the block's
     // lookup table, 9-48 expand the 8 code words (5 stages each, the last one
     // storing the word's 8 bf16 weights), 49-56 store the activation chunk of
@@ -560,7 +570,10 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
       for (int ij = 0; ij < 16; ++ij) {
         const int i = ij >> 2, j = ij & 3;
         acc[i][j] = mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
-        if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
+        if (ij == 0 && kk < 3) {  // after the sub-step's first MFMA, whose reads come first
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
+        }
         {
           const int sl = kk * 16 + ij;  // slots 0, 16, 32 issue the fragment reads and take no item
           if (sl != 0 && sl != 16 && sl != 32) item(sl - 1 - (sl > 16) - (sl > 32));
@@ -770,14 +783,21 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   };
 
   bf16x8 fa[2][4], fb[2][2];
+  // reads in the order the MFMAs consume them (a0, b0, b1, a1..a3)
   auto read_frags = [&](int buf, int kk, int slot, bool b_rc, int pitch_b) {
+    fa[slot][0] = frag_kc(sA[buf], PK, wm * 128, kk, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
       fb[slot][j] = b_rc ? (BWD ? frag_rc_bwd(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane)
                                 : frag_rc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane))
                          : frag_kc(sB[buf], pitch_b, wn * 64 + 32 * j, kk, lane);
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      fa[slot][i] = frag_kc(sA[buf], PK, wm * 128 + 32 * i, kk, lane);
+    }
   };
 
   // ---- one k-step: multiply stage `cur` while producing stage `nxt`
@@ -791,6 +811,7 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
     WordState ws[4];
     load_codes(k2, cl, ql, fl);
     read_frags(cur, 0, 0, BWD, BWD ? PRC : PK);
+    __builtin_amdgcn_sched_barrier(0);
     // items 0..32 interleaved with the 32 MFMAs, in order (slot 0 takes
     // items 0 and 1, slot s item s + 1)
     auto item = [&](int it) {
@@ -841,7 +862,10 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
       for (int ij = 0; ij < 8; ++ij) {
         const int i = ij >> 1, j = ij & 1;
         acc[i][j] = mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
-        if (ij == 0 && kk < 3) read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
+        if (ij == 0 && kk < 3) {  // after the sub-step's first MFMA, whose reads come first
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(cur, 16 * (kk + 1), slot ^ 1, BWD, BWD ? PRC : PK);
+        }
         const int sl = kk * 8 + ij;
         if (sl == 0) {
           item(0);
