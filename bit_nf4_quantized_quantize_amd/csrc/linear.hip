@@ -698,8 +698,9 @@ __device__ __forceinline__ bf16x8 frag_rc_bwd(const __bf16* s, int pitch, int r0
 constexpr int V6_T = 512;
 
 
-template <bool BWD, bool DQ>
+template <bool BWD, bool DQ, bool I8 = false>
 __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
+  constexpr int CW = I8 ? 2 : 1;  // 16-byte code pieces per thread and step
   constexpr int BM = 256, BN = 256;
   constexpr int PRC = BN + kRcPad;
   constexpr int SA = BM * PK;
@@ -728,9 +729,9 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   const int nk = ke;
   const int64_t kblocks = a.Kw >> 6;
   const float mu = DQ ? *a.dq.offset : 0.0f;
-  const float* cv = kCodeValues[a.dq.code_type];
+  const float* cv = kCodeValues[I8 ? 0 : a.dq.code_type];
 
-  // dequantisation task: half (t_half) of one NF4 block per thread; the 16
+  // dequantisation task: half (t_half) of one block per thread; the 16
   // lanes of a store group take 16 different rows (fwd) or 4 rows x 4 blocks
   // (bwd)
   const int tq = tid & 255, t_half = tid >> 8;
@@ -749,7 +750,7 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   uint4 xr[XCH];
-  uint4 cwA, cwB;
+  uint4 cwA[CW], cwB[CW];
   uint8_t qbA = 0, qbB = 0;
   float sfA = 0.0f, sfB = 0.0f;
 
@@ -762,10 +763,16 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
     const int id = tid + V6_T * i, row = id >> 3, ch = id & 7;
     return &sA[buf][row * PK + ch * 8];
   };
-  auto load_codes = [&](int kt, uint4& c, uint8_t& q, float& f) {
+  auto load_codes = [&](int kt, uint4* c, uint8_t& q, float& f) {
     const int64_t n = BWD ? (int64_t)kt * 64 + t_row : t_n;
     const int64_t k = BWD ? t_k : (int64_t)kt * 64;
-    c = *reinterpret_cast<const uint4*>(a.codes + ((n * a.Kw + k) >> 1) + 16 * t_half);
+    if (I8) {  // one byte per weight
+      const uint8_t* src = a.codes + n * a.Kw + k + 32 * t_half;
+      c[0] = *reinterpret_cast<const uint4*>(src);
+      c[CW - 1] = *reinterpret_cast<const uint4*>(src + 16);
+    } else {
+      c[0] = *reinterpret_cast<const uint4*>(a.codes + ((n * a.Kw + k) >> 1) + 16 * t_half);
+    }
     const int64_t blk = n * kblocks + (k >> 6);
     if (DQ) {
       q = a.dq.absmax_q[blk];
@@ -801,10 +808,12 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   };
 
   // ---- one k-step: multiply stage `cur` while producing stage `nxt`
-  auto step = [&](int kt, const int cur, const uint4& cu, uint8_t qu, float fu, uint4& cl, uint8_t& ql, float& fl) {
+  auto step = [&](int kt, const int cur, const uint4* cu, uint8_t qu, float fu, uint4* cl, uint8_t& ql, float& fl) {
     const int nxt = cur ^ 1;
     const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;  // past the end: a harmless repeat
-    const uint32_t words[4] = {cu.x, cu.y, cu.z, cu.w};
+    // 4-bit codes: 4 words of 8 codes; Int8: 8 words of 4 codes
+    const uint32_t words[8] = {cu[0].x,      cu[0].y,      cu[0].z,      cu[0].w,
+                               cu[CW - 1].x, cu[CW - 1].y, cu[CW - 1].z, cu[CW - 1].w};
     float sc = 0.0f;
     uint32_t pw[8];
     BlockLUT lut;
@@ -813,9 +822,21 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
     read_frags(cur, 0, 0, BWD, BWD ? PRC : PK);
     __builtin_amdgcn_sched_barrier(0);
     // items 0..32 interleaved with the 32 MFMAs, in order (slot 0 takes
-    // items 0 and 1, slot s item s + 1)
+    // items 0 and 1, slot s item s + 1).  Int8: item 0 forms the block's
+    // constant, items 9..24 expand 2 code bytes each (the 8 weights of
+    // 16-byte chunk w in items 9 + 4w .. 12 + 4w, the last one storing them)
     auto item = [&](int it) {
-      if (it == 0) {
+      if (I8 && it < 9) {
+        if (it == 0) {
+          const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
+          sc = t_ok ? bs : 0.0f;
+        }
+      } else if (I8 && it < 9 + 16) {
+        const int w = (it - 9) >> 2, stg = (it - 9) & 3;
+        const uint32_t wd = words[2 * w + (stg >> 1)] >> (16 * (stg & 1));
+        pw[stg] = pack_bf2(i8_value(wd & 0xFFu) * sc, i8_value((wd >> 8) & 0xFFu) * sc);
+        if (stg == 3) sts16(wdst(nxt, w), make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      } else if (it == 0) {
         const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qu), fu), mu) : fu;
         sc = t_ok ? bs : 0.0f;
         pw[0] = pack_bf2(cv[0] * sc, cv[1] * sc);
@@ -930,13 +951,30 @@ __global__ __launch_bounds__(V6_T, 1) void main_v6_kernel(const MainArgs a) {
   for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
   {
     const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
-    const BlockLUT lut = lut_for(t_ok ? bs : 0.0f, cv);
-    const uint32_t words[4] = {cwB.x, cwB.y, cwB.z, cwB.w};
+    const float c = t_ok ? bs : 0.0f;
+    if (I8) {
+      const uint32_t words[8] = {cwB[0].x, cwB[0].y, cwB[0].z, cwB[0].w,
+                                 cwB[CW - 1].x, cwB[CW - 1].y, cwB[CW - 1].z, cwB[CW - 1].w};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t o[4];
-      lut_lookup8(lut, words[w], o);
-      sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
+      for (int w = 0; w < 4; ++w) {
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t cwd = words[2 * w + h];
+          o[2 * h] = pack_bf2(i8_value(cwd & 0xFFu) * c, i8_value((cwd >> 8) & 0xFFu) * c);
+          o[2 * h + 1] = pack_bf2(i8_value((cwd >> 16) & 0xFFu) * c, i8_value(cwd >> 24) * c);
+        }
+        sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    } else {
+      const BlockLUT lut = lut_for(c, cv);
+      const uint32_t words[4] = {cwB[0].x, cwB[0].y, cwB[0].z, cwB[0].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t o[4];
+        lut_lookup8(lut, words[w], o);
+        sts16(wdst(0, w), make_uint4(o[0], o[1], o[2], o[3]));
+      }
     }
   }
   load_codes(ks + 1 < nk ? ks + 1 : ks, cwA, qbA, sfA);
@@ -1808,10 +1846,15 @@ hipError_t launch_main(const MainArgs& a, hipStream_t stream) {
 
 template <bool BWD>
 hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
-  // Int8 weights: the generic kernel with 8-bit code loads (the 256 x 256
-  // kernels and their split plans take 4-bit codes only)
-  if (a.dq.code_type == CODE_INT8) return launch_main<256, 256, BWD, true>(a, stream);
-  switch (pick_tile(a.M, a.ncols, a.L)) {
+  // Int8 weights: the 8-wave 256 x 256 kernel with 8-bit code loads in both
+  // directions on that tile, else the generic kernel's 8-bit variant, which
+  // splits nothing.  A forward of at most kGemvMaxM tokens takes the generic
+  // kernel too: its workspace is sized for the 4-bit weight-streaming path,
+  // not for split tiles.
+  const bool i8 = a.dq.code_type == CODE_INT8;
+  const MainTile tk = pick_tile(a.M, a.ncols, a.L);
+  if (i8 && (tk != T256x256 || (!BWD && a.M <= kGemvMaxM))) return launch_main<256, 256, BWD, true>(a, stream);
+  switch (tk) {
     case T256x256: {
       const SplitPlan p = plan_256(a.M, a.ncols, a.L);
       a.full_tiles = p.full;
@@ -1822,7 +1865,12 @@ hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
       // forward: one wave per SIMD (128 x 128 wave tiles); backward: two
       // waves per SIMD (128 x 64), whose transpose-load fragment reads and
       // dequantisation gain more from a second wave to hide them
-      if (BWD) {
+      if (i8) {
+        if (a.dq.double_quant)
+          hipLaunchKernelGGL((main_v6_kernel<BWD, true, true>), grid1, dim3(V6_T), 0, stream, a);
+        else
+          hipLaunchKernelGGL((main_v6_kernel<BWD, false, true>), grid1, dim3(V6_T), 0, stream, a);
+      } else if (BWD) {
         if (a.dq.double_quant)
           hipLaunchKernelGGL((main_v6_kernel<true, true>), grid1, dim3(V6_T), 0, stream, a);
         else
