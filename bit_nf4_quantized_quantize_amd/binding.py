@@ -30,8 +30,8 @@ QLORA_DTYPE_BF16 = 1
 # qlora_code_type: the codebook of a quantised weight.  CODE_TYPES are the
 # 4-bit types; INT8 (one byte per weight) is QLORA_CODE_INT8.  Every entry
 # point takes every type; the linear layer runs Int8 weights on its 256 x 256
-# GEMM kernel, and Int8 forwards of 1-16 tokens on the generic tiles (the
-# weight-streaming kernel for few tokens takes 4-bit codes only).
+# GEMM kernel at every token count (the weight-streaming kernel for few
+# tokens takes 4-bit codes only).
 QLORA_CODE_NF4 = 0
 QLORA_CODE_FP4_E2M1 = 1
 QLORA_CODE_FP4_E3M0 = 2

@@ -129,7 +129,11 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int64_t r) {
   w.part = 0;
   w.xas = w.part + round_up((int64_t)w.splits * M * rp * 4, kAlign);
   w.gv = w.xas + round_up(M * rp * 2, kAlign);
-  const int64_t gv_bytes = w.gemv_splits > 0 ? (int64_t)w.gemv_splits * M * N * 4 : main_split_bytes(M, N, K);
+  // the small-token region also holds the split tiles of the 256 x 256
+  // kernel, which takes Int8 weights at any token count
+  const int64_t st_bytes = main_split_bytes(M, N, K);
+  const int64_t gm_bytes = w.gemv_splits > 0 ? (int64_t)w.gemv_splits * M * N * 4 : 0;
+  const int64_t gv_bytes = gm_bytes > st_bytes ? gm_bytes : st_bytes;
   w.total = w.gv + round_up(gv_bytes, kAlign);
   return w;
 }

@@ -1847,13 +1847,11 @@ hipError_t launch_main(const MainArgs& a, hipStream_t stream) {
 template <bool BWD>
 hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
   // Int8 weights: the 8-wave 256 x 256 kernel with 8-bit code loads in both
-  // directions on that tile, else the generic kernel's 8-bit variant, which
-  // splits nothing.  A forward of at most kGemvMaxM tokens takes the generic
-  // kernel too: its workspace is sized for the 4-bit weight-streaming path,
-  // not for split tiles.
+  // directions on that tile (few-token forwards included), else the generic
+  // kernel's 8-bit variant
   const bool i8 = a.dq.code_type == CODE_INT8;
   const MainTile tk = pick_tile(a.M, a.ncols, a.L);
-  if (i8 && (tk != T256x256 || (!BWD && a.M <= kGemvMaxM))) return launch_main<256, 256, BWD, true>(a, stream);
+  if (i8 && tk != T256x256) return launch_main<256, 256, BWD, true>(a, stream);
   switch (tk) {
     case T256x256: {
       const SplitPlan p = plan_256(a.M, a.ncols, a.L);

@@ -83,7 +83,8 @@ typedef enum {
  * weight, the two's complement of k, value k / 127 (256 entries; byte 0x80,
  * -128/127, is never produced by quantisation).  Every entry point accepts
  * INT8 weights; the linear layer runs them on its 256 x 256 GEMM kernel
- * (forwards of 1-16 tokens: the generic tiles).
+ * at every token count (the few-token weight-streaming kernel takes 4-bit
+ * codes only).
  * Values are fp32 (the ratios rounded to nearest); qlora_codebook() returns
  * them. */
 typedef enum {
@@ -256,8 +257,8 @@ int qlora_nf4_dequantize(const qlora_nf4_t* q, void* out, int32_t out_dtype, voi
  *   X        device bf16 [M, K]; M >= 0 (M = 0 enqueues nothing).
  *   W        host pointer to the descriptor of the frozen weight [N, K];
  *            K % 64 == 0 and N % 64 == 0; any code type (INT8 weights
- *            of 1-16 tokens run on the generic GEMM tiles, slower than the
- *            4-bit weight-streaming path).
+ *            of 1-16 tokens run on the 256 x 256 GEMM kernel with split
+ *            tiles, slower than the 4-bit weight-streaming path).
  *   A        device bf16 [K, r]  (QLoRA L1).
  *   B        device bf16 [r, N]  (QLoRA L2).
  *   r        LoRA rank, 1 <= r <= QLORA_MAX_RANK.

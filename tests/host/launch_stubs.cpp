@@ -76,8 +76,7 @@ hipError_t launch_fwd_main(const uint16_t*, int64_t M, int64_t K, const uint8_t*
   ++stub::calls;
   region(XAs, 2 * M * rp, "s*XA read");
   region(Y, 2 * M * N, "Y");
-  // Int8 forwards of at most kGemvMaxM tokens run on the generic tiles, which split nothing
-  region(split_ws, dq.code_type == CODE_INT8 && M <= kGemvMaxM ? 0 : main_split_bytes(M, N, K), "fwd split tiles");
+  region(split_ws, main_split_bytes(M, N, K), "fwd split tiles");
   return hipSuccess;
 }
 hipError_t launch_gemv(const uint16_t*, int64_t M, int64_t K, const uint8_t*, const DQParams&, int64_t N, float* part,
