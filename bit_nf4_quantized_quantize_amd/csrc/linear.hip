@@ -1386,7 +1386,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* __restrict__ d
 // MFMA-layout reads below (16 rows x 8 bytes per half wave) hit 64 distinct
 // banks.  The chunk's block constants travel with it (one row's four
 // blocks per thread of the first four waves, decoded to fp32 as they are
-// stored).  Three chunks are in
+// stored); with double quantisation and splits of at most G3_PREMAX
+// chunks their E4M3 bytes come from an LDS copy of the whole split's bytes,
+// loaded once at the start as contiguous runs of each row, instead of
+// three scattered loads per chunk.  Three chunks are in
 // flight in registers (a set's codes are reloaded as soon as they are in LDS,
 // its activations once they have been used), LDS is double buffered, and one
 // barrier per chunk orders the two.
@@ -1415,6 +1418,7 @@ constexpr int G3_CHUNK16 = G3_ROWS * 2 * G3_CB;  // 16-byte pieces per chunk (20
 constexpr int G3_LPT = G3_CHUNK16 / G3_T;        // piece loads per thread per chunk (4)
 constexpr int G3_D = 3;                          // chunks in flight in registers
 constexpr int G3_XA4 = 7;                        // an X A chunk's cost in code chunks, times 4
+constexpr int G3_PREMAX = 16;                    // longest split whose E4M3 bytes are preloaded
 static_assert(G3_T == 2 * G3_ROWS && G3_CB == 4, "threads 0 .. G3_ROWS - 1 take a row's 4 block constants");
 static_assert(G3_CB * kGemvMaxM * G3_ROWS * 4 <= 2 * G3_CHUNK16 * 16, "reduction buffer aliases the stages");
 
@@ -1522,7 +1526,25 @@ __global__ __launch_bounds__(512) void xa_chunks_kernel(const uint16_t* __restri
   xa_chunk_partial(X, M, K, A, r, rp, keep, blockIdx.x, xpart, la, lx);
 }
 
-template <bool DQ>
+// First chunk of reduction split y of row tile x (split_lo(S) = nchunks):
+// the splits whose workgroup also computes an X A chunk (the first nxc
+// workgroups, one chunk each when the grid has that many) are G3_XA4 / 4
+// chunks shorter, the others longer, so that every workgroup of the tile
+// streams for about as long.  T row tiles, S splits.
+__host__ __device__ inline int gemv_split_lo(int y, int64_t x, int64_t T, int S, int nchunks, int64_t nxc) {
+  const int nx = x < nxc ? (int)((int64_t)S < (nxc - x + T - 1) / T ? (int64_t)S : (nxc - x + T - 1) / T) : 0;
+  int x4 = T * S >= nxc ? G3_XA4 : 0;
+  if (4 * (int64_t)nchunks - 4 * (int64_t)S < (int64_t)x4 * (S - nx)) x4 = 0;  // every split keeps a chunk
+  return (int)((4 * (int64_t)y * nchunks + (int64_t)x4 * ((int64_t)y * nx - (int64_t)S * (y < nx ? y : nx))) /
+               (4 * (int64_t)S));
+}
+
+// PRE (double quantisation, whole-word constants, splits of at most
+// G3_PREMAX chunks): the E4M3 bytes of the workgroup's whole split are
+// loaded once at the start, as contiguous runs of each row, into LDS, and
+// the row's one or two second-level scales into registers; a chunk step
+// then reads its row's word from LDS instead of three scattered loads.
+template <bool DQ, bool PRE = false>
 __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
                                                        const uint8_t* __restrict__ codes, const DQParams dq,
                                                        int64_t N, int S, float* __restrict__ part,
@@ -1531,27 +1553,19 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   __shared__ uint32_t tab[256 * 64];
   __shared__ u32x4 stage[2][G3_CHUNK16];  // code chunks; the partial tiles at the end
   __shared__ float4 cst[2][G3_ROWS];  // block constants cst[buf][row][block]
+  __shared__ uint32_t qpre[PRE ? G3_PREMAX * G3_ROWS : 1];  // E4M3 words qpre[chunk - c_lo][row]
   static_assert(sizeof(stage) >= XA_LDS_A && sizeof(tab) >= XA_LDS_X, "the X A tiles fit in the stages and table");
+  static_assert(!PRE || DQ, "preloaded constants are E4M3 bytes");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* cv = kCodeValues[dq.code_type];
 
   const int64_t nbk = K >> 6, half_k = K >> 1;
   const int64_t n0 = (int64_t)blockIdx.x * G3_ROWS;
   const int nchunks = (int)((nbk + G3_CB - 1) / G3_CB);
-  // the reduction splits of this row tile: the splits whose workgroup also
-  // computes an X A chunk (the first nxc workgroups, one chunk each when the
-  // grid has that many) are G3_XA4 / 4 chunks shorter, the others longer,
-  // so that every workgroup of the tile streams for about as long
-  const int64_t nxc = (K + XA_CHUNK - 1) / XA_CHUNK, T = gridDim.x;
-  const int nx = (int64_t)blockIdx.x < nxc ? (int)min((int64_t)S, (nxc - blockIdx.x + T - 1) / T) : 0;
-  int x4 = T * S >= nxc ? G3_XA4 : 0;
-  if (4 * (int64_t)nchunks - 4 * (int64_t)S < (int64_t)x4 * (S - nx)) x4 = 0;  // every split keeps a chunk
-  auto split_lo = [&](int y) -> int {
-    return (int)((4 * (int64_t)y * nchunks + (int64_t)x4 * ((int64_t)y * nx - (int64_t)S * (y < nx ? y : nx))) /
-                 (4 * (int64_t)S));
-  };
-  const int c_lo = split_lo(blockIdx.y);
-  const int c_hi = split_lo(blockIdx.y + 1);  // c_hi > c_lo, split_lo(S) = nchunks
+  // the reduction split of this workgroup
+  const int64_t nxc = (K + XA_CHUNK - 1) / XA_CHUNK;
+  const int c_lo = gemv_split_lo(blockIdx.y, blockIdx.x, gridDim.x, S, nchunks, nxc);
+  const int c_hi = gemv_split_lo(blockIdx.y + 1, blockIdx.x, gridDim.x, S, nchunks, nxc);  // c_hi > c_lo
   const float mu = DQ ? *dq.offset : 0.0f;
 
   // code pieces: load u of thread tid fills LDS slot P = u * G3_T + tid, i.e.
@@ -1573,6 +1587,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   const int64_t cbase = (crow_ok ? n0 + tid : N - 1) * nbk;
   const bool cwhole = (nbk & 3) == 0 && ((uintptr_t)(DQ ? (const void*)dq.absmax_q : (const void*)dq.absmax) &
                                             (DQ ? 3 : 15)) == 0;  // uniform
+  float fpre[2] = {0.0f, 0.0f};  // PRE: second-level scales of the split's first and last block
   // activations: lane (t, g) of wave w, block w % 4 of the chunk
   const int t = lane & 15, g = lane >> 4, q = wave & 3, hrow = 128 * (wave >> 2);
   const uint16_t* xrow = X + (int64_t)(t < M ? t : M - 1) * K + 16 * g;
@@ -1590,7 +1605,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   auto issue_codes = [&](int kc, G3Set<DQ>& d) {
 #pragma unroll
     for (int u = 0; u < G3_LPT; ++u) d.c[u] = *reinterpret_cast<const u32x4*>(gsrc[u] + blk(kc, gblk[u]) * 32);
-    if (tid < G3_ROWS) {
+    if (!PRE && tid < G3_ROWS) {
       if constexpr (DQ) {
         if (cwhole) {
           d.q4 = *reinterpret_cast<const uint32_t*>(dq.absmax_q + cbase + blk(kc, 0));
@@ -1633,11 +1648,16 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
     for (int u = 0; u < G3_LPT; ++u) stage[sbuf][u * G3_T + tid] = d.c[u];
     if (tid < G3_ROWS) {
       float c[4];
+      const uint32_t qp = PRE ? qpre[(kc - c_lo) * G3_ROWS + tid] : 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool ok = crow_ok && (int64_t)G3_CB * kc + j < nbk;
         float v;
-        if constexpr (DQ) {
+        if constexpr (PRE) {
+          // the split's blocks lie in at most two groups of 256
+          const bool first = ((cbase + (int64_t)G3_CB * kc + j) >> 8) == ((cbase + (int64_t)G3_CB * c_lo) >> 8);
+          v = __fadd_rn(__fmul_rn(e4m3_decode((qp >> (8 * j)) & 0xFFu), first ? fpre[0] : fpre[1]), mu);
+        } else if constexpr (DQ) {
           const bool first = ((cbase + blk(kc, j)) >> 8) == ((cbase + blk(kc, 0)) >> 8);
           v = __fadd_rn(__fmul_rn(e4m3_decode((d.q4 >> (8 * j)) & 0xFFu), first ? d.f[0] : d.f[1]), mu);
         } else {
@@ -1682,12 +1702,39 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
   };
 
   G3Set<DQ> A, B, C;  // G3_D register sets in rotation
+  // PRE: the split's E4M3 words, loaded first (so that storing them waits
+  // for nothing else) as runs of consecutive chunks of each row, and the
+  // row's second-level scales of the split's first and last block
+  constexpr int QPL = G3_PREMAX * G3_ROWS / G3_T;  // preload words per thread
+  uint32_t qv[PRE ? QPL : 1];
+  if constexpr (PRE) {
+    const int nc = c_hi - c_lo;  // <= G3_PREMAX (the host checks)
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const int i = k * G3_T + tid, row = i / nc, c = i - row * nc;
+      const int64_t rr = n0 + row < N ? n0 + row : N - 1;
+      if (i < G3_ROWS * nc)
+        qv[k] = *reinterpret_cast<const uint32_t*>(dq.absmax_q + rr * nbk + (int64_t)G3_CB * (c_lo + c));
+    }
+    if (tid < G3_ROWS) {
+      fpre[0] = dq.scale2[(cbase + (int64_t)G3_CB * c_lo) >> 8];
+      fpre[1] = dq.scale2[(cbase + (int64_t)G3_CB * c_hi - 1) >> 8];
+    }
+  }
   issue_codes(c_lo, A);
   issue_x(c_lo, A);
   issue_codes(c_lo + 1, B);
   issue_x(c_lo + 1, B);
   issue_codes(c_lo + 2, C);
   issue_x(c_lo + 2, C);
+  if constexpr (PRE) {
+    const int nc = c_hi - c_lo;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const int i = k * G3_T + tid, row = i / nc, c = i - row * nc;
+      if (i < G3_ROWS * nc) qpre[c * G3_ROWS + row] = qv[k];
+    }
+  }
 
   // while the first chunks are in flight, the first workgroups each take
   // one reduction chunk of X A (more when the grid is smaller than the
@@ -1713,6 +1760,7 @@ __global__ __launch_bounds__(G3_T, 1) void gemv3_kernel(const uint16_t* __restri
       tv[i] = u32x4{v, v, v, v};
     }
   }
+  if constexpr (PRE) __syncthreads();  // the preloaded words are in LDS (the first step reads them)
 
   int kc = c_lo;
   for (; kc + G3_D <= c_hi; kc += G3_D) {
@@ -1982,7 +2030,19 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* c
   if (K % 64 || rp % 64 || rp > 256 || r > rp) return hipErrorInvalidValue;
   static_assert(G3_T == 512, "the X A chunks are computed by 512-thread workgroups");
   const dim3 grid(cdiv(N, G3_ROWS), (unsigned)splits);
-  if (dq.double_quant)
+  // the split lengths of this grid (they depend on the row tile through the
+  // X A chunks): preload the E4M3 bytes when every split fits G3_PREMAX
+  const int64_t nbk = K >> 6, T = grid.x, nxc = (K + XA_CHUNK - 1) / XA_CHUNK;
+  const int nchunks = (int)((nbk + G3_CB - 1) / G3_CB);
+  bool pre = dq.double_quant && nbk % G3_CB == 0 && ((uintptr_t)dq.absmax_q & 3) == 0;
+  for (int64_t x = 0; pre && x < T && x < nxc + 1; ++x)  // tiles x >= nxc split alike
+    for (int y = 0; pre && y < splits; ++y)
+      pre = gemv_split_lo(y + 1, x, T, splits, nchunks, nxc) - gemv_split_lo(y, x, T, splits, nchunks, nxc) <=
+            G3_PREMAX;
+  if (pre)
+    hipLaunchKernelGGL((gemv3_kernel<true, true>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits,
+                       part, A, (int)r, (int)rp, keep, xpart);
+  else if (dq.double_quant)
     hipLaunchKernelGGL((gemv3_kernel<true>), grid, dim3(G3_T), 0, stream, X, (int)M, K, codes, dq, N, splits, part,
                        A, (int)r, (int)rp, keep, xpart);
   else

@@ -18,7 +18,9 @@ tens of percent in that term through.  These tests isolate it:
     the forward and the backward both have split tails;
   * Int8 weights (reading G17) with dropout, at 1, 4 and 16 tokens against
     the 8192 x 22016 weight, and on a weight whose blocks hold all 255
-    levels, forward and backward bit for bit against the dequantiser.
+    levels, forward and backward bit for bit against the dequantiser;
+  * the few-token forward at both lengths of its reduction splits (the
+    E4M3 bytes preloaded per split, or loaded per chunk).
 """
 
 import sys
@@ -228,6 +230,38 @@ def test_int8_small_token_65b_weight(B):
         _close("dX[sample]", _np(dX)[:, kcols], dYn @ Wcols + s * T @ A[kcols].T)
         _close("dA", _np(dA), s * (Xn.T @ T))
         _close("dB", _np(dB), s * ((Xn @ A).T @ dYn))
+
+
+@pytest.mark.parametrize("N,K", [(8000, 22016), (16384, 22016)])
+def test_small_token_split_lengths(B, N, K):
+    """The few-token forward with NF4+DQ weights at the two lengths of its
+    reduction splits: 8000 x 22016 (splits of about 11 chunks, whose E4M3
+    bytes are loaded once per workgroup; 8000 rows leave a ragged last
+    256-row tile) and 16384 x 22016 (splits of about 21 chunks, more than
+    that preload holds, so the bytes are loaded chunk by chunk).  Y and XA at
+    1 and 16 tokens on sampled rows against the fp64 oracle."""
+    g = torch.Generator(device="cuda").manual_seed(N * 7 + K)
+    W = torch.randn(N, K, device="cuda", generator=g) * 0.02
+    r, s = 64, 0.25
+    A = (torch.randn(K, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    Bm = (torch.randn(r, N, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    qw = B.qlora_nf4_quantize(W)
+    ow = OracleWeight(_np(W))
+    del W
+    rng = np.random.default_rng(N + K)
+    ns = np.unique(np.concatenate([rng.integers(0, N, 192), [0, 255, 256, N - 257, N - 256, N - 1]]))
+    Wrows = ow.rows(ns).astype(np.float64)
+    An, Bn = _np(A).astype(np.float64), _np(Bm).astype(np.float64)
+    for M in (1, 16):
+        _log(f"small token split lengths N={N} K={K} M={M}")
+        X = (torch.randn(M, K, device="cuda", generator=g)).to(torch.bfloat16)
+        Y, XA = B.qlora_linear_fwd(X, qw, A, Bm, s)
+        torch.cuda.synchronize()
+        Xn = _np(X).astype(np.float64)
+        _close("XA", _np(XA), Xn @ An)
+        _close("Y[sample]", _np(Y)[:, ns], Xn @ Wrows.T + s * (Xn @ An) @ Bn[:, ns])
+    del qw, ow
+    torch.cuda.empty_cache()
 
 
 def _all_level_int8_weight(N=128, K=256):
