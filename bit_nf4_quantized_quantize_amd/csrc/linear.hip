@@ -1417,7 +1417,7 @@ constexpr int G3_RT = G3_ROWS * G3_CB / (16 * G3_WAVES);  // 16-row tiles per wa
 constexpr int G3_CHUNK16 = G3_ROWS * 2 * G3_CB;  // 16-byte pieces per chunk (2048)
 constexpr int G3_LPT = G3_CHUNK16 / G3_T;        // piece loads per thread per chunk (4)
 constexpr int G3_D = 3;                          // chunks in flight in registers
-constexpr int G3_XA4 = 7;                        // an X A chunk's cost in code chunks, times 4
+constexpr int G3_XA4 = 14;                       // an X A chunk's cost in code chunks, times 4 (measured)
 constexpr int G3_PREMAX = 16;                    // longest split whose E4M3 bytes are preloaded
 static_assert(G3_T == 2 * G3_ROWS && G3_CB == 4, "threads 0 .. G3_ROWS - 1 take a row's 4 block constants");
 static_assert(G3_CB * kGemvMaxM * G3_ROWS * 4 <= 2 * G3_CHUNK16 * 16, "reduction buffer aliases the stages");
