@@ -165,7 +165,7 @@ SplitPlan plan_256(int64_t M, int64_t ncols, int64_t L) {
   const int nkt = (int)(L >> 6);
   const int R = p.tiles % kCUs;
   int split = R > 0 ? kCUs / R : 1;
-  if (split > nkt / 2) split = nkt / 2;  // at least two k-steps per range
+  if (split > nkt / 4) split = nkt / 4;  // at least four k-steps per range (the forward's ranges start on multiples of four)
   if (split < 2) {
     p.full = p.tiles;
     p.split = 1;

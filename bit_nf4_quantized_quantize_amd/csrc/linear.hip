@@ -401,8 +401,15 @@ struct WordState {
   uint32_t e7, o7, me, mo, loE, hiE, loO, hiO;
 };
 
-template <bool BWD, bool DQ>
+// GW (forward, double quantisation, K / 64 a multiple of 4, aligned E4M3
+// bytes): a thread's four E4M3 bytes of k-steps 4g .. 4g+3 are one aligned
+// word, loaded once per four k-steps instead of one byte per k-step (each
+// load instruction touches 64 rows); the k-loop is unrolled by four so the
+// words rotate with fixed roles, and reduction ranges start on multiples of
+// four k-steps.
+template <bool BWD, bool DQ, bool GW = false>
 __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
+  static_assert(!GW || (!BWD && DQ), "grouped E4M3 words: forward, double quantisation");
   constexpr int BM = 256, BN = 256;
   constexpr int PRC = BN + kRcPad;
   constexpr int SA = BM * PK;
@@ -428,6 +435,10 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     lid = F + unit / a.split;
     ks = (int)((int64_t)sp * nkt / a.split);
     ke = (int)((int64_t)(sp + 1) * nkt / a.split);
+    if constexpr (GW) {  // ranges of whole four-step groups (nkt % 4 == 0, at least four steps each)
+      ks &= ~3;
+      ke &= ~3;
+    }
   }
   const bool last_range = ke == nkt;  // the range that also adds the adapter term
   const int64_t m0 = (int64_t)(lid / tn) * BM, c0 = (int64_t)(lid % tn) * BN;
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     c[1] = *reinterpret_cast<const uint4*>(src + 16);
     const int64_t blk = n * kblocks + (k >> 6);
     if (DQ) {
-      q = a.dq.absmax_q[blk];
+      if constexpr (!GW) q = a.dq.absmax_q[blk];
       f = a.dq.scale2[blk >> 8];
     } else {
       f = a.dq.absmax[blk];
@@ -585,12 +596,23 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
   };
 
   // ---- prologue: stage 0 filled; X(ks+1) and codes(ks+1) in flight
+  // GW: the E4M3 words of the thread's row, groups ks/4 and ks/4 + 1 first
+  uint32_t wcur = 0, wnxt = 0, wnew = 0;
+  const int lastg = (int)(kblocks >> 2) - 1;
+  auto ldw = [&](int g) -> uint32_t {
+    return *reinterpret_cast<const uint32_t*>(a.dq.absmax_q + t_n * kblocks + 4 * (int64_t)(g < lastg ? g : lastg));
+  };
+  if constexpr (GW) {
+    wcur = ldw(ks >> 2);
+    wnxt = ldw((ks >> 2) + 1);
+  }
   load_codes(ks, cwB, qbB, sfB);
 #pragma unroll
   for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks));
 #pragma unroll
   for (int i = 0; i < XCH; ++i) sts16(x_dst(i, 0), xr[i]);
   {
+    if constexpr (GW) qbB = (uint8_t)(wcur & 0xFFu);  // k-step ks = 4 (ks / 4)
     const float bs = DQ ? __fadd_rn(__fmul_rn(e4m3_decode(qbB), sfB), mu) : sfB;
     const BlockLUT lut = lut_for(t_ok ? bs : 0.0f, cv);
     const uint32_t words[8] = {cwB[0].x, cwB[0].y, cwB[0].z, cwB[0].w, cwB[1].x, cwB[1].y, cwB[1].z, cwB[1].w};
@@ -602,13 +624,31 @@ __global__ __launch_bounds__(V5_T, 1) void main_v5_kernel(const MainArgs a) {
     }
   }
   load_codes(ks + 1 < nk ? ks + 1 : ks, cwA, qbA, sfA);
+  // the codes and constants of ks + 1 go out before the activations, as in
+  // the loop, so that the loop's load counts are the same on entry as after
+  // a pass (the compiler waits for the stricter of the two)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < XCH; ++i) xr[i] = ldg16(x_src(i, ks + 1 < nk ? ks + 1 : ks));
   __syncthreads();
 
-  for (int kt = ks; kt < nk; kt += 2) {
-    step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
-    if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
+  if constexpr (GW) {
+    // four k-steps per pass: step kt decodes the block of k-step kt + 1
+    uint8_t qd = 0;  // the byte slot load_codes leaves alone
+    for (int kt = ks; kt < nk; kt += 4) {
+      wnew = ldw((kt >> 2) + 2);
+      step(kt, 0, cwA, (uint8_t)(wcur >> 8), sfA, cwB, qd, sfB);
+      step(kt + 1, 1, cwB, (uint8_t)(wcur >> 16), sfB, cwA, qd, sfA);
+      step(kt + 2, 0, cwA, (uint8_t)(wcur >> 24), sfA, cwB, qd, sfB);
+      step(kt + 3, 1, cwB, (uint8_t)wnxt, sfB, cwA, qd, sfA);
+      wcur = wnxt;
+      wnxt = wnew;
+    }
+  } else {
+    for (int kt = ks; kt < nk; kt += 2) {
+      step(kt, 0, cwA, qbA, sfA, cwB, qbB, sfB);
+      if (kt + 1 < nk) step(kt + 1, 1, cwB, qbB, sfB, cwA, qbA, sfA);
+    }
   }
 
   // ---- adapter term over bf16 operands (stage 0 is free)
@@ -1922,7 +1962,10 @@ hipError_t launch_main_any(MainArgs a, float* split_ws, hipStream_t stream) {
         else
           hipLaunchKernelGGL((main_v6_kernel<true, false>), grid1, dim3(V6_T), 0, stream, a);
       } else {
-        if (a.dq.double_quant)
+        const bool gw = a.dq.double_quant && (a.Kw >> 6) % 4 == 0 && ((uintptr_t)a.dq.absmax_q & 3) == 0;
+        if (gw)
+          hipLaunchKernelGGL((main_v5_kernel<false, true, true>), grid1, dim3(V5_T), 0, stream, a);
+        else if (a.dq.double_quant)
           hipLaunchKernelGGL((main_v5_kernel<false, true>), grid1, dim3(V5_T), 0, stream, a);
         else
           hipLaunchKernelGGL((main_v5_kernel<false, false>), grid1, dim3(V5_T), 0, stream, a);
